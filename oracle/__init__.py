@@ -1,0 +1,202 @@
+"""CPU oracle for the speculative-sampling verify step.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+CPU-baseline leg of the benchmark may import this module.  The product path
+(the HIP library and its binding) never imports, links or calls it, and it
+imports nothing from the product path.
+
+The arithmetic lives in ``sv_oracle.c`` (plain C, double precision,
+sequential); this module only builds it with gcc and marshals numpy arrays
+through ctypes.  See ``sv_oracle.c`` for the method and its sources.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sv_oracle.c")
+_LIB = os.path.join(_HERE, "libsvoracle.so")
+
+F32, BF16 = 0, 1
+MODE_PROB, MODE_ONEHOT = 0, 1
+FLAG_BAD_DRAFT_ID, FLAG_BAD_NUM_DRAFTS, FLAG_ZERO_RESIDUAL = 1, 2, 4
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle's C source into a shared library with gcc
+    (-O2, no fast-math)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-std=gnu11", "-O2", "-fPIC", "-shared", "-Wall",
+             "-Werror", src, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
+def open_library(path: str):
+    """Load a compiled oracle library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, u64, u32, dbl, flt = (ctypes.c_int, ctypes.c_uint64,
+                               ctypes.c_uint32, ctypes.c_double,
+                               ctypes.c_float)
+    lib.svo_philox4x64_10.argtypes = [P, P, P]
+    lib.svo_philox4x64_10.restype = None
+    lib.svo_uniforms.argtypes = [u64, u64, u64, u64, P, P]
+    lib.svo_uniforms.restype = None
+    lib.svo_is_sampling.argtypes = [flt]
+    lib.svo_is_sampling.restype = i32
+    lib.svo_softmax.argtypes = [P, i32, dbl, P]
+    lib.svo_softmax.restype = None
+    lib.svo_argmax.argtypes = [P, i32]
+    lib.svo_argmax.restype = i32
+    lib.svo_accept_ratio.argtypes = [dbl, dbl]
+    lib.svo_accept_ratio.restype = dbl
+    lib.svo_residual.argtypes = [P, P, i32, i32, i32, P]
+    lib.svo_residual.restype = None
+    lib.svo_draw.argtypes = [P, i32, dbl, P]
+    lib.svo_draw.restype = i32
+    common = [i32, i32, i32, i32, P, i32, P, i32, P, P, P, P]
+    lib.svo_verify_with_uniforms.argtypes = common + [P, P] + [P] * 6
+    lib.svo_verify_with_uniforms.restype = u32
+    lib.svo_verify.argtypes = common + [u64, u64] + [P] * 6
+    lib.svo_verify.restype = u32
+    return lib
+
+
+_lib = None
+_override = None  # a library handle installed by use_library()
+
+
+def use_library(lib):
+    """Route this module's functions through another compiled oracle (the
+    pin tests use this to check that planted mistakes are caught).  Pass
+    None to restore the default."""
+    global _override
+    _override = lib
+
+
+def _load():
+    global _lib
+    if _override is not None:
+        return _override
+    if _lib is None:
+        if not os.path.exists(_LIB) or (
+                os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+            build()
+        _lib = open_library(_LIB)
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def philox4x64_10(counter, key):
+    """Philox4x64-10 block for a 4-word counter and a 2-word key."""
+    c = np.ascontiguousarray(counter, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.zeros(4, dtype=np.uint64)
+    _load().svo_philox4x64_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def uniforms(seed, offset, b, j):
+    """(u_acc, u_rec) of request b at position j."""
+    ua, ur = ctypes.c_double(), ctypes.c_double()
+    _load().svo_uniforms(seed, offset, b, j, ctypes.byref(ua), ctypes.byref(ur))
+    return ua.value, ur.value
+
+
+def is_sampling(T: float) -> bool:
+    return bool(_load().svo_is_sampling(float(T)))
+
+
+def softmax(logits, T):
+    l = np.ascontiguousarray(logits, dtype=np.float64)
+    p = np.empty_like(l)
+    _load().svo_softmax(_ptr(l), l.size, float(T), _ptr(p))
+    return p
+
+
+def argmax(v):
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    return int(_load().svo_argmax(_ptr(v), v.size))
+
+
+def accept_ratio(px, qx):
+    return float(_load().svo_accept_ratio(float(px), float(qx)))
+
+
+def residual(p, q, mode, x):
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    q = np.ascontiguousarray(q if q is not None else p, dtype=np.float64)
+    r = np.empty_like(p)
+    _load().svo_residual(_ptr(p), _ptr(q), int(mode), int(x), p.size, _ptr(r))
+    return r
+
+
+def draw(r, u):
+    """(token, margin) of the inverse-CDF draw from unnormalized law r."""
+    r = np.ascontiguousarray(r, dtype=np.float64)
+    m = ctypes.c_double()
+    y = _load().svo_draw(_ptr(r), r.size, float(u), ctypes.byref(m))
+    return int(y), m.value
+
+
+def _dtype_code(a):
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:  # raw bf16 bits
+        return BF16
+    raise TypeError("oracle inputs are float32 or raw bf16 bits (uint16)")
+
+
+def verify(target, draft, draft_ids, num_drafts, temperatures, *,
+           draft_mode=None, draft_is_probs=False, seed=0, offset=0,
+           u_acc=None, u_rec=None):
+    """Run the oracle on host arrays.
+
+    target: [B, K+1, V] float32, or uint16 holding bf16 bits.
+    draft:  [B, K, V] (same convention) or None for all one-hot.
+    Uniforms come from Philox(seed, offset) unless u_acc/u_rec ([B, K+1])
+    are given.  Returns a dict with tokens, num_accepted, p, q, margin_acc,
+    margin_rec and flags.
+    """
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    if draft is not None:
+        draft = np.ascontiguousarray(draft)
+        assert draft.shape == (B, K, V)
+    ids = np.ascontiguousarray(draft_ids, dtype=np.int32).reshape(B, K)
+    nd = np.ascontiguousarray(num_drafts, dtype=np.int32).reshape(B)
+    temps = np.ascontiguousarray(temperatures, dtype=np.float32).reshape(B)
+    mode = None if draft_mode is None else np.ascontiguousarray(
+        draft_mode, dtype=np.uint8).reshape(B)
+    tokens = np.empty((B, K + 1), dtype=np.int32)
+    nacc = np.empty(B, dtype=np.int32)
+    p = np.empty((B, K), dtype=np.float64)
+    q = np.empty((B, K), dtype=np.float64)
+    macc = np.empty((B, K), dtype=np.float64)
+    mrec = np.empty(B, dtype=np.float64)
+    lib = _load()
+    head = [B, K, V, _dtype_code(target), _ptr(target),
+            _dtype_code(draft) if draft is not None else F32, _ptr(draft),
+            int(bool(draft_is_probs)), _ptr(mode), _ptr(ids), _ptr(nd),
+            _ptr(temps)]
+    tail = [_ptr(tokens), _ptr(nacc), _ptr(p), _ptr(q), _ptr(macc),
+            _ptr(mrec)]
+    if u_acc is not None or u_rec is not None:
+        ua = np.ascontiguousarray(u_acc, dtype=np.float64).reshape(B, K + 1)
+        ur = np.ascontiguousarray(u_rec, dtype=np.float64).reshape(B, K + 1)
+        flags = lib.svo_verify_with_uniforms(*head, _ptr(ua), _ptr(ur), *tail)
+    else:
+        flags = lib.svo_verify(*head, int(seed), int(offset), *tail)
+    return dict(tokens=tokens, num_accepted=nacc, p=p, q=q, margin_acc=macc,
+                margin_rec=mrec, flags=int(flags))

@@ -1,0 +1,388 @@
+/*
+ * sv_oracle.c -- plain, slow, sequential CPU oracle for the speculative-
+ * sampling verify step.  TEST INFRASTRUCTURE ONLY: it is linked or called by
+ * the tests, by the package's smoke check and by the CPU-baseline leg of the
+ * benchmark, never by the product path.  It shares no code, header, table or
+ * constant with the HIP library.
+ *
+ * Everything is double precision and sequential, in the order the pages state
+ * the algorithm.  Sources (page title, section):
+ *
+ *   [P1] "深入推测解码：从概念到实现" (Exploring Speculative Decoding: From
+ *        Concept to Implementation), section "保证原始分布": sample x from the
+ *        draft q, accept with probability min(1, p(x)/q(x)) (case a p>=q
+ *        accept, case b p<q accept with p/q), on rejection resample from
+ *        max(0, p - q); worked example q=0.4, p=0.2 -> accept half the time.
+ *   [P2] "RTP-LLM Speculative Engine 深度解析", section "拒绝采样算法"
+ *        (SpeculativeSampler::stochasticSample): per proposed position compare
+ *        a Uniform(0,1) draw with p_score/p_draft, on rejection sample from
+ *        normalize(max(0, p_score - p_draft)) and stop.
+ *   [P3] "投机采样" (razer666.cn), section "投机解码算法", steps 3-5: the
+ *        accepted count n, the adjusted distribution norm(max(0, p_{n+1} -
+ *        q_{n+1})), the extra token from p_{gamma+1} when every guess passes,
+ *        output length in [1, gamma+1]; section "验证阶段的策略 / 精确匹配":
+ *        greedy exact match against the max-probability token.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *   - p = softmax(l / T) for target logits, and the same T for draft logits;
+ *   - T that is not a positive, normal, finite float selects greedy: accept
+ *     iff the draft's logit equals the row maximum (ties accepted), the
+ *     emitted token is the lowest index attaining the maximum, no uniforms;
+ *   - acceptance is the strict test u < ratio with u in [0,1);
+ *   - q(x) = 0 gives ratio +inf when p(x) > 0, else 0;
+ *   - one-hot (n-gram) drafts: ratio = p(x), residual = p with p(x) zeroed;
+ *   - a draft id outside [0, V) is never accepted and zeroes nothing;
+ *   - inverse CDF: smallest i with C_i > u * S, C_i the running sum;
+ *     if none, the largest i with r_i > 0; if S = 0, draw from p instead;
+ *   - uniforms from Philox4x64-10 with key (seed, 0) and counter
+ *     (offset, b, j, 0); word 0 -> acceptance uniform, word 1 -> draw
+ *     uniform; u = (w >> 40) * 2^-24.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define SVO_F32 0
+#define SVO_BF16 1
+
+#define SVO_MODE_PROB 0
+#define SVO_MODE_ONEHOT 1
+
+#define SVO_FLAG_BAD_DRAFT_ID 1u
+#define SVO_FLAG_BAD_NUM_DRAFTS 2u
+#define SVO_FLAG_ZERO_RESIDUAL 4u
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x64-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As   */
+/* Easy as 1, 2, 3" (SC'11).  Ten rounds; each round multiplies counter      */
+/* words 0 and 2 by the two round multipliers, mixes the high halves with    */
+/* the other words and the key, and the key is bumped by the two Weyl        */
+/* constants between rounds.                                                 */
+/* ------------------------------------------------------------------------ */
+static void mul_hilo64(uint64_t a, uint64_t b, uint64_t *hi, uint64_t *lo) {
+  unsigned __int128 prod = (unsigned __int128)a * (unsigned __int128)b;
+  *hi = (uint64_t)(prod >> 64);
+  *lo = (uint64_t)prod;
+}
+
+void svo_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2],
+                       uint64_t out[4]) {
+  const uint64_t mult0 = 0xD2E7470EE14C6C93ULL, mult1 = 0xCA5A826395121157ULL;
+  const uint64_t weyl0 = 0x9E3779B97F4A7C15ULL, weyl1 = 0xBB67AE8584CAA73BULL;
+  uint64_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint64_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    uint64_t hi0, lo0, hi1, lo1;
+    mul_hilo64(mult0, c0, &hi0, &lo0);
+    mul_hilo64(mult1, c2, &hi1, &lo1);
+    uint64_t n0 = hi1 ^ c1 ^ k0;
+    uint64_t n1 = lo1;
+    uint64_t n2 = hi0 ^ c3 ^ k1;
+    uint64_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    k0 += weyl0;
+    k1 += weyl1;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The two uniforms of request b at position j (see the header comment). */
+void svo_uniforms(uint64_t seed, uint64_t offset, uint64_t b, uint64_t j,
+                  double *u_acc, double *u_rec) {
+  uint64_t ctr[4] = {offset, b, j, 0};
+  uint64_t key[2] = {seed, 0};
+  uint64_t w[4];
+  svo_philox4x64_10(ctr, key, w);
+  *u_acc = (double)(w[0] >> 40) * 0x1p-24;
+  *u_rec = (double)(w[1] >> 40) * 0x1p-24;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Element access: bf16 is the top half of an IEEE float.                    */
+/* ------------------------------------------------------------------------ */
+static double load_elem(const void *base, int dtype, size_t idx) {
+  if (dtype == SVO_BF16) {
+    uint16_t bits = ((const uint16_t *)base)[idx];
+    uint32_t wide = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &wide, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float *)base)[idx];
+}
+
+static void load_row(const void *base, int dtype, size_t row, int V,
+                     double *dst) {
+  for (int i = 0; i < V; ++i) dst[i] = load_elem(base, dtype, row * (size_t)V + i);
+}
+
+/* Sampling is selected by a positive, normal, finite temperature. */
+int svo_is_sampling(float T) { return isnormal(T) && T > 0.0f; }
+
+/* Neumaier-compensated sequential sum. */
+static double sum_compensated(const double *v, int n) {
+  double s = 0.0, c = 0.0;
+  for (int i = 0; i < n; ++i) {
+    double t = s + v[i];
+    if (fabs(s) >= fabs(v[i]))
+      c += (s - t) + v[i];
+    else
+      c += (v[i] - t) + s;
+    s = t;
+  }
+  return s + c;
+}
+
+/* p_i = exp((l_i - m) / T) / sum_k exp((l_k - m) / T), m = max_i l_i. */
+void svo_softmax(const double *logits, int V, double T, double *p) {
+  double m = -INFINITY;
+  for (int i = 0; i < V; ++i)
+    if (logits[i] > m) m = logits[i];
+  for (int i = 0; i < V; ++i) p[i] = exp((logits[i] - m) / T);
+  double Z = sum_compensated(p, V);
+  for (int i = 0; i < V; ++i) p[i] /= Z;
+}
+
+/* Lowest index attaining the maximum. */
+int svo_argmax(const double *v, int V) {
+  int best = 0;
+  for (int i = 1; i < V; ++i)
+    if (v[i] > v[best]) best = i;
+  return best;
+}
+
+/* Acceptance ratio p(x)/q(x) with q(x) = 0 read as +inf (p(x) > 0) or 0. */
+double svo_accept_ratio(double px, double qx) {
+  if (qx > 0.0) return px / qx;
+  return px > 0.0 ? INFINITY : 0.0;
+}
+
+/* Residual law after a rejection of draft x (unnormalized):
+ *   probabilistic draft: r_i = max(0, p_i - q_i)   [P1 step 4, P2, P3 step 4]
+ *   one-hot draft:       r_i = p_i, r_x = 0        (q is the point mass at x)
+ * x outside [0, V) zeroes nothing. */
+void svo_residual(const double *p, const double *q, int mode, int x, int V,
+                  double *r) {
+  if (mode == SVO_MODE_PROB) {
+    for (int i = 0; i < V; ++i) {
+      double d = p[i] - q[i];
+      r[i] = d > 0.0 ? d : 0.0;
+    }
+  } else {
+    for (int i = 0; i < V; ++i) r[i] = p[i];
+    if (x >= 0 && x < V) r[x] = 0.0;
+  }
+}
+
+/* Inverse-CDF draw from the unnormalized law r with uniform u in [0, 1).
+ * Returns the token, or -1 when S = sum r is not positive.  *margin is the
+ * distance of u*S to the nearer CDF boundary of the chosen token, over S. */
+int svo_draw(const double *r, int V, double u, double *margin) {
+  double S = sum_compensated(r, V);
+  if (!(S > 0.0)) {
+    *margin = 0.0;
+    return -1;
+  }
+  double theta = u * S;
+  double below = 0.0, C = 0.0;
+  int y = -1;
+  for (int i = 0; i < V; ++i) {
+    below = C;
+    C += r[i];
+    if (C > theta) {
+      y = i;
+      break;
+    }
+  }
+  if (y < 0) { /* rounding left theta past the last boundary */
+    for (int i = V - 1; i >= 0; --i)
+      if (r[i] > 0.0) { y = i; break; }
+    *margin = 0.0;
+    return y;
+  }
+  double lo = theta - below, hi = C - theta;
+  *margin = (lo < hi ? lo : hi) / S;
+  return y;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The verify step, driven by explicit uniforms.                              */
+/*                                                                          */
+/*   target      [B][K+1][V] logits, target_dtype                            */
+/*   draft       [B][K][V] draft logits (draft_is_probs = 0) or normalized   */
+/*               probabilities (draft_is_probs = 1); NULL = all one-hot      */
+/*   draft_mode  [B] 0 = probabilistic, 1 = one-hot; NULL = all probabilistic*/
+/*   draft_ids   [B][K]; num_drafts [B]; temperatures [B]                    */
+/*   u_acc,u_rec [B][K+1]                                                     */
+/*   out_tokens  [B][K+1]: accepted drafts, the emitted token, then -1       */
+/*   out_num_accepted [B]                                                     */
+/*   out_p,out_q [B][K] or NULL: p_j(x_j), q_j(x_j) for every j < n_b of a   */
+/*               sampling request (q = 1 for one-hot), NaN elsewhere         */
+/*   out_margin_acc [B][K] or NULL: |u - ratio| of each evaluated sampling   */
+/*               decision, +inf for greedy decisions, NaN if not evaluated   */
+/*   out_margin_rec [B] or NULL: draw margin (+inf for greedy)               */
+/* Returns the OR of the SVO_FLAG_* conditions met.                          */
+/* ------------------------------------------------------------------------ */
+uint32_t svo_verify_with_uniforms(
+    int B, int K, int V, int target_dtype, const void *target, int draft_dtype,
+    const void *draft, int draft_is_probs, const uint8_t *draft_mode,
+    const int32_t *draft_ids, const int32_t *num_drafts,
+    const float *temperatures, const double *u_acc, const double *u_rec,
+    int32_t *out_tokens, int32_t *out_num_accepted, double *out_p,
+    double *out_q, double *out_margin_acc, double *out_margin_rec) {
+  uint32_t flags = 0;
+  double *tl = malloc(sizeof(double) * (size_t)V); /* target logits row */
+  double *dl = malloc(sizeof(double) * (size_t)V); /* draft row */
+  double *p = malloc(sizeof(double) * (size_t)V);
+  double *q = malloc(sizeof(double) * (size_t)V);
+  double *r = malloc(sizeof(double) * (size_t)V);
+
+  for (int b = 0; b < B; ++b) {
+    int n = num_drafts[b];
+    if (n < 0 || n > K) {
+      flags |= SVO_FLAG_BAD_NUM_DRAFTS;
+      n = n < 0 ? 0 : K;
+    }
+    const float T = temperatures[b];
+    const int sampling = svo_is_sampling(T);
+    int mode = SVO_MODE_PROB;
+    if (draft == NULL || (draft_mode != NULL && draft_mode[b] != 0))
+      mode = SVO_MODE_ONEHOT;
+    const size_t trow0 = (size_t)b * (K + 1); /* target row index of j = 0 */
+    const size_t drow0 = (size_t)b * K;
+
+    for (int j = 0; j < K; ++j) {
+      if (out_p) out_p[(size_t)b * K + j] = NAN;
+      if (out_q) out_q[(size_t)b * K + j] = NAN;
+      if (out_margin_acc) out_margin_acc[(size_t)b * K + j] = NAN;
+    }
+
+    /* Sequential decisions, stopping at the first rejection. */
+    int n_acc = 0, rejected = 0;
+    for (int j = 0; j < n; ++j) {
+      const int x = draft_ids[(size_t)b * K + j];
+      const int valid = x >= 0 && x < V;
+      if (!valid) flags |= SVO_FLAG_BAD_DRAFT_ID;
+      load_row(target, target_dtype, trow0 + j, V, tl);
+      int accept;
+      if (!sampling) {
+        double m = tl[svo_argmax(tl, V)];
+        accept = valid && tl[x] == m;
+        if (out_margin_acc) out_margin_acc[(size_t)b * K + j] = INFINITY;
+      } else {
+        svo_softmax(tl, V, (double)T, p);
+        double px = valid ? p[x] : 0.0, qx;
+        if (mode == SVO_MODE_PROB) {
+          load_row(draft, draft_dtype, drow0 + j, V, dl);
+          if (draft_is_probs)
+            memcpy(q, dl, sizeof(double) * (size_t)V);
+          else
+            svo_softmax(dl, V, (double)T, q);
+          qx = valid ? q[x] : 0.0;
+        } else {
+          qx = 1.0;
+        }
+        double ratio = valid ? svo_accept_ratio(px, qx) : 0.0;
+        double u = u_acc[(size_t)b * (K + 1) + j];
+        accept = u < ratio;
+        if (out_margin_acc)
+          out_margin_acc[(size_t)b * K + j] = fabs(u - ratio);
+      }
+      if (!accept) {
+        rejected = 1;
+        break;
+      }
+      n_acc++;
+    }
+
+    /* The emitted token: correction at the rejected position, else bonus. */
+    const int jemit = n_acc; /* == rejected position, or n when all passed */
+    int y;
+    double margin_rec = INFINITY;
+    load_row(target, target_dtype, trow0 + jemit, V, tl);
+    if (!sampling) {
+      y = svo_argmax(tl, V);
+    } else {
+      svo_softmax(tl, V, (double)T, p);
+      if (rejected) {
+        const int x = draft_ids[(size_t)b * K + jemit];
+        if (mode == SVO_MODE_PROB) {
+          load_row(draft, draft_dtype, drow0 + jemit, V, dl);
+          if (draft_is_probs)
+            memcpy(q, dl, sizeof(double) * (size_t)V);
+          else
+            svo_softmax(dl, V, (double)T, q);
+        }
+        svo_residual(p, q, mode, x, V, r);
+      } else {
+        memcpy(r, p, sizeof(double) * (size_t)V);
+      }
+      double u = u_rec[(size_t)b * (K + 1) + jemit];
+      y = svo_draw(r, V, u, &margin_rec);
+      if (y < 0) { /* no residual mass: draw from p itself */
+        flags |= SVO_FLAG_ZERO_RESIDUAL;
+        y = svo_draw(p, V, u, &margin_rec);
+        margin_rec = 0.0;
+      }
+    }
+
+    for (int j = 0; j < K + 1; ++j) {
+      int32_t tok = -1;
+      if (j < n_acc) tok = draft_ids[(size_t)b * K + j];
+      else if (j == n_acc) tok = y;
+      out_tokens[(size_t)b * (K + 1) + j] = tok;
+    }
+    out_num_accepted[b] = n_acc;
+    if (out_margin_rec) out_margin_rec[b] = margin_rec;
+
+    /* Diagnostics: p_j(x_j) and q_j(x_j) for every drafted position. */
+    if (sampling && (out_p || out_q)) {
+      for (int j = 0; j < n; ++j) {
+        const int x = draft_ids[(size_t)b * K + j];
+        if (x < 0 || x >= V) continue;
+        load_row(target, target_dtype, trow0 + j, V, tl);
+        svo_softmax(tl, V, (double)T, p);
+        double qx = 1.0;
+        if (mode == SVO_MODE_PROB) {
+          load_row(draft, draft_dtype, drow0 + j, V, dl);
+          if (draft_is_probs)
+            qx = dl[x];
+          else {
+            svo_softmax(dl, V, (double)T, q);
+            qx = q[x];
+          }
+        }
+        if (out_p) out_p[(size_t)b * K + j] = p[x];
+        if (out_q) out_q[(size_t)b * K + j] = qx;
+      }
+    }
+  }
+  free(tl); free(dl); free(p); free(q); free(r);
+  return flags;
+}
+
+/* The verify step with uniforms from the Philox stream (seed, offset). */
+uint32_t svo_verify(int B, int K, int V, int target_dtype, const void *target,
+                    int draft_dtype, const void *draft, int draft_is_probs,
+                    const uint8_t *draft_mode, const int32_t *draft_ids,
+                    const int32_t *num_drafts, const float *temperatures,
+                    uint64_t seed, uint64_t offset, int32_t *out_tokens,
+                    int32_t *out_num_accepted, double *out_p, double *out_q,
+                    double *out_margin_acc, double *out_margin_rec) {
+  size_t n = (size_t)(B > 0 ? B : 1) * (K + 1);
+  double *ua = malloc(sizeof(double) * n), *ur = malloc(sizeof(double) * n);
+  for (int b = 0; b < B; ++b)
+    for (int j = 0; j <= K; ++j)
+      svo_uniforms(seed, offset, (uint64_t)b, (uint64_t)j,
+                   &ua[(size_t)b * (K + 1) + j], &ur[(size_t)b * (K + 1) + j]);
+  uint32_t flags = svo_verify_with_uniforms(
+      B, K, V, target_dtype, target, draft_dtype, draft, draft_is_probs,
+      draft_mode, draft_ids, num_drafts, temperatures, ua, ur, out_tokens,
+      out_num_accepted, out_p, out_q, out_margin_acc, out_margin_rec);
+  free(ua);
+  free(ur);
+  return flags;
+}

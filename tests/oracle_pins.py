@@ -1,0 +1,380 @@
+"""Pins for the CPU oracle: checks against facts the pages and the mathematics
+fix, written so that they can also be run against a deliberately broken copy
+of the oracle (see test_oracle_pins.py::test_planted_mistakes_are_caught).
+
+Every check raises AssertionError on failure.  None of them re-types the
+oracle's own formulas: they compare with the pages' worked examples, with
+numpy / scipy routines the oracle does not use, with exact enumeration of the
+output law, with brute force on tiny inputs and with statistical tests.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import scipy.special
+import scipy.stats
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# Philox4x64-10 against numpy's independent implementation
+# --------------------------------------------------------------------------
+def _numpy_block(counter, key):
+    """numpy's Philox advances its 256-bit counter before producing a block,
+    so the block of counter c is the first output of a generator started at
+    c - 1."""
+    c = sum(int(w) << (64 * i) for i, w in enumerate(counter))
+    c = (c - 1) % (1 << 256)
+    words = [(c >> (64 * i)) & ((1 << 64) - 1) for i in range(4)]
+    g = np.random.Philox(counter=np.array(words, dtype=np.uint64),
+                         key=np.array([int(k) for k in key], dtype=np.uint64))
+    return g.random_raw(4)
+
+
+def check_philox_known_answers(n=4000, seed=1234):
+    rng = np.random.default_rng(seed)
+    counters = [[0, 0, 0, 0], [(1 << 64) - 1, 0, 0, 0],
+                [(1 << 64) - 1, (1 << 64) - 1, 7, 0], [5, 6, 7, 8]]
+    for _ in range(n):
+        counters.append([int(x) for x in rng.integers(0, 1 << 63, 4, dtype=np.uint64)])
+    for i, c in enumerate(counters):
+        key = [int(rng.integers(0, 1 << 63)), 0] if i % 2 else [i, i * 3]
+        ours = oracle.philox4x64_10(c, key)
+        ref = _numpy_block(c, key)
+        assert np.array_equal(ours, ref), (c, key, ours, ref)
+
+
+def check_uniform_mapping(n=2000, seed=99):
+    """u_acc / u_rec are words 0 / 1 of the block at counter (offset, b, j, 0)
+    with key (seed, 0), mapped as (w >> 40) * 2^-24."""
+    rng = np.random.default_rng(seed)
+    for _ in range(n):
+        s, o = (int(x) for x in rng.integers(0, 1 << 62, 2, dtype=np.uint64))
+        b, j = int(rng.integers(0, 4096)), int(rng.integers(0, 8))
+        w = _numpy_block([o, b, j, 0], [s, 0])
+        ua, ur = oracle.uniforms(s, o, b, j)
+        assert ua == (int(w[0]) >> 40) / 2.0 ** 24
+        assert ur == (int(w[1]) >> 40) / 2.0 ** 24
+
+
+# --------------------------------------------------------------------------
+# The pages' acceptance example: q(x) = 0.4, p(x) = 0.2 -> accept half the time
+# --------------------------------------------------------------------------
+def _accept_example_inputs(B):
+    ex = _golden("accept_worked_example.json")
+    p, q = ex["p_x"], ex["q_x"]
+    target = np.empty((B, 2, 2), np.float32)
+    target[:, 0] = [np.log(p), np.log(1 - p)]   # p_0 = (0.2, 0.8)
+    target[:, 1] = [np.log(0.3), np.log(0.7)]   # bonus row p_1 = (0.3, 0.7)
+    draft = np.empty((B, 1, 2), np.float32)
+    draft[:, 0] = [q, 1 - q]                    # normalized q_0 = (0.4, 0.6)
+    return ex, target, draft
+
+
+def check_accept_example_grid(chunk=1 << 21):
+    """Over every u on the 2^24 grid, exactly half (up to the rounding of
+    ln / exp, i.e. +-1 grid point) of the decisions accept."""
+    ex, target, draft = _accept_example_inputs(chunk)
+    accepted = 0
+    for start in range(0, 1 << 24, chunk):
+        ua = np.zeros((chunk, 2))
+        ua[:, 0] = (start + np.arange(chunk)) / 2.0 ** 24
+        r = oracle.verify(target, draft, np.zeros((chunk, 1)), np.ones(chunk),
+                          np.ones(chunk), draft_is_probs=True, u_acc=ua,
+                          u_rec=np.full((chunk, 2), 0.5))
+        accepted += int(r["num_accepted"].sum())
+        # a rejected x = 0 is replaced by a draw from max(0, p - q) = (0, 0.4)
+        rej = r["num_accepted"] == 0
+        assert np.all(r["tokens"][rej, 0] == 1)
+    expect = ex["accept_probability"] * 2 ** 24
+    assert abs(accepted - expect) <= 1, (accepted, expect)
+
+
+def check_accept_example_philox(B=1 << 20):
+    """With Philox uniforms (seed 0, request index b) the acceptance rate is
+    0.5 within 3 sigma; rejections always emit token 1; after an acceptance
+    the bonus token follows p_1 = (0.3, 0.7)."""
+    ex, target, draft = _accept_example_inputs(B)
+    r = oracle.verify(target, draft, np.zeros((B, 1)), np.ones(B), np.ones(B),
+                      draft_is_probs=True, seed=0, offset=0)
+    acc = r["num_accepted"] == 1
+    rate = acc.mean()
+    sigma = np.sqrt(0.25 / B)
+    assert abs(rate - ex["accept_probability"]) < 3 * sigma, rate
+    assert np.all(r["tokens"][~acc, 0] == 1)
+    bonus0 = (r["tokens"][acc, 1] == 0).mean()
+    s2 = np.sqrt(0.21 / acc.sum())
+    assert abs(bonus0 - 0.3) < 4 * s2, bonus0
+
+
+# --------------------------------------------------------------------------
+# Greedy (temperature 0): exact match against the target's top-1
+# --------------------------------------------------------------------------
+def check_bpd_greedy_example():
+    ex = _golden("bpd_greedy_example.json")
+    vocab = ex["vocab"]
+    V, K = len(vocab), len(ex["drafts"])
+    rng = np.random.default_rng(7)
+    target = rng.normal(0, 1, (1, K + 1, V)).astype(np.float32)
+    for j, w in enumerate(ex["target_top1"]):
+        target[0, j, vocab.index(w)] = 10.0
+    ids = [[vocab.index(w) for w in ex["drafts"]]]
+    r = oracle.verify(target, None, ids, [K], [0.0])
+    n = int(r["num_accepted"][0])
+    toks = [vocab[t] for t in r["tokens"][0, : n + 1]]
+    assert toks[:n] == ex["expected_accepted"], toks
+    assert toks[n] == ex["expected_emitted"], toks
+    assert list(r["tokens"][0, n + 1:]) == [-1] * (K - n)
+
+
+def check_greedy_bruteforce(cases=300, seed=3):
+    """Integer-valued logits (many ties): n_acc is the longest prefix whose
+    draft attains the row maximum; the emitted token is numpy's argmax (lowest
+    index among ties) of the row after that prefix."""
+    rng = np.random.default_rng(seed)
+    for _ in range(cases):
+        V = int(rng.choice([1, 2, 3, 5, 8]))
+        K = int(rng.integers(0, 5))
+        B = 4
+        target = rng.integers(-2, 3, (B, K + 1, V)).astype(np.float32)
+        ids = rng.integers(0, V, (B, K)).astype(np.int32)
+        nd = rng.integers(0, K + 1, B).astype(np.int32)
+        T = rng.choice([0.0, -1.0, np.nan], B).astype(np.float32)
+        r = oracle.verify(target, None, ids, nd, T)
+        for b in range(B):
+            n = 0
+            while n < nd[b] and target[b, n, ids[b, n]] == target[b, n].max():
+                n += 1
+            assert r["num_accepted"][b] == n
+            assert r["tokens"][b, n] == int(np.argmax(target[b, n]))
+            assert np.array_equal(r["tokens"][b, :n], ids[b, :n])
+            assert np.all(r["tokens"][b, n + 1:] == -1)
+
+
+# --------------------------------------------------------------------------
+# Exact output law (V = 4, K = 2): every emitted position follows p_j
+# --------------------------------------------------------------------------
+def _position_law(p, q, mode, x_fixed=None):
+    """Law of the token emitted at a position, by enumeration over the draft
+    x ~ q (or the fixed one-hot draft), the acceptance probability
+    min(1, ratio) and the oracle's residual law r / sum(r)."""
+    V = len(p)
+    law = np.zeros(V)
+    drafts = [(x, q[x]) for x in range(V)] if mode == oracle.MODE_PROB else [(x_fixed, 1.0)]
+    for x, wx in drafts:
+        if wx == 0:
+            continue
+        ratio = oracle.accept_ratio(p[x], q[x] if mode == oracle.MODE_PROB else 1.0)
+        a = min(1.0, ratio)
+        law[x] += wx * a
+        if a < 1:
+            r = oracle.residual(p, q if mode == oracle.MODE_PROB else None, mode, x)
+            law += wx * (1 - a) * r / r.sum()
+    return law
+
+
+def check_enumeration_law(cases=60, seed=11):
+    rng = np.random.default_rng(seed)
+    for c in range(cases):
+        V = 4
+        T = float(rng.choice([0.4, 1.0, 1.7]))
+        for j in range(2):
+            lt = rng.normal(0, 2, V)
+            ld = lt + rng.normal(0, 1.5, V)
+            p = oracle.softmax(lt, T)
+            # the oracle's softmax itself against scipy's
+            assert np.allclose(p, scipy.special.softmax(lt / T), rtol=1e-13, atol=0)
+            q = oracle.softmax(ld, T)
+            law = _position_law(p, q, oracle.MODE_PROB)
+            assert np.max(np.abs(law - p)) < 1e-12, (law, p)
+            x = int(rng.integers(0, V))
+            law1 = _position_law(p, None, oracle.MODE_ONEHOT, x_fixed=x)
+            assert np.max(np.abs(law1 - p)) < 1e-12, (law1, p)
+
+
+def check_grid_law_through_verify(G=1 << 14, seed=5):
+    """The same law, but through the full verify entry on a grid of uniforms:
+    per draft x0 of a V=4 row, the acceptance count over a u_acc grid and the
+    emitted-token histogram over a u_rec grid (forced rejection) rebuild p_0
+    within 3/G."""
+    rng = np.random.default_rng(seed)
+    V, K = 4, 2
+    lt = rng.normal(0, 2, (K + 1, V)).astype(np.float32)
+    ld = (lt[:K] + rng.normal(0, 1.5, (K, V))).astype(np.float32)
+    p0 = scipy.special.softmax(lt[0].astype(np.float64))
+    q0 = scipy.special.softmax(ld[0].astype(np.float64))
+    grid = np.arange(G) / G
+    law = np.zeros(V)
+    for x0 in range(V):
+        target = np.broadcast_to(lt, (G, K + 1, V)).copy()
+        draft = np.broadcast_to(ld, (G, K, V)).copy()
+        ids = np.tile([[x0, 0]], (G, 1))
+        ua = np.zeros((G, K + 1)); ua[:, 0] = grid; ua[:, 1] = 0.0
+        ur = np.full((G, K + 1), 0.25)
+        r = oracle.verify(target, draft, ids, np.full(G, 2), np.ones(G),
+                          u_acc=ua, u_rec=ur)
+        acc = (r["num_accepted"] >= 1).mean()
+        ua2 = np.full((G, K + 1), 1.0 - 2.0 ** -24)
+        ur2 = np.zeros((G, K + 1)); ur2[:, 0] = grid
+        r2 = oracle.verify(target, draft, ids, np.full(G, 2), np.ones(G),
+                           u_acc=ua2, u_rec=ur2)
+        if (r2["num_accepted"] == 0).all():
+            hist = np.bincount(r2["tokens"][:, 0], minlength=V) / G
+        else:
+            hist = np.zeros(V)  # ratio >= 1: never rejected
+        law[x0] += q0[x0] * acc
+        law += q0[x0] * (1 - acc) * hist
+    assert np.max(np.abs(law - p0)) < 3.0 / G, (law, p0)
+
+
+# --------------------------------------------------------------------------
+# Monte Carlo: first and second emitted tokens, acceptance rate closed form
+# --------------------------------------------------------------------------
+def _chisq_ok(counts, probs, alpha=1e-3):
+    exp = probs * counts.sum()
+    keep = exp >= 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    ex = np.append(exp[keep], exp[~keep].sum())
+    if ex[-1] == 0:
+        obs, ex = obs[:-1], ex[:-1]
+    return scipy.stats.chisquare(obs, ex).pvalue > alpha
+
+
+def check_monte_carlo(B=1 << 19, V=8, T=0.7, seed=21):
+    rng = np.random.default_rng(seed)
+    K = 2
+    lt = rng.normal(0, 2, (K + 1, V)).astype(np.float32)
+    ld = (lt[:K] + rng.normal(0, 1.0, (K, V))).astype(np.float32)
+    p = [scipy.special.softmax(lt[j].astype(np.float64) / T) for j in range(K + 1)]
+    q = [scipy.special.softmax(ld[j].astype(np.float64) / T) for j in range(K)]
+    # drafts drawn from q_j with a generator of the test's own
+    ids = np.stack([rng.choice(V, B, p=q[j]) for j in range(K)], 1).astype(np.int32)
+    target = np.broadcast_to(lt, (B, K + 1, V)).copy()
+    draft = np.broadcast_to(ld, (B, K, V)).copy()
+    r = oracle.verify(target, draft, ids, np.full(B, K), np.full(B, T),
+                      seed=seed, offset=3)
+    first = r["tokens"][:, 0]
+    assert _chisq_ok(np.bincount(first, minlength=V), p[0])
+    reached = r["num_accepted"] >= 1
+    second = r["tokens"][reached, 1]
+    assert _chisq_ok(np.bincount(second, minlength=V), p[1])
+    # P(accept at 0) = sum_x min(p(x), q(x)) = 1 - TV(p, q)
+    pa = np.minimum(p[0], q[0]).sum()
+    rate = reached.mean()
+    assert abs(rate - pa) < 4 * np.sqrt(pa * (1 - pa) / B), (rate, pa)
+
+
+def check_monte_carlo_onehot(B=1 << 18, V=6, T=1.3, seed=8):
+    rng = np.random.default_rng(seed)
+    K = 1
+    lt = rng.normal(0, 1.5, (K + 1, V)).astype(np.float32)
+    p0 = scipy.special.softmax(lt[0].astype(np.float64) / T)
+    x = int(np.argsort(p0)[-2])
+    target = np.broadcast_to(lt, (B, K + 1, V)).copy()
+    r = oracle.verify(target, None, np.full((B, K), x), np.full(B, K),
+                      np.full(B, T), seed=seed, offset=0)
+    assert _chisq_ok(np.bincount(r["tokens"][:, 0], minlength=V), p0)
+    rate = (r["num_accepted"] == 1).mean()
+    assert abs(rate - p0[x]) < 4 * np.sqrt(p0[x] * (1 - p0[x]) / B)
+
+
+# --------------------------------------------------------------------------
+# Special cases that reduce to library routines, and invariants
+# --------------------------------------------------------------------------
+def check_no_draft_is_plain_sampling(cases=200, seed=31):
+    """n_b = 0: the step is one inverse-CDF draw from softmax(l/T), i.e.
+    searchsorted(cumsum(p), u * sum(p), 'right') with scipy's softmax."""
+    rng = np.random.default_rng(seed)
+    for c in range(cases):
+        V = int(rng.integers(1, 300))
+        T = float(rng.uniform(0.2, 2.0))
+        l = rng.normal(0, 3, (1, 1, V)).astype(np.float32)
+        r = oracle.verify(l, None, np.zeros((1, 0)), [0], [T], seed=c, offset=c)
+        p = scipy.special.softmax(l[0, 0].astype(np.float64) / T)
+        _, u = oracle.uniforms(c, c, 0, 0)
+        cdf = np.cumsum(p)
+        y = int(np.searchsorted(cdf, u * cdf[-1], side="right"))
+        if r["margin_rec"][0] > 1e-9:
+            assert r["tokens"][0, 0] == y, (r["tokens"], y)
+        assert r["num_accepted"][0] == 0
+
+
+def check_identical_draft_always_accepted(seed=41):
+    """q = p (draft logits equal to target logits): ratio is exactly 1, so
+    every draft is accepted and the bonus row is sampled."""
+    rng = np.random.default_rng(seed)
+    B, K, V = 64, 5, 50
+    lt = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    ids = rng.integers(0, V, (B, K)).astype(np.int32)
+    r = oracle.verify(lt, lt[:, :K].copy(), ids, np.full(B, K),
+                      rng.uniform(0.3, 2, B), seed=1, offset=2)
+    assert np.all(r["num_accepted"] == K)
+
+
+def check_certain_onehot_always_accepted(seed=43):
+    rng = np.random.default_rng(seed)
+    B, K, V = 32, 3, 40
+    lt = np.full((B, K + 1, V), -100.0, np.float32)
+    ids = rng.integers(0, V, (B, K)).astype(np.int32)
+    for b in range(B):
+        for j in range(K):
+            lt[b, j, ids[b, j]] = 100.0
+    lt[:, K, 0] = 0.0
+    r = oracle.verify(lt, None, ids, np.full(B, K), np.ones(B), seed=2)
+    assert np.all(r["num_accepted"] == K)
+
+
+def check_zero_mass_never_drawn():
+    """The inverse CDF skips tokens of zero mass even at u = 0."""
+    y, _ = oracle.draw(np.array([0.0, 0.0, 0.5, 0.5]), 0.0)
+    assert y == 2
+    y, _ = oracle.draw(np.array([0.3, 0.0, 0.7, 0.0]), 1.0 - 2.0 ** -24)
+    assert y == 2
+
+
+def check_invariants(seed=51):
+    """0 <= n_acc <= n_b, accepted prefix = drafts, one emitted token then -1
+    padding, a rejected sampling draft is never re-emitted, and NaN padding
+    rows are never read."""
+    import torch
+    import synth
+    for i, kw in enumerate([dict(temps=(1.0, 0.0, 0.6), n_mode="ragged"),
+                            dict(temps=(0.8,), onehot_frac=0.5, n_mode="ragged"),
+                            dict(temps=(1.2, 0.0), dtype=torch.bfloat16),
+                            dict(temps=(0.9,), draft_is_probs=True)]):
+        w = synth.make_random(48, 6, 300, seed=seed + i, **kw)
+        h = w.host_arrays()
+        r = oracle.verify(h["target"], h["draft"], h["draft_ids"],
+                          h["num_drafts"], h["temperatures"],
+                          draft_mode=h["draft_mode"],
+                          draft_is_probs=h["draft_is_probs"], seed=i, offset=7)
+        assert r["flags"] == 0
+        for b in range(w.B):
+            n = int(r["num_accepted"][b]); nb = int(h["num_drafts"][b])
+            assert 0 <= n <= nb
+            assert np.array_equal(r["tokens"][b, :n], h["draft_ids"][b, :n])
+            y = int(r["tokens"][b, n])
+            assert 0 <= y < w.V
+            assert np.all(r["tokens"][b, n + 1:] == -1)
+            if n < nb and oracle.is_sampling(h["temperatures"][b]):
+                assert y != h["draft_ids"][b, n]
+
+
+ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
+             check_accept_example_philox, check_bpd_greedy_example,
+             check_greedy_bruteforce, check_enumeration_law,
+             check_grid_law_through_verify, check_monte_carlo,
+             check_monte_carlo_onehot, check_no_draft_is_plain_sampling,
+             check_identical_draft_always_accepted,
+             check_certain_onehot_always_accepted, check_zero_mass_never_drawn,
+             check_invariants]

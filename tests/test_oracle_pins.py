@@ -1,0 +1,58 @@
+"""The CPU oracle against its pins (no GPU).  See oracle_pins.py."""
+import os
+import re
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+
+@pytest.mark.parametrize("check", pins.ALL_QUICK, ids=lambda f: f.__name__)
+def test_pin(check):
+    check()
+
+
+def test_accept_example_full_grid():
+    pins.check_accept_example_grid()
+
+
+# Planted mistakes: each is a plausible slip in the oracle's source.  A copy
+# of the source with the slip is compiled and the pins must reject it.
+MUTANTS = {
+    "residual_q_minus_p": ("double d = p[i] - q[i];", "double d = q[i] - p[i];"),
+    "ratio_inverted": ("if (qx > 0.0) return px / qx;", "if (qx > 0.0) return qx / px;"),
+    "draw_not_strict": ("if (C > theta) {", "if (C >= theta) {"),
+    "uniform_words_swapped": ("*u_acc = (double)(w[0] >> 40)", "*u_acc = (double)(w[1] >> 40)"),
+    "philox_constant": ("0xD2E7470EE14C6C93ULL", "0xD2E7470EE14C6C95ULL"),
+    "greedy_last_tie": ("if (v[i] > v[best]) best = i;", "if (v[i] >= v[best]) best = i;"),
+    "temperature_ignored": ("p[i] = exp((logits[i] - m) / T);", "p[i] = exp((logits[i] - m));"),
+    "no_stop_at_rejection": ("rejected = 1;\n        break;", "rejected = 1;"),
+    "onehot_x_not_zeroed": ("if (x >= 0 && x < V) r[x] = 0.0;", "(void)x;"),
+    "bonus_from_draft": ("memcpy(r, p, sizeof(double) * (size_t)V);\n      }",
+                         "memcpy(r, p, sizeof(double) * (size_t)V);\n        if (mode == SVO_MODE_PROB && n > 0) { load_row(draft, draft_dtype, drow0 + n - 1, V, dl); svo_softmax(dl, V, (double)T, r); }\n      }"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistakes_are_caught(name):
+    src = open(oracle._SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = oracle.open_library(oracle.build(src=path, out=os.path.join(d, "m.so")))
+        oracle.use_library(lib)
+        caught = []
+        try:
+            for check in pins.ALL_QUICK:
+                try:
+                    check()
+                except AssertionError:
+                    caught.append(check.__name__)
+        finally:
+            oracle.use_library(None)
+    assert caught, f"no pin caught the planted mistake {name}"
