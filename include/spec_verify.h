@@ -1,0 +1,164 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-sampling verify step on
+ * MI355X (gfx950).
+ *
+ * The operation (sources by page title and section):
+ *   - "深入推测解码：从概念到实现" (Exploring Speculative Decoding), section
+ *     保证原始分布: a draft token x sampled from the draft law q is accepted
+ *     with probability min(1, p(x)/q(x)); on rejection a correction token is
+ *     sampled from max(0, p - q).
+ *   - "RTP-LLM Speculative Engine 深度解析", section 拒绝采样算法: per drafted
+ *     position a Uniform(0,1) draw is compared with p/q, the first rejection
+ *     resamples from normalize(max(0, p - q)) and stops the walk; full
+ *     probability rows per position are the inputs.
+ *   - "投机采样" (razer666.cn), section 投机解码算法, steps 3-5: the accepted
+ *     count n, the adjusted law norm(max(0, p_{n+1} - q_{n+1})), and one
+ *     extra token from the last target row when every draft passes, so the
+ *     output length is n + 1 in [1, K + 1]; section 验证阶段的策略 / 精确匹配:
+ *     greedy exact match against the max-probability token.
+ *
+ * Conventions
+ *   - p = softmax(target_logits / T_b); q = softmax(draft_logits / T_b), or
+ *     the draft rows as given when the handle was created with
+ *     draft_is_probs = 1.
+ *   - T_b that is not a positive, normal, finite float selects greedy for
+ *     request b: a draft is accepted iff its target logit equals the row
+ *     maximum, and the emitted token is the lowest index of the maximum.
+ *   - One-hot (n-gram) drafts have no q: x is accepted with probability p(x)
+ *     and the correction is drawn from p with x removed.
+ *   - Uniforms come from Philox4x64-10 (Salmon et al., SC'11) with key
+ *     (philox_seed, 0) and counter (philox_offset, b, j, 0); output word 0
+ *     is the acceptance uniform of position j, word 1 the draw uniform;
+ *     u = (w >> 40) * 2^-24.  A decision accepts iff u < p(x)/q(x); a draw
+ *     takes the smallest i whose running sum exceeds u * S.
+ *
+ * Ownership and execution
+ *   - The caller owns every input and output buffer (device memory).  The
+ *     library owns only the workspace it allocates in spec_verify_create.
+ *   - spec_verify_run only enqueues kernels on `stream` (a hipStream_t;
+ *     NULL = the null stream).  It neither allocates nor synchronizes.  One
+ *     handle must not be used by two streams at once: its workspace is
+ *     reused by every run.
+ *   - Errors are returned as sv_status codes before anything is enqueued;
+ *     nothing is thrown across the ABI.  Bad device-side data (draft ids
+ *     outside [0, V), draft counts outside [0, K]) never faults: it is
+ *     clamped or rejected and recorded in a sticky bitmask that
+ *     spec_verify_get_device_errors returns.
+ *   - The same inputs and (seed, offset) give bit-identical outputs.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spec_verify_s *spec_verify_t;
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad size */
+  SV_ERR_UNSUPPORTED = -2, /* dtype or option not supported */
+  SV_ERR_CAPACITY = -3,    /* B or K above the handle's maxima */
+  SV_ERR_HIP = -4          /* a HIP runtime call failed */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Sticky device-side conditions (spec_verify_get_device_errors). */
+#define SV_DEVERR_BAD_DRAFT_ID 1u   /* id outside [0, V): never accepted */
+#define SV_DEVERR_BAD_NUM_DRAFTS 2u /* count clamped into [0, K] */
+#define SV_DEVERR_ZERO_RESIDUAL 4u  /* residual mass 0: drawn from p */
+#define SV_DEVERR_DRAW_ROUNDING 8u  /* draw landed past a chunk's recomputed
+                                       total (a rounding tie); nearest token
+                                       with mass taken */
+
+typedef struct {
+  int32_t max_batch;      /* largest B of any run, >= 1 */
+  int32_t max_drafts;     /* largest K of any run, 0..63 */
+  int32_t vocab;          /* V, 1 .. 2^24 */
+  int32_t target_dtype;   /* sv_dtype of target_logits */
+  int32_t draft_dtype;    /* sv_dtype of draft_probs */
+  int32_t draft_is_probs; /* 0: draft rows are logits (softmax at T_b);
+                             1: draft rows are normalized probabilities */
+  int32_t device;         /* HIP device ordinal */
+  int32_t chunk_elems;    /* vocabulary elements per work chunk; 0 picks a
+                             default; else a multiple of 64 in [256, 16384] */
+} sv_config;
+
+/* Creates a handle on cfg->device and allocates its workspace.
+ * Returns SV_ERR_INVALID_ARG for a null argument or a field out of range,
+ * SV_ERR_UNSUPPORTED for an unknown dtype, SV_ERR_HIP if allocation fails.
+ * On failure *out is set to NULL. */
+int spec_verify_create(const sv_config *cfg, spec_verify_t *out);
+
+/* Enqueues one verify step for B requests with up to K drafts each.
+ *
+ *   target_logits      device [B][K+1][V], cfg.target_dtype, row-major,
+ *                      aligned to its element size.  Rows j > n_b are never
+ *                      read.
+ *   draft_probs        device [B][K][V], cfg.draft_dtype: draft logits, or
+ *                      probabilities if cfg.draft_is_probs.  Rows j >= n_b,
+ *                      rows of one-hot requests and rows of greedy requests
+ *                      are never read.  NULL: every request is one-hot.
+ *   draft_mode         device [B] uint8: 0 probabilistic, nonzero one-hot.
+ *                      NULL: every request is probabilistic (if draft_probs
+ *                      is given).
+ *   draft_ids          device [B][K] int32: the drafted tokens x_j.
+ *   num_drafts_per_req device [B] int32: n_b, expected in [0, K].
+ *   temperatures       device [B] float: T_b (see Conventions).
+ *   philox_seed, philox_offset: the uniform stream; advance the offset by
+ *                      one per step.
+ *   out_tokens         device [B][K+1] int32: x_0..x_{n_acc-1}, then the
+ *                      emitted token, then -1.
+ *   out_num_accepted   device [B] int32: n_acc in [0, n_b].
+ *   out_debug_probs    device [B][K][2] float (p_j(x_j), q_j(x_j)) for every
+ *                      j < n_b of a sampling request (q = 1 for one-hot),
+ *                      NaN elsewhere; or NULL.
+ *   stream             hipStream_t to enqueue on.
+ *
+ * Returns SV_ERR_INVALID_ARG (null or misaligned pointer, B < 0, K < 0),
+ * SV_ERR_CAPACITY (B > max_batch or K > max_drafts) or SV_ERR_HIP (launch
+ * failure).  B == 0 enqueues nothing and returns SV_OK. */
+int spec_verify_run(spec_verify_t h, int32_t B, int32_t K,
+                    const void *target_logits, const void *draft_probs,
+                    const uint8_t *draft_mode, const int32_t *draft_ids,
+                    const int32_t *num_drafts_per_req,
+                    const float *temperatures, uint64_t philox_seed,
+                    uint64_t philox_offset, int32_t *out_tokens,
+                    int32_t *out_num_accepted, float *out_debug_probs,
+                    void *stream);
+
+/* Waits for the handle's last run, copies the sticky SV_DEVERR_* bitmask to
+ * *host_flags and, if clear != 0, resets it.  Synchronizing call. */
+int spec_verify_get_device_errors(spec_verify_t h, uint32_t *host_flags,
+                                  int32_t clear);
+
+/* Per-kernel timing with HIP events recorded on the run's stream.
+ * enable != 0 starts recording (and resets the totals); each later run adds
+ * the duration of each of its kernels.  spec_verify_timing_read waits for
+ * the last run and writes up to n totals in milliseconds (kernel order as
+ * spec_verify_kernel_name) and the number of timed runs. */
+int spec_verify_timing_enable(spec_verify_t h, int32_t enable);
+int spec_verify_timing_read(spec_verify_t h, float *total_ms, int32_t n,
+                            int32_t *runs);
+/* Name of kernel i of a run (NULL past the last one). */
+const char *spec_verify_kernel_name(int32_t i);
+
+/* Chunk length (vocabulary elements per work item) the handle uses. */
+int32_t spec_verify_chunk_elems(spec_verify_t h);
+
+/* Frees the workspace and the handle (waits for the device first).
+ * NULL is accepted. */
+int spec_verify_destroy(spec_verify_t h);
+
+/* Static text for a status code. */
+const char *spec_verify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

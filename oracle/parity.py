@@ -1,0 +1,123 @@
+"""Parity rule between an implementation's verify outputs and the oracle's.
+
+TEST INFRASTRUCTURE (see the package docstring).  Works on numpy arrays only.
+
+Rule: a request is flagged when one of the decisions the oracle evaluated
+lies within ``band`` of its threshold (|u - p(x)/q(x)| < band) or the draw
+uniform lies within ``band`` of a CDF boundary (relative to the law's total).
+Unflagged requests must match bit for bit in the accepted count and in every
+token.  A request flagged at decision j must still agree on tokens 0..j-1; a
+request flagged only at the draw must agree on the accepted count and the
+accepted tokens.  Every output must be valid whatever the flags.  Acceptance
+probabilities p_j(x_j), q_j(x_j) must agree to ``prob_rtol`` relative (an
+absolute floor of 1e-35 below 1e-30).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+@dataclasses.dataclass
+class ParityReport:
+    requests: int = 0
+    flagged: int = 0
+    flagged_mismatch: int = 0   # flagged requests whose outputs differ
+    mismatches: list = dataclasses.field(default_factory=list)
+    prob_checked: int = 0
+    prob_max_rel: float = 0.0
+    accepted: int = 0
+    proposed: int = 0
+
+    def ok(self):
+        return not self.mismatches
+
+
+def _is_sampling(T):
+    T = np.asarray(T, dtype=np.float32)
+    return (T >= np.finfo(np.float32).tiny) & (T <= np.finfo(np.float32).max)
+
+
+def compare(host, ref, tokens, nacc, dbg=None, *, band=1e-6, prob_rtol=1e-5,
+            max_report=20) -> ParityReport:
+    """host: the input arrays (synth.Workload.host_arrays()); ref: the
+    oracle's result dict; tokens [B, K+1], nacc [B], dbg [B, K, 2] or None:
+    the implementation's outputs."""
+    tokens = np.asarray(tokens)
+    nacc = np.asarray(nacc)
+    B, K1 = tokens.shape
+    K = K1 - 1
+    V = host["target"].shape[2]
+    nd = np.clip(np.asarray(host["num_drafts"]), 0, K)
+    ids = np.asarray(host["draft_ids"]).reshape(B, K)
+    samp = _is_sampling(host["temperatures"])
+    rep = ParityReport(requests=B)
+
+    def bad(b, why):
+        if len(rep.mismatches) < max_report:
+            rep.mismatches.append((b, why))
+        else:
+            rep.mismatches.append((b, "..."))
+
+    for b in range(B):
+        n = int(nd[b])
+        ga, oa = int(nacc[b]), int(ref["num_accepted"][b])
+        rep.accepted += ga
+        rep.proposed += n
+        # validity, whatever the flags
+        if not (0 <= ga <= n):
+            bad(b, f"n_acc {ga} outside [0, {n}]")
+            continue
+        if not np.array_equal(tokens[b, :ga], ids[b, :ga]):
+            bad(b, "accepted prefix differs from the drafts")
+        y = int(tokens[b, ga])
+        if not (0 <= y < V):
+            bad(b, f"emitted token {y} outside [0, {V})")
+        if np.any(tokens[b, ga + 1:] != -1):
+            bad(b, "padding after the emitted token is not -1")
+        # flag position
+        flag_at = None
+        for j in range(oa + 1 if oa < n else n):
+            m = ref["margin_acc"][b, j]
+            if np.isfinite(m) and m < band:
+                flag_at = j
+                break
+        rec_flag = flag_at is None and ref["margin_rec"][b] < band
+        if flag_at is not None or rec_flag:
+            rep.flagged += 1
+            if ga != oa or not np.array_equal(tokens[b], ref["tokens"][b]):
+                rep.flagged_mismatch += 1
+            if flag_at is not None:
+                if ga < flag_at:
+                    bad(b, f"flagged at decision {flag_at} but n_acc {ga} < {flag_at}")
+            elif ga != oa:
+                bad(b, f"flagged at the draw only but n_acc {ga} != oracle {oa}")
+            continue
+        if ga != oa:
+            bad(b, f"n_acc {ga} != oracle {oa}")
+        elif not np.array_equal(tokens[b], ref["tokens"][b]):
+            bad(b, f"tokens {tokens[b].tolist()} != oracle {ref['tokens'][b].tolist()}")
+
+    if dbg is not None:
+        dbg = np.asarray(dbg, dtype=np.float64)
+        for b in range(B):
+            for j in range(K):
+                op, oq = ref["p"][b, j], ref["q"][b, j]
+                gp, gq = dbg[b, j, 0], dbg[b, j, 1]
+                live = samp[b] and j < nd[b] and 0 <= ids[b, j] < V
+                if not live:
+                    if not (np.isnan(gp) and np.isnan(gq)):
+                        bad(b, f"debug probs at j={j} should be NaN")
+                    continue
+                for o, g in ((op, gp), (oq, gq)):
+                    rep.prob_checked += 1
+                    if abs(o) < 1e-30:
+                        if abs(g - o) > 1e-35:
+                            bad(b, f"prob at j={j}: {g} vs {o} (abs floor)")
+                        continue
+                    rel = abs(g - o) / abs(o)
+                    rep.prob_max_rel = max(rep.prob_max_rel, rel)
+                    if not rel <= prob_rtol:
+                        bad(b, f"prob at j={j}: {g} vs {o} rel {rel:.3g}")
+    return rep

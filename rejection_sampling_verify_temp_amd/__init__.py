@@ -1,0 +1,13 @@
+"""Speculative-sampling verify step on MI355X (gfx950).
+
+The compute lives in the HIP library ``lib/libspecverify.so`` (kernels and
+C ABI under ``csrc/``, declared in ``include/spec_verify.h``); ``binding``
+holds the ctypes binding with the C entry-point names and a small
+torch-tensor wrapper.
+"""
+from .binding import (SpecVerify, SpecVerifyError, load_library, sv_config,  # noqa: F401
+                      spec_verify_create, spec_verify_destroy,
+                      spec_verify_get_device_errors, spec_verify_kernel_name,
+                      spec_verify_run, spec_verify_status_string,
+                      spec_verify_timing_enable, spec_verify_timing_read,
+                      spec_verify_chunk_elems, header_functions)

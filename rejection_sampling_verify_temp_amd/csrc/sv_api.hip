@@ -1,0 +1,283 @@
+// Host side of the verify-step C ABI: argument checks, the workspace, and
+// the launches (see spec_verify.h for the contract).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "sv_internal.h"
+
+namespace {
+
+constexpr int kTimingSlots = 64;
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(dev) == hipSuccess) ok = true;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elt_bytes(int dt) { return dt == SV_BF16 ? 2 : 4; }
+
+// Chunk length: about 32 KiB of the wider input per workgroup, balanced so
+// the chunks of a row are of near-equal length, a multiple of 64 elements,
+// and small enough for the draw kernel to hold one chunk in LDS.
+int pick_chunk(const sv_config& c, int lds_cap_elems) {
+  int want = c.chunk_elems;
+  if (want == 0) {
+    const int wide = elt_bytes(c.target_dtype) > elt_bytes(c.draft_dtype)
+                         ? elt_bytes(c.target_dtype) : elt_bytes(c.draft_dtype);
+    want = 32768 / wide;
+  }
+  if (want > lds_cap_elems) want = lds_cap_elems;
+  const int V = c.vocab;
+  int n = (V + want - 1) / want;
+  if (n > sv::kMaxChunks) n = sv::kMaxChunks;
+  int ch = (V + n - 1) / n;
+  ch = ((ch + 63) / 64) * 64;
+  if (ch < sv::kMinChunkElems) ch = sv::kMinChunkElems;
+  if (ch > lds_cap_elems) ch = lds_cap_elems;
+  return ch;
+}
+
+}  // namespace
+
+struct spec_verify_s {
+  sv_config cfg;
+  int chunk = 0;
+  int nchunk = 0;
+  sv::Partial* part = nullptr;
+  sv::DrawDesc* desc = nullptr;
+  double* rsum = nullptr;
+  uint32_t* flags = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool has_run = false;
+  // timing
+  bool timing = false;
+  hipEvent_t ev[kTimingSlots][2 * sv::kNumKernels] = {};
+  int ev_pending = 0;  // event sets recorded and not yet read
+  int ev_next = 0;     // next ring slot
+  double tot_ms[sv::kNumKernels] = {};
+  int runs = 0;
+};
+
+namespace {
+
+void free_all(spec_verify_s* h) {
+  if (h->part) (void)hipFree(h->part);
+  if (h->desc) (void)hipFree(h->desc);
+  if (h->rsum) (void)hipFree(h->rsum);
+  if (h->flags) (void)hipFree(h->flags);
+  for (int s = 0; s < kTimingSlots; ++s)
+    for (int k = 0; k < 2 * sv::kNumKernels; ++k)
+      if (h->ev[s][k]) (void)hipEventDestroy(h->ev[s][k]);
+}
+
+// Fold the oldest pending event set into the totals.
+hipError_t drain_one(spec_verify_s* h) {
+  const int slot = (h->ev_next - h->ev_pending + kTimingSlots) % kTimingSlots;
+  hipError_t e = hipEventSynchronize(h->ev[slot][2 * sv::kNumKernels - 1]);
+  if (e != hipSuccess) return e;
+  for (int k = 0; k < sv::kNumKernels; ++k) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, h->ev[slot][2 * k], h->ev[slot][2 * k + 1]);
+    if (e != hipSuccess) return e;
+    h->tot_ms[k] += ms;
+  }
+  h->runs++;
+  h->ev_pending--;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_verify_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported dtype or option";
+    case SV_ERR_CAPACITY: return "batch or draft count above the handle's maxima";
+    case SV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* spec_verify_kernel_name(int32_t i) { return sv::kernel_name(i); }
+
+int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
+  if (out == nullptr) return SV_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (cfg == nullptr) return SV_ERR_INVALID_ARG;
+  const sv_config c = *cfg;
+  if (c.max_batch < 1 || c.max_drafts < 0 || c.max_drafts > sv::kMaxDrafts ||
+      c.vocab < 1 || c.vocab > (1 << 24) || c.device < 0)
+    return SV_ERR_INVALID_ARG;
+  if ((c.target_dtype != SV_F32 && c.target_dtype != SV_BF16) ||
+      (c.draft_dtype != SV_F32 && c.draft_dtype != SV_BF16) ||
+      (c.draft_is_probs != 0 && c.draft_is_probs != 1))
+    return SV_ERR_UNSUPPORTED;
+  if (c.chunk_elems != 0 &&
+      (c.chunk_elems % 64 != 0 || c.chunk_elems < sv::kMinChunkElems ||
+       c.chunk_elems > sv::kMaxChunkElems))
+    return SV_ERR_INVALID_ARG;
+
+  DeviceGuard g(c.device);
+  if (!g.ok) return SV_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c.device) != hipSuccess) return SV_ERR_HIP;
+  // the draw kernel keeps one chunk of floats in LDS next to ~5 KiB of its own
+  int lds_cap = (int)((prop.sharedMemPerBlock - 8192) / sizeof(float));
+  lds_cap = (lds_cap / 64) * 64;
+  if (lds_cap > sv::kMaxChunkElems) lds_cap = sv::kMaxChunkElems;
+  if (lds_cap < sv::kMinChunkElems) return SV_ERR_UNSUPPORTED;
+  const int chunk = pick_chunk(c, lds_cap);
+  const int nchunk = (c.vocab + chunk - 1) / chunk;
+  if (nchunk > sv::kMaxChunks) return SV_ERR_UNSUPPORTED;
+
+  spec_verify_s* h = new (std::nothrow) spec_verify_s();
+  if (h == nullptr) return SV_ERR_HIP;
+  h->cfg = c;
+  h->chunk = chunk;
+  h->nchunk = nchunk;
+  const size_t rows = (size_t)c.max_batch * (2 * (size_t)c.max_drafts + 1);
+  bool ok = hipMalloc(&h->part, rows * nchunk * sizeof(sv::Partial)) == hipSuccess &&
+            hipMalloc(&h->desc, (size_t)c.max_batch * sizeof(sv::DrawDesc)) == hipSuccess &&
+            hipMalloc(&h->rsum, (size_t)c.max_batch * nchunk * sizeof(double)) == hipSuccess &&
+            hipMalloc(&h->flags, sizeof(uint32_t)) == hipSuccess &&
+            hipMemset(h->flags, 0, sizeof(uint32_t)) == hipSuccess;
+  if (!ok) {
+    free_all(h);
+    delete h;
+    return SV_ERR_HIP;
+  }
+  *out = h;
+  return SV_OK;
+}
+
+int spec_verify_run(spec_verify_t h, int32_t B, int32_t K, const void* target_logits,
+                    const void* draft_probs, const uint8_t* draft_mode,
+                    const int32_t* draft_ids, const int32_t* num_drafts_per_req,
+                    const float* temperatures, uint64_t philox_seed,
+                    uint64_t philox_offset, int32_t* out_tokens,
+                    int32_t* out_num_accepted, float* out_debug_probs, void* stream) {
+  if (h == nullptr || B < 0 || K < 0) return SV_ERR_INVALID_ARG;
+  if (B > h->cfg.max_batch || K > h->cfg.max_drafts) return SV_ERR_CAPACITY;
+  if (B == 0) return SV_OK;
+  const sv_config& c = h->cfg;
+  if (target_logits == nullptr || num_drafts_per_req == nullptr ||
+      temperatures == nullptr || out_tokens == nullptr || out_num_accepted == nullptr ||
+      (K > 0 && draft_ids == nullptr))
+    return SV_ERR_INVALID_ARG;
+  if (!aligned(target_logits, elt_bytes(c.target_dtype)) ||
+      (draft_probs != nullptr && !aligned(draft_probs, elt_bytes(c.draft_dtype))) ||
+      (draft_ids != nullptr && !aligned(draft_ids, 4)) || !aligned(num_drafts_per_req, 4) ||
+      !aligned(temperatures, 4) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      (out_debug_probs != nullptr && !aligned(out_debug_probs, 4)))
+    return SV_ERR_INVALID_ARG;
+
+  sv::RunParams p;
+  p.target = target_logits;
+  p.draft = draft_probs;
+  p.mode = draft_mode;
+  p.ids = draft_ids;
+  p.nd = num_drafts_per_req;
+  p.temps = temperatures;
+  p.out_tokens = out_tokens;
+  p.out_nacc = out_num_accepted;
+  p.out_dbg = out_debug_probs;
+  p.part = h->part;
+  p.desc = h->desc;
+  p.rsum = h->rsum;
+  p.flags = h->flags;
+  p.seed = philox_seed;
+  p.offset = philox_offset;
+  p.B = B;
+  p.K = K;
+  p.V = c.vocab;
+  p.chunk = h->chunk;
+  p.nchunk = h->nchunk;
+  p.draft_is_probs = c.draft_is_probs;
+  p.has_draft = draft_probs != nullptr;
+
+  DeviceGuard g(c.device);
+  if (!g.ok) return SV_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = nullptr;
+  if (h->timing) {
+    if (h->ev_pending == kTimingSlots && drain_one(h) != hipSuccess) return SV_ERR_HIP;
+    ev = h->ev[h->ev_next];
+  }
+  if (sv::launch_step(p, c.target_dtype, c.draft_dtype, s, ev) != hipSuccess) return SV_ERR_HIP;
+  if (h->timing) {
+    h->ev_next = (h->ev_next + 1) % kTimingSlots;
+    h->ev_pending++;
+  }
+  h->last_stream = s;
+  h->has_run = true;
+  return SV_OK;
+}
+
+int spec_verify_get_device_errors(spec_verify_t h, uint32_t* host_flags, int32_t clear) {
+  if (h == nullptr || host_flags == nullptr) return SV_ERR_INVALID_ARG;
+  DeviceGuard g(h->cfg.device);
+  if (!g.ok) return SV_ERR_HIP;
+  if (h->has_run && hipStreamSynchronize(h->last_stream) != hipSuccess) return SV_ERR_HIP;
+  if (hipMemcpy(host_flags, h->flags, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return SV_ERR_HIP;
+  if (clear && hipMemset(h->flags, 0, sizeof(uint32_t)) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int spec_verify_timing_enable(spec_verify_t h, int32_t enable) {
+  if (h == nullptr) return SV_ERR_INVALID_ARG;
+  DeviceGuard g(h->cfg.device);
+  if (!g.ok) return SV_ERR_HIP;
+  if (enable && h->ev[0][0] == nullptr) {
+    for (int s = 0; s < kTimingSlots; ++s)
+      for (int k = 0; k < 2 * sv::kNumKernels; ++k)
+        if (hipEventCreate(&h->ev[s][k]) != hipSuccess) return SV_ERR_HIP;
+  }
+  while (h->ev_pending > 0)
+    if (drain_one(h) != hipSuccess) return SV_ERR_HIP;
+  for (int k = 0; k < sv::kNumKernels; ++k) h->tot_ms[k] = 0.0;
+  h->runs = 0;
+  h->timing = enable != 0;
+  return SV_OK;
+}
+
+int spec_verify_timing_read(spec_verify_t h, float* total_ms, int32_t n, int32_t* runs) {
+  if (h == nullptr || (n > 0 && total_ms == nullptr)) return SV_ERR_INVALID_ARG;
+  DeviceGuard g(h->cfg.device);
+  if (!g.ok) return SV_ERR_HIP;
+  while (h->ev_pending > 0)
+    if (drain_one(h) != hipSuccess) return SV_ERR_HIP;
+  for (int k = 0; k < n && k < sv::kNumKernels; ++k) total_ms[k] = (float)h->tot_ms[k];
+  if (runs) *runs = h->runs;
+  return SV_OK;
+}
+
+int32_t spec_verify_chunk_elems(spec_verify_t h) { return h ? h->chunk : 0; }
+
+int spec_verify_destroy(spec_verify_t h) {
+  if (h == nullptr) return SV_OK;
+  int rc = SV_OK;
+  {
+    DeviceGuard g(h->cfg.device);
+    if (!g.ok || hipDeviceSynchronize() != hipSuccess) rc = SV_ERR_HIP;
+    free_all(h);
+  }
+  delete h;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal types shared by the host API and the kernels of the verify step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+constexpr int kStatsThreads = 256;   // row-statistics and residual-sum workgroups
+constexpr int kDecideThreads = 64;   // one wavefront per request
+constexpr int kLocateThreads = 512;  // one workgroup per request draw
+constexpr int kMaxChunkElems = 16384;
+constexpr int kMinChunkElems = 256;
+constexpr int kMaxChunks = 1024;
+constexpr int kMaxDrafts = 63;       // positions 0..K fit one wavefront
+
+// Per (row, vocabulary chunk) statistics.  Sampling rows: m = chunk max,
+// z = sum over the chunk of exp2(l_i * c + ref(m, c)).  Greedy rows: m =
+// chunk max, idx = lowest index attaining it.
+struct __align__(16) Partial {
+  float m;
+  int32_t idx;
+  double z;
+};
+
+enum DrawKind : int32_t {
+  kDrawNone = 0,    // greedy request: token already written
+  kDrawSingle = 1,  // draw from the target row (x removed if x >= 0)
+  kDrawPair = 2     // draw from max(0, p - q) of a row pair
+};
+
+// Per-request draw descriptor written by the decision kernel.
+struct __align__(16) DrawDesc {
+  int32_t kind;
+  int32_t j;       // position whose token is drawn
+  int32_t x;       // token removed from the law, or -1
+  int32_t pad0;
+  float c;         // log2(e) / T
+  float ref_p;     // exponent reference of the target row
+  float ref_q;     // exponent reference of the draft row (logit drafts)
+  float kap_hi;    // kappa = Z_p / Z_q (or Z_p for probability drafts),
+  float kap_lo;    //   split into two floats
+  float pad1;
+  double z_p;      // target row total relative to ref_p
+  double u;        // draw uniform
+};
+
+struct RunParams {
+  const void* target;
+  const void* draft;
+  const uint8_t* mode;
+  const int32_t* ids;
+  const int32_t* nd;
+  const float* temps;
+  int32_t* out_tokens;
+  int32_t* out_nacc;
+  float* out_dbg;
+  Partial* part;
+  DrawDesc* desc;
+  double* rsum;
+  uint32_t* flags;
+  uint64_t seed;
+  uint64_t offset;
+  int32_t B, K, V;
+  int32_t chunk;    // elements per chunk
+  int32_t nchunk;   // ceil(V / chunk)
+  int32_t draft_is_probs;
+  int32_t has_draft;
+};
+
+constexpr int kNumKernels = 4;
+
+// Enqueue the kernels of one step; t_events (2 * kNumKernels events or
+// null) bracket each kernel for timing.
+hipError_t launch_step(const RunParams& p, int target_dtype, int draft_dtype,
+                       hipStream_t stream, hipEvent_t* t_events);
+
+const char* kernel_name(int i);
+
+}  // namespace sv

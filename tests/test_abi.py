@@ -1,0 +1,63 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function
+include/spec_verify.h declares, and rejects bad arguments before touching
+the device."""
+import ctypes
+
+import rejection_sampling_verify_temp_amd as sv
+from rejection_sampling_verify_temp_amd import binding
+
+
+def test_library_exports_header_functions():
+    lib = sv.load_library()
+    names = sv.header_functions()
+    assert "spec_verify_run" in names and "spec_verify_create" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert sv.spec_verify_status_string(code)
+    assert sv.spec_verify_status_string(99) == "unknown status"
+
+
+def test_kernel_names():
+    names = [sv.spec_verify_kernel_name(i) for i in range(4)]
+    assert names == ["row_stats", "decide", "resid_sums", "locate"]
+    assert sv.spec_verify_kernel_name(4) is None
+
+
+def test_create_rejects_bad_config_without_device():
+    lib = sv.load_library()
+    h = ctypes.c_void_p(1)
+    assert lib.spec_verify_create(None, ctypes.byref(h)) == binding.SV_ERR_INVALID_ARG
+    assert h.value is None
+    bad = [dict(max_batch=0), dict(max_drafts=-1), dict(max_drafts=64),
+           dict(vocab=0), dict(vocab=(1 << 24) + 1), dict(chunk_elems=100),
+           dict(chunk_elems=32768), dict(device=-1)]
+    for b in bad:
+        f = dict(max_batch=4, max_drafts=4, vocab=1000, target_dtype=0,
+                 draft_dtype=0, draft_is_probs=0, device=0, chunk_elems=0)
+        f.update(b)
+        cfg = binding.sv_config(**f)
+        assert lib.spec_verify_create(ctypes.byref(cfg), ctypes.byref(h)) == \
+            binding.SV_ERR_INVALID_ARG, b
+    for b in [dict(target_dtype=2), dict(draft_dtype=-1), dict(draft_is_probs=2)]:
+        f = dict(max_batch=4, max_drafts=4, vocab=1000, target_dtype=0,
+                 draft_dtype=0, draft_is_probs=0, device=0, chunk_elems=0)
+        f.update(b)
+        cfg = binding.sv_config(**f)
+        assert lib.spec_verify_create(ctypes.byref(cfg), ctypes.byref(h)) == \
+            binding.SV_ERR_UNSUPPORTED, b
+
+
+def test_run_and_queries_reject_null_handle():
+    assert sv.spec_verify_run(None, 1, 1, 1, 0, 0, 1, 1, 1, 0, 0, 1, 1, 0, None) == \
+        binding.SV_ERR_INVALID_ARG
+    lib = sv.load_library()
+    f = ctypes.c_uint32()
+    assert lib.spec_verify_get_device_errors(None, ctypes.byref(f), 0) == binding.SV_ERR_INVALID_ARG
+    assert lib.spec_verify_timing_enable(None, 1) == binding.SV_ERR_INVALID_ARG
+    assert lib.spec_verify_timing_read(None, None, 0, None) == binding.SV_ERR_INVALID_ARG
+    assert lib.spec_verify_chunk_elems(None) == 0
+    assert lib.spec_verify_destroy(None) == 0
