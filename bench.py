@@ -1,0 +1,205 @@
+"""Benchmark of the speculative-sampling verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+One step = one spec_verify_run over a whole batch (row statistics, decisions,
+residual sums, draw).  Inputs are generated on the GPU and stay resident;
+steps rotate through --rotate copies of them so each step's rows were last
+touched more than the 256 MB Infinity Cache earlier.  The timed region is
+bracketed by torch.cuda.synchronize() and timed with events on the stream
+the library launches on.  A second loop of the same length times each kernel
+with the library's own HIP events (spec_verify_timing_*), which gives the
+dominant kernel's duration for the roofline.
+
+Prints ONE JSON line.  value = verified (request x position x vocabulary)
+elements per second = sum_b (n_b + 1) * V / step time.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified (req×pos×vocab) elems/s + achieved HBM GB/s vs peak, spec-verify step"
+HBM_PEAK_GBPS = 8000.0
+DOMINANT = "stats"  # the kernel that streams every needed logits row
+KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", "sv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_traffic_B256_K7_V152064_bf16.txt")
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload_idx):
+    """HBM bytes per stats launch measured with rocprofv3 --pmc
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), valid only
+    for the kernel source it was taken on."""
+    if workload_idx != 3 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seconds=12.0):
+    """Time the CPU oracle, as it stands, on a bounded sample: slices of 8
+    requests of the same batch, cycling through the batch (a new Philox offset
+    each pass) until about `seconds` of single-threaded work is done."""
+    import oracle
+    hs = w.host_arrays()
+    V = w.V
+    n_req, elems, t, passes = 0, 0, 0.0, 0
+    start = 0
+    while t < seconds and passes < 64:
+        sl = slice(start, min(w.B, start + 8))
+        sub = {k: (v[sl] if hasattr(v, "shape") and v.shape[:1] == (w.B,) else v)
+               for k, v in hs.items()}
+        t0 = time.perf_counter()
+        oracle.verify(sub["target"], sub["draft"], sub["draft_ids"],
+                      sub["num_drafts"], sub["temperatures"],
+                      draft_mode=sub["draft_mode"],
+                      draft_is_probs=sub["draft_is_probs"], seed=0,
+                      offset=passes, diagnostics=False)
+        t += time.perf_counter() - t0
+        n = sub["num_drafts"].clip(0, w.K)
+        elems += int((n + 1).sum()) * V
+        n_req += sl.stop - sl.start
+        start = sl.stop
+        if start >= w.B:
+            start, passes = 0, passes + 1
+    return dict(value=elems / t, unit="elems/s", cores=1, kind="oracle",
+                sample=f"{n_req} requests of the same batch (the batch cycled "
+                       f"with a new Philox offset per pass), {elems} verified "
+                       f"elems, {t:.1f} s of the single-threaded fp64 C oracle")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the steps, run one plain device copy of this "
+                         "size (a known-size reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import rejection_sampling_verify_temp_amd as sv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = synth.make_config(args.workload, device=dev)
+    copies = [base] + [base.clone() for _ in range(max(0, args.rotate - 1))]
+    torch.cuda.synchronize()
+    w = base
+    h = sv.SpecVerify(w.B, w.K, w.V, w.target.dtype,
+                      draft_dtype=w.draft.dtype if w.draft is not None else None,
+                      draft_is_probs=w.draft_is_probs, device=0,
+                      chunk_elems=args.chunk)
+    tok = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
+    nacc = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        c = copies[i % len(copies)]
+        h.run(c.target, c.draft, c.draft_mode, c.draft_ids, c.num_drafts,
+              c.temperatures, seed=0, offset=i, out_tokens=tok,
+              out_num_accepted=nacc, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel timing (library events on the same stream), separate loop
+    sv.spec_verify_timing_enable(h.handle, True)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    nk = 0
+    while sv.spec_verify_kernel_name(nk) is not None:
+        nk += 1
+    tot, runs = sv.spec_verify_timing_read(h.handle, nk)
+    sv.spec_verify_timing_enable(h.handle, False)
+    torch.cuda.synchronize()
+    kern_ms = {sv.spec_verify_kernel_name(k): tot[k] / runs for k in range(nk)}
+    assert h.device_errors() == 0
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    elems = w.verified_elems()
+    alg = w.algorithmic_bytes()
+    stats_ms = kern_ms[DOMINANT]
+    achieved = alg / (stats_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.workload)
+    dt = {torch.bfloat16: "bf16", torch.float32: "f32"}[w.target.dtype]
+    out = {
+        "metric": METRIC,
+        "value": elems / (ms_step * 1e-3),
+        "unit": "elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"configs[{args.workload}]: {w.name}",
+                   "B": w.B, "K": w.K, "V": w.V, "logits": dt,
+                   "verified_elems": elems, "algorithmic_bytes": alg,
+                   "nominal_bytes": w.nominal_bytes(),
+                   "chunk_elems": h.chunk_elems, "input_copies": len(copies),
+                   "parallelism": "single GPU"},
+        "step_hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
+        "kernels_ms": kern_ms,
+        "roofline": {"bound": "hbm", "kernel": DOMINANT,
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    h.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -77,15 +77,16 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 typedef struct {
   int32_t max_batch;      /* largest B of any run, >= 1 */
-  int32_t max_drafts;     /* largest K of any run, 0..63 */
-  int32_t vocab;          /* V, 1 .. 2^24 */
+  int32_t max_drafts;     /* largest K of any run, 0..31 */
+  int32_t vocab;          /* V, 1 .. 983040 (64 chunks of at most 15360) */
   int32_t target_dtype;   /* sv_dtype of target_logits */
   int32_t draft_dtype;    /* sv_dtype of draft_probs */
   int32_t draft_is_probs; /* 0: draft rows are logits (softmax at T_b);
                              1: draft rows are normalized probabilities */
   int32_t device;         /* HIP device ordinal */
   int32_t chunk_elems;    /* vocabulary elements per work chunk; 0 picks a
-                             default; else a multiple of 64 in [256, 16384] */
+                             default; else a multiple of 64 in [256, 15360]
+                             (raised to ceil(V / 64) if smaller) */
 } sv_config;
 
 /* Creates a handle on cfg->device and allocates its workspace.

@@ -159,14 +159,15 @@ def _dtype_code(a):
 
 def verify(target, draft, draft_ids, num_drafts, temperatures, *,
            draft_mode=None, draft_is_probs=False, seed=0, offset=0,
-           u_acc=None, u_rec=None):
+           u_acc=None, u_rec=None, diagnostics=True):
     """Run the oracle on host arrays.
 
     target: [B, K+1, V] float32, or uint16 holding bf16 bits.
     draft:  [B, K, V] (same convention) or None for all one-hot.
     Uniforms come from Philox(seed, offset) unless u_acc/u_rec ([B, K+1])
     are given.  Returns a dict with tokens, num_accepted, p, q, margin_acc,
-    margin_rec and flags.
+    margin_rec and flags; with diagnostics=False only tokens, num_accepted
+    and flags are computed.
     """
     target = np.ascontiguousarray(target)
     B, K1, V = target.shape
@@ -190,8 +191,11 @@ def verify(target, draft, draft_ids, num_drafts, temperatures, *,
             _dtype_code(draft) if draft is not None else F32, _ptr(draft),
             int(bool(draft_is_probs)), _ptr(mode), _ptr(ids), _ptr(nd),
             _ptr(temps)]
-    tail = [_ptr(tokens), _ptr(nacc), _ptr(p), _ptr(q), _ptr(macc),
-            _ptr(mrec)]
+    if diagnostics:
+        tail = [_ptr(tokens), _ptr(nacc), _ptr(p), _ptr(q), _ptr(macc),
+                _ptr(mrec)]
+    else:
+        tail = [_ptr(tokens), _ptr(nacc), None, None, None, None]
     if u_acc is not None or u_rec is not None:
         ua = np.ascontiguousarray(u_acc, dtype=np.float64).reshape(B, K + 1)
         ur = np.ascontiguousarray(u_rec, dtype=np.float64).reshape(B, K + 1)

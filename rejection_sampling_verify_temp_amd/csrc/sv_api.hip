@@ -27,24 +27,23 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int elt_bytes(int dt) { return dt == SV_BF16 ? 2 : 4; }
 
-// Chunk length: about 32 KiB of the wider input per workgroup, balanced so
-// the chunks of a row are of near-equal length, a multiple of 64 elements,
-// and small enough for the draw kernel to hold one chunk in LDS.
-int pick_chunk(const sv_config& c, int lds_cap_elems) {
+// Chunk length: about 32 KiB of the wider input per workgroup, at least
+// V / 64 (a request's chunks are combined one per lane), balanced so the
+// chunks of a row are of near-equal length, a multiple of 64 elements.
+int pick_chunk(const sv_config& c) {
   int want = c.chunk_elems;
   if (want == 0) {
     const int wide = elt_bytes(c.target_dtype) > elt_bytes(c.draft_dtype)
                          ? elt_bytes(c.target_dtype) : elt_bytes(c.draft_dtype);
     want = 32768 / wide;
   }
-  if (want > lds_cap_elems) want = lds_cap_elems;
   const int V = c.vocab;
   int n = (V + want - 1) / want;
   if (n > sv::kMaxChunks) n = sv::kMaxChunks;
   int ch = (V + n - 1) / n;
   ch = ((ch + 63) / 64) * 64;
   if (ch < sv::kMinChunkElems) ch = sv::kMinChunkElems;
-  if (ch > lds_cap_elems) ch = lds_cap_elems;
+  if (ch > sv::kMaxChunkElems) ch = sv::kMaxChunkElems;
   return ch;
 }
 
@@ -120,7 +119,7 @@ int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
   if (cfg == nullptr) return SV_ERR_INVALID_ARG;
   const sv_config c = *cfg;
   if (c.max_batch < 1 || c.max_drafts < 0 || c.max_drafts > sv::kMaxDrafts ||
-      c.vocab < 1 || c.vocab > (1 << 24) || c.device < 0)
+      c.vocab < 1 || c.vocab > sv::kMaxVocab || c.device < 0)
     return SV_ERR_INVALID_ARG;
   if ((c.target_dtype != SV_F32 && c.target_dtype != SV_BF16) ||
       (c.draft_dtype != SV_F32 && c.draft_dtype != SV_BF16) ||
@@ -133,14 +132,7 @@ int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
 
   DeviceGuard g(c.device);
   if (!g.ok) return SV_ERR_HIP;
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, c.device) != hipSuccess) return SV_ERR_HIP;
-  // the draw kernel keeps one chunk of floats in LDS next to ~5 KiB of its own
-  int lds_cap = (int)((prop.sharedMemPerBlock - 8192) / sizeof(float));
-  lds_cap = (lds_cap / 64) * 64;
-  if (lds_cap > sv::kMaxChunkElems) lds_cap = sv::kMaxChunkElems;
-  if (lds_cap < sv::kMinChunkElems) return SV_ERR_UNSUPPORTED;
-  const int chunk = pick_chunk(c, lds_cap);
+  const int chunk = pick_chunk(c);
   const int nchunk = (c.vocab + chunk - 1) / chunk;
   if (nchunk > sv::kMaxChunks) return SV_ERR_UNSUPPORTED;
 

@@ -8,13 +8,12 @@
 
 namespace sv {
 
-constexpr int kStatsThreads = 256;   // row-statistics and residual-sum workgroups
-constexpr int kDecideThreads = 64;   // one wavefront per request
-constexpr int kLocateThreads = 512;  // one workgroup per request draw
-constexpr int kMaxChunkElems = 16384;
+constexpr int kThreads = 256;        // every workgroup: four wavefronts
+constexpr int kMaxChunkElems = 15360; // the draw stages one chunk of floats in LDS
 constexpr int kMinChunkElems = 256;
-constexpr int kMaxChunks = 1024;
-constexpr int kMaxDrafts = 63;       // positions 0..K fit one wavefront
+constexpr int kMaxChunks = 64;     // one lane per chunk when a request is combined
+constexpr int kMaxVocab = kMaxChunks * kMaxChunkElems;
+constexpr int kMaxDrafts = 31;       // the 2K+1 row slots fit one wavefront
 
 // Per (row, vocabulary chunk) statistics.  Sampling rows: m = chunk max,
 // z = sum over the chunk of exp2(l_i * c + ref(m, c)).  Greedy rows: m =

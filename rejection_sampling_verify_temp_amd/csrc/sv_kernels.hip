@@ -1,18 +1,21 @@
 // HIP kernels of the speculative-sampling verify step for gfx950 (CDNA4).
 //
 // One step is four launches on the caller's stream:
-//   1. row_stats   streams every needed logits row once, split into
-//                  vocabulary chunks: per chunk the max and the sum of
-//                  exp2(l * c + ref) (sampling rows) or the max and its lowest
-//                  index (greedy rows).  HBM-bound; this is the hot loop.
-//   2. decide      one wavefront per request, one lane per drafted position:
-//                  combines the chunk partials, draws the Philox uniforms,
-//                  forms p(x)/q(x) in fp64, ballots the accept bits and takes
-//                  the first rejection with a count-trailing-zeros.
-//   3. resid_sums  for requests rejected on a probabilistic draft: per chunk
-//                  the sum of max(0, p - q) over the rejected row pair.
-//   4. locate      one workgroup per sampling request: prefix over the chunk
-//                  sums, then an LDS scan of the one chunk holding u * S.
+//   1. stats   streams every needed logits row once, split into vocabulary
+//              chunks: per chunk the max and the sum of exp2(l * c + ref)
+//              (sampling rows) or the max and its lowest index (greedy rows).
+//              HBM-bound; this is the hot loop.
+//   2. decide  one wavefront per request: lane s folds the chunk partials
+//              of row slot s; then lane j draws the Philox uniforms of
+//              position j, forms p(x)/q(x) in fp64, a ballot of the accept
+//              bits gives the first rejection by count-trailing-zeros, and
+//              the outputs and a draw descriptor are written.
+//   3. resid   requests rejected on a probabilistic draft: per chunk the sum
+//              of max(0, p - q) over that row pair.
+//   4. locate  one workgroup per sampling request: a prefix over the chunk
+//              sums finds the chunk holding u * S; each thread takes 64
+//              consecutive residuals of it in registers, and a workgroup
+//              scan of the segment sums finds the token.
 //
 // Method (page title, section): "深入推测解码：从概念到实现" 保证原始分布
 // (accept with min(1, p/q), resample from max(0, p - q)); "RTP-LLM
@@ -300,6 +303,16 @@ __device__ void block_argmax(float& m, int& i, float* ldsm, int* ldsi) {
   __syncthreads();
 }
 
+
+__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Chunk streaming
 // ---------------------------------------------------------------------------
@@ -318,11 +331,11 @@ __device__ __forceinline__ SmAcc chunk_softmax_stats(const void* row, int c0, in
   }
   const u32x4* vp = reinterpret_cast<const u32x4*>(
       static_cast<const char*>(row) + (size_t)g.v0 * E::kBytes);
-  for (int v = tid; v < g.nvec; v += kStatsThreads * kUnroll) {
+  for (int v = tid; v < g.nvec; v += kThreads * kUnroll) {
     u32x4 d[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int vi = v + u * kStatsThreads;
+      const int vi = v + u * kThreads;
       d[u] = vi < g.nvec ? __builtin_nontemporal_load(vp + vi) : E::neg_inf();
     }
     float x[kN];
@@ -351,11 +364,11 @@ __device__ __forceinline__ AmAcc chunk_argmax(const void* row, int c0, int c1) {
   }
   const u32x4* vp = reinterpret_cast<const u32x4*>(
       static_cast<const char*>(row) + (size_t)g.v0 * E::kBytes);
-  for (int v = tid; v < g.nvec; v += kStatsThreads * kUnroll) {
+  for (int v = tid; v < g.nvec; v += kThreads * kUnroll) {
     u32x4 d[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int vi = v + u * kStatsThreads;
+      const int vi = v + u * kThreads;
       d[u] = vi < g.nvec ? __builtin_nontemporal_load(vp + vi) : E::neg_inf();
     }
     float x[kN];
@@ -363,7 +376,7 @@ __device__ __forceinline__ AmAcc chunk_argmax(const void* row, int c0, int c1) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       E::unpack(d[u], x + u * E::kVec);
-      const int vi = v + u * kStatsThreads;
+      const int vi = v + u * kThreads;
 #pragma unroll
       for (int e = 0; e < E::kVec; ++e)
         ix[u * E::kVec + e] = vi < g.nvec ? g.v0 + vi * E::kVec + e : INT32_MAX;
@@ -381,24 +394,28 @@ __device__ __forceinline__ AmAcc chunk_argmax(const void* row, int c0, int c1) {
 // Reduce a workgroup's softmax accumulators to (chunk max, chunk sum relative
 // to ref_of(chunk max)).  The rescale of each thread's sum is exact in fp64
 // up to the final rounding of exp2.
-__device__ __forceinline__ void reduce_softmax(const SmAcc& a, float c, float* ldsf, double* ldsd,
-                               float* m_out, double* z_out) {
-  const float m = block_max<kStatsThreads>(a.M, ldsf);
+__device__ __forceinline__ void reduce_softmax(const SmAcc& a, float c, float* ldsf,
+                                               double* ldsd, float* m_out, double* z_out) {
+  const float m = block_max<kThreads>(a.M, ldsf);
   double contrib = 0.0;
   if (a.S != 0.f && m != kNegInf)
     contrib = (double)a.S * exp2((double)ref_of(m, c) - (double)a.R);
-  const double z = block_sum<kStatsThreads>(contrib, ldsd);
+  const double z = block_sum<kThreads>(contrib, ldsd);
   *m_out = m;
   *z_out = z;
 }
 
-// Which rows a request needs.  Slots 0..K are target rows j = slot, slots
-// K+1..2K are draft rows j = slot - K - 1.
+// ---------------------------------------------------------------------------
+// Requests
+// ---------------------------------------------------------------------------
+// Row slots of request b: 0..K are target rows j = slot, K+1..2K draft rows
+// j = slot - K - 1.
 struct ReqInfo {
-  int n;
+  int n;             // drafts, clamped into [0, K]
   float T;
-  bool sampling;
-  bool onehot;
+  bool sampling;     // else greedy
+  bool onehot;       // no draft distribution
+  bool draft_stats;  // draft rows are logits whose softmax is needed
 };
 
 __device__ __forceinline__ ReqInfo req_info(const RunParams& p, int b) {
@@ -407,186 +424,153 @@ __device__ __forceinline__ ReqInfo req_info(const RunParams& p, int b) {
   r.T = p.temps[b];
   r.sampling = is_sampling(r.T);
   r.onehot = !p.has_draft || (p.mode != nullptr && p.mode[b] != 0);
+  r.draft_stats = r.sampling && !r.onehot && !p.draft_is_probs;
   return r;
 }
 
-// ---------------------------------------------------------------------------
-// Kernel 1: row statistics
-// ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ void row_stats_body(const void* row, int c0, int c1, const ReqInfo& ri,
-                               Partial* out) {
-  __shared__ float ldsf[kStatsThreads / 64];
-  __shared__ double ldsd[kStatsThreads / 64];
-  __shared__ int ldsi[kStatsThreads / 64];
-  Partial r;
-  if (ri.sampling) {
-    const float c = temp_scale(ri.T);
-    const SmAcc a = chunk_softmax_stats<DT>(row, c0, c1, c);
-    reduce_softmax(a, c, ldsf, ldsd, &r.m, &r.z);
-    r.idx = -1;
-  } else {
-    AmAcc a = chunk_argmax<DT>(row, c0, c1);
-    block_argmax<kStatsThreads>(a.M, a.I, ldsf, ldsi);
-    r.m = a.M;
-    r.idx = a.I == INT32_MAX ? c0 : a.I;
-    r.z = 0.0;
-  }
-  if (threadIdx.x == 0) *out = r;
+__device__ __forceinline__ bool slot_needed(const ReqInfo& r, int s, int K) {
+  return s <= K ? s <= r.n : (s - K - 1 < r.n && r.draft_stats);
 }
 
+__device__ __forceinline__ int rows_needed(const ReqInfo& r) {
+  return r.n + 1 + (r.draft_stats ? r.n : 0);
+}
+
+// ---------------------------------------------------------------------------
+// Decisions of one request (one wavefront)
+// ---------------------------------------------------------------------------
+// Lane = vocabulary chunk while combining a row; lane = drafted position j
+// afterwards.  Lane j keeps the combined target row j and draft row j.  The
+// draw descriptor goes to *d_out (shared memory); with `outputs` the accepted
+// tokens, counts, debug probabilities, greedy tokens and the descriptor in
+// global memory are written too.  Every workgroup of the residual kernel
+// runs this for its request (the combine reads a few hundred bytes), so the
+// decisions need no hand-off between workgroups.
 template <int TDT, int DDT>
-__global__ __launch_bounds__(kStatsThreads) void k_row_stats(const RunParams p) {
-  const int nslot = 2 * p.K + 1;
-  const int bid = blockIdx.x;
-  const int row = bid / p.nchunk, chunk = bid - row * p.nchunk;
-  const int b = row / nslot, s = row - b * nslot;
-  const ReqInfo ri = req_info(p, b);
-  const int c0 = chunk * p.chunk;
-  const int c1 = min(p.V, c0 + p.chunk);
-  Partial* out = p.part + (size_t)row * p.nchunk + chunk;
-  if (s <= p.K) {
-    if (s > ri.n) return;
-    const void* r = row_ptr(p.target, TDT, (size_t)b * (p.K + 1) + s, p.V);
-    row_stats_body<TDT>(r, c0, c1, ri, out);
-  } else {
-    const int j = s - p.K - 1;
-    if (j >= ri.n || !ri.sampling || ri.onehot || p.draft_is_probs) return;
-    const void* r = row_ptr(p.draft, DDT, (size_t)b * p.K + j, p.V);
-    row_stats_body<DDT>(r, c0, c1, ri, out);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 2: decisions
-// ---------------------------------------------------------------------------
-// Combine the chunk partials of a sampling row: reference of the row max and
-// the row total relative to it.
-__device__ void combine_softmax(const Partial* part, int nchunk, float c,
-                                float* ref_out, double* z_out) {
-  float m = kNegInf;
-  for (int k = 0; k < nchunk; ++k) m = fmaxf(m, part[k].m);
-  const float ref = ref_of(m, c);
-  double z = 0.0;
-  for (int k = 0; k < nchunk; ++k)
-    if (part[k].z != 0.0)
-      z += part[k].z * exp2((double)ref - (double)ref_of(part[k].m, c));
-  *ref_out = ref;
-  *z_out = z;
-}
-
-// Greedy row: max and lowest index attaining it (chunks are in index order).
-__device__ void combine_argmax(const Partial* part, int nchunk, float* m_out,
-                               int* i_out) {
-  float m = part[0].m;
-  int i = part[0].idx;
-  for (int k = 1; k < nchunk; ++k)
-    if (part[k].m > m) {
-      m = part[k].m;
-      i = part[k].idx;
-    }
-  *m_out = m;
-  *i_out = i;
-}
-
-__device__ __forceinline__ double prob_of(float l, float c, float ref, double z) {
-  return exp2((double)l * (double)c + (double)ref) / z;
-}
-
-template <int TDT, int DDT>
-__global__ __launch_bounds__(kDecideThreads) void k_decide(const RunParams p) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int K = p.K, V = p.V, nslot = 2 * K + 1;
-  const int nraw = p.nd[b];
-  const ReqInfo ri = req_info(p, b);
-  const int n = ri.n;
-  if (lane == 0 && nraw != n) atomicOr(p.flags, SV_DEVERR_BAD_NUM_DRAFTS);
+__device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, bool outputs,
+                               DrawDesc* d_out) {
+  const int K = p.K, V = p.V, nslot = 2 * K + 1, n = ri.n;
+  const int lane = threadIdx.x & 63;
   const float c = ri.sampling ? temp_scale(ri.T) : 0.f;
-  const Partial* part_b = p.part + (size_t)b * nslot * p.nchunk;
 
-  // Decision of position j = lane.
-  const int j = lane;
+  // values of the drafted tokens (loads issued before the combine)
+  int x = -1;
+  float lt = __builtin_nanf(""), ld = __builtin_nanf("");
+  if (lane < n) {
+    x = p.ids[(size_t)b * K + lane];
+    if (x >= 0 && x < V) {
+      lt = load_elem(p.target, TDT, (size_t)b * (K + 1) + lane, V, x);
+      if (ri.sampling && !ri.onehot) ld = load_elem(p.draft, DDT, (size_t)b * K + lane, V, x);
+    }
+  }
+
+  // combine: lane s owns row slot s (target rows 0..K, draft rows K+1..2K)
+  // and folds its chunk partials sequentially, so no cross-lane traffic
+  float r_ref = 0.f;  // sampling: exponent reference; greedy: row max
+  double r_z = 0.0;   // sampling: row total relative to the reference
+  int r_idx = 0;      // greedy: lowest index of the max
+  if (lane < nslot && slot_needed(ri, lane, K)) {
+    const Partial* pr = p.part + ((size_t)b * nslot + lane) * p.nchunk;
+    constexpr int kBatch = 16;  // partial loads in flight per lane
+    float m = kNegInf;
+    int im = INT32_MAX;
+    for (int k0 = 0; k0 < p.nchunk; k0 += kBatch) {
+      Partial q[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) q[u] = pr[min(k0 + u, p.nchunk - 1)];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (k0 + u < p.nchunk && q[u].m > m) {  // chunks ascend: first max wins
+          m = q[u].m;
+          im = q[u].idx;
+        }
+    }
+    if (ri.sampling) {
+      r_ref = ref_of(m, c);
+      for (int k0 = 0; k0 < p.nchunk; k0 += kBatch) {
+        Partial q[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) q[u] = pr[min(k0 + u, p.nchunk - 1)];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (k0 + u < p.nchunk && q[u].z != 0.0)
+            r_z += q[u].z * exp2((double)r_ref - (double)ref_of(q[u].m, c));
+      }
+    } else {
+      r_ref = m;
+      r_idx = im == INT32_MAX ? 0 : im;
+    }
+  }
+  // lane j gathers its target row (own) and its draft row (lane K + 1 + j)
+  const float t_ref = r_ref;
+  const double t_z = r_z;
+  const int t_idx = r_idx;
+  const int dl = min(K + 1 + lane, 63);
+  const float d_ref = __shfl(r_ref, dl, 64);
+  const double d_z = __shfl(r_z, dl, 64);
+
+  // decision of position j = lane
   bool accept = false;
   float dbg_p = __builtin_nanf(""), dbg_q = __builtin_nanf("");
-  if (j < n) {
-    const int x = p.ids[(size_t)b * K + j];
+  if (lane < n) {
     const bool valid = x >= 0 && x < V;
-    if (!valid) atomicOr(p.flags, SV_DEVERR_BAD_DRAFT_ID);
-    const Partial* pt = part_b + (size_t)j * p.nchunk;
-    const size_t trow = (size_t)b * (K + 1) + j;
+    if (!valid && outputs) atomicOr(p.flags, SV_DEVERR_BAD_DRAFT_ID);
     if (!ri.sampling) {
-      float m;
-      int im;
-      combine_argmax(pt, p.nchunk, &m, &im);
-      accept = valid && load_elem(p.target, TDT, trow, V, x) == m;
-    } else {
-      float ref_p;
-      double z_p;
-      combine_softmax(pt, p.nchunk, c, &ref_p, &z_p);
-      const double px = valid ? prob_of(load_elem(p.target, TDT, trow, V, x), c, ref_p, z_p) : 0.0;
+      accept = valid && lt == t_ref;
+    } else if (valid) {
+      const double px = exp2((double)lt * (double)c + (double)t_ref) / t_z;
       double qx = 1.0;
       if (!ri.onehot) {
-        const size_t drow = (size_t)b * K + j;
-        if (p.draft_is_probs) {
-          qx = valid ? (double)load_elem(p.draft, DDT, drow, V, x) : 0.0;
-        } else {
-          float ref_q;
-          double z_q;
-          combine_softmax(part_b + (size_t)(K + 1 + j) * p.nchunk, p.nchunk, c, &ref_q, &z_q);
-          qx = valid ? prob_of(load_elem(p.draft, DDT, drow, V, x), c, ref_q, z_q) : 0.0;
-        }
+        if (p.draft_is_probs)
+          qx = (double)ld;
+        else
+          qx = exp2((double)ld * (double)c + (double)d_ref) / d_z;
       }
       double ratio;
-      if (!valid) ratio = 0.0;
-      else if (qx > 0.0) ratio = px / qx;
+      if (qx > 0.0) ratio = px / qx;
       else ratio = px > 0.0 ? __builtin_inf() : 0.0;
       double u_acc, u_rec;
-      uniforms(p.seed, p.offset, b, j, &u_acc, &u_rec);
+      uniforms(p.seed, p.offset, b, lane, &u_acc, &u_rec);
       accept = u_acc < ratio;
-      dbg_p = valid ? (float)px : dbg_p;
-      dbg_q = valid ? (float)qx : dbg_q;
+      dbg_p = (float)px;
+      dbg_q = (float)qx;
     }
   }
-  // First rejection: lanes >= n vote false, so ~mask has a bit at n or below.
+  // first rejection: lanes >= n vote false, so ~mask has a bit at n or below
   const uint64_t mask = __ballot(accept);
   const int first_rej = (int)__builtin_ctzll(~mask);
   const int n_acc = first_rej < n ? first_rej : n;
 
-  // Outputs other than the emitted token.
-  if (lane <= K && lane != n_acc) {
-    const int32_t tok = lane < n_acc ? p.ids[(size_t)b * K + lane] : -1;
-    p.out_tokens[(size_t)b * (K + 1) + lane] = tok;
+  if (outputs && lane <= K && lane != n_acc)
+    p.out_tokens[(size_t)b * (K + 1) + lane] = lane < n_acc ? x : -1;
+  if (outputs && lane == 0) {
+    p.out_nacc[b] = n_acc;
+    if (p.nd[b] != n) atomicOr(p.flags, SV_DEVERR_BAD_NUM_DRAFTS);
   }
-  if (lane == 0) p.out_nacc[b] = n_acc;
-  if (p.out_dbg != nullptr && lane < K) {
+  if (outputs && p.out_dbg != nullptr && lane < K) {
     p.out_dbg[((size_t)b * K + lane) * 2 + 0] = dbg_p;
     p.out_dbg[((size_t)b * K + lane) * 2 + 1] = dbg_q;
   }
 
-  // The emitted position: greedy writes its argmax now, sampling requests
-  // leave a draw descriptor for the locate kernel.
+  // the emitted position: greedy writes its argmax, sampling requests leave a
+  // draw descriptor for the residual kernel
   if (lane == n_acc) {
     const int je = n_acc;
-    const Partial* pt = part_b + (size_t)je * p.nchunk;
     DrawDesc d{};
     d.j = je;
     d.x = -1;
     if (!ri.sampling) {
-      float m;
-      int im;
-      combine_argmax(pt, p.nchunk, &m, &im);
-      p.out_tokens[(size_t)b * (K + 1) + je] = im;
+      if (outputs) p.out_tokens[(size_t)b * (K + 1) + je] = t_idx;
       d.kind = kDrawNone;
     } else {
       d.c = c;
-      combine_softmax(pt, p.nchunk, c, &d.ref_p, &d.z_p);
+      d.ref_p = t_ref;
+      d.z_p = t_z;
       double u_acc, u_rec;
       uniforms(p.seed, p.offset, b, je, &u_acc, &u_rec);
       d.u = u_rec;
       d.kind = kDrawSingle;
       if (je < n) {  // rejected at je
-        const int x = p.ids[(size_t)b * K + je];
         d.x = (x >= 0 && x < V) ? x : -1;
         if (!ri.onehot) {
           d.kind = kDrawPair;
@@ -595,25 +579,61 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(const RunParams p) {
             d.ref_q = 0.f;
             kap = d.z_p;  // p - q = (p~ - Z_p q) / Z_p
           } else {
-            double z_q;
-            combine_softmax(part_b + (size_t)(K + 1 + je) * p.nchunk, p.nchunk, c, &d.ref_q, &z_q);
-            kap = d.z_p / z_q;  // p - q = (p~ - (Z_p / Z_q) q~) / Z_p
+            d.ref_q = d_ref;
+            kap = d.z_p / d_z;  // p - q = (p~ - (Z_p / Z_q) q~) / Z_p
           }
           d.kap_hi = (float)kap;
           d.kap_lo = (float)(kap - (double)d.kap_hi);
         }
       }
     }
-    p.desc[b] = d;
+    *d_out = d;
+    if (outputs) p.desc[b] = d;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1: row statistics
+// ---------------------------------------------------------------------------
+template <int TDT, int DDT>
+__global__ __launch_bounds__(kThreads) void k_stats(const RunParams p) {
+  __shared__ float ldsf[kThreads / 64];
+  __shared__ double ldsd[kThreads / 64];
+  __shared__ int ldsi[kThreads / 64];
+  const int nslot = 2 * p.K + 1;
+  const int bid = blockIdx.x;
+  const int row = bid / p.nchunk, chunk = bid - row * p.nchunk;
+  const int b = row / nslot, s = row - b * nslot;
+  const ReqInfo ri = req_info(p, b);
+  if (!slot_needed(ri, s, p.K)) return;
+  const int c0 = chunk * p.chunk;
+  const int c1 = min(p.V, c0 + p.chunk);
+  const bool is_target = s <= p.K;
+  const void* r = is_target ? row_ptr(p.target, TDT, (size_t)b * (p.K + 1) + s, p.V)
+                            : row_ptr(p.draft, DDT, (size_t)b * p.K + (s - p.K - 1), p.V);
+  Partial out;
+  if (ri.sampling) {
+    const float c = temp_scale(ri.T);
+    const SmAcc a = is_target ? chunk_softmax_stats<TDT>(r, c0, c1, c)
+                              : chunk_softmax_stats<DDT>(r, c0, c1, c);
+    reduce_softmax(a, c, ldsf, ldsd, &out.m, &out.z);
+    out.idx = -1;
+  } else {  // greedy rows are target rows
+    AmAcc a = chunk_argmax<TDT>(r, c0, c1);
+    block_argmax<kThreads>(a.M, a.I, ldsf, ldsi);
+    out.m = a.M;
+    out.idx = a.I == INT32_MAX ? c0 : a.I;
+    out.z = 0.0;
+  }
+  if (threadIdx.x == 0) p.part[(size_t)row * p.nchunk + chunk] = out;
 }
 
 // ---------------------------------------------------------------------------
 // Residual elements (unnormalized, relative to the draw descriptor)
 // ---------------------------------------------------------------------------
 // Pair: r~ = max(0, p~ - kappa q~) with p~ = exp2(l_p c + ref_p) and q~ =
-// exp2(l_q c + ref_q) (or q itself for probability drafts); the split kappa
-// keeps the difference accurate to the rounding of p~ and q~.
+// exp2(l_q c + ref_q) (or q itself for probability drafts); kappa split in
+// two floats keeps the difference accurate to the rounding of p~ and q~.
 __device__ __forceinline__ float pair_resid(float lp, float lq, const DrawDesc& d,
                                             bool probs) {
   const float pt = fast_exp2(fmaf(lp, d.c, d.ref_p));
@@ -627,286 +647,288 @@ __device__ __forceinline__ float single_resid(float lp, const DrawDesc& d) {
   return fast_exp2(fmaf(lp, d.c, d.ref_p));
 }
 
-// ---------------------------------------------------------------------------
-// Kernel 3: per-chunk sums of max(0, p - q) for rejected probabilistic drafts
-// ---------------------------------------------------------------------------
+// Eight consecutive elements from a 16-byte aligned address.
+template <int DT>
+__device__ __forceinline__ void load8(const void* row, int i, float* x) {
+  const u32x4* v = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
+                                                  (size_t)i * Elt<DT>::kBytes);
+  if (DT == SV_BF16) {
+    Elt<SV_BF16>::unpack(__builtin_nontemporal_load(v), x);
+  } else {
+    Elt<SV_F32>::unpack(__builtin_nontemporal_load(v), x);
+    Elt<SV_F32>::unpack(__builtin_nontemporal_load(v + 1), x + 4);
+  }
+}
+
+// Sum over [c0, c1) of max(0, p~ - kappa q~), token x excluded.
 template <int TDT, int DDT>
-__global__ __launch_bounds__(kStatsThreads) void k_resid_sums(const RunParams p) {
-  __shared__ double ldsd[kStatsThreads / 64];
-  const int bid = blockIdx.x;
-  const int b = bid / p.nchunk, chunk = bid - b * p.nchunk;
-  const DrawDesc d = p.desc[b];
-  if (d.kind != kDrawPair) return;
-  const int K = p.K, V = p.V;
-  const void* prow = row_ptr(p.target, TDT, (size_t)b * (K + 1) + d.j, V);
-  const void* qrow = row_ptr(p.draft, DDT, (size_t)b * K + d.j, V);
-  const bool probs = p.draft_is_probs != 0;
-  const int c0 = chunk * p.chunk, c1 = min(V, c0 + p.chunk);
+__device__ __forceinline__ double pair_chunk_sum(const void* prow, const void* qrow, int c0,
+                                                 int c1, const DrawDesc& d, bool probs,
+                                                 double* ldsd) {
+  constexpr int kGroups = 4;  // groups of eight elements per thread per step
   const int tid = threadIdx.x;
   float acc = 0.f;
   const uintptr_t pa = reinterpret_cast<uintptr_t>(prow) + (uintptr_t)c0 * Elt<TDT>::kBytes;
   const uintptr_t qa = reinterpret_cast<uintptr_t>(qrow) + (uintptr_t)c0 * Elt<DDT>::kBytes;
-  const bool aligned = ((pa | qa) & 15u) == 0;
   int done = c0;
-  if (aligned) {
-    // groups of 8 elements: one or two 16-byte loads per row
+  if (((pa | qa) & 15u) == 0) {
     const int ngrp = (c1 - c0) / 8;
-    for (int g = tid; g < ngrp; g += kStatsThreads) {
-      const int i0 = c0 + g * 8;
-      float lp[8], lq[8];
-      if (TDT == SV_BF16) {
-        Elt<SV_BF16>::unpack(__builtin_nontemporal_load(
-                                 reinterpret_cast<const u32x4*>(static_cast<const char*>(prow) + (size_t)i0 * 2)),
-                             lp);
-      } else {
-        const u32x4* v = reinterpret_cast<const u32x4*>(static_cast<const char*>(prow) + (size_t)i0 * 4);
-        Elt<SV_F32>::unpack(__builtin_nontemporal_load(v), lp);
-        Elt<SV_F32>::unpack(__builtin_nontemporal_load(v + 1), lp + 4);
-      }
-      if (DDT == SV_BF16) {
-        Elt<SV_BF16>::unpack(__builtin_nontemporal_load(
-                                 reinterpret_cast<const u32x4*>(static_cast<const char*>(qrow) + (size_t)i0 * 2)),
-                             lq);
-      } else {
-        const u32x4* v = reinterpret_cast<const u32x4*>(static_cast<const char*>(qrow) + (size_t)i0 * 4);
-        Elt<SV_F32>::unpack(__builtin_nontemporal_load(v), lq);
-        Elt<SV_F32>::unpack(__builtin_nontemporal_load(v + 1), lq + 4);
-      }
-      float e[8];
+    for (int g = tid; g < ngrp; g += kThreads * kGroups) {
+      float lp[kGroups][8], lq[kGroups][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) e[k] = (i0 + k == d.x) ? 0.f : pair_resid(lp[k], lq[k], d, probs);
-      acc += pairwise_sum(e);
+      for (int u = 0; u < kGroups; ++u) {  // clamped: every load in bounds
+        const int gi = min(g + u * kThreads, ngrp - 1);
+        load8<TDT>(prow, c0 + gi * 8, lp[u]);
+        load8<DDT>(qrow, c0 + gi * 8, lq[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) {
+        const int gi = g + u * kThreads;
+        float e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = c0 + gi * 8 + k;
+          e[k] = (gi < ngrp && i != d.x) ? pair_resid(lp[u][k], lq[u][k], d, probs) : 0.f;
+        }
+        acc += pairwise_sum(e);
+      }
     }
     done = c0 + ngrp * 8;
   }
-  for (int i = done + tid; i < c1; i += kStatsThreads) {
-    const float r = (i == d.x) ? 0.f
-                               : pair_resid(Elt<TDT>::at(prow, i), Elt<DDT>::at(qrow, i), d, probs);
-    acc += r;
-  }
-  const double s = block_sum<kStatsThreads>((double)acc, ldsd);
-  if (tid == 0) p.rsum[(size_t)b * p.nchunk + chunk] = s;
+  for (int i = done + tid; i < c1; i += kThreads)
+    if (i != d.x) acc += pair_resid(Elt<TDT>::at(prow, i), Elt<DDT>::at(qrow, i), d, probs);
+  return block_sum<kThreads>((double)acc, ldsd);
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 4: inverse-CDF draw of the emitted token
+// Inverse-CDF draw of the emitted token (one workgroup)
 // ---------------------------------------------------------------------------
-// Sum of chunk k of the draw law, from the first-pass partials (single) or
-// the residual sums (pair).
-__device__ double chunk_mass(const RunParams& p, const DrawDesc& d, int b, int k,
-                             int kind, double excl_mass, int excl_chunk) {
-  if (kind == kDrawPair) return p.rsum[(size_t)b * p.nchunk + k];
-  const Partial& q = p.part[((size_t)b * (2 * p.K + 1) + d.j) * p.nchunk + k];
-  double s = 0.0;
-  if (q.z != 0.0) s = q.z * exp2((double)d.ref_p - (double)ref_of(q.m, d.c));
-  if (k == excl_chunk) s -= excl_mass;
-  return s > 0.0 ? s : 0.0;
+// Residual of element i from its loaded logits (lp target, lq draft).
+__device__ __forceinline__ float resid_of(float lp, float lq, int kind, int i, int excl,
+                                          const DrawDesc& d, bool probs) {
+  const float r = kind == kDrawPair ? pair_resid(lp, lq, d, probs) : single_resid(lp, d);
+  return i == excl ? 0.f : r;
+}
+
+// Segment of kSeg consecutive elements per thread: with kThreads threads a
+// segment scan covers a whole chunk (kSeg * kThreads >= kMaxChunkElems).
+constexpr int kSeg = 64;
+static_assert(kSeg * kThreads >= kMaxChunkElems, "a chunk must fit the segments");
+
+// Logits of elements [i0, i0 + kSeg) of a row (i0 a multiple of kSeg; n of
+// them valid, the rest set to 0).  16-byte loads where the row allows.
+template <int DT>
+__device__ __forceinline__ void load_segment(const void* row, int i0, int n, float* x) {
+  using E = Elt<DT>;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(row) + (uintptr_t)i0 * E::kBytes;
+  if (n == kSeg && (a & 15u) == 0) {
+    const u32x4* v = reinterpret_cast<const u32x4*>(a);
+#pragma unroll
+    for (int k = 0; k < kSeg / E::kVec; ++k) E::unpack(v[k], x + k * E::kVec);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k) x[k] = E::at(row, i0 + min(k, max(n - 1, 0)));
+  }
 }
 
 template <int TDT, int DDT>
-__global__ __launch_bounds__(kLocateThreads) void k_locate(const RunParams p) {
-  extern __shared__ float lds_r[];  // chunk residuals, then scan scratch
-  __shared__ double sh_q[kLocateThreads + 1];
-  __shared__ double sh_wave[kLocateThreads / 64];
-  __shared__ int sh_cstar, sh_y, sh_last;
-  __shared__ double sh_theta;
-  __shared__ int sh_kind, sh_excl;
-
-  const int b = blockIdx.x;
-  const DrawDesc d = p.desc[b];
-  if (d.kind == kDrawNone) return;
-  const int K = p.K, V = p.V, tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+__device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
+  __shared__ int s_cstar, s_kind, s_excl, s_y, s_last;
+  __shared__ double s_theta;
+  __shared__ double s_woff[kThreads / 64];
+  const int K = p.K, V = p.V, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const size_t trow = (size_t)b * (K + 1) + d.j;
   const void* prow = row_ptr(p.target, TDT, trow, V);
   const void* qrow = d.kind == kDrawPair ? row_ptr(p.draft, DDT, (size_t)b * K + d.j, V) : nullptr;
   const bool probs = p.draft_is_probs != 0;
 
-  // --- chunk selection (wavefront 0) ---
+  // (a) the chunk holding u * S: wavefront 0, lane = chunk
   if (w == 0) {
-    int kind = d.kind;
-    double excl_mass = 0.0;
-    int excl_chunk = -1;
-    if (kind == kDrawSingle && d.x >= 0) {
-      excl_chunk = d.x / p.chunk;
-      excl_mass = exp2((double)load_elem(p.target, TDT, trow, V, d.x) * (double)d.c + (double)d.ref_p);
-    }
+    int kind = d.kind, excl = d.x;
     for (int attempt = 0; attempt < 2; ++attempt) {
-      const int per = (p.nchunk + 63) / 64;
-      const int k0 = lane * per, k1 = min(p.nchunk, k0 + per);
-      double tot = 0.0;
-      for (int k = k0; k < k1; ++k) tot += chunk_mass(p, d, b, k, kind, excl_mass, excl_chunk);
-      // inclusive scan of lane totals (Hillis-Steele, fixed order)
-      double incl = tot;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
+      double mass = 0.0;
+      if (lane < p.nchunk) {
+        if (kind == kDrawPair) {
+          mass = p.rsum[(size_t)b * p.nchunk + lane];
+        } else {
+          const Partial q = p.part[((size_t)b * (2 * K + 1) + d.j) * p.nchunk + lane];
+          if (q.z != 0.0) mass = q.z * exp2((double)d.ref_p - (double)ref_of(q.m, d.c));
+          if (excl >= 0 && excl / p.chunk == lane)
+            mass -= exp2((double)Elt<TDT>::at(prow, excl) * (double)d.c + (double)d.ref_p);
+        }
+        if (!(mass > 0.0)) mass = 0.0;
       }
+      const double incl = wave_incl_scan(mass, lane);
       const double S = __shfl(incl, 63, 64);
       if (!(S > 0.0) && attempt == 0) {  // no residual mass: draw from p
         if (lane == 0) atomicOr(p.flags, SV_DEVERR_ZERO_RESIDUAL);
         kind = kDrawSingle;
-        excl_chunk = -1;
-        excl_mass = 0.0;
+        excl = -1;
         continue;
       }
       const double theta = d.u * S;
-      const double before = incl - tot;  // exclusive prefix of this lane
-      int found = -1;
-      double th = 0.0;
-      if (before <= theta && tot > 0.0) {
-        double acc = before;
-        for (int k = k0; k < k1; ++k) {
-          const double s = chunk_mass(p, d, b, k, kind, excl_mass, excl_chunk);
-          if (s > 0.0 && acc + s > theta) {
-            found = k;
-            th = theta - acc;
-            break;
-          }
-          acc += s;
-        }
-      }
-      const uint64_t hit = __ballot(found >= 0);
-      int src = hit ? (int)__builtin_ctzll(hit) : -1;
+      double before = __shfl_up(incl, 1, 64);
+      if (lane == 0) before = 0.0;
+      const bool hit = mass > 0.0 && before <= theta && theta < incl;
+      const uint64_t hits = __ballot(hit);
       int cstar;
-      double thp;
-      if (src >= 0) {
-        cstar = __shfl(found, src, 64);
-        thp = __shfl(th, src, 64);
-      } else {
-        // rounding left theta at or past the total: last chunk with mass
-        int lastk = -1;
-        for (int k = k1 - 1; k >= k0; --k)
-          if (chunk_mass(p, d, b, k, kind, excl_mass, excl_chunk) > 0.0) {
-            lastk = k;
-            break;
-          }
-        const uint64_t has = __ballot(lastk >= 0);
-        const int srcl = has ? 63 - (int)__builtin_clzll(has) : 0;
-        cstar = __shfl(lastk, srcl, 64);
-        thp = __builtin_inf();
+      double th;
+      if (hits) {
+        const int src = (int)__builtin_ctzll(hits);
+        cstar = src;
+        th = theta - __shfl(before, src, 64);
+      } else {  // rounding left theta at or past the total: last chunk with mass
+        const uint64_t has = __ballot(mass > 0.0);
+        cstar = has ? 63 - (int)__builtin_clzll(has) : 0;
+        th = __builtin_inf();
         if (lane == 0) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
       }
       if (lane == 0) {
-        sh_cstar = cstar < 0 ? 0 : cstar;
-        sh_theta = thp;
-        sh_kind = kind;
-        sh_excl = attempt == 0 ? d.x : -1;  // the fallback draws from p whole
+        s_cstar = cstar;
+        s_theta = th;
+        s_kind = kind;
+        s_excl = excl;
+        s_y = INT32_MAX;
+        s_last = -1;
       }
       break;
-    }
-    if (lane == 0) {
-      sh_y = INT32_MAX;
-      sh_last = -1;
     }
   }
   __syncthreads();
 
-  // --- scan of the selected chunk ---
-  const int kind = sh_kind;
-  const int c0 = sh_cstar * p.chunk, c1 = min(V, c0 + p.chunk);
-  const int len = c1 - c0;
-  const int xr = sh_excl;
-  for (int i = tid; i < len; i += kLocateThreads) {
-    const int gi = c0 + i;
-    float r;
-    if (gi == xr) r = 0.f;
-    else if (kind == kDrawPair) r = pair_resid(Elt<TDT>::at(prow, gi), Elt<DDT>::at(qrow, gi), d, probs);
-    else r = single_resid(Elt<TDT>::at(prow, gi), d);
-    lds_r[i] = r;
-  }
-  __syncthreads();
-  const int per = (len + kLocateThreads - 1) / kLocateThreads;
-  const int s0 = min(len, tid * per), s1 = min(len, s0 + per);
-  double s = 0.0;
-  int lastpos = -1;
-  for (int i = s0; i < s1; ++i) {
-    s += (double)lds_r[i];
-    if (lds_r[i] > 0.f) lastpos = i;
-  }
-  // exclusive scan across the workgroup: wave scans + sequential wave offsets
-  double incl = s;
+  // (b) thread t owns chunk elements [t kSeg, t kSeg + kSeg): residuals in
+  // registers, their sum in fp64
+  const int kind = s_kind, excl = s_excl;
+  const int c0 = s_cstar * p.chunk;
+  const int len = min(V, c0 + p.chunk) - c0;
+  const int i0 = tid * kSeg;
+  const int nseg = max(0, min(kSeg, len - i0));
+  float r[kSeg];
+  {
+    float lp[kSeg];
+    load_segment<TDT>(prow, c0 + min(i0, len - 1), nseg, lp);
+    if (kind == kDrawPair) {
+      float lq[kSeg];
+      load_segment<DDT>(qrow, c0 + min(i0, len - 1), nseg, lq);
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) sh_wave[w] = incl;
-  __syncthreads();
-  if (tid == 0) {
-    double acc = 0.0;
-    for (int k = 0; k < kLocateThreads / 64; ++k) {
-      const double t = sh_wave[k];
-      sh_wave[k] = acc;
-      acc += t;
+      for (int k = 0; k < kSeg; ++k) r[k] = pair_resid(lp[k], lq[k], d, probs);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) r[k] = single_resid(lp[k], d);
     }
-    sh_q[kLocateThreads] = acc;
   }
+  double seg = 0.0;
+  int lastpos = -1;
+#pragma unroll
+  for (int k = 0; k < kSeg; ++k) {
+    if (k >= nseg || c0 + i0 + k == excl) r[k] = 0.f;
+    seg += (double)r[k];
+    if (r[k] > 0.f) lastpos = i0 + k;
+  }
+
+  // (c) exclusive scan of the segment sums
+  const double incl = wave_incl_scan(seg, lane);
+  if (lane == 63) s_woff[w] = incl;
+  double q = __shfl_up(incl, 1, 64);
+  if (lane == 0) q = 0.0;
+  if (lastpos >= 0) atomicMax(&s_last, lastpos);
   __syncthreads();
-  const double q = sh_wave[w] + (incl - s);
-  sh_q[tid] = q;
-  if (lastpos >= 0) atomicMax(&sh_last, lastpos);
-  __syncthreads();
-  const double qn = sh_q[tid + 1];
-  const double theta = sh_theta;
-  if (s1 > s0 && q <= theta && theta < qn) {
-    int y = -1, lp = -1;
+  for (int k = 0; k < w; ++k) q += s_woff[k];
+
+  // (d) the segment holding theta walks its registers
+  const double theta = s_theta;
+  if (seg > 0.0 && q <= theta && theta < q + seg) {
     double L = 0.0;
-    for (int i = s0; i < s1; ++i) {
-      const float r = lds_r[i];
-      L += (double)r;
-      if (r > 0.f) lp = i;
-      if (r > 0.f && q + L > theta) {
-        y = i;
-        break;
+    int y = -1, lp = -1;
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k) {
+      L += (double)r[k];
+      if (r[k] > 0.f) {
+        if (y < 0 && q + L > theta) y = i0 + k;
+        lp = i0 + k;
       }
     }
     if (y < 0) y = lp;  // rounding tie inside the segment
-    if (y >= 0) atomicMin(&sh_y, y);
+    atomicMin(&s_y, y);
   }
   __syncthreads();
   if (tid == 0) {
-    int y = sh_y;
-    if (y == INT32_MAX) {  // theta past the recomputed chunk total
-      y = sh_last >= 0 ? sh_last : 0;
+    int y = s_y;
+    if (y == INT32_MAX) {  // theta past the chunk's recomputed total
+      y = s_last >= 0 ? s_last : 0;
       if (theta != __builtin_inf()) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
     }
     p.out_tokens[(size_t)b * (K + 1) + d.j] = c0 + y;
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel 2: decisions (one wavefront per request)
+// ---------------------------------------------------------------------------
+template <int TDT, int DDT>
+__global__ __launch_bounds__(64) void k_decide(const RunParams p) {
+  __shared__ DrawDesc s_d;
+  const int b = blockIdx.x;
+  decide_request<TDT, DDT>(p, b, req_info(p, b), true, &s_d);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 3: residual chunk sums of requests rejected on a probabilistic draft
+// ---------------------------------------------------------------------------
+template <int TDT, int DDT>
+__global__ __launch_bounds__(kThreads) void k_resid(const RunParams p) {
+  __shared__ double ldsd[kThreads / 64];
+  const int bid = blockIdx.x;
+  const int rb = bid / p.nchunk, chunk = bid - rb * p.nchunk;
+  const int b = p.B - 1 - rb;  // the most recently streamed requests first
+  const DrawDesc d = p.desc[b];
+  if (d.kind != kDrawPair) return;
+  const int K = p.K, V = p.V;
+  const void* prow = row_ptr(p.target, TDT, (size_t)b * (K + 1) + d.j, V);
+  const void* qrow = row_ptr(p.draft, DDT, (size_t)b * K + d.j, V);
+  const int c0 = chunk * p.chunk, c1 = min(V, c0 + p.chunk);
+  const double s = pair_chunk_sum<TDT, DDT>(prow, qrow, c0, c1, d, p.draft_is_probs != 0, ldsd);
+  if (threadIdx.x == 0) p.rsum[(size_t)b * p.nchunk + chunk] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 4: the draw of every sampling request
+// ---------------------------------------------------------------------------
+template <int TDT, int DDT>
+__global__ __launch_bounds__(kThreads) void k_locate(const RunParams p) {
+  const int b = blockIdx.x;
+  const DrawDesc d = p.desc[b];
+  if (d.kind == kDrawNone) return;
+  locate<TDT, DDT>(p, b, d);
+}
+
 template <int TDT, int DDT>
 hipError_t launch_all(const RunParams& p, hipStream_t s, hipEvent_t* ev) {
   const int nslot = 2 * p.K + 1;
-  auto rec = [&](int k) -> hipError_t {
-    return ev ? hipEventRecord(ev[k], s) : hipSuccess;
-  };
+  auto rec = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], s) : hipSuccess; };
   hipError_t e;
   if ((e = rec(0)) != hipSuccess) return e;
   const uint64_t g1 = (uint64_t)p.B * nslot * p.nchunk;
-  hipLaunchKernelGGL((k_row_stats<TDT, DDT>), dim3((unsigned)g1), dim3(kStatsThreads), 0, s, p);
+  hipLaunchKernelGGL((k_stats<TDT, DDT>), dim3((unsigned)g1), dim3(kThreads), 0, s, p);
   if ((e = rec(1)) != hipSuccess) return e;
   if ((e = rec(2)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decide<TDT, DDT>), dim3(p.B), dim3(kDecideThreads), 0, s, p);
+  hipLaunchKernelGGL((k_decide<TDT, DDT>), dim3(p.B), dim3(64), 0, s, p);
   if ((e = rec(3)) != hipSuccess) return e;
   if ((e = rec(4)) != hipSuccess) return e;
   if (p.has_draft) {
     const uint64_t g3 = (uint64_t)p.B * p.nchunk;
-    hipLaunchKernelGGL((k_resid_sums<TDT, DDT>), dim3((unsigned)g3), dim3(kStatsThreads), 0, s, p);
+    hipLaunchKernelGGL((k_resid<TDT, DDT>), dim3((unsigned)g3), dim3(kThreads), 0, s, p);
   }
   if ((e = rec(5)) != hipSuccess) return e;
   if ((e = rec(6)) != hipSuccess) return e;
-  const size_t lds = (size_t)p.chunk * sizeof(float);
-  hipLaunchKernelGGL((k_locate<TDT, DDT>), dim3(p.B), dim3(kLocateThreads), lds, s, p);
+  hipLaunchKernelGGL((k_locate<TDT, DDT>), dim3(p.B), dim3(kThreads), 0, s, p);
   if ((e = rec(7)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_step(const RunParams& p, int tdt, int ddt, hipStream_t s,
-                       hipEvent_t* ev) {
+hipError_t launch_step(const RunParams& p, int tdt, int ddt, hipStream_t s, hipEvent_t* ev) {
   if (tdt == SV_F32 && ddt == SV_F32) return launch_all<SV_F32, SV_F32>(p, s, ev);
   if (tdt == SV_F32 && ddt == SV_BF16) return launch_all<SV_F32, SV_BF16>(p, s, ev);
   if (tdt == SV_BF16 && ddt == SV_F32) return launch_all<SV_BF16, SV_F32>(p, s, ev);
@@ -914,7 +936,7 @@ hipError_t launch_step(const RunParams& p, int tdt, int ddt, hipStream_t s,
 }
 
 const char* kernel_name(int i) {
-  static const char* names[kNumKernels] = {"row_stats", "decide", "resid_sums", "locate"};
+  static const char* names[kNumKernels] = {"stats", "decide", "resid", "locate"};
   return (i >= 0 && i < kNumKernels) ? names[i] : nullptr;
 }
 

@@ -23,7 +23,7 @@ def test_status_strings():
 
 def test_kernel_names():
     names = [sv.spec_verify_kernel_name(i) for i in range(4)]
-    assert names == ["row_stats", "decide", "resid_sums", "locate"]
+    assert names == ["stats", "decide", "resid", "locate"]
     assert sv.spec_verify_kernel_name(4) is None
 
 
@@ -32,9 +32,9 @@ def test_create_rejects_bad_config_without_device():
     h = ctypes.c_void_p(1)
     assert lib.spec_verify_create(None, ctypes.byref(h)) == binding.SV_ERR_INVALID_ARG
     assert h.value is None
-    bad = [dict(max_batch=0), dict(max_drafts=-1), dict(max_drafts=64),
-           dict(vocab=0), dict(vocab=(1 << 24) + 1), dict(chunk_elems=100),
-           dict(chunk_elems=32768), dict(device=-1)]
+    bad = [dict(max_batch=0), dict(max_drafts=-1), dict(max_drafts=32),
+           dict(vocab=0), dict(vocab=983041), dict(chunk_elems=100),
+           dict(chunk_elems=15424), dict(device=-1)]
     for b in bad:
         f = dict(max_batch=4, max_drafts=4, vocab=1000, target_dtype=0,
                  draft_dtype=0, draft_is_probs=0, device=0, chunk_elems=0)

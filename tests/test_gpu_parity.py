@@ -125,7 +125,7 @@ def test_random_case(svlib, name):
         check(svlib, w, seed=seed, offset=seed * 3)
 
 
-@pytest.mark.parametrize("chunk", [256, 320, 1024, 4096, 16384])
+@pytest.mark.parametrize("chunk", [256, 320, 1024, 4096, 15360])
 def test_chunk_sizes(svlib, chunk):
     w = synth.make_random(20, 4, 20000, dtype=torch.bfloat16, temps=(1.0, 0.0, 0.6),
                           n_mode="ragged", onehot_frac=0.3, seed=9)
