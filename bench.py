@@ -165,6 +165,16 @@ def main():
 
     elems = w.verified_elems()
     alg = w.algorithmic_bytes()
+    # bytes the residual pass re-reads: the rejected row pair of every
+    # probabilistic sampling request (from the last step's outputs)
+    n_b = w.num_drafts.clamp(0, w.K).cpu()
+    T = w.temperatures.float().cpu()
+    samp = (T >= torch.finfo(torch.float32).tiny) & torch.isfinite(T)
+    prob = torch.zeros_like(samp) if w.draft is None else (
+        torch.ones_like(samp) if w.draft_mode is None else w.draft_mode.cpu() == 0)
+    pairs = int(((nacc.cpu() < n_b) & samp & prob).sum())
+    delt = w.draft.element_size() if w.draft is not None else 0
+    resid_bytes = pairs * w.V * (w.elt() + delt)
     stats_ms = kern_ms[DOMINANT]
     achieved = alg / (stats_ms * 1e-3) / 1e9
     traffic = read_traffic(args.workload)
@@ -189,6 +199,8 @@ def main():
                    "chunk_elems": h.chunk_elems, "input_copies": len(copies),
                    "parallelism": "single GPU"},
         "step_hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
+        "resid_pairs": pairs, "resid_bytes": resid_bytes,
+        "resid_gbps": resid_bytes / (kern_ms["resid"] * 1e-3) / 1e9,
         "kernels_ms": kern_ms,
         "roofline": {"bound": "hbm", "kernel": DOMINANT,
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

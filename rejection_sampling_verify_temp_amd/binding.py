@@ -40,11 +40,14 @@ class SpecVerifyError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libspecverify.so (raises if it has not been built)."""
+def load_library(path: str = None) -> ctypes.CDLL:
+    """Load libspecverify.so (raises if it has not been built).  The
+    SPEC_VERIFY_LIB environment variable names another build of the same
+    library (for comparing compile-time variants)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("SPEC_VERIFY_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with __graft_entry__.build() "

@@ -26,15 +26,16 @@ def command(out: str = LIB, extra=()) -> list[str]:
             "-o", out, f"-Wl,-rpath,{ROCM}/lib", *extra]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source into `out`; `defines` are extra -D flags."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = command(tmp, extra=[f"-D{d}" for d in defines])
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

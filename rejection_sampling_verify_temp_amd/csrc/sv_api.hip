@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int kTimingSlots = 64;
+constexpr int kEventsPerRun = 2 * sv::kNumKernels;
 
 struct DeviceGuard {
   int prev = -1;
@@ -59,9 +60,9 @@ struct spec_verify_s {
   uint32_t* flags = nullptr;
   hipStream_t last_stream = nullptr;
   bool has_run = false;
-  // timing
+  // timing: per run, one start/stop pair per kernel
   bool timing = false;
-  hipEvent_t ev[kTimingSlots][2 * sv::kNumKernels] = {};
+  hipEvent_t ev[kTimingSlots][kEventsPerRun] = {};
   int ev_pending = 0;  // event sets recorded and not yet read
   int ev_next = 0;     // next ring slot
   double tot_ms[sv::kNumKernels] = {};
@@ -76,19 +77,20 @@ void free_all(spec_verify_s* h) {
   if (h->rsum) (void)hipFree(h->rsum);
   if (h->flags) (void)hipFree(h->flags);
   for (int s = 0; s < kTimingSlots; ++s)
-    for (int k = 0; k < 2 * sv::kNumKernels; ++k)
+    for (int k = 0; k < kEventsPerRun; ++k)
       if (h->ev[s][k]) (void)hipEventDestroy(h->ev[s][k]);
 }
 
 // Fold the oldest pending event set into the totals.
 hipError_t drain_one(spec_verify_s* h) {
   const int slot = (h->ev_next - h->ev_pending + kTimingSlots) % kTimingSlots;
-  hipError_t e = hipEventSynchronize(h->ev[slot][2 * sv::kNumKernels - 1]);
-  if (e != hipSuccess) return e;
   for (int k = 0; k < sv::kNumKernels; ++k) {
+    hipEvent_t* e = &h->ev[slot][2 * k];
+    hipError_t err = hipEventSynchronize(e[1]);
+    if (err != hipSuccess) return err;
     float ms = 0.f;
-    e = hipEventElapsedTime(&ms, h->ev[slot][2 * k], h->ev[slot][2 * k + 1]);
-    if (e != hipSuccess) return e;
+    err = hipEventElapsedTime(&ms, e[0], e[1]);
+    if (err != hipSuccess) return err;
     h->tot_ms[k] += ms;
   }
   h->runs++;
@@ -177,29 +179,30 @@ int spec_verify_run(spec_verify_t h, int32_t B, int32_t K, const void* target_lo
       (out_debug_probs != nullptr && !aligned(out_debug_probs, 4)))
     return SV_ERR_INVALID_ARG;
 
-  sv::RunParams p;
-  p.target = target_logits;
-  p.draft = draft_probs;
-  p.mode = draft_mode;
-  p.ids = draft_ids;
-  p.nd = num_drafts_per_req;
-  p.temps = temperatures;
-  p.out_tokens = out_tokens;
-  p.out_nacc = out_num_accepted;
-  p.out_dbg = out_debug_probs;
-  p.part = h->part;
-  p.desc = h->desc;
-  p.rsum = h->rsum;
-  p.flags = h->flags;
-  p.seed = philox_seed;
-  p.offset = philox_offset;
-  p.B = B;
-  p.K = K;
-  p.V = c.vocab;
-  p.chunk = h->chunk;
-  p.nchunk = h->nchunk;
-  p.draft_is_probs = c.draft_is_probs;
-  p.has_draft = draft_probs != nullptr;
+  sv::RunParams full{};
+  full.target = target_logits;
+  full.draft = draft_probs;
+  full.mode = draft_mode;
+  full.ids = draft_ids;
+  full.nd = num_drafts_per_req;
+  full.temps = temperatures;
+  full.out_tokens = out_tokens;
+  full.out_nacc = out_num_accepted;
+  full.out_dbg = out_debug_probs;
+  full.part = h->part;
+  full.desc = h->desc;
+  full.rsum = h->rsum;
+  full.flags = h->flags;
+  full.seed = philox_seed;
+  full.offset = philox_offset;
+  full.B = B;
+  full.K = K;
+  full.V = c.vocab;
+  full.chunk = h->chunk;
+  full.nchunk = h->nchunk;
+  full.draft_is_probs = c.draft_is_probs;
+  full.has_draft = draft_probs != nullptr;
+  full.b_base = 0;
 
   DeviceGuard g(c.device);
   if (!g.ok) return SV_ERR_HIP;
@@ -209,7 +212,14 @@ int spec_verify_run(spec_verify_t h, int32_t B, int32_t K, const void* target_lo
     if (h->ev_pending == kTimingSlots && drain_one(h) != hipSuccess) return SV_ERR_HIP;
     ev = h->ev[h->ev_next];
   }
-  if (sv::launch_step(p, c.target_dtype, c.draft_dtype, s, ev) != hipSuccess) return SV_ERR_HIP;
+  bool ok = true;
+  for (int k = 0; ok && k < sv::kNumKernels; ++k) {
+    hipEvent_t* e = ev ? &ev[2 * k] : nullptr;
+    ok = (!e || hipEventRecord(e[0], s) == hipSuccess) &&
+         sv::launch_kernel(k, full, c.target_dtype, c.draft_dtype, s) == hipSuccess &&
+         (!e || hipEventRecord(e[1], s) == hipSuccess);
+  }
+  if (!ok) return SV_ERR_HIP;
   if (h->timing) {
     h->ev_next = (h->ev_next + 1) % kTimingSlots;
     h->ev_pending++;
@@ -236,7 +246,7 @@ int spec_verify_timing_enable(spec_verify_t h, int32_t enable) {
   if (!g.ok) return SV_ERR_HIP;
   if (enable && h->ev[0][0] == nullptr) {
     for (int s = 0; s < kTimingSlots; ++s)
-      for (int k = 0; k < 2 * sv::kNumKernels; ++k)
+      for (int k = 0; k < kEventsPerRun; ++k)
         if (hipEventCreate(&h->ev[s][k]) != hipSuccess) return SV_ERR_HIP;
   }
   while (h->ev_pending > 0)

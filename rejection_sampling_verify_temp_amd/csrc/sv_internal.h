@@ -67,14 +67,15 @@ struct RunParams {
   int32_t nchunk;   // ceil(V / chunk)
   int32_t draft_is_probs;
   int32_t has_draft;
+  int32_t b_base;      // batch index of request 0 (Philox counters use b_base + b)
 };
 
 constexpr int kNumKernels = 4;
+enum KernelId { kKernelStats = 0, kKernelDecide = 1, kKernelResid = 2, kKernelLocate = 3 };
 
-// Enqueue the kernels of one step; t_events (2 * kNumKernels events or
-// null) bracket each kernel for timing.
-hipError_t launch_step(const RunParams& p, int target_dtype, int draft_dtype,
-                       hipStream_t stream, hipEvent_t* t_events);
+// Enqueue kernel k of a step (for the requests p describes) on `stream`.
+hipError_t launch_kernel(int k, const RunParams& p, int target_dtype, int draft_dtype,
+                         hipStream_t stream);
 
 const char* kernel_name(int i);
 

@@ -13,9 +13,9 @@
 //   3. resid   requests rejected on a probabilistic draft: per chunk the sum
 //              of max(0, p - q) over that row pair.
 //   4. locate  one workgroup per sampling request: a prefix over the chunk
-//              sums finds the chunk holding u * S; each thread takes 64
-//              consecutive residuals of it in registers, and a workgroup
-//              scan of the segment sums finds the token.
+//              sums finds the chunk holding u * S; each of 1024 threads
+//              takes 16 consecutive residuals of it in registers, and a
+//              workgroup scan of the segment sums finds the token.
 //
 // Method (page title, section): "深入推测解码：从概念到实现" 保证原始分布
 // (accept with min(1, p/q), resample from max(0, p - q)); "RTP-LLM
@@ -316,12 +316,27 @@ __device__ __forceinline__ double wave_incl_scan(double v, int lane) {
 // ---------------------------------------------------------------------------
 // Chunk streaming
 // ---------------------------------------------------------------------------
-constexpr int kUnroll = 4;  // 16-byte loads in flight per thread per step
+#ifndef SV_LOADS_IN_FLIGHT
+#define SV_LOADS_IN_FLIGHT 8
+#endif
+#ifndef SV_STREAM_NT
+#define SV_STREAM_NT 1
+#endif
+constexpr int kUnroll = SV_LOADS_IN_FLIGHT;  // 16-byte loads in flight per thread
+
+// Streaming 16-byte load; rows are read once per step.
+__device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
+#if SV_STREAM_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
 
 template <int DT>
 __device__ __forceinline__ SmAcc chunk_softmax_stats(const void* row, int c0, int c1, float c) {
   using E = Elt<DT>;
-  constexpr int kN = kUnroll * E::kVec;
+  constexpr int kSub = 16 / E::kVec;  // loads folded together: 16 values
   SmAcc a{kNegInf, 0.f, 0.f};
   const Geo g = chunk_geo<DT>(row, c0, c1);
   const int tid = threadIdx.x;
@@ -332,16 +347,21 @@ __device__ __forceinline__ SmAcc chunk_softmax_stats(const void* row, int c0, in
   const u32x4* vp = reinterpret_cast<const u32x4*>(
       static_cast<const char*>(row) + (size_t)g.v0 * E::kBytes);
   for (int v = tid; v < g.nvec; v += kThreads * kUnroll) {
+    // all loads first, so they are in flight together; lanes past the end
+    // of the chunk load nothing and read -inf
     u32x4 d[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int vi = v + u * kThreads;
-      d[u] = vi < g.nvec ? __builtin_nontemporal_load(vp + vi) : E::neg_inf();
+      d[u] = E::neg_inf();
+      if (v + u * kThreads < g.nvec) d[u] = stream_load(vp + v + u * kThreads);
     }
-    float x[kN];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) E::unpack(d[u], x + u * E::kVec);
-    sm_tile(a, x, c);
+    for (int u0 = 0; u0 < kUnroll; u0 += kSub) {
+      float x[kSub * E::kVec];
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) E::unpack(d[u0 + u], x + u * E::kVec);
+      sm_tile(a, x, c);
+    }
   }
   if (g.t0 + tid < g.c1) {  // tail (< one vector)
     const float x[1] = {E::at(row, g.t0 + tid)};
@@ -353,7 +373,7 @@ __device__ __forceinline__ SmAcc chunk_softmax_stats(const void* row, int c0, in
 template <int DT>
 __device__ __forceinline__ AmAcc chunk_argmax(const void* row, int c0, int c1) {
   using E = Elt<DT>;
-  constexpr int kN = kUnroll * E::kVec;
+  constexpr int kSub = 16 / E::kVec;
   AmAcc a{kNegInf, INT32_MAX};
   const Geo g = chunk_geo<DT>(row, c0, c1);
   const int tid = threadIdx.x;
@@ -368,20 +388,30 @@ __device__ __forceinline__ AmAcc chunk_argmax(const void* row, int c0, int c1) {
     u32x4 d[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int vi = v + u * kThreads;
-      d[u] = vi < g.nvec ? __builtin_nontemporal_load(vp + vi) : E::neg_inf();
+      d[u] = E::neg_inf();
+      if (v + u * kThreads < g.nvec) d[u] = stream_load(vp + v + u * kThreads);
     }
-    float x[kN];
-    int ix[kN];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      E::unpack(d[u], x + u * E::kVec);
-      const int vi = v + u * kThreads;
+    for (int u0 = 0; u0 < kUnroll; u0 += kSub) {
+      float x[kSub * E::kVec];
 #pragma unroll
-      for (int e = 0; e < E::kVec; ++e)
-        ix[u * E::kVec + e] = vi < g.nvec ? g.v0 + vi * E::kVec + e : INT32_MAX;
+      for (int u = 0; u < kSub; ++u) E::unpack(d[u0 + u], x + u * E::kVec);
+      float t = x[0];
+#pragma unroll
+      for (int k = 1; k < kSub * E::kVec; ++k) t = fmaxf(t, x[k]);
+      if (t > a.M || (t == a.M && a.I == INT32_MAX)) {  // rare: locate it
+        int best = INT32_MAX;
+#pragma unroll
+        for (int k = kSub * E::kVec - 1; k >= 0; --k) {
+          const int vi = v + (u0 + k / E::kVec) * kThreads;
+          if (x[k] == t && vi < g.nvec) best = g.v0 + vi * E::kVec + k % E::kVec;
+        }
+        if (best != INT32_MAX) {
+          a.M = t;
+          a.I = best;
+        }
+      }
     }
-    am_tile(a, x, ix);
   }
   if (g.t0 + tid < g.c1) {
     const float x[1] = {E::at(row, g.t0 + tid)};
@@ -439,13 +469,11 @@ __device__ __forceinline__ int rows_needed(const ReqInfo& r) {
 // ---------------------------------------------------------------------------
 // Decisions of one request (one wavefront)
 // ---------------------------------------------------------------------------
-// Lane = vocabulary chunk while combining a row; lane = drafted position j
-// afterwards.  Lane j keeps the combined target row j and draft row j.  The
-// draw descriptor goes to *d_out (shared memory); with `outputs` the accepted
-// tokens, counts, debug probabilities, greedy tokens and the descriptor in
-// global memory are written too.  Every workgroup of the residual kernel
-// runs this for its request (the combine reads a few hundred bytes), so the
-// decisions need no hand-off between workgroups.
+// Lane s first owns row slot s and folds that row's chunk partials; lane j
+// then decides drafted position j with the combined target row j and draft
+// row j.  The draw descriptor goes to *d_out (shared memory); with `outputs`
+// the accepted tokens, counts, debug probabilities, greedy tokens and the
+// descriptor in global memory are written too.
 template <int TDT, int DDT>
 __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, bool outputs,
                                DrawDesc* d_out) {
@@ -453,15 +481,22 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
   const int lane = threadIdx.x & 63;
   const float c = ri.sampling ? temp_scale(ri.T) : 0.f;
 
-  // values of the drafted tokens (loads issued before the combine)
+  // independent loads first, so they share one round trip: the first
+  // kBatch chunk partials of row slot `lane` (clamped into the request's
+  // slots and chunks; unused ones are ignored) and this lane's draft id
+  constexpr int kBatch = 16;
+  const Partial* pr = p.part + ((size_t)b * nslot + min(lane, nslot - 1)) * p.nchunk;
+  Partial q[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) q[u] = pr[min(u, p.nchunk - 1)];
   int x = -1;
+  if (lane < n) x = p.ids[(size_t)b * K + lane];
+
+  // values of the drafted tokens
   float lt = __builtin_nanf(""), ld = __builtin_nanf("");
-  if (lane < n) {
-    x = p.ids[(size_t)b * K + lane];
-    if (x >= 0 && x < V) {
-      lt = load_elem(p.target, TDT, (size_t)b * (K + 1) + lane, V, x);
-      if (ri.sampling && !ri.onehot) ld = load_elem(p.draft, DDT, (size_t)b * K + lane, V, x);
-    }
+  if (lane < n && x >= 0 && x < V) {
+    lt = load_elem(p.target, TDT, (size_t)b * (K + 1) + lane, V, x);
+    if (ri.sampling && !ri.onehot) ld = load_elem(p.draft, DDT, (size_t)b * K + lane, V, x);
   }
 
   // combine: lane s owns row slot s (target rows 0..K, draft rows K+1..2K)
@@ -470,14 +505,13 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
   double r_z = 0.0;   // sampling: row total relative to the reference
   int r_idx = 0;      // greedy: lowest index of the max
   if (lane < nslot && slot_needed(ri, lane, K)) {
-    const Partial* pr = p.part + ((size_t)b * nslot + lane) * p.nchunk;
-    constexpr int kBatch = 16;  // partial loads in flight per lane
     float m = kNegInf;
     int im = INT32_MAX;
     for (int k0 = 0; k0 < p.nchunk; k0 += kBatch) {
-      Partial q[kBatch];
+      if (k0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) q[u] = pr[min(k0 + u, p.nchunk - 1)];
+        for (int u = 0; u < kBatch; ++u) q[u] = pr[min(k0 + u, p.nchunk - 1)];
+      }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
         if (k0 + u < p.nchunk && q[u].m > m) {  // chunks ascend: first max wins
@@ -488,9 +522,10 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
     if (ri.sampling) {
       r_ref = ref_of(m, c);
       for (int k0 = 0; k0 < p.nchunk; k0 += kBatch) {
-        Partial q[kBatch];
+        if (k0 > 0 || p.nchunk > kBatch) {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) q[u] = pr[min(k0 + u, p.nchunk - 1)];
+          for (int u = 0; u < kBatch; ++u) q[u] = pr[min(k0 + u, p.nchunk - 1)];
+        }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
           if (k0 + u < p.nchunk && q[u].z != 0.0)
@@ -530,7 +565,7 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
       if (qx > 0.0) ratio = px / qx;
       else ratio = px > 0.0 ? __builtin_inf() : 0.0;
       double u_acc, u_rec;
-      uniforms(p.seed, p.offset, b, lane, &u_acc, &u_rec);
+      uniforms(p.seed, p.offset, p.b_base + b, lane, &u_acc, &u_rec);
       accept = u_acc < ratio;
       dbg_p = (float)px;
       dbg_q = (float)qx;
@@ -567,7 +602,7 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
       d.ref_p = t_ref;
       d.z_p = t_z;
       double u_acc, u_rec;
-      uniforms(p.seed, p.offset, b, je, &u_acc, &u_rec);
+      uniforms(p.seed, p.offset, p.b_base + b, je, &u_acc, &u_rec);
       d.u = u_rec;
       d.kind = kDrawSingle;
       if (je < n) {  // rejected at je
@@ -595,17 +630,11 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
 // ---------------------------------------------------------------------------
 // Kernel 1: row statistics
 // ---------------------------------------------------------------------------
+// Statistics of chunk `chunk` of row slot s of request b (all threads).
 template <int TDT, int DDT>
-__global__ __launch_bounds__(kThreads) void k_stats(const RunParams p) {
-  __shared__ float ldsf[kThreads / 64];
-  __shared__ double ldsd[kThreads / 64];
-  __shared__ int ldsi[kThreads / 64];
-  const int nslot = 2 * p.K + 1;
-  const int bid = blockIdx.x;
-  const int row = bid / p.nchunk, chunk = bid - row * p.nchunk;
-  const int b = row / nslot, s = row - b * nslot;
-  const ReqInfo ri = req_info(p, b);
-  if (!slot_needed(ri, s, p.K)) return;
+__device__ __forceinline__ void stats_item(const RunParams& p, int b, int s, int chunk,
+                                           const ReqInfo& ri, float* ldsf, double* ldsd,
+                                           int* ldsi) {
   const int c0 = chunk * p.chunk;
   const int c1 = min(p.V, c0 + p.chunk);
   const bool is_target = s <= p.K;
@@ -625,7 +654,23 @@ __global__ __launch_bounds__(kThreads) void k_stats(const RunParams p) {
     out.idx = a.I == INT32_MAX ? c0 : a.I;
     out.z = 0.0;
   }
-  if (threadIdx.x == 0) p.part[(size_t)row * p.nchunk + chunk] = out;
+  if (threadIdx.x == 0)
+    p.part[((size_t)b * (2 * p.K + 1) + s) * p.nchunk + chunk] = out;
+}
+
+// One workgroup per (request, row slot, chunk); unneeded slots exit at once.
+template <int TDT, int DDT>
+__global__ __launch_bounds__(kThreads) void k_stats(const RunParams p) {
+  __shared__ float ldsf[kThreads / 64];
+  __shared__ double ldsd[kThreads / 64];
+  __shared__ int ldsi[kThreads / 64];
+  const int nslot = 2 * p.K + 1;
+  const int bid = blockIdx.x;
+  const int row = bid / p.nchunk, chunk = bid - row * p.nchunk;
+  const int b = row / nslot, s = row - b * nslot;
+  const ReqInfo ri = req_info(p, b);
+  if (!slot_needed(ri, s, p.K)) return;
+  stats_item<TDT, DDT>(p, b, s, chunk, ri, ldsf, ldsd, ldsi);
 }
 
 // ---------------------------------------------------------------------------
@@ -647,16 +692,30 @@ __device__ __forceinline__ float single_resid(float lp, const DrawDesc& d) {
   return fast_exp2(fmaf(lp, d.c, d.ref_p));
 }
 
-// Eight consecutive elements from a 16-byte aligned address.
+// Eight consecutive elements from a 16-byte aligned address, as raw words
+// (one 16-byte load for bf16, two for f32) and unpacked later.
 template <int DT>
-__device__ __forceinline__ void load8(const void* row, int i, float* x) {
+struct Raw8 {
+  u32x4 w[DT == SV_BF16 ? 1 : 2];
+};
+
+template <int DT>
+__device__ __forceinline__ Raw8<DT> load8(const void* row, int i) {
   const u32x4* v = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
                                                   (size_t)i * Elt<DT>::kBytes);
+  Raw8<DT> r;
+  r.w[0] = stream_load(v);
+  if (DT == SV_F32) r.w[DT == SV_BF16 ? 0 : 1] = stream_load(v + 1);
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack8(const Raw8<DT>& r, float* x) {
   if (DT == SV_BF16) {
-    Elt<SV_BF16>::unpack(__builtin_nontemporal_load(v), x);
+    Elt<SV_BF16>::unpack(r.w[0], x);
   } else {
-    Elt<SV_F32>::unpack(__builtin_nontemporal_load(v), x);
-    Elt<SV_F32>::unpack(__builtin_nontemporal_load(v + 1), x + 4);
+    Elt<SV_F32>::unpack(r.w[0], x);
+    Elt<SV_F32>::unpack(r.w[DT == SV_BF16 ? 0 : 1], x + 4);
   }
 }
 
@@ -665,7 +724,8 @@ template <int TDT, int DDT>
 __device__ __forceinline__ double pair_chunk_sum(const void* prow, const void* qrow, int c0,
                                                  int c1, const DrawDesc& d, bool probs,
                                                  double* ldsd) {
-  constexpr int kGroups = 4;  // groups of eight elements per thread per step
+  // groups of eight elements per thread per step
+  constexpr int kGroups = 4;
   const int tid = threadIdx.x;
   float acc = 0.f;
   const uintptr_t pa = reinterpret_cast<uintptr_t>(prow) + (uintptr_t)c0 * Elt<TDT>::kBytes;
@@ -674,21 +734,26 @@ __device__ __forceinline__ double pair_chunk_sum(const void* prow, const void* q
   if (((pa | qa) & 15u) == 0) {
     const int ngrp = (c1 - c0) / 8;
     for (int g = tid; g < ngrp; g += kThreads * kGroups) {
-      float lp[kGroups][8], lq[kGroups][8];
+      Raw8<TDT> rp[kGroups];
+      Raw8<DDT> rq[kGroups];
 #pragma unroll
-      for (int u = 0; u < kGroups; ++u) {  // clamped: every load in bounds
-        const int gi = min(g + u * kThreads, ngrp - 1);
-        load8<TDT>(prow, c0 + gi * 8, lp[u]);
-        load8<DDT>(qrow, c0 + gi * 8, lq[u]);
+      for (int u = 0; u < kGroups; ++u) {
+        const int gi = g + u * kThreads;
+        if (gi < ngrp) {
+          rp[u] = load8<TDT>(prow, c0 + gi * 8);
+          rq[u] = load8<DDT>(qrow, c0 + gi * 8);
+        }
       }
 #pragma unroll
       for (int u = 0; u < kGroups; ++u) {
         const int gi = g + u * kThreads;
-        float e[8];
+        float lp[8], lq[8], e[8];
+        unpack8<TDT>(rp[u], lp);
+        unpack8<DDT>(rq[u], lq);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int i = c0 + gi * 8 + k;
-          e[k] = (gi < ngrp && i != d.x) ? pair_resid(lp[u][k], lq[u][k], d, probs) : 0.f;
+          e[k] = (gi < ngrp && i != d.x) ? pair_resid(lp[k], lq[k], d, probs) : 0.f;
         }
         acc += pairwise_sum(e);
       }
@@ -710,10 +775,11 @@ __device__ __forceinline__ float resid_of(float lp, float lq, int kind, int i, i
   return i == excl ? 0.f : r;
 }
 
-// Segment of kSeg consecutive elements per thread: with kThreads threads a
-// segment scan covers a whole chunk (kSeg * kThreads >= kMaxChunkElems).
-constexpr int kSeg = 64;
-static_assert(kSeg * kThreads >= kMaxChunkElems, "a chunk must fit the segments");
+// The draw runs kLocThreads threads, each owning kSeg consecutive elements
+// of the chosen chunk (kSeg * kLocThreads >= kMaxChunkElems).
+constexpr int kLocThreads = 1024;
+constexpr int kSeg = 16;
+static_assert(kSeg * kLocThreads >= kMaxChunkElems, "a chunk must fit the segments");
 
 // Logits of elements [i0, i0 + kSeg) of a row (i0 a multiple of kSeg; n of
 // them valid, the rest set to 0).  16-byte loads where the row allows.
@@ -735,7 +801,7 @@ template <int TDT, int DDT>
 __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
   __shared__ int s_cstar, s_kind, s_excl, s_y, s_last;
   __shared__ double s_theta;
-  __shared__ double s_woff[kThreads / 64];
+  __shared__ double s_woff[kLocThreads / 64];
   const int K = p.K, V = p.V, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const size_t trow = (size_t)b * (K + 1) + d.j;
   const void* prow = row_ptr(p.target, TDT, trow, V);
@@ -876,7 +942,8 @@ __global__ __launch_bounds__(64) void k_decide(const RunParams p) {
 // Kernel 3: residual chunk sums of requests rejected on a probabilistic draft
 // ---------------------------------------------------------------------------
 template <int TDT, int DDT>
-__global__ __launch_bounds__(kThreads) void k_resid(const RunParams p) {
+__global__ __launch_bounds__(kThreads) void k_resid(
+    const RunParams p) {
   __shared__ double ldsd[kThreads / 64];
   const int bid = blockIdx.x;
   const int rb = bid / p.nchunk, chunk = bid - rb * p.nchunk;
@@ -895,7 +962,7 @@ __global__ __launch_bounds__(kThreads) void k_resid(const RunParams p) {
 // Kernel 4: the draw of every sampling request
 // ---------------------------------------------------------------------------
 template <int TDT, int DDT>
-__global__ __launch_bounds__(kThreads) void k_locate(const RunParams p) {
+__global__ __launch_bounds__(kLocThreads) void k_locate(const RunParams p) {
   const int b = blockIdx.x;
   const DrawDesc d = p.desc[b];
   if (d.kind == kDrawNone) return;
@@ -903,36 +970,35 @@ __global__ __launch_bounds__(kThreads) void k_locate(const RunParams p) {
 }
 
 template <int TDT, int DDT>
-hipError_t launch_all(const RunParams& p, hipStream_t s, hipEvent_t* ev) {
-  const int nslot = 2 * p.K + 1;
-  auto rec = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], s) : hipSuccess; };
-  hipError_t e;
-  if ((e = rec(0)) != hipSuccess) return e;
-  const uint64_t g1 = (uint64_t)p.B * nslot * p.nchunk;
-  hipLaunchKernelGGL((k_stats<TDT, DDT>), dim3((unsigned)g1), dim3(kThreads), 0, s, p);
-  if ((e = rec(1)) != hipSuccess) return e;
-  if ((e = rec(2)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decide<TDT, DDT>), dim3(p.B), dim3(64), 0, s, p);
-  if ((e = rec(3)) != hipSuccess) return e;
-  if ((e = rec(4)) != hipSuccess) return e;
-  if (p.has_draft) {
-    const uint64_t g3 = (uint64_t)p.B * p.nchunk;
-    hipLaunchKernelGGL((k_resid<TDT, DDT>), dim3((unsigned)g3), dim3(kThreads), 0, s, p);
+void launch_one(int k, const RunParams& p, hipStream_t s) {
+  switch (k) {
+    case kKernelStats: {
+      const uint64_t g = (uint64_t)p.B * (2 * p.K + 1) * p.nchunk;
+      hipLaunchKernelGGL((k_stats<TDT, DDT>), dim3((unsigned)g), dim3(kThreads), 0, s, p);
+      break;
+    }
+    case kKernelDecide:
+      hipLaunchKernelGGL((k_decide<TDT, DDT>), dim3(p.B), dim3(64), 0, s, p);
+      break;
+    case kKernelResid:
+      if (p.has_draft)
+        hipLaunchKernelGGL((k_resid<TDT, DDT>), dim3((unsigned)((uint64_t)p.B * p.nchunk)),
+                           dim3(kThreads), 0, s, p);
+      break;
+    default:
+      hipLaunchKernelGGL((k_locate<TDT, DDT>), dim3(p.B), dim3(kLocThreads), 0, s, p);
+      break;
   }
-  if ((e = rec(5)) != hipSuccess) return e;
-  if ((e = rec(6)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_locate<TDT, DDT>), dim3(p.B), dim3(kThreads), 0, s, p);
-  if ((e = rec(7)) != hipSuccess) return e;
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_step(const RunParams& p, int tdt, int ddt, hipStream_t s, hipEvent_t* ev) {
-  if (tdt == SV_F32 && ddt == SV_F32) return launch_all<SV_F32, SV_F32>(p, s, ev);
-  if (tdt == SV_F32 && ddt == SV_BF16) return launch_all<SV_F32, SV_BF16>(p, s, ev);
-  if (tdt == SV_BF16 && ddt == SV_F32) return launch_all<SV_BF16, SV_F32>(p, s, ev);
-  return launch_all<SV_BF16, SV_BF16>(p, s, ev);
+hipError_t launch_kernel(int k, const RunParams& p, int tdt, int ddt, hipStream_t s) {
+  if (tdt == SV_F32 && ddt == SV_F32) launch_one<SV_F32, SV_F32>(k, p, s);
+  else if (tdt == SV_F32 && ddt == SV_BF16) launch_one<SV_F32, SV_BF16>(k, p, s);
+  else if (tdt == SV_BF16 && ddt == SV_F32) launch_one<SV_BF16, SV_F32>(k, p, s);
+  else launch_one<SV_BF16, SV_BF16>(k, p, s);
+  return hipGetLastError();
 }
 
 const char* kernel_name(int i) {
