@@ -2,9 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
 
-One step = one spec_verify_run over a whole batch (row statistics, decisions,
-residual sums, draw).  Inputs are generated on the GPU and stay resident;
-steps rotate through --rotate copies of them so each step's rows were last
+One step = one spec_verify_run over a whole batch: row statistics, decisions,
+residual sums of rejected probabilistic drafts, and the draws.  Inputs are
+generated on the GPU and stay resident; steps rotate through --rotate copies
+of them so each step's rows were last
 touched more than the 256 MB Infinity Cache earlier.  The timed region is
 bracketed by torch.cuda.synchronize() and timed with events on the stream
 the library launches on.  A second loop of the same length times each kernel
@@ -200,7 +201,8 @@ def main():
                    "parallelism": "single GPU"},
         "step_hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
         "resid_pairs": pairs, "resid_bytes": resid_bytes,
-        "resid_gbps": resid_bytes / (kern_ms["resid"] * 1e-3) / 1e9,
+        "resid_gbps": (resid_bytes / (kern_ms["resid"] * 1e-3) / 1e9
+                       if "resid" in kern_ms else None),
         "kernels_ms": kern_ms,
         "roofline": {"bound": "hbm", "kernel": DOMINANT,
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
