@@ -193,7 +193,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"configs[{args.workload}]: {w.name}",
+        "config": {"workload": f"verify step, {w.name}",
                    "B": w.B, "K": w.K, "V": w.V, "logits": dt,
                    "verified_elems": elems, "algorithmic_bytes": alg,
                    "nominal_bytes": w.nominal_bytes(),
