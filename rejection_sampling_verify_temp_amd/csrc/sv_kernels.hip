@@ -171,14 +171,6 @@ __device__ __forceinline__ Geo chunk_geo(const void* row, int c0, int c1) {
 // ---------------------------------------------------------------------------
 // Per-thread accumulators
 // ---------------------------------------------------------------------------
-// Online softmax statistics: S = sum exp2(l * c + R) over the thread's
-// elements, R = ref_of(M, c), M the running max.  The reference is moved
-// only when the max grows, and the exponent reference stays an exact float
-// so the chunk combine can rescale without bias.
-struct SmAcc {
-  float M, R, S;
-};
-
 template <int N>
 __device__ __forceinline__ float pairwise_sum(float (&e)[N]) {
 #pragma unroll
@@ -187,23 +179,6 @@ __device__ __forceinline__ float pairwise_sum(float (&e)[N]) {
     for (int i = 0; i + stride < N; i += 2 * stride) e[i] += e[i + stride];
   }
   return e[0];
-}
-
-template <int N>
-__device__ __forceinline__ void sm_tile(SmAcc& a, const float (&x)[N], float c) {
-  float t = x[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) t = fmaxf(t, x[i]);
-  if (t > a.M) {
-    const float rn = ref_of(t, c);
-    a.S = (a.M == kNegInf) ? 0.f : a.S * fast_exp2(rn - a.R);
-    a.R = rn;
-    a.M = t;
-  }
-  float e[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) e[i] = fast_exp2(fmaf(x[i], c, a.R));
-  a.S += pairwise_sum(e);
 }
 
 // Running max and the lowest index attaining it (elements are visited in
@@ -333,41 +308,70 @@ __device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
 #endif
 }
 
+// Softmax statistics of one chunk, by the whole workgroup.  A pass holds
+// kUnroll 16-byte vectors per thread in registers (all loads in flight
+// together); the workgroup takes the max of the pass first, moves the shared
+// exponent reference R = ref_of(M, c) if the max grew, and only then sums
+// exp2(l * c + R).  With one reference for the workgroup the thread sums add
+// without rescaling, and no element needs a running-max test.  Vectors past
+// the chunk's end are neither loaded nor folded (the test is uniform in all
+// but one wave of a pass).
 template <int DT>
-__device__ __forceinline__ SmAcc chunk_softmax_stats(const void* row, int c0, int c1, float c) {
+__device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int c1, float c,
+                                                    float* ldsf, double* ldsd, float* m_out,
+                                                    double* z_out) {
   using E = Elt<DT>;
-  constexpr int kSub = 16 / E::kVec;  // loads folded together: 16 values
-  SmAcc a{kNegInf, 0.f, 0.f};
   const Geo g = chunk_geo<DT>(row, c0, c1);
   const int tid = threadIdx.x;
-  if (g.c0 + tid < g.v0) {  // head (< one vector)
-    const float x[1] = {E::at(row, g.c0 + tid)};
-    sm_tile(a, x, c);
-  }
   const u32x4* vp = reinterpret_cast<const u32x4*>(
       static_cast<const char*>(row) + (size_t)g.v0 * E::kBytes);
-  for (int v = tid; v < g.nvec; v += kThreads * kUnroll) {
-    // all loads first, so they are in flight together; lanes past the end
-    // of the chunk load nothing and read -inf
+  float M = kNegInf, R = 0.f, S = 0.f;
+  for (int base = 0; base == 0 || base < g.nvec; base += kThreads * kUnroll) {
+    const int v = base + tid;
     u32x4 d[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      d[u] = E::neg_inf();
+    for (int u = 0; u < kUnroll; ++u)
       if (v + u * kThreads < g.nvec) d[u] = stream_load(vp + v + u * kThreads);
-    }
+    // head and tail (each under one vector) ride along with the first pass
+    float ht[2] = {kNegInf, kNegInf};
+    if (base == 0 && g.c0 + tid < g.v0) ht[0] = E::at(row, g.c0 + tid);
+    if (base == 0 && g.t0 + tid < g.c1) ht[1] = E::at(row, g.t0 + tid);
+    float t = fmaxf(ht[0], ht[1]);
 #pragma unroll
-    for (int u0 = 0; u0 < kUnroll; u0 += kSub) {
-      float x[kSub * E::kVec];
+    for (int u = 0; u < kUnroll; ++u) {
+      if (v + u * kThreads < g.nvec) {
+        float x[E::kVec];
+        E::unpack(d[u], x);
 #pragma unroll
-      for (int u = 0; u < kSub; ++u) E::unpack(d[u0 + u], x + u * E::kVec);
-      sm_tile(a, x, c);
+        for (int k = 0; k < E::kVec; ++k) t = fmaxf(t, x[k]);
+      }
     }
+    const float pm = block_max<kThreads>(t, ldsf);
+    if (pm > M) {  // uniform across the workgroup
+      const float rn = ref_of(pm, c);
+      S = (M == kNegInf) ? 0.f : S * fast_exp2(rn - R);
+      R = rn;
+      M = pm;
+    }
+    float s = fast_exp2(fmaf(ht[0], c, R)) + fast_exp2(fmaf(ht[1], c, R));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (v + u * kThreads < g.nvec) {
+        // unpack again rather than keep 64 floats live: the empty asm hides
+        // the first unpack from common-subexpression elimination
+        u32x4 w = d[u];
+        asm volatile("" : "+v"(w));
+        float e[E::kVec];
+        E::unpack(w, e);
+#pragma unroll
+        for (int k = 0; k < E::kVec; ++k) e[k] = fast_exp2(fmaf(e[k], c, R));
+        s += pairwise_sum(e);
+      }
+    }
+    S += s;
   }
-  if (g.t0 + tid < g.c1) {  // tail (< one vector)
-    const float x[1] = {E::at(row, g.t0 + tid)};
-    sm_tile(a, x, c);
-  }
-  return a;
+  *z_out = block_sum<kThreads>((double)S, ldsd);
+  *m_out = M;
 }
 
 template <int DT>
@@ -419,20 +423,6 @@ __device__ __forceinline__ AmAcc chunk_argmax(const void* row, int c0, int c1) {
     am_tile(a, x, ix);
   }
   return a;
-}
-
-// Reduce a workgroup's softmax accumulators to (chunk max, chunk sum relative
-// to ref_of(chunk max)).  The rescale of each thread's sum is exact in fp64
-// up to the final rounding of exp2.
-__device__ __forceinline__ void reduce_softmax(const SmAcc& a, float c, float* ldsf,
-                                               double* ldsd, float* m_out, double* z_out) {
-  const float m = block_max<kThreads>(a.M, ldsf);
-  double contrib = 0.0;
-  if (a.S != 0.f && m != kNegInf)
-    contrib = (double)a.S * exp2((double)ref_of(m, c) - (double)a.R);
-  const double z = block_sum<kThreads>(contrib, ldsd);
-  *m_out = m;
-  *z_out = z;
 }
 
 // ---------------------------------------------------------------------------
@@ -643,9 +633,10 @@ __device__ __forceinline__ void stats_item(const RunParams& p, int b, int s, int
   Partial out;
   if (ri.sampling) {
     const float c = temp_scale(ri.T);
-    const SmAcc a = is_target ? chunk_softmax_stats<TDT>(r, c0, c1, c)
-                              : chunk_softmax_stats<DDT>(r, c0, c1, c);
-    reduce_softmax(a, c, ldsf, ldsd, &out.m, &out.z);
+    if (is_target)
+      chunk_softmax_block<TDT>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z);
+    else
+      chunk_softmax_block<DDT>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z);
     out.idx = -1;
   } else {  // greedy rows are target rows
     AmAcc a = chunk_argmax<TDT>(r, c0, c1);
@@ -658,9 +649,12 @@ __device__ __forceinline__ void stats_item(const RunParams& p, int b, int s, int
     p.part[((size_t)b * (2 * p.K + 1) + s) * p.nchunk + chunk] = out;
 }
 
+#ifndef SV_STATS_WAVES_PER_EU
+#define SV_STATS_WAVES_PER_EU 1
+#endif
 // One workgroup per (request, row slot, chunk); unneeded slots exit at once.
 template <int TDT, int DDT>
-__global__ __launch_bounds__(kThreads) void k_stats(const RunParams p) {
+__global__ __launch_bounds__(kThreads, SV_STATS_WAVES_PER_EU) void k_stats(const RunParams p) {
   __shared__ float ldsf[kThreads / 64];
   __shared__ double ldsd[kThreads / 64];
   __shared__ int ldsi[kThreads / 64];
