@@ -1,4 +1,5 @@
-"""CPU oracle for the speculative-sampling verify step.
+"""CPU oracle for the speculative-sampling verify step and the draft-token
+sampler that feeds it.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
 CPU-baseline leg of the benchmark may import this module.  The product path
@@ -66,6 +67,11 @@ def open_library(path: str):
     lib.svo_verify_with_uniforms.restype = u32
     lib.svo_verify.argtypes = common + [u64, u64] + [P] * 6
     lib.svo_verify.restype = u32
+    lib.svo_draft_uniform.argtypes = [u64, u64, u64, u64]
+    lib.svo_draft_uniform.restype = dbl
+    lib.svo_draft_sample.argtypes = [i32, i32, i32, i32, P, P, P, u64, u64,
+                                     P, P, P]
+    lib.svo_draft_sample.restype = u32
     return lib
 
 
@@ -204,3 +210,31 @@ def verify(target, draft, draft_ids, num_drafts, temperatures, *,
         flags = lib.svo_verify(*head, int(seed), int(offset), *tail)
     return dict(tokens=tokens, num_accepted=nacc, p=p, q=q, margin_acc=macc,
                 margin_rec=mrec, flags=int(flags))
+
+
+def draft_uniform(seed, offset, b, j):
+    """The draft sampler's uniform for request b, position j."""
+    return float(_load().svo_draft_uniform(int(seed), int(offset), int(b), int(j)))
+
+
+def draft_sample(draft, num_drafts, temperatures, *, seed=0, offset=0,
+                 diagnostics=True):
+    """Sample draft tokens x_j ~ softmax(l_j / T_b) for rows j < n_b.
+
+    draft: [B, K, V] float32, or uint16 holding bf16 bits.  num_drafts [B]
+    or None (all K rows).  Returns a dict with ids [B, K] (-1 past n_b),
+    q [B, K] = q_j(x_j), margin [B, K] (draw margins) and flags.
+    """
+    draft = np.ascontiguousarray(draft)
+    B, K, V = draft.shape
+    nd = None if num_drafts is None else np.ascontiguousarray(
+        num_drafts, dtype=np.int32).reshape(B)
+    temps = np.ascontiguousarray(temperatures, dtype=np.float32).reshape(B)
+    ids = np.empty((B, K), dtype=np.int32)
+    q = np.empty((B, K), dtype=np.float64)
+    margin = np.empty((B, K), dtype=np.float64)
+    flags = _load().svo_draft_sample(
+        B, K, V, _dtype_code(draft), _ptr(draft), _ptr(nd), _ptr(temps),
+        int(seed), int(offset), _ptr(ids),
+        _ptr(q) if diagnostics else None, _ptr(margin) if diagnostics else None)
+    return dict(ids=ids, q=q, margin=margin, flags=int(flags))

@@ -121,3 +121,51 @@ def compare(host, ref, tokens, nacc, dbg=None, *, band=1e-6, prob_rtol=1e-5,
                     if not rel <= prob_rtol:
                         bad(b, f"prob at j={j}: {g} vs {o} rel {rel:.3g}")
     return rep
+
+
+def compare_draft(ref, ids, qx=None, *, band=1e-6, prob_rtol=1e-5,
+                  max_report=20) -> ParityReport:
+    """Parity of the draft sampler's outputs.  ref: oracle.draft_sample's
+    result; ids [B, K] and qx [B, K] (or None): the implementation's.
+
+    A row is flagged when its draw uniform lies within ``band`` of a CDF
+    boundary (relative to the total).  Unflagged rows must match the oracle's
+    token exactly; a flagged row must still be a valid token.  Rows past n_b
+    must be -1.  q_j(x_j) must agree to ``prob_rtol`` relative wherever the
+    token matches (an absolute floor of 1e-35 below 1e-30)."""
+    ids = np.asarray(ids)
+    B, K = ids.shape
+    rep = ParityReport(requests=B * K)
+
+    def bad(where, why):
+        rep.mismatches.append((where, why) if len(rep.mismatches) < max_report else (where, "..."))
+
+    for b in range(B):
+        for j in range(K):
+            o, g = int(ref["ids"][b, j]), int(ids[b, j])
+            if o < 0:
+                if g != -1:
+                    bad((b, j), f"row past n_b holds {g}, not -1")
+                continue
+            rep.proposed += 1
+            if g < 0:
+                bad((b, j), f"no token ({g}) where the oracle drew {o}")
+                continue
+            if ref["margin"][b, j] < band:
+                rep.flagged += 1
+                rep.flagged_mismatch += int(g != o)
+            elif g != o:
+                bad((b, j), f"token {g} != oracle {o}")
+            if qx is None or g != o:
+                continue
+            oq, gq = float(ref["q"][b, j]), float(qx[b, j])
+            rep.prob_checked += 1
+            if abs(oq) < 1e-30:
+                if abs(gq - oq) > 1e-35:
+                    bad((b, j), f"q(x) {gq} vs {oq} (abs floor)")
+                continue
+            rel = abs(gq - oq) / abs(oq)
+            rep.prob_max_rel = max(rep.prob_max_rel, rel)
+            if not rel <= prob_rtol:
+                bad((b, j), f"q(x) {gq} vs {oq} rel {rel:.3g}")
+    return rep

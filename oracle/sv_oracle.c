@@ -386,3 +386,73 @@ uint32_t svo_verify(int B, int K, int V, int target_dtype, const void *target,
   free(ur);
   return flags;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Draft-token sampler: the step that produces the drafts the verify step    */
+/* checks.  [P1] section "引言", the propose pseudo-code: every draft step    */
+/* samples one token from the draft model's logits and appends it.  [P3]     */
+/* section "投机解码算法", 第一步 - 采样: for each guess i, q_i is the draft     */
+/* model's distribution given the prefix and the earlier guesses, and x_i is */
+/* sampled from q_i.                                                         */
+/*                                                                          */
+/* Readings: q_j = softmax(l_j / T_b), the temperature the verify step also  */
+/* applies to draft logits; a greedy temperature takes the lowest argmax;    */
+/* the draw is the verify step's inverse CDF with a uniform of its own: word */
+/* 0 of the Philox block at counter (offset, b, j, 1), key (seed, 0).  The   */
+/* verify step's counters have word 3 = 0, so no uniform is shared.          */
+/* ------------------------------------------------------------------------ */
+double svo_draft_uniform(uint64_t seed, uint64_t offset, uint64_t b, uint64_t j) {
+  uint64_t ctr[4] = {offset, b, j, 1};
+  uint64_t key[2] = {seed, 0};
+  uint64_t w[4];
+  svo_philox4x64_10(ctr, key, w);
+  return (double)(w[0] >> 40) * 0x1p-24;
+}
+
+/*   draft       [B][K][V] draft logits, dtype                                */
+/*   num_drafts  [B]: rows j < n_b are sampled; NULL samples all K rows.      */
+/*               Counts outside [0, K] are clamped and flagged.               */
+/*   out_ids     [B][K]: x_j, or -1 for j >= n_b                              */
+/*   out_q       [B][K] or NULL: q_j(x_j); 1 for greedy rows, NaN if unused   */
+/*   out_margin  [B][K] or NULL: draw margin; +inf greedy, NaN if unused      */
+/* Returns the OR of the SVO_FLAG_* conditions met.                          */
+uint32_t svo_draft_sample(int B, int K, int V, int dtype, const void *draft,
+                          const int32_t *num_drafts, const float *temperatures,
+                          uint64_t seed, uint64_t offset, int32_t *out_ids,
+                          double *out_q, double *out_margin) {
+  uint32_t flags = 0;
+  double *l = malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+  double *q = malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+  for (int b = 0; b < B; ++b) {
+    int n = num_drafts ? num_drafts[b] : K;
+    if (n < 0 || n > K) {
+      flags |= SVO_FLAG_BAD_NUM_DRAFTS;
+      n = n < 0 ? 0 : K;
+    }
+    const float T = temperatures[b];
+    for (int j = 0; j < K; ++j) {
+      const size_t o = (size_t)b * K + j;
+      int32_t x = -1;
+      double qx = NAN, margin = NAN;
+      if (j < n) {
+        load_row(draft, dtype, o, V, l);
+        if (!svo_is_sampling(T)) {
+          x = svo_argmax(l, V);
+          qx = 1.0;
+          margin = INFINITY;
+        } else {
+          svo_softmax(l, V, (double)T, q);
+          x = svo_draw(q, V, svo_draft_uniform(seed, offset, (uint64_t)b, (uint64_t)j),
+                       &margin);
+          qx = q[x];
+        }
+      }
+      out_ids[o] = x;
+      if (out_q) out_q[o] = qx;
+      if (out_margin) out_margin[o] = margin;
+    }
+  }
+  free(l);
+  free(q);
+  return flags;
+}

@@ -370,6 +370,80 @@ def check_invariants(seed=51):
                 assert y != h["draft_ids"][b, n]
 
 
+# --------------------------------------------------------------------------
+# Draft-token sampler
+# --------------------------------------------------------------------------
+def check_draft_uniform_mapping(n=2000, seed=7):
+    """The sampler's uniform is word 0 of the block at counter
+    (offset, b, j, 1) with key (seed, 0), mapped as (w >> 40) * 2^-24."""
+    rng = np.random.default_rng(seed)
+    for _ in range(n):
+        s, o = (int(x) for x in rng.integers(0, 1 << 62, 2, dtype=np.uint64))
+        b, j = int(rng.integers(0, 4096)), int(rng.integers(0, 32))
+        w = _numpy_block([o, b, j, 1], [s, 0])
+        assert oracle.draft_uniform(s, o, b, j) == (int(w[0]) >> 40) / 2.0 ** 24
+
+
+def _greedy_temperature(T):
+    T = np.float32(T)
+    return not (np.isfinite(T) and T >= np.finfo(np.float32).tiny)
+
+
+def check_draft_sample_vs_library(cases=120, seed=61):
+    """Every sampled row equals an independent computation: scipy's softmax
+    of l/T, numpy's Philox for the uniform, searchsorted over the cumulative
+    sum.  Greedy rows equal np.argmax (lowest index on ties) with q = 1; rows
+    past n_b are -1; an out-of-range count is clamped and flagged."""
+    rng = np.random.default_rng(seed)
+    temps_pool = [1.0, 0.7, 1.6, 0.05, 0.0, -1.0, float("nan"), 1e-40]
+    for c in range(cases):
+        B, K, V = int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 300))
+        l = rng.normal(0, 3, (B, K, V)).astype(np.float32)
+        if c % 3 == 0:
+            l = np.round(l)  # integer logits: ties for the greedy rows
+        temps = np.array([temps_pool[i] for i in rng.integers(0, len(temps_pool), B)],
+                         dtype=np.float32)
+        nd = rng.integers(0, K + 1, B).astype(np.int32)
+        bad = c % 10 == 5
+        if bad:
+            nd[0] = K + 2
+        r = oracle.draft_sample(l, nd, temps, seed=c, offset=3 * c)
+        assert r["flags"] == (2 if bad else 0)
+        for b in range(B):
+            n = min(int(nd[b]), K)
+            for j in range(K):
+                x, qx = int(r["ids"][b, j]), r["q"][b, j]
+                if j >= n:
+                    assert x == -1 and np.isnan(qx)
+                    continue
+                row = l[b, j].astype(np.float64)
+                if _greedy_temperature(temps[b]):
+                    assert x == int(np.argmax(row)) and qx == 1.0
+                    continue
+                p = scipy.special.softmax(row / float(temps[b]))
+                w = _numpy_block([3 * c, b, j, 1], [c, 0])
+                u = (int(w[0]) >> 40) / 2.0 ** 24
+                cdf = np.cumsum(p)
+                y = min(int(np.searchsorted(cdf, u * cdf[-1], side="right")), V - 1)
+                if r["margin"][b, j] > 1e-9:
+                    assert x == y, (c, b, j, x, y)
+                assert abs(qx - p[x]) <= 1e-12 * p[x] + 1e-300
+
+
+def check_draft_sample_monte_carlo(B=1 << 17, V=8, T=0.8, seed=71):
+    """One draft row repeated over B requests (each has its own Philox
+    counter): the histogram of the sampled tokens follows softmax(l/T), at
+    both positions of a two-position draft."""
+    rng = np.random.default_rng(seed)
+    l1 = rng.normal(0, 1.5, (2, V)).astype(np.float32)
+    l = np.broadcast_to(l1, (B, 2, V)).copy()
+    r = oracle.draft_sample(l, None, np.full(B, T, np.float32), seed=seed,
+                            offset=1, diagnostics=False)
+    for j in range(2):
+        q = scipy.special.softmax(l1[j].astype(np.float64) / T)
+        assert _chisq_ok(np.bincount(r["ids"][:, j], minlength=V), q), j
+
+
 ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_accept_example_philox, check_bpd_greedy_example,
              check_greedy_bruteforce, check_enumeration_law,
@@ -377,4 +451,5 @@ ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_monte_carlo_onehot, check_no_draft_is_plain_sampling,
              check_identical_draft_always_accepted,
              check_certain_onehot_always_accepted, check_zero_mass_never_drawn,
-             check_invariants]
+             check_invariants, check_draft_uniform_mapping,
+             check_draft_sample_vs_library, check_draft_sample_monte_carlo]

@@ -32,6 +32,10 @@ MUTANTS = {
     "onehot_x_not_zeroed": ("if (x >= 0 && x < V) r[x] = 0.0;", "(void)x;"),
     "bonus_from_draft": ("memcpy(r, p, sizeof(double) * (size_t)V);\n      }",
                          "memcpy(r, p, sizeof(double) * (size_t)V);\n        if (mode == SVO_MODE_PROB && n > 0) { load_row(draft, draft_dtype, drow0 + n - 1, V, dl); svo_softmax(dl, V, (double)T, r); }\n      }"),
+    "draft_counter_word": ("uint64_t ctr[4] = {offset, b, j, 1};", "uint64_t ctr[4] = {offset, b, j, 0};"),
+    "draft_temperature_ignored": ("svo_softmax(l, V, (double)T, q);", "svo_softmax(l, V, 1.0, q);"),
+    "draft_rows_past_n": ("      if (j < n) {", "      if (j <= n && j < K) {"),
+    "draft_same_uniform_all_rows": ("(uint64_t)b, (uint64_t)j),\n", "(uint64_t)b, 0),\n"),
 }
 
 

@@ -61,3 +61,21 @@ def test_planted_differences_are_reported():
     i, j = dead[0]
     d3[i, j] = 0.5
     assert not compare(h, ref, ref["tokens"], ref["num_accepted"], d3).ok()
+
+
+def test_draft_rule_accepts_oracle_and_rejects_differences():
+    from oracle.parity import compare_draft
+    rng = np.random.default_rng(3)
+    l = rng.normal(0, 2, (6, 4, 300)).astype(np.float32)
+    ref = oracle.draft_sample(l, np.array([4, 3, 0, 2, 4, 1]),
+                              np.array([1.0, 0.5, 1.0, 0.0, 2.0, 1.0]), seed=5, offset=1)
+    assert compare_draft(ref, ref["ids"], ref["q"]).ok()
+    ids = ref["ids"].copy()
+    ids[0, 1] = (ids[0, 1] + 1) % 300
+    assert not compare_draft(ref, ids, ref["q"]).ok()
+    ids = ref["ids"].copy()
+    ids[2, 0] = 7  # a row past n_b must stay -1
+    assert not compare_draft(ref, ids, ref["q"]).ok()
+    q = ref["q"].copy()
+    q[1, 0] *= 1.001
+    assert not compare_draft(ref, ref["ids"], q).ok()
