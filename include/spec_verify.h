@@ -1,6 +1,6 @@
 /*
- * spec_verify.h -- C ABI of the speculative-sampling verify step on
- * MI355X (gfx950).
+ * spec_verify.h -- C ABI of the speculative-sampling verify step, and of
+ * the draft-token sampler that feeds it, on MI355X (gfx950).
  *
  * The operation (sources by page title and section):
  *   - "深入推测解码：从概念到实现" (Exploring Speculative Decoding), section
@@ -131,6 +131,44 @@ int spec_verify_run(spec_verify_t h, int32_t B, int32_t K,
                     uint64_t philox_offset, int32_t *out_tokens,
                     int32_t *out_num_accepted, float *out_debug_probs,
                     void *stream);
+
+/* Enqueues the draft-token sampler: the step that produces the drafts the
+ * verify step checks.  Sources: "深入推测解码：从概念到实现" (Exploring
+ * Speculative Decoding), section 引言, the propose pseudo-code (each draft
+ * step samples one token from the draft model's logits); "投机采样"
+ * (razer666.cn), section 投机解码算法, 第一步 - 采样 (guess x_i is sampled
+ * from the draft model's distribution q_i).
+ *
+ * For every request b and draft position j < n_b, x_j is drawn from
+ * q_j = softmax(draft_logits[b][j] / T_b) by the same inverse CDF as the
+ * verify step's draws, with the uniform u = word 0 of the Philox block at
+ * counter (philox_offset, b, j, 1), key (philox_seed, 0).  Counter word 3 is
+ * 1 here and 0 in spec_verify_run, so the two never share a uniform.  A
+ * greedy T_b (see Conventions) takes the lowest index of the row maximum.
+ * Rows are independent: a caller drafting autoregressively calls this once
+ * per position with K = 1 (and that position's index folded into
+ * philox_offset or the row layout).
+ *
+ *   draft_logits       device [B][K][V], cfg.draft_dtype, row-major, aligned
+ *                      to its element size.  Rows j >= n_b are never read.
+ *   num_drafts_per_req device [B] int32: n_b, expected in [0, K]; counts
+ *                      outside are clamped and flagged.  NULL: n_b = K.
+ *   temperatures       device [B] float: T_b.
+ *   out_ids            device [B][K] int32: x_j, or -1 for j >= n_b.
+ *   out_q              device [B][K] float: q_j(x_j) (1 for greedy rows,
+ *                      NaN for j >= n_b), or NULL.
+ *
+ * Shares the handle's workspace with spec_verify_run (same stream rules).
+ * Returns SV_ERR_UNSUPPORTED if the handle was created with
+ * draft_is_probs = 1 (the sampler needs logits), SV_ERR_INVALID_ARG (null
+ * or misaligned pointer, B < 0, K < 0), SV_ERR_CAPACITY (B > max_batch or
+ * K > max_drafts) or SV_ERR_HIP.  B == 0 or K == 0 enqueues nothing. */
+int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K,
+                      const void *draft_logits,
+                      const int32_t *num_drafts_per_req,
+                      const float *temperatures, uint64_t philox_seed,
+                      uint64_t philox_offset, int32_t *out_ids, float *out_q,
+                      void *stream);
 
 /* Waits for the handle's last run, copies the sticky SV_DEVERR_* bitmask to
  * *host_flags and, if clear != 0, resets it.  Synchronizing call. */

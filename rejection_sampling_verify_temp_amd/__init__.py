@@ -1,4 +1,5 @@
-"""Speculative-sampling verify step on MI355X (gfx950).
+"""Speculative-sampling verify step, and the draft-token sampler that feeds
+it, on MI355X (gfx950).
 
 The compute lives in the HIP library ``lib/libspecverify.so`` (kernels and
 C ABI under ``csrc/``, declared in ``include/spec_verify.h``); ``binding``
@@ -10,4 +11,5 @@ from .binding import (SpecVerify, SpecVerifyError, load_library, sv_config,  # n
                       spec_verify_get_device_errors, spec_verify_kernel_name,
                       spec_verify_run, spec_verify_status_string,
                       spec_verify_timing_enable, spec_verify_timing_read,
-                      spec_verify_chunk_elems, header_functions)
+                      spec_verify_chunk_elems, spec_draft_sample,
+                      header_functions)

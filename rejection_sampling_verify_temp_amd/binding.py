@@ -1,4 +1,5 @@
-"""ctypes binding of the verify-step C ABI (include/spec_verify.h).
+"""ctypes binding of the C ABI in include/spec_verify.h (the verify step and
+the draft-token sampler).
 
 The functions here carry the C names and only marshal arguments: every step
 of the verify path runs in the HIP kernels of libspecverify.so.  There is no
@@ -60,6 +61,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.spec_verify_run.argtypes = [P, i32, i32, P, P, P, P, P, P, u64, u64,
                                     P, P, P, P]
     lib.spec_verify_run.restype = ctypes.c_int
+    lib.spec_draft_sample.argtypes = [P, i32, i32, P, P, P, u64, u64, P, P, P]
+    lib.spec_draft_sample.restype = ctypes.c_int
     lib.spec_verify_get_device_errors.argtypes = [P, ctypes.POINTER(u32), i32]
     lib.spec_verify_get_device_errors.restype = ctypes.c_int
     lib.spec_verify_timing_enable.argtypes = [P, i32]
@@ -83,7 +86,7 @@ def header_functions(path: str = HEADER_PATH) -> list[str]:
     """Names of the functions include/spec_verify.h declares."""
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
 
 
 # --- the C entry points, same names ---------------------------------------
@@ -113,6 +116,15 @@ def spec_verify_run(h, B, K, target_logits, draft_probs, draft_mode, draft_ids,
         num_drafts_per_req, temperatures, int(philox_seed) & (2 ** 64 - 1),
         int(philox_offset) & (2 ** 64 - 1), out_tokens, out_num_accepted,
         out_debug_probs, stream)
+
+
+def spec_draft_sample(h, B, K, draft_logits, num_drafts_per_req, temperatures,
+                      philox_seed, philox_offset, out_ids, out_q, stream) -> int:
+    """Pointers are integers (device addresses); returns the status code."""
+    return load_library().spec_draft_sample(
+        h, int(B), int(K), draft_logits, num_drafts_per_req, temperatures,
+        int(philox_seed) & (2 ** 64 - 1), int(philox_offset) & (2 ** 64 - 1),
+        out_ids, out_q, stream)
 
 
 def spec_verify_get_device_errors(h, clear: bool = False) -> int:
@@ -231,6 +243,42 @@ class SpecVerify:
         if rc != SV_OK:
             raise SpecVerifyError("spec_verify_run", rc)
         return out_tokens, out_num_accepted
+
+    def sample(self, draft, num_drafts, temperatures, seed=0, offset=0,
+               out_ids=None, out_q=None, stream=None):
+        """Draft-token sampler: draft [B, K, V] logits (the handle's draft
+        dtype) -> ids [B, K] (-1 past n_b); q(x) into out_q if given."""
+        import torch
+        B, K, V = draft.shape
+        if V != self.cfg.vocab:
+            raise ValueError(f"vocab {V} != handle vocab {self.cfg.vocab}")
+        if _dtype_code(draft) != self.cfg.draft_dtype:
+            raise TypeError("draft dtype differs from the handle's")
+        dev = draft.device
+        if out_ids is None:
+            out_ids = torch.empty((B, K), dtype=torch.int32, device=dev)
+
+        def chk(t, shape, dtype=None):
+            if t is None:
+                return None
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("inputs must be contiguous device tensors")
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"shape {tuple(t.shape)} != {tuple(shape)}")
+            if dtype is not None and t.dtype != dtype:
+                raise TypeError(f"dtype {t.dtype} != {dtype}")
+            return t.data_ptr()
+
+        ptrs = [chk(draft, (B, K, V)), chk(num_drafts, (B,), torch.int32),
+                chk(temperatures, (B,), torch.float32)]
+        outs = [chk(out_ids, (B, K), torch.int32), chk(out_q, (B, K), torch.float32)]
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        rc = spec_draft_sample(self.handle, B, K, *ptrs, seed, offset, *outs,
+                               stream.cuda_stream)
+        if rc != SV_OK:
+            raise SpecVerifyError("spec_draft_sample", rc)
+        return out_ids
 
     def device_errors(self, clear=False):
         return spec_verify_get_device_errors(self.handle, clear)

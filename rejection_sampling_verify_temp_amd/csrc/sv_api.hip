@@ -98,6 +98,34 @@ hipError_t drain_one(spec_verify_s* h) {
   return hipSuccess;
 }
 
+// Enqueue the step's kernels on `stream`, with per-kernel events when
+// timing is on.
+int enqueue(spec_verify_s* h, const sv::RunParams& p, int tdt, int ddt, void* stream) {
+  DeviceGuard g(h->cfg.device);
+  if (!g.ok) return SV_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = nullptr;
+  if (h->timing) {
+    if (h->ev_pending == kTimingSlots && drain_one(h) != hipSuccess) return SV_ERR_HIP;
+    ev = h->ev[h->ev_next];
+  }
+  bool ok = true;
+  for (int k = 0; ok && k < sv::kNumKernels; ++k) {
+    hipEvent_t* e = ev ? &ev[2 * k] : nullptr;
+    ok = (!e || hipEventRecord(e[0], s) == hipSuccess) &&
+         sv::launch_kernel(k, p, tdt, ddt, s) == hipSuccess &&
+         (!e || hipEventRecord(e[1], s) == hipSuccess);
+  }
+  if (!ok) return SV_ERR_HIP;
+  if (h->timing) {
+    h->ev_next = (h->ev_next + 1) % kTimingSlots;
+    h->ev_pending++;
+  }
+  h->last_stream = s;
+  h->has_run = true;
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,7 +173,8 @@ int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
   h->nchunk = nchunk;
   const size_t rows = (size_t)c.max_batch * (2 * (size_t)c.max_drafts + 1);
   bool ok = hipMalloc(&h->part, rows * nchunk * sizeof(sv::Partial)) == hipSuccess &&
-            hipMalloc(&h->desc, (size_t)c.max_batch * sizeof(sv::DrawDesc)) == hipSuccess &&
+            hipMalloc(&h->desc, (size_t)c.max_batch * (c.max_drafts > 1 ? c.max_drafts : 1) *
+                                    sizeof(sv::DrawDesc)) == hipSuccess &&
             hipMalloc(&h->rsum, (size_t)c.max_batch * nchunk * sizeof(double)) == hipSuccess &&
             hipMalloc(&h->flags, sizeof(uint32_t)) == hipSuccess &&
             hipMemset(h->flags, 0, sizeof(uint32_t)) == hipSuccess;
@@ -204,29 +233,45 @@ int spec_verify_run(spec_verify_t h, int32_t B, int32_t K, const void* target_lo
   full.has_draft = draft_probs != nullptr;
   full.b_base = 0;
 
-  DeviceGuard g(c.device);
-  if (!g.ok) return SV_ERR_HIP;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t* ev = nullptr;
-  if (h->timing) {
-    if (h->ev_pending == kTimingSlots && drain_one(h) != hipSuccess) return SV_ERR_HIP;
-    ev = h->ev[h->ev_next];
-  }
-  bool ok = true;
-  for (int k = 0; ok && k < sv::kNumKernels; ++k) {
-    hipEvent_t* e = ev ? &ev[2 * k] : nullptr;
-    ok = (!e || hipEventRecord(e[0], s) == hipSuccess) &&
-         sv::launch_kernel(k, full, c.target_dtype, c.draft_dtype, s) == hipSuccess &&
-         (!e || hipEventRecord(e[1], s) == hipSuccess);
-  }
-  if (!ok) return SV_ERR_HIP;
-  if (h->timing) {
-    h->ev_next = (h->ev_next + 1) % kTimingSlots;
-    h->ev_pending++;
-  }
-  h->last_stream = s;
-  h->has_run = true;
-  return SV_OK;
+  return enqueue(h, full, c.target_dtype, c.draft_dtype, stream);
+}
+
+int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K, const void* draft_logits,
+                      const int32_t* num_drafts_per_req, const float* temperatures,
+                      uint64_t philox_seed, uint64_t philox_offset, int32_t* out_ids,
+                      float* out_q, void* stream) {
+  if (h == nullptr || B < 0 || K < 0) return SV_ERR_INVALID_ARG;
+  if (B > h->cfg.max_batch || K > h->cfg.max_drafts) return SV_ERR_CAPACITY;
+  const sv_config& c = h->cfg;
+  if (c.draft_is_probs) return SV_ERR_UNSUPPORTED;  // needs draft logits
+  if (B == 0 || K == 0) return SV_OK;
+  if (draft_logits == nullptr || temperatures == nullptr || out_ids == nullptr)
+    return SV_ERR_INVALID_ARG;
+  if (!aligned(draft_logits, elt_bytes(c.draft_dtype)) ||
+      (num_drafts_per_req != nullptr && !aligned(num_drafts_per_req, 4)) ||
+      !aligned(temperatures, 4) || !aligned(out_ids, 4) ||
+      (out_q != nullptr && !aligned(out_q, 4)))
+    return SV_ERR_INVALID_ARG;
+
+  sv::RunParams full{};
+  full.target = draft_logits;  // row (b, j) is "request" b * K + j, slot 0
+  full.nd = num_drafts_per_req;
+  full.temps = temperatures;
+  full.out_tokens = out_ids;
+  full.out_q = out_q;
+  full.part = h->part;
+  full.desc = h->desc;
+  full.rsum = h->rsum;
+  full.flags = h->flags;
+  full.seed = philox_seed;
+  full.offset = philox_offset;
+  full.B = B * K;
+  full.K = 0;
+  full.V = c.vocab;
+  full.chunk = h->chunk;
+  full.nchunk = h->nchunk;
+  full.sample_k = K;
+  return enqueue(h, full, c.draft_dtype, c.draft_dtype, stream);
 }
 
 int spec_verify_get_device_errors(spec_verify_t h, uint32_t* host_flags, int32_t clear) {

@@ -68,6 +68,11 @@ struct RunParams {
   int32_t draft_is_probs;
   int32_t has_draft;
   int32_t b_base;      // batch index of request 0 (Philox counters use b_base + b)
+  // Draft sampler: 0 for the verify step.  Otherwise each "request" is one
+  // draft row (b / sample_k, b % sample_k) of a [B][sample_k][V] logits
+  // buffer (passed as `target`, K = 0), drawn from softmax(l / T_b).
+  int32_t sample_k;
+  float* out_q;        // sampler: q(x) of each drawn token, or nullptr
 };
 
 constexpr int kNumKernels = 4;

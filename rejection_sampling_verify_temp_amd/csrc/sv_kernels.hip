@@ -89,6 +89,14 @@ __device__ void uniforms(uint64_t seed, uint64_t offset, int b, int j,
   *u_rec = (double)(ctr[1] >> 40) * 0x1p-24;
 }
 
+// The draft sampler's uniform for row j of request b: word 0 of the block at
+// counter (offset, b, j, 1); the verify step's counters have word 3 = 0.
+__device__ double draft_uniform(uint64_t seed, uint64_t offset, int b, int j) {
+  uint64_t ctr[4] = {offset, (uint64_t)b, (uint64_t)j, 1};
+  philox4x64_10(ctr, seed, 0);
+  return (double)(ctr[0] >> 40) * 0x1p-24;
+}
+
 // ---------------------------------------------------------------------------
 // Element formats
 // ---------------------------------------------------------------------------
@@ -429,27 +437,47 @@ __device__ __forceinline__ AmAcc chunk_argmax(const void* row, int c0, int c1) {
 // Requests
 // ---------------------------------------------------------------------------
 // Row slots of request b: 0..K are target rows j = slot, K+1..2K draft rows
-// j = slot - K - 1.
+// j = slot - K - 1.  In the draft sampler a request is one draft row, with
+// K = 0 and the row in slot 0.
 struct ReqInfo {
   int n;             // drafts, clamped into [0, K]
   float T;
   bool sampling;     // else greedy
   bool onehot;       // no draft distribution
   bool draft_stats;  // draft rows are logits whose softmax is needed
+  bool active;       // sampler: the row is below the request's draft count
+  bool bad_n;        // the request's draft count was outside [0, K]
+  int rb, rj;        // sampler: request and position of the row
 };
 
 __device__ __forceinline__ ReqInfo req_info(const RunParams& p, int b) {
   ReqInfo r;
-  r.n = clamp_drafts(p.nd[b], p.K);
-  r.T = p.temps[b];
+  if (p.sample_k > 0) {
+    r.rb = b / p.sample_k;
+    r.rj = b - r.rb * p.sample_k;
+    const int nb = p.nd != nullptr ? p.nd[r.rb] : p.sample_k;
+    r.bad_n = nb < 0 || nb > p.sample_k;
+    r.active = r.rj < clamp_drafts(nb, p.sample_k);
+    r.n = 0;
+    r.T = p.temps[r.rb];
+    r.onehot = true;
+  } else {
+    r.rb = b;
+    r.rj = 0;
+    const int nb = p.nd[b];
+    r.n = clamp_drafts(nb, p.K);
+    r.bad_n = nb != r.n;
+    r.active = true;
+    r.T = p.temps[b];
+    r.onehot = !p.has_draft || (p.mode != nullptr && p.mode[b] != 0);
+  }
   r.sampling = is_sampling(r.T);
-  r.onehot = !p.has_draft || (p.mode != nullptr && p.mode[b] != 0);
   r.draft_stats = r.sampling && !r.onehot && !p.draft_is_probs;
   return r;
 }
 
 __device__ __forceinline__ bool slot_needed(const ReqInfo& r, int s, int K) {
-  return s <= K ? s <= r.n : (s - K - 1 < r.n && r.draft_stats);
+  return r.active && (s <= K ? s <= r.n : (s - K - 1 < r.n && r.draft_stats));
 }
 
 __device__ __forceinline__ int rows_needed(const ReqInfo& r) {
@@ -569,8 +597,8 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
   if (outputs && lane <= K && lane != n_acc)
     p.out_tokens[(size_t)b * (K + 1) + lane] = lane < n_acc ? x : -1;
   if (outputs && lane == 0) {
-    p.out_nacc[b] = n_acc;
-    if (p.nd[b] != n) atomicOr(p.flags, SV_DEVERR_BAD_NUM_DRAFTS);
+    if (p.out_nacc != nullptr) p.out_nacc[b] = n_acc;
+    if (ri.bad_n && ri.rj == 0) atomicOr(p.flags, SV_DEVERR_BAD_NUM_DRAFTS);
   }
   if (outputs && p.out_dbg != nullptr && lane < K) {
     p.out_dbg[((size_t)b * K + lane) * 2 + 0] = dbg_p;
@@ -584,16 +612,25 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
     DrawDesc d{};
     d.j = je;
     d.x = -1;
-    if (!ri.sampling) {
+    if (!ri.active) {  // sampler row past the request's draft count
+      if (outputs) p.out_tokens[b] = -1;
+      if (outputs && p.out_q != nullptr) p.out_q[b] = __builtin_nanf("");
+      d.kind = kDrawNone;
+    } else if (!ri.sampling) {
       if (outputs) p.out_tokens[(size_t)b * (K + 1) + je] = t_idx;
+      if (outputs && p.out_q != nullptr) p.out_q[b] = 1.f;  // a point mass
       d.kind = kDrawNone;
     } else {
       d.c = c;
       d.ref_p = t_ref;
       d.z_p = t_z;
-      double u_acc, u_rec;
-      uniforms(p.seed, p.offset, p.b_base + b, je, &u_acc, &u_rec);
-      d.u = u_rec;
+      if (p.sample_k > 0) {
+        d.u = draft_uniform(p.seed, p.offset, p.b_base + ri.rb, ri.rj);
+      } else {
+        double u_acc, u_rec;
+        uniforms(p.seed, p.offset, p.b_base + b, je, &u_acc, &u_rec);
+        d.u = u_rec;
+      }
       d.kind = kDrawSingle;
       if (je < n) {  // rejected at je
         d.x = (x >= 0 && x < V) ? x : -1;
@@ -919,6 +956,10 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
       if (theta != __builtin_inf()) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
     }
     p.out_tokens[(size_t)b * (K + 1) + d.j] = c0 + y;
+    if (p.out_q != nullptr) {  // sampler: q(x) of the drawn token
+      const double l = Elt<TDT>::at(prow, c0 + y);
+      p.out_q[b] = (float)(exp2(l * (double)d.c + (double)d.ref_p) / d.z_p);
+    }
   }
 }
 

@@ -11,6 +11,7 @@ def test_library_exports_header_functions():
     lib = sv.load_library()
     names = sv.header_functions()
     assert "spec_verify_run" in names and "spec_verify_create" in names
+    assert "spec_draft_sample" in names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -53,6 +54,8 @@ def test_create_rejects_bad_config_without_device():
 
 def test_run_and_queries_reject_null_handle():
     assert sv.spec_verify_run(None, 1, 1, 1, 0, 0, 1, 1, 1, 0, 0, 1, 1, 0, None) == \
+        binding.SV_ERR_INVALID_ARG
+    assert sv.spec_draft_sample(None, 1, 1, 1, 0, 1, 0, 0, 1, 0, None) == \
         binding.SV_ERR_INVALID_ARG
     lib = sv.load_library()
     f = ctypes.c_uint32()
