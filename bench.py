@@ -1,6 +1,7 @@
 """Benchmark of the speculative-sampling verify step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+    python bench.py --op draft_sample     # the draft-token sampler instead
 
 One step = one spec_verify_run over a whole batch: row statistics, decisions,
 residual sums of rejected probabilistic drafts, and the draws.  Inputs are
@@ -13,7 +14,9 @@ with the library's own HIP events (spec_verify_timing_*), which gives the
 dominant kernel's duration for the roofline.
 
 Prints ONE JSON line.  value = verified (request x position x vocabulary)
-elements per second = sum_b (n_b + 1) * V / step time.
+elements per second = sum_b (n_b + 1) * V / step time.  With --op
+draft_sample a step is one spec_draft_sample over the workload's draft rows
+(j < n_b) and value = sampled elements per second = sum_b n_b * V / step time.
 """
 import argparse
 import hashlib
@@ -26,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "verified (req×pos×vocab) elems/s + achieved HBM GB/s vs peak, spec-verify step"
+METRIC_SAMPLE = "sampled (row×vocab) elems/s + achieved HBM GB/s vs peak, draft-token sampler"
 HBM_PEAK_GBPS = 8000.0
 DOMINANT = "stats"  # the kernel that streams every needed logits row
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", "sv_kernels.hip")
@@ -88,6 +92,32 @@ def cpu_baseline(w, seconds=12.0):
                        f"elems, {t:.1f} s of the single-threaded fp64 C oracle")
 
 
+def cpu_baseline_sample(w, nd, seconds=12.0):
+    """The CPU oracle's draft sampler, as it stands, on slices of 8 requests
+    of the same batch until about `seconds` of single-threaded work."""
+    import oracle
+    hs = w.host_arrays()
+    hs["num_drafts"] = nd.cpu().numpy()
+    V = w.V
+    n_req, elems, t, passes, start = 0, 0, 0.0, 0, 0
+    while t < seconds and passes < 64:
+        sl = slice(start, min(w.B, start + 8))
+        t0 = time.perf_counter()
+        oracle.draft_sample(hs["draft"][sl], hs["num_drafts"][sl],
+                            hs["temperatures"][sl], seed=0, offset=passes,
+                            diagnostics=False)
+        t += time.perf_counter() - t0
+        elems += int(hs["num_drafts"][sl].clip(0, w.K).sum()) * V
+        n_req += sl.stop - sl.start
+        start = sl.stop
+        if start >= w.B:
+            start, passes = 0, passes + 1
+    return dict(value=elems / t, unit="elems/s", cores=1, kind="oracle",
+                sample=f"{n_req} requests of the same batch (the batch cycled "
+                       f"with a new Philox offset per pass), {elems} sampled "
+                       f"elems, {t:.1f} s of the single-threaded fp64 C oracle")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +127,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--op", choices=["verify", "draft_sample"], default="verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run one plain device copy of this "
@@ -125,11 +156,25 @@ def main():
     nacc = torch.empty((w.B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    sample = args.op == "draft_sample"
+    if sample and (w.draft is None or w.draft_is_probs):
+        print("--op draft_sample needs a workload with draft logits", file=sys.stderr)
+        sys.exit(2)
+    ids = torch.empty((w.B, w.K), dtype=torch.int32, device=dev)
+    # the sampler draws the draft rows that hold logits: rows j < n_b of the
+    # probabilistic requests (one-hot requests have no draft distribution)
+    nd_sample = w.num_drafts if w.draft_mode is None else torch.where(
+        w.draft_mode == 0, w.num_drafts, torch.zeros_like(w.num_drafts))
+
     def step(i):
         c = copies[i % len(copies)]
-        h.run(c.target, c.draft, c.draft_mode, c.draft_ids, c.num_drafts,
-              c.temperatures, seed=0, offset=i, out_tokens=tok,
-              out_num_accepted=nacc, stream=stream)
+        if sample:
+            h.sample(c.draft, nd_sample, c.temperatures, seed=0, offset=i,
+                     out_ids=ids, stream=stream)
+        else:
+            h.run(c.target, c.draft, c.draft_mode, c.draft_ids, c.num_drafts,
+                  c.temperatures, seed=0, offset=i, out_tokens=tok,
+                  out_num_accepted=nacc, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -165,8 +210,13 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    elems = w.verified_elems()
-    alg = w.algorithmic_bytes()
+    if sample:
+        n_rows = int(nd_sample.clamp(0, w.K).sum().item())
+        elems = n_rows * w.V
+        alg = n_rows * w.V * w.draft.element_size()  # each sampled row read once
+    else:
+        elems = w.verified_elems()
+        alg = w.algorithmic_bytes()
     # bytes the residual pass re-reads: the rejected row pair of every
     # probabilistic sampling request (from the last step's outputs)
     n_b = w.num_drafts.clamp(0, w.K).cpu()
@@ -179,10 +229,10 @@ def main():
     resid_bytes = pairs * w.V * (w.elt() + delt)
     stats_ms = kern_ms[DOMINANT]
     achieved = alg / (stats_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.workload)
+    traffic = None if sample else read_traffic(args.workload)
     dt = {torch.bfloat16: "bf16", torch.float32: "f32"}[w.target.dtype]
     out = {
-        "metric": METRIC,
+        "metric": METRIC_SAMPLE if sample else METRIC,
         "value": elems / (ms_step * 1e-3),
         "unit": "elems/s",
         "n_gpus": 1,
@@ -194,16 +244,19 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"verify step, {w.name}",
+        "config": {"workload": (f"draft-token sampler, draft rows of {w.name}" if sample
+                                else f"verify step, {w.name}"),
                    "B": w.B, "K": w.K, "V": w.V, "logits": dt,
-                   "verified_elems": elems, "algorithmic_bytes": alg,
+                   ("sampled_elems" if sample else "verified_elems"): elems,
+                   "algorithmic_bytes": alg,
                    "nominal_bytes": w.nominal_bytes(),
                    "chunk_elems": h.chunk_elems, "input_copies": len(copies),
                    "parallelism": "single GPU"},
         "step_hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
-        "resid_pairs": pairs, "resid_bytes": resid_bytes,
+        "resid_pairs": None if sample else pairs,
+        "resid_bytes": None if sample else resid_bytes,
         "resid_gbps": (resid_bytes / (kern_ms["resid"] * 1e-3) / 1e9
-                       if "resid" in kern_ms else None),
+                       if "resid" in kern_ms and not sample else None),
         "kernels_ms": kern_ms,
         "roofline": {"bound": "hbm", "kernel": DOMINANT,
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -211,7 +264,7 @@ def main():
                      "traffic": traffic},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline_sample(w, nd_sample) if sample else cpu_baseline(w)
     h.close()
     print(json.dumps(out), flush=True)
 

@@ -35,7 +35,7 @@ struct __align__(16) DrawDesc {
   int32_t kind;
   int32_t j;       // position whose token is drawn
   int32_t x;       // token removed from the law, or -1
-  int32_t pad0;
+  int32_t cstar;   // chunk holding the draw, or -1 if the draw kernel picks it
   float c;         // log2(e) / T
   float ref_p;     // exponent reference of the target row
   float ref_q;     // exponent reference of the draft row (logit drafts)
@@ -44,6 +44,8 @@ struct __align__(16) DrawDesc {
   float pad1;
   double z_p;      // target row total relative to ref_p
   double u;        // draw uniform
+  double th;       // with cstar >= 0: u * S less the mass of chunks before cstar
+                   // (relative to ref_p); +inf if rounding left u * S past the end
 };
 
 struct RunParams {

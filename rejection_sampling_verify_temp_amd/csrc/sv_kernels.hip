@@ -606,12 +606,13 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
   }
 
   // the emitted position: greedy writes its argmax, sampling requests leave a
-  // draw descriptor for the residual kernel
+  // draw descriptor for the residual and draw kernels
+  DrawDesc d{};
   if (lane == n_acc) {
     const int je = n_acc;
-    DrawDesc d{};
     d.j = je;
     d.x = -1;
+    d.cstar = -1;
     if (!ri.active) {  // sampler row past the request's draft count
       if (outputs) p.out_tokens[b] = -1;
       if (outputs && p.out_q != nullptr) p.out_q[b] = __builtin_nanf("");
@@ -649,6 +650,56 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
         }
       }
     }
+  }
+
+  // a single-row draw (from p, less an excluded one-hot draft) is placed in
+  // its chunk here, one lane per chunk: chunk masses are the row's partials
+  // rescaled to ref_p, the values the fold above summed
+  if (__shfl(d.kind, n_acc, 64) == kDrawSingle) {
+    const int je = n_acc;
+    const float dc = __shfl(d.c, je, 64), dref = __shfl(d.ref_p, je, 64);
+    const double du = __shfl(d.u, je, 64);
+    int excl = __shfl(d.x, je, 64);
+    const float lx = __shfl(lt, je, 64);
+    double mass = 0.0, px = 0.0;
+    if (lane < p.nchunk) {
+      const Partial q = p.part[((size_t)b * nslot + je) * p.nchunk + lane];
+      if (q.z != 0.0) mass = q.z * exp2((double)dref - (double)ref_of(q.m, dc));
+      if (excl >= 0 && excl / p.chunk == lane) px = exp2((double)lx * (double)dc + (double)dref);
+    }
+    double mx = mass - px;
+    if (!(mx > 0.0)) mx = 0.0;
+    double incl = wave_incl_scan(mx, lane);
+    double S = __shfl(incl, 63, 64);
+    if (!(S > 0.0) && excl >= 0) {  // no residual mass: draw from p itself
+      if (outputs && lane == 0) atomicOr(p.flags, SV_DEVERR_ZERO_RESIDUAL);
+      excl = -1;
+      mx = mass > 0.0 ? mass : 0.0;
+      incl = wave_incl_scan(mx, lane);
+      S = __shfl(incl, 63, 64);
+    }
+    const double theta = du * S;
+    double before = __shfl_up(incl, 1, 64);
+    if (lane == 0) before = 0.0;
+    const uint64_t hits = __ballot(mx > 0.0 && before <= theta && theta < incl);
+    int cstar;
+    double th;
+    if (hits) {
+      cstar = (int)__builtin_ctzll(hits);
+      th = theta - __shfl(before, cstar, 64);
+    } else {  // rounding left theta at or past the total: last chunk with mass
+      const uint64_t has = __ballot(mx > 0.0);
+      cstar = has ? 63 - (int)__builtin_clzll(has) : 0;
+      th = __builtin_inf();
+      if (outputs && lane == 0) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
+    }
+    if (lane == je) {
+      d.cstar = cstar;
+      d.th = th;
+      d.x = excl;
+    }
+  }
+  if (lane == n_acc) {
     *d_out = d;
     if (outputs) p.desc[b] = d;
   }
@@ -806,41 +857,183 @@ __device__ __forceinline__ float resid_of(float lp, float lq, int kind, int i, i
   return i == excl ? 0.f : r;
 }
 
-// The draw runs kLocThreads threads, each owning kSeg consecutive elements
-// of the chosen chunk (kSeg * kLocThreads >= kMaxChunkElems).
-constexpr int kLocThreads = 1024;
-constexpr int kSeg = 16;
-static_assert(kSeg * kLocThreads >= kMaxChunkElems, "a chunk must fit the segments");
+// The draw of one request runs NT threads, each owning 16384 / NT
+// consecutive elements of the chosen chunk.  Few draws take 1024 threads
+// (short per-thread work); many draws take 256 (more draws resident per CU).
+template <int NT>
+constexpr int seg_len() { return 16384 / NT; }
+static_assert(seg_len<1024>() * 1024 >= kMaxChunkElems, "a chunk must fit the segments");
 
-// Logits of elements [i0, i0 + kSeg) of a row (i0 a multiple of kSeg; n of
-// them valid, the rest set to 0).  16-byte loads where the row allows.
-template <int DT>
-__device__ __forceinline__ void load_segment(const void* row, int i0, int n, float* x) {
+// Raw bits of SEG consecutive elements of a row, kept in registers instead
+// of floats (half the registers for bf16); element k is unpacked on use.
+template <int DT, int SEG>
+struct SegWords {
+  static constexpr int kWords = SEG * Elt<DT>::kBytes / 4;
+  uint32_t w[kWords];
+  __device__ __forceinline__ float at(int k) const {
+    if constexpr (DT == SV_BF16)
+      return __uint_as_float((k & 1) ? (w[k >> 1] & 0xffff0000u) : (w[k >> 1] << 16));
+    else
+      return __uint_as_float(w[k]);
+  }
+};
+
+// Elements [i0, i0 + n) of a row, n <= SEG (16-byte loads when the segment
+// is whole and aligned).  Words past n hold `pad` (a bit pattern whose
+// residual is 0), so no element needs a validity test later.
+template <int DT, int SEG>
+__device__ __forceinline__ void load_words(const void* row, int i0, int n, uint32_t pad,
+                                           SegWords<DT, SEG>& s) {
   using E = Elt<DT>;
   const uintptr_t a = reinterpret_cast<uintptr_t>(row) + (uintptr_t)i0 * E::kBytes;
-  if (n == kSeg && (a & 15u) == 0) {
+  if (n == SEG && (a & 15u) == 0) {
     const u32x4* v = reinterpret_cast<const u32x4*>(a);
 #pragma unroll
-    for (int k = 0; k < kSeg / E::kVec; ++k) E::unpack(v[k], x + k * E::kVec);
+    for (int k = 0; k < SegWords<DT, SEG>::kWords / 4; ++k) {
+      const u32x4 d = v[k];
+      s.w[4 * k] = d.x;
+      s.w[4 * k + 1] = d.y;
+      s.w[4 * k + 2] = d.z;
+      s.w[4 * k + 3] = d.w;
+    }
   } else {
 #pragma unroll
-    for (int k = 0; k < kSeg; ++k) x[k] = E::at(row, i0 + min(k, max(n - 1, 0)));
+    for (int k = 0; k < SEG; ++k) {
+      if constexpr (DT == SV_BF16) {
+        const uint32_t h = k < n ? static_cast<const uint16_t*>(row)[i0 + k] : (pad & 0xffffu);
+        s.w[k >> 1] = (k & 1) ? (s.w[k >> 1] | (h << 16)) : h;
+      } else {
+        s.w[k] = k < n ? static_cast<const uint32_t*>(row)[i0 + k] : pad;
+      }
+    }
   }
 }
 
-template <int TDT, int DDT>
+template <bool IS_PAIR, int TDT, int DDT, int SEG>
+__device__ __forceinline__ float seg_resid(const SegWords<TDT, SEG>& P,
+                                           const SegWords<DDT, SEG>& Q, const DrawDesc& d,
+                                           bool probs, int k) {
+  return IS_PAIR ? pair_resid(P.at(k), Q.at(k), d, probs) : single_resid(P.at(k), d);
+}
+
+// Residual sum of a whole segment, excluded token included (fp32 within
+// groups of 8, fp64 across them).
+template <bool IS_PAIR, int TDT, int DDT, int SEG>
+__device__ __forceinline__ double seg_sum(const SegWords<TDT, SEG>& P,
+                                          const SegWords<DDT, SEG>& Q, const DrawDesc& d,
+                                          bool probs) {
+  double seg = 0.0;
+#pragma unroll
+  for (int g = 0; g < SEG; g += 8) {
+    float r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = seg_resid<IS_PAIR>(P, Q, d, probs, g + k);
+    seg += (double)pairwise_sum(r);
+  }
+  return seg;
+}
+
+// Walk of a segment (q = mass before it, ex = excluded offset or -1, rx
+// its residual): the offset of the first element whose running sum passes
+// theta, else of the last element with positive residual (-1 if none).  Two
+// levels keep the serial fp64 chain short: the group sums of seg_sum
+// (recomputed bit for bit) find the group, then that group's 8 elements are
+// walked.  *logit receives the target logit of the chosen element.
+template <bool IS_PAIR, int TDT, int DDT, int SEG>
+__device__ __forceinline__ int seg_walk(const SegWords<TDT, SEG>& P,
+                                        const SegWords<DDT, SEG>& Q, const DrawDesc& d,
+                                        bool probs, int ex, float rx, double q, double theta,
+                                        float* logit) {
+  constexpr int NG = SEG / 8;
+  // (1) the group holding theta, else the last group with mass
+  double L = q;
+  int gstar = -1, glast = -1;
+  double Lstar = 0.0, Llast = 0.0;  // mass before gstar / glast
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = seg_resid<IS_PAIR>(P, Q, d, probs, 8 * g + k);
+    double sg = (double)pairwise_sum(r);
+    if (ex >= 8 * g && ex < 8 * g + 8) sg -= (double)rx;
+    const bool has = sg > 0.0;
+    const bool hit = gstar < 0 && has && L + sg > theta;
+    Lstar = hit ? L : Lstar;
+    gstar = hit ? g : gstar;
+    Llast = has ? L : Llast;
+    glast = has ? g : glast;
+    L += sg;
+    asm volatile("" : "+v"(gstar), "+v"(glast), "+v"(L), "+v"(Lstar), "+v"(Llast));
+  }
+  const int gw = gstar >= 0 ? gstar : glast;
+  if (gw < 0) return -1;
+  L = gstar >= 0 ? Lstar : Llast;
+  // (2) walk that group: its words are picked out with selects (a dynamic
+  // register index would go to scratch)
+  SegWords<TDT, 8> P8;
+  SegWords<DDT, 8> Q8;
+#pragma unroll
+  for (int i = 0; i < SegWords<TDT, 8>::kWords; ++i) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) v = g == gw ? P.w[g * SegWords<TDT, 8>::kWords + i] : v;
+    P8.w[i] = v;
+  }
+  if (IS_PAIR) {
+#pragma unroll
+    for (int i = 0; i < SegWords<DDT, 8>::kWords; ++i) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) v = g == gw ? Q.w[g * SegWords<DDT, 8>::kWords + i] : v;
+      Q8.w[i] = v;
+    }
+  }
+  const int exg = ex - 8 * gw;
+  int y = -1, lp = -1;
+  float ly = 0.f, llp = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float r = seg_resid<IS_PAIR>(P8, Q8, d, probs, k);
+    r = k != exg ? r : 0.f;
+    L += (double)r;
+    const bool pos = r > 0.f;
+    const bool hit = y < 0 && pos && L > theta;
+    y = hit ? k : y;
+    ly = hit ? P8.at(k) : ly;
+    lp = pos ? k : lp;
+    llp = pos ? P8.at(k) : llp;
+  }
+  *logit = y < 0 ? llp : ly;
+  const int yk = y < 0 ? lp : y;
+  return yk < 0 ? -1 : 8 * gw + yk;
+}
+
+// PAIR = false: a batch with no draft rows (no residual pairs).
+template <int TDT, int DDT, bool PAIR, int NT>
 __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
-  __shared__ int s_cstar, s_kind, s_excl, s_y, s_last;
+  constexpr int SEG = seg_len<NT>();
+  __shared__ int s_cstar, s_kind, s_excl, s_y, s_lastseg;
   __shared__ double s_theta;
-  __shared__ double s_woff[kLocThreads / 64];
+  __shared__ double s_woff[NT / 64];
   const int K = p.K, V = p.V, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const size_t trow = (size_t)b * (K + 1) + d.j;
   const void* prow = row_ptr(p.target, TDT, trow, V);
   const void* qrow = d.kind == kDrawPair ? row_ptr(p.draft, DDT, (size_t)b * K + d.j, V) : nullptr;
   const bool probs = p.draft_is_probs != 0;
 
-  // (a) the chunk holding u * S: wavefront 0, lane = chunk
-  if (w == 0) {
+  // (a) the chunk holding u * S.  Single-row draws were placed by the
+  // decision kernel; pair draws scan the residual chunk sums here
+  // (wavefront 0, lane = chunk).
+  if (d.cstar >= 0) {
+    if (tid == 0) {
+      s_cstar = d.cstar;
+      s_theta = d.th;
+      s_kind = d.kind;
+      s_excl = d.x;
+      s_y = INT32_MAX;
+      s_lastseg = -1;
+    }
+  } else if (w == 0) {
     int kind = d.kind, excl = d.x;
     for (int attempt = 0; attempt < 2; ++attempt) {
       double mass = 0.0;
@@ -886,80 +1079,85 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
         s_kind = kind;
         s_excl = excl;
         s_y = INT32_MAX;
-        s_last = -1;
+        s_lastseg = -1;
       }
       break;
     }
   }
   __syncthreads();
 
-  // (b) thread t owns chunk elements [t kSeg, t kSeg + kSeg): residuals in
-  // registers, their sum in fp64
+  // (b) thread t owns chunk elements [t SEG, t SEG + SEG): their raw words
+  // stay in registers, the residual sum is taken in fp64
   const int kind = s_kind, excl = s_excl;
   const int c0 = s_cstar * p.chunk;
   const int len = min(V, c0 + p.chunk) - c0;
-  const int i0 = tid * kSeg;
-  const int nseg = max(0, min(kSeg, len - i0));
-  float r[kSeg];
-  {
-    float lp[kSeg];
-    load_segment<TDT>(prow, c0 + min(i0, len - 1), nseg, lp);
-    if (kind == kDrawPair) {
-      float lq[kSeg];
-      load_segment<DDT>(qrow, c0 + min(i0, len - 1), nseg, lq);
-#pragma unroll
-      for (int k = 0; k < kSeg; ++k) r[k] = pair_resid(lp[k], lq[k], d, probs);
-    } else {
-#pragma unroll
-      for (int k = 0; k < kSeg; ++k) r[k] = single_resid(lp[k], d);
-    }
+  const int i0 = tid * SEG;
+  const int nseg = max(0, min(SEG, len - i0));
+  const bool pair = PAIR && kind == kDrawPair;
+  SegWords<TDT, SEG> P;
+  SegWords<DDT, SEG> Q;
+  // padding with residual 0: a -inf logit, or probability 0
+  const uint32_t pad_p = Elt<TDT>::kBytes == 2 ? 0xff80ff80u : 0xff800000u;
+  const uint32_t pad_q = probs ? 0u : (Elt<DDT>::kBytes == 2 ? 0xff80ff80u : 0xff800000u);
+  load_words<TDT>(prow, c0 + min(i0, len), nseg, pad_p, P);
+  if (pair) load_words<DDT>(qrow, c0 + min(i0, len), nseg, pad_q, Q);
+  int ex = excl >= 0 ? excl - c0 - i0 : -1;  // excluded token in the segment
+  if (ex >= nseg) ex = -1;
+  float rx = 0.f;  // its residual, from its own loads
+  if (ex >= 0) {
+    const float lp = Elt<TDT>::at(prow, excl);
+    rx = pair ? pair_resid(lp, Elt<DDT>::at(qrow, excl), d, probs) : single_resid(lp, d);
   }
-  double seg = 0.0;
-  int lastpos = -1;
-#pragma unroll
-  for (int k = 0; k < kSeg; ++k) {
-    if (k >= nseg || c0 + i0 + k == excl) r[k] = 0.f;
-    seg += (double)r[k];
-    if (r[k] > 0.f) lastpos = i0 + k;
-  }
+  double seg = pair ? seg_sum<true>(P, Q, d, probs) : seg_sum<false>(P, Q, d, probs);
+  seg -= (double)rx;
+  if (!(seg > 0.0)) seg = 0.0;
 
   // (c) exclusive scan of the segment sums
   const double incl = wave_incl_scan(seg, lane);
   if (lane == 63) s_woff[w] = incl;
   double q = __shfl_up(incl, 1, 64);
   if (lane == 0) q = 0.0;
-  if (lastpos >= 0) atomicMax(&s_last, lastpos);
+  if (seg > 0.0) atomicMax(&s_lastseg, tid);
   __syncthreads();
   for (int k = 0; k < w; ++k) q += s_woff[k];
 
-  // (d) the segment holding theta walks its registers
+  // (d) the segment holding theta walks its registers; if rounding left
+  // theta past every segment, the last segment with mass takes its last
+  // positive element
   const double theta = s_theta;
-  if (seg > 0.0 && q <= theta && theta < q + seg) {
-    double L = 0.0;
-    int y = -1, lp = -1;
+  const bool mine = seg > 0.0 && q <= theta && theta < q + seg;
+  const bool past = s_lastseg == tid && !(theta < q + seg);
+  int ymine = INT32_MAX;
+  float lmine = 0.f;  // target logit at ymine
+  if (mine || past) {
+    // recompute the residuals rather than keep SEG floats live across the
+    // barrier: the empty asm hides the first computation from CSE
 #pragma unroll
-    for (int k = 0; k < kSeg; ++k) {
-      L += (double)r[k];
-      if (r[k] > 0.f) {
-        if (y < 0 && q + L > theta) y = i0 + k;
-        lp = i0 + k;
-      }
+    for (int k = 0; k < SegWords<TDT, SEG>::kWords; ++k) asm volatile("" : "+v"(P.w[k]));
+    if (pair) {
+#pragma unroll
+      for (int k = 0; k < SegWords<DDT, SEG>::kWords; ++k) asm volatile("" : "+v"(Q.w[k]));
     }
-    if (y < 0) y = lp;  // rounding tie inside the segment
-    atomicMin(&s_y, y);
+    const double th = mine ? theta : __builtin_inf();
+    const int yo = pair ? seg_walk<true>(P, Q, d, probs, ex, rx, q, th, &lmine)
+                        : seg_walk<false>(P, Q, d, probs, ex, rx, q, th, &lmine);
+    if (yo >= 0) ymine = i0 + yo;
+    if (mine) atomicMin(&s_y, ymine);
   }
   __syncthreads();
-  if (tid == 0) {
-    int y = s_y;
-    if (y == INT32_MAX) {  // theta past the chunk's recomputed total
-      y = s_last >= 0 ? s_last : 0;
-      if (theta != __builtin_inf()) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
-    }
+  int y = s_y;
+  bool writer = y != INT32_MAX && y == ymine;  // segments are disjoint: one thread
+  if (y == INT32_MAX) {  // theta past the chunk's recomputed total
+    writer = s_lastseg >= 0 ? s_lastseg == tid : tid == 0;
+    const bool have = s_lastseg >= 0 && ymine != INT32_MAX;
+    y = have ? ymine : 0;
+    if (!have) lmine = Elt<TDT>::at(prow, c0);
+    if (writer && theta != __builtin_inf()) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
+  }
+  if (writer) {
     p.out_tokens[(size_t)b * (K + 1) + d.j] = c0 + y;
-    if (p.out_q != nullptr) {  // sampler: q(x) of the drawn token
-      const double l = Elt<TDT>::at(prow, c0 + y);
-      p.out_q[b] = (float)(exp2(l * (double)d.c + (double)d.ref_p) / d.z_p);
-    }
+    if (p.out_q != nullptr)  // sampler: q(x) of the drawn token
+      p.out_q[b] = (float)(exp2((double)lmine * (double)d.c + (double)d.ref_p) / d.z_p);
   }
 }
 
@@ -996,12 +1194,98 @@ __global__ __launch_bounds__(kThreads) void k_resid(
 // ---------------------------------------------------------------------------
 // Kernel 4: the draw of every sampling request
 // ---------------------------------------------------------------------------
-template <int TDT, int DDT>
-__global__ __launch_bounds__(kLocThreads) void k_locate(const RunParams p) {
+template <int TDT, int DDT, bool PAIR, int NT>
+__global__ __launch_bounds__(NT) void k_locate(const RunParams p) {
   const int b = blockIdx.x;
   const DrawDesc d = p.desc[b];
   if (d.kind == kDrawNone) return;
-  locate<TDT, DDT>(p, b, d);
+  locate<TDT, DDT, PAIR, NT>(p, b, d);
+}
+
+// Draft sampler: the draw of one row without a decision kernel.  Wavefront 0
+// folds the row's chunk partials (lane = chunk) into the row max and total
+// and places u * S in its chunk; the workgroup then walks that chunk.
+template <int DT, int NT>
+__global__ __launch_bounds__(NT) void k_sample(const RunParams p) {
+  __shared__ DrawDesc s_d;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  // the row's partials are loaded with the request's count and temperature
+  // (a row past the count wastes one small load)
+  Partial q{kNegInf, INT32_MAX, 0.0};
+  if (tid < 64 && lane < p.nchunk) q = p.part[(size_t)b * p.nchunk + lane];
+  const ReqInfo ri = req_info(p, b);
+  if (tid == 0 && ri.bad_n && ri.rj == 0) atomicOr(p.flags, SV_DEVERR_BAD_NUM_DRAFTS);
+  if (!ri.active) {  // row past the request's draft count
+    if (tid == 0) {
+      p.out_tokens[b] = -1;
+      if (p.out_q != nullptr) p.out_q[b] = __builtin_nanf("");
+    }
+    return;
+  }
+  if (tid < 64) {
+    if (!ri.sampling) {  // greedy: the lowest index of the row max
+      float m = q.m;
+      int i = lane < p.nchunk ? q.idx : INT32_MAX;
+      wave_argmax(m, i);
+      if (lane == 0) {
+        p.out_tokens[b] = i == INT32_MAX ? 0 : i;
+        if (p.out_q != nullptr) p.out_q[b] = 1.f;
+      }
+    } else {
+      const float c = temp_scale(ri.T);
+      const float ref = ref_of(wave_max(q.m), c);
+      double mass = 0.0;
+      if (lane < p.nchunk && q.z != 0.0) mass = q.z * exp2((double)ref - (double)ref_of(q.m, c));
+      const double incl = wave_incl_scan(mass, lane);
+      const double S = __shfl(incl, 63, 64);
+      const double u = draft_uniform(p.seed, p.offset, p.b_base + ri.rb, ri.rj);
+      const double theta = u * S;
+      double before = __shfl_up(incl, 1, 64);
+      if (lane == 0) before = 0.0;
+      const uint64_t hits = __ballot(mass > 0.0 && before <= theta && theta < incl);
+      int cstar;
+      double th;
+      if (hits) {
+        cstar = (int)__builtin_ctzll(hits);
+        th = theta - __shfl(before, cstar, 64);
+      } else {  // rounding left theta at or past the total: last chunk with mass
+        const uint64_t has = __ballot(mass > 0.0);
+        cstar = has ? 63 - (int)__builtin_clzll(has) : 0;
+        th = __builtin_inf();
+        if (lane == 0) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
+      }
+      if (lane == 0) {
+        DrawDesc d{};
+        d.kind = kDrawSingle;
+        d.j = 0;
+        d.x = -1;
+        d.cstar = cstar;
+        d.c = c;
+        d.ref_p = ref;
+        d.z_p = S;
+        d.u = u;
+        d.th = th;
+        s_d = d;
+      }
+    }
+  }
+  if (!ri.sampling) return;  // uniform across the workgroup
+  __syncthreads();
+  locate<DT, DT, false, NT>(p, b, s_d);
+}
+
+#ifndef SV_LOC_WIDE_MAX_DRAWS
+#define SV_LOC_WIDE_MAX_DRAWS 384
+#endif
+// Batches of at most this many draws use 1024-thread draws.
+constexpr int kLocWideMaxDraws = SV_LOC_WIDE_MAX_DRAWS;
+
+template <int TDT, int DDT, bool PAIR>
+void launch_locate(const RunParams& p, hipStream_t s) {
+  if (p.B <= kLocWideMaxDraws)
+    hipLaunchKernelGGL((k_locate<TDT, DDT, PAIR, 1024>), dim3(p.B), dim3(1024), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_locate<TDT, DDT, PAIR, 256>), dim3(p.B), dim3(256), 0, s, p);
 }
 
 template <int TDT, int DDT>
@@ -1012,8 +1296,8 @@ void launch_one(int k, const RunParams& p, hipStream_t s) {
       hipLaunchKernelGGL((k_stats<TDT, DDT>), dim3((unsigned)g), dim3(kThreads), 0, s, p);
       break;
     }
-    case kKernelDecide:
-      hipLaunchKernelGGL((k_decide<TDT, DDT>), dim3(p.B), dim3(64), 0, s, p);
+    case kKernelDecide:  // the draft sampler has no decisions
+      if (p.sample_k == 0) hipLaunchKernelGGL((k_decide<TDT, DDT>), dim3(p.B), dim3(64), 0, s, p);
       break;
     case kKernelResid:
       if (p.has_draft)
@@ -1021,7 +1305,16 @@ void launch_one(int k, const RunParams& p, hipStream_t s) {
                            dim3(kThreads), 0, s, p);
       break;
     default:
-      hipLaunchKernelGGL((k_locate<TDT, DDT>), dim3(p.B), dim3(kLocThreads), 0, s, p);
+      if (p.sample_k > 0) {
+        if (p.B <= kLocWideMaxDraws)
+          hipLaunchKernelGGL((k_sample<TDT, 1024>), dim3(p.B), dim3(1024), 0, s, p);
+        else
+          hipLaunchKernelGGL((k_sample<TDT, 256>), dim3(p.B), dim3(256), 0, s, p);
+      } else if (p.has_draft) {
+        launch_locate<TDT, DDT, true>(p, s);
+      } else {
+        launch_locate<TDT, DDT, false>(p, s);
+      }
       break;
   }
 }
