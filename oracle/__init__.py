@@ -1,5 +1,5 @@
-"""CPU oracle for the speculative-sampling verify step and the draft-token
-sampler that feeds it.
+"""CPU oracle for the speculative-sampling verify step, the draft-token
+sampler and the n-gram prompt-lookup proposer that feed it.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
 CPU-baseline leg of the benchmark may import this module.  The product path
@@ -72,6 +72,8 @@ def open_library(path: str):
     lib.svo_draft_sample.argtypes = [i32, i32, i32, i32, P, P, P, u64, u64,
                                      P, P, P]
     lib.svo_draft_sample.restype = u32
+    lib.svo_ngram_propose.argtypes = [i32, P, i32, P, i32, i32, i32, i32, P, P]
+    lib.svo_ngram_propose.restype = None
     return lib
 
 
@@ -238,3 +240,17 @@ def draft_sample(draft, num_drafts, temperatures, *, seed=0, offset=0,
         int(seed), int(offset), _ptr(ids),
         _ptr(q) if diagnostics else None, _ptr(margin) if diagnostics else None)
     return dict(ids=ids, q=q, margin=margin, flags=int(flags))
+
+
+def ngram_propose(context, lens, *, min_n, max_n, k, max_model_len):
+    """n-gram prompt lookup: context [B, stride] int32, lens [B] ->
+    (drafts [B, k] with -1 padding, num [B])."""
+    ctx = np.ascontiguousarray(context, dtype=np.int32)
+    B, stride = ctx.shape
+    ln = np.ascontiguousarray(lens, dtype=np.int32).reshape(B)
+    drafts = np.empty((B, k), dtype=np.int32)
+    num = np.empty(B, dtype=np.int32)
+    _load().svo_ngram_propose(B, _ptr(ctx), stride, _ptr(ln), int(min_n),
+                              int(max_n), int(k), int(max_model_len),
+                              _ptr(drafts), _ptr(num))
+    return drafts, num

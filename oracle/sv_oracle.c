@@ -456,3 +456,51 @@ uint32_t svo_draft_sample(int B, int K, int V, int dtype, const void *draft,
   free(q);
   return flags;
 }
+
+/* ------------------------------------------------------------------------ */
+/* n-gram prompt-lookup proposer.  [P1] section "n-gram": take the last n    */
+/* tokens of the sequence, find where they occurred before, and propose the  */
+/* k tokens that followed that earlier occurrence; the match is the longest  */
+/* one with n in [min_n, max_n] (prompt_lookup_min / max), and proposals     */
+/* stop at max_model_len.                                                    */
+/*                                                                          */
+/* Readings where the page is silent: the earlier occurrence must end before */
+/* the last token (it may overlap the suffix); among occurrences of the      */
+/* longest matching n-gram the most recent one is taken (the one a search    */
+/* over the reversed sequence meets first); the count is                     */
+/* min(k, tokens after the occurrence, max_model_len - N); no match gives no */
+/* drafts.  This is the definition written out: every n from the longest    */
+/* down, every end position from the latest down.                           */
+/*                                                                          */
+/*   context   [B][stride] int32; lens [B] (clamped into [0, stride])        */
+/*   out_drafts [B][k]: the proposed tokens, then -1; out_num [B]            */
+/* ------------------------------------------------------------------------ */
+void svo_ngram_propose(int B, const int32_t *context, int stride,
+                       const int32_t *lens, int min_n, int max_n, int k,
+                       int max_model_len, int32_t *out_drafts, int32_t *out_num) {
+  for (int b = 0; b < B; ++b) {
+    const int32_t *t = context + (size_t)b * stride;
+    int N = lens[b];
+    if (N < 0) N = 0;
+    if (N > stride) N = stride;
+    int count = 0, start = -1;
+    for (int n = max_n; n >= min_n && start < 0; --n) {
+      if (n > N - 1) continue;
+      for (int e = N - 2; e >= n - 1; --e) { /* occurrence t[e-n+1 .. e] */
+        int match = 1;
+        for (int i = 0; i < n; ++i)
+          if (t[e - i] != t[N - 1 - i]) { match = 0; break; }
+        if (match) { start = e + 1; break; }
+      }
+    }
+    if (start >= 0) {
+      count = k;
+      if (count > N - start) count = N - start;
+      if (count > max_model_len - N) count = max_model_len - N;
+      if (count < 0) count = 0;
+    }
+    for (int i = 0; i < k; ++i)
+      out_drafts[(size_t)b * k + i] = i < count ? t[start + i] : -1;
+    out_num[b] = count;
+  }
+}

@@ -444,6 +444,67 @@ def check_draft_sample_monte_carlo(B=1 << 17, V=8, T=0.8, seed=71):
         assert _chisq_ok(np.bincount(r["ids"][:, j], minlength=V), q), j
 
 
+# --------------------------------------------------------------------------
+# n-gram prompt-lookup proposer
+# --------------------------------------------------------------------------
+def _rfind_propose(tokens, N, min_n, max_n, k, max_model_len):
+    """The same rule through CPython's string search: tokens become code
+    points, and str.rfind over s[0:N-1] gives the latest occurrence of each
+    suffix that ends before the last token."""
+    s = "".join(chr(0x100 + int(t)) for t in tokens[:N])
+    for n in range(min(max_n, N - 1), min_n - 1, -1):
+        pos = s.rfind(s[N - n:], 0, N - 1)
+        if pos >= 0:
+            start = pos + n
+            count = max(0, min(k, N - start, max_model_len - N))
+            return [int(t) for t in tokens[start:start + count]]
+    return []
+
+
+def check_ngram_golden():
+    ex = _golden("ngram_lookup_example.json")
+    d, n = oracle.ngram_propose(np.array([ex["context"]]), [len(ex["context"])],
+                                min_n=ex["min_n"], max_n=ex["max_n"], k=ex["k"],
+                                max_model_len=ex["max_model_len"])
+    assert int(n[0]) == ex["num_drafts"] and d[0, :n[0]].tolist() == ex["drafts"], (d, n)
+
+
+def check_ngram_vs_rfind(cases=400, seed=81):
+    rng = np.random.default_rng(seed)
+    for c in range(cases):
+        B, stride = int(rng.integers(1, 5)), int(rng.integers(1, 120))
+        alphabet = int(rng.integers(2, 9))
+        ctx = rng.integers(0, alphabet, (B, stride)).astype(np.int32)
+        lens = rng.integers(0, stride + 1, B).astype(np.int32)
+        min_n = int(rng.integers(1, 4))
+        max_n = min_n + int(rng.integers(0, 5))
+        k = int(rng.integers(1, 8))
+        mml = int(rng.integers(1, 2 * stride + 2))
+        d, n = oracle.ngram_propose(ctx, lens, min_n=min_n, max_n=max_n, k=k, max_model_len=mml)
+        for b in range(B):
+            ref = _rfind_propose(ctx[b], int(lens[b]), min_n, max_n, k, mml)
+            assert int(n[b]) == len(ref) and d[b, :n[b]].tolist() == ref, (c, b, ref, d[b], n[b])
+            assert np.all(d[b, n[b]:] == -1)
+
+
+def check_ngram_edge_cases():
+    prop = lambda ctx, N, **kw: oracle.ngram_propose(np.array([ctx]), [N], **kw)
+    kw = dict(min_n=1, max_n=4, k=3, max_model_len=100)
+    for N in (0, 1):  # nothing to match against
+        assert prop([4, 4, 4], N, **kw)[1][0] == 0
+    assert prop([1, 2, 3, 4, 5], 5, **kw)[1][0] == 0            # no repeated token
+    d, n = prop([7, 7, 7, 7], 4, **kw)                          # overlapping occurrence
+    assert n[0] == 1 and d[0, 0] == 7
+    d, n = prop([1, 2, 9, 1, 2], 5, **kw)                       # only 3 tokens follow
+    assert n[0] == 3 and d[0].tolist() == [9, 1, 2]
+    d, n = prop([1, 2, 9, 1, 2], 5, min_n=1, max_n=4, k=3, max_model_len=6)
+    assert n[0] == 1 and d[0].tolist() == [9, -1, -1]           # stops at max_model_len
+    assert prop([1, 2, 9, 1, 2], 5, min_n=1, max_n=4, k=3, max_model_len=5)[1][0] == 0
+    assert prop([1, 2, 9, 1, 2], 5, min_n=3, max_n=4, k=3, max_model_len=100)[1][0] == 0
+    d, n = prop([3, 1, 5, 3, 1, 6, 3, 1], 8, **kw)              # latest of equal matches
+    assert n[0] == 3 and d[0].tolist() == [6, 3, 1]
+
+
 ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_accept_example_philox, check_bpd_greedy_example,
              check_greedy_bruteforce, check_enumeration_law,
@@ -452,4 +513,5 @@ ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_identical_draft_always_accepted,
              check_certain_onehot_always_accepted, check_zero_mass_never_drawn,
              check_invariants, check_draft_uniform_mapping,
-             check_draft_sample_vs_library, check_draft_sample_monte_carlo]
+             check_draft_sample_vs_library, check_draft_sample_monte_carlo,
+             check_ngram_golden, check_ngram_vs_rfind, check_ngram_edge_cases]

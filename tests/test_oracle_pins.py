@@ -36,6 +36,11 @@ MUTANTS = {
     "draft_temperature_ignored": ("svo_softmax(l, V, (double)T, q);", "svo_softmax(l, V, 1.0, q);"),
     "draft_rows_past_n": ("      if (j < n) {", "      if (j <= n && j < K) {"),
     "draft_same_uniform_all_rows": ("(uint64_t)b, (uint64_t)j),\n", "(uint64_t)b, 0),\n"),
+    "ngram_earliest_occurrence": ("for (int e = N - 2; e >= n - 1; --e) {", "for (int e = n - 1; e <= N - 2; ++e) {"),
+    "ngram_shortest_first": ("for (int n = max_n; n >= min_n && start < 0; --n) {",
+                             "for (int n = min_n; n <= max_n && start < 0; ++n) {"),
+    "ngram_self_match": ("for (int e = N - 2; e >= n - 1; --e) {", "for (int e = N - 1; e >= n - 1; --e) {"),
+    "ngram_no_length_limit": ("if (count > max_model_len - N) count = max_model_len - N;", ""),
 }
 
 
