@@ -1,6 +1,7 @@
 /*
  * spec_verify.h -- C ABI of the speculative-sampling verify step, and of
- * the draft-token sampler that feeds it, on MI355X (gfx950).
+ * the draft-token sampler and the n-gram proposer that feed it, on MI355X
+ * (gfx950).
  *
  * The operation (sources by page title and section):
  *   - "深入推测解码：从概念到实现" (Exploring Speculative Decoding), section
@@ -169,6 +170,43 @@ int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K,
                       const float *temperatures, uint64_t philox_seed,
                       uint64_t philox_offset, int32_t *out_ids, float *out_q,
                       void *stream);
+
+/* Longest n-gram spec_ngram_propose matches. */
+#define SPEC_NGRAM_MAX_N 32
+
+/* Enqueues the n-gram prompt-lookup proposer.  Source: "深入推测解码：从概念
+ * 到实现" (Exploring Speculative Decoding), section n-gram: the last n tokens
+ * of a request's context are found earlier in the context, and the k tokens
+ * that followed that occurrence are proposed; n is the longest match in
+ * [min_n, max_n] (prompt_lookup_min / max), and proposals stop at
+ * max_model_len.
+ *
+ * Readings where the page is silent: the earlier occurrence must end before
+ * the last token (it may overlap the suffix); among occurrences of the
+ * longest matching n-gram the most recent is used; the count is
+ * min(k, tokens after the occurrence, max_model_len - N); no match of length
+ * >= min_n gives no drafts.  The output feeds spec_verify_run as one-hot
+ * drafts (draft_mode 1, draft_ids = out_drafts, num_drafts = out_num).
+ *
+ *   context        device [B][stride] int32 token ids, row-major.
+ *   context_lens   device [B] int32: N_b, the tokens of row b in use;
+ *                  clamped into [0, stride].
+ *   min_n, max_n   1 <= min_n <= max_n <= SPEC_NGRAM_MAX_N.
+ *   k              drafts per request, >= 0.
+ *   max_model_len  >= 0; a request with N_b >= max_model_len gets none.
+ *   out_drafts     device [B][k] int32: the proposed tokens, then -1 (may
+ *                  be NULL when k == 0).
+ *   out_num_drafts device [B] int32: the count.
+ *
+ * Needs no handle; runs on the device of `stream` (a hipStream_t).  Only
+ * enqueues.  Returns SV_ERR_INVALID_ARG for a bad size or a null or
+ * misaligned pointer, SV_ERR_HIP on a launch failure.  B == 0 enqueues
+ * nothing. */
+int spec_ngram_propose(int32_t B, const int32_t *context, int32_t stride,
+                       const int32_t *context_lens, int32_t min_n,
+                       int32_t max_n, int32_t k, int32_t max_model_len,
+                       int32_t *out_drafts, int32_t *out_num_drafts,
+                       void *stream);
 
 /* Waits for the handle's last run, copies the sticky SV_DEVERR_* bitmask to
  * *host_flags and, if clear != 0, resets it.  Synchronizing call. */

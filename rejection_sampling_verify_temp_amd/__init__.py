@@ -1,5 +1,5 @@
-"""Speculative-sampling verify step, and the draft-token sampler that feeds
-it, on MI355X (gfx950).
+"""Speculative-sampling verify step, and the draft-token sampler and n-gram
+proposer that feed it, on MI355X (gfx950).
 
 The compute lives in the HIP library ``lib/libspecverify.so`` (kernels and
 C ABI under ``csrc/``, declared in ``include/spec_verify.h``); ``binding``
@@ -12,4 +12,4 @@ from .binding import (SpecVerify, SpecVerifyError, load_library, sv_config,  # n
                       spec_verify_run, spec_verify_status_string,
                       spec_verify_timing_enable, spec_verify_timing_read,
                       spec_verify_chunk_elems, spec_draft_sample,
-                      header_functions)
+                      spec_ngram_propose, ngram_propose, header_functions)

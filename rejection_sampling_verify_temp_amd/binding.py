@@ -1,5 +1,5 @@
-"""ctypes binding of the C ABI in include/spec_verify.h (the verify step and
-the draft-token sampler).
+"""ctypes binding of the C ABI in include/spec_verify.h (the verify step, the
+draft-token sampler and the n-gram proposer).
 
 The functions here carry the C names and only marshal arguments: every step
 of the verify path runs in the HIP kernels of libspecverify.so.  There is no
@@ -63,6 +63,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.spec_verify_run.restype = ctypes.c_int
     lib.spec_draft_sample.argtypes = [P, i32, i32, P, P, P, u64, u64, P, P, P]
     lib.spec_draft_sample.restype = ctypes.c_int
+    lib.spec_ngram_propose.argtypes = [i32, P, i32, P, i32, i32, i32, i32, P, P, P]
+    lib.spec_ngram_propose.restype = ctypes.c_int
     lib.spec_verify_get_device_errors.argtypes = [P, ctypes.POINTER(u32), i32]
     lib.spec_verify_get_device_errors.restype = ctypes.c_int
     lib.spec_verify_timing_enable.argtypes = [P, i32]
@@ -125,6 +127,43 @@ def spec_draft_sample(h, B, K, draft_logits, num_drafts_per_req, temperatures,
         h, int(B), int(K), draft_logits, num_drafts_per_req, temperatures,
         int(philox_seed) & (2 ** 64 - 1), int(philox_offset) & (2 ** 64 - 1),
         out_ids, out_q, stream)
+
+
+def spec_ngram_propose(B, context, stride, context_lens, min_n, max_n, k,
+                       max_model_len, out_drafts, out_num_drafts, stream) -> int:
+    """Pointers are integers (device addresses); returns the status code."""
+    return load_library().spec_ngram_propose(
+        int(B), context, int(stride), context_lens, int(min_n), int(max_n),
+        int(k), int(max_model_len), out_drafts, out_num_drafts, stream)
+
+
+def ngram_propose(context, context_lens, *, min_n, max_n, k, max_model_len,
+                  out_drafts=None, out_num=None, stream=None):
+    """torch wrapper: context [B, stride] int32 and context_lens [B] int32
+    device tensors -> (drafts [B, k] with -1 padding, num [B])."""
+    import torch
+    if context.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("context and context_lens must be int32")
+    if not (context.is_cuda and context.is_contiguous() and context_lens.is_cuda
+            and context_lens.is_contiguous()):
+        raise ValueError("inputs must be contiguous device tensors")
+    B, stride = context.shape
+    if tuple(context_lens.shape) != (B,):
+        raise ValueError("context_lens must be [B]")
+    dev = context.device
+    if out_drafts is None:
+        out_drafts = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if out_num is None:
+        out_num = torch.empty((B,), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = spec_ngram_propose(B, context.data_ptr(), stride, context_lens.data_ptr(),
+                            min_n, max_n, k, max_model_len,
+                            out_drafts.data_ptr() if k > 0 else None,
+                            out_num.data_ptr(), stream.cuda_stream)
+    if rc != SV_OK:
+        raise SpecVerifyError("spec_ngram_propose", rc)
+    return out_drafts, out_num
 
 
 def spec_verify_get_device_errors(h, clear: bool = False) -> int:

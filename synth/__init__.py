@@ -156,6 +156,52 @@ def _zipf_base(g, B, R, V, device):
     return out, ranks
 
 
+def make_contexts(B, N, V, *, seed=0, device="cpu", alpha=1.1, ragged=False,
+                  copy_spans=0, span=(8, 33), tail_copy_frac=0.0):
+    """Token contexts for the n-gram proposer: row b holds N ids drawn i.i.d.
+    from request b's Zipf unigram law (weight rank^-alpha under a per-request
+    permutation of the V ids), as the n-gram requests of the B=512 workload.
+    With copy_spans > 0, that many spans (lengths in [span[0], span[1])) are
+    copied from earlier in the row to later positions, the repeats that make
+    prompt lookup pay off; with tail_copy_frac, that fraction of rows also
+    ends in a copy of an earlier span (a suffix that occurred before).
+    ragged: lengths uniform in [1, N], else all N.
+    Returns (context [B, N] int32, lens [B] int32)."""
+    device = torch.device(device)
+    g = _gen(device, seed)
+    ctx = torch.empty((B, N), dtype=torch.int64, device=device)
+    for b0 in range(0, B, 64):
+        b1 = min(B, b0 + 64)
+        w = torch.empty((b1 - b0, V), device=device, dtype=torch.float32)
+        for b in range(b0, b1):
+            perm = torch.randperm(V, generator=g, device=device)
+            w[b - b0] = (perm + 1).to(torch.float32).pow(-alpha)
+        ctx[b0:b1] = torch.multinomial(w, N, replacement=True, generator=g)
+    if copy_spans > 0 and N > 2 * span[0]:
+        for b in range(B):
+            for _ in range(copy_spans):
+                L = int(torch.randint(span[0], span[1], (1,), generator=g, device=device))
+                L = min(L, N // 2)
+                src = int(torch.randint(0, N - 2 * L + 1, (1,), generator=g, device=device))
+                dst = int(torch.randint(src + L, N - L + 1, (1,), generator=g, device=device))
+                ctx[b, dst:dst + L] = ctx[b, src:src + L].clone()
+    if ragged:
+        lens = torch.randint(1, N + 1, (B,), generator=g, device=device)
+    else:
+        lens = torch.full((B,), N, device=device)
+    if tail_copy_frac > 0 and N > 2 * span[0]:
+        pick = torch.rand(B, generator=g, device=device) < tail_copy_frac
+        for b in range(B):
+            n_b = int(lens[b])
+            if not bool(pick[b]) or n_b <= 2 * span[0]:
+                continue
+            L = min(int(torch.randint(span[0], span[1], (1,), generator=g, device=device)),
+                    n_b // 2)
+            src = int(torch.randint(0, n_b - 2 * L + 1, (1,), generator=g, device=device))
+            ctx[b, n_b - L:n_b] = ctx[b, src:src + L].clone()
+    return ctx.to(torch.int32).contiguous(), lens.to(torch.int32)
+
+
 def make_config(idx: int, device="cpu", seed: int | None = None) -> Workload:
     """The five verify workloads (shapes, value laws and draft structure)."""
     device = torch.device(device)

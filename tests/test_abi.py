@@ -11,7 +11,7 @@ def test_library_exports_header_functions():
     lib = sv.load_library()
     names = sv.header_functions()
     assert "spec_verify_run" in names and "spec_verify_create" in names
-    assert "spec_draft_sample" in names
+    assert "spec_draft_sample" in names and "spec_ngram_propose" in names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -57,6 +57,18 @@ def test_run_and_queries_reject_null_handle():
         binding.SV_ERR_INVALID_ARG
     assert sv.spec_draft_sample(None, 1, 1, 1, 0, 1, 0, 0, 1, 0, None) == \
         binding.SV_ERR_INVALID_ARG
+
+
+def test_ngram_rejects_bad_arguments_without_device():
+    bad = [dict(B=-1), dict(min_n=0), dict(max_n=0), dict(min_n=3, max_n=2),
+           dict(max_n=33), dict(k=-1), dict(max_model_len=-1), dict(stride=0),
+           dict(context=None), dict(context=2)]
+    for b in bad:
+        a = dict(B=1, context=4, stride=8, context_lens=4, min_n=1, max_n=4, k=3,
+                 max_model_len=100, out_drafts=4, out_num_drafts=4, stream=None)
+        a.update(b)
+        assert sv.spec_ngram_propose(**a) == binding.SV_ERR_INVALID_ARG, b
+    assert sv.spec_ngram_propose(0, None, 0, None, 1, 4, 3, 100, None, None, None) == 0
     lib = sv.load_library()
     f = ctypes.c_uint32()
     assert lib.spec_verify_get_device_errors(None, ctypes.byref(f), 0) == binding.SV_ERR_INVALID_ARG
