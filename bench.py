@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
     python bench.py --op draft_sample     # the draft-token sampler instead
+    python bench.py --op ngram            # the n-gram prompt-lookup proposer
 
 One step = one spec_verify_run over a whole batch: row statistics, decisions,
 residual sums of rejected probabilistic drafts, and the draws.  Inputs are
@@ -118,6 +119,74 @@ def cpu_baseline_sample(w, nd, seconds=12.0):
                        f"elems, {t:.1f} s of the single-threaded fp64 C oracle")
 
 
+METRIC_NGRAM = "scanned context tokens/s + achieved HBM GB/s vs peak, n-gram prompt-lookup proposer"
+NGRAM = dict(B=512, N=2048, V=129280, min_n=2, max_n=5, k=3, max_model_len=8192)
+
+
+def bench_ngram(args):
+    """n-gram proposer: 512 Zipf-unigram contexts of 2048 tokens (V = 129280,
+    four copied spans each, half ending in a copy of an earlier span), n in
+    [2, 5], k = 3.  A step is one spec_ngram_propose over the batch."""
+    import torch
+    import synth
+    import rejection_sampling_verify_temp_amd as sv
+    c = NGRAM
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copies = [synth.make_contexts(c["B"], c["N"], c["V"], seed=21 + i, copy_spans=4,
+                                  tail_copy_frac=0.5, device=dev) for i in range(args.rotate)]
+    drafts = torch.empty((c["B"], c["k"]), dtype=torch.int32, device=dev)
+    num = torch.empty((c["B"],), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    kw = {k: c[k] for k in ("min_n", "max_n", "k", "max_model_len")}
+
+    def step(i):
+        ctx, lens = copies[i % len(copies)]
+        sv.ngram_propose(ctx, lens, out_drafts=drafts, out_num=num, stream=stream, **kw)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tokens = sum(int(l.sum().item()) for _, l in copies) / len(copies)
+    alg = tokens * 4 + c["B"] * (c["k"] + 1) * 4  # each context token read once, outputs
+    proposals = int((num > 0).sum().item())
+    out = {
+        "metric": METRIC_NGRAM,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "n-gram proposer, B=512 Zipf(1.1) contexts of 2048 tokens, "
+                               "V=129280, n in [2, 5], k=3",
+                   **c, "input_copies": len(copies), "requests_with_drafts": proposals,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "ngram", "achieved": alg / (ms_step * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        ctx, lens = (t.cpu().numpy() for t in copies[0])
+        t0, reps = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.ngram_propose(ctx, lens, **kw)
+            reps += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(value=reps * float(lens.sum()) / dt, unit="tokens/s", cores=1,
+                                   kind="oracle",
+                                   sample=f"{reps} passes over the same 512 contexts, {dt:.1f} s "
+                                          "of the single-threaded C oracle")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,7 +196,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--op", choices=["verify", "draft_sample"], default="verify")
+    ap.add_argument("--op", choices=["verify", "draft_sample", "ngram"], default="verify")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run one plain device copy of this "
@@ -137,6 +206,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU "
               "path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.op == "ngram":
+        return bench_ngram(args)
 
     import torch
     import synth

@@ -7,9 +7,12 @@
 // runs a KMP search per request on the CPU.  Here one workgroup per request
 // tests every end position in parallel: thread t compares the tokens ending
 // at positions N-2-t, N-2-t-256, ... backwards against the suffix and stops at
-// the first mismatch, so on ordinary text most positions cost one load.  The
-// best (length, end) pair is a 64-bit max over the workgroup: the longest
-// match, and among equals the most recent one.
+// the first mismatch, so on ordinary text most positions cost one compare.
+// The context is staged through LDS in tiles of 4096 tokens (plus the 31
+// tokens before a tile that a comparison can reach), so the comparisons read
+// LDS and each tile costs one round trip to memory.  The best (length, end)
+// pair is a 64-bit max over the workgroup: the longest match, and among
+// equals the most recent one.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,12 +35,17 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+constexpr int kTile = 4096;               // context tokens per LDS tile
+constexpr int kHalo = kMaxNgram - 1;      // earlier tokens a comparison can reach
+
 __global__ __launch_bounds__(kNgramThreads) void k_ngram(const int32_t* __restrict__ ctx,
                                                          int stride,
                                                          const int32_t* __restrict__ lens,
                                                          int min_n, int max_n, int k,
                                                          int max_model_len, int32_t* out,
                                                          int32_t* out_num) {
+  // tile [e0 - kHalo, e0 + kTile) of the context; lds[kHalo + i] = t[e0 + i]
+  __shared__ int32_t lds[kHalo + kTile];
   __shared__ uint64_t s_best[kNgramThreads / 64];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int32_t* t = ctx + (size_t)b * stride;
@@ -50,21 +58,45 @@ __global__ __launch_bounds__(kNgramThreads) void k_ngram(const int32_t* __restri
 #pragma unroll
   for (int i = 0; i < kMaxNgram; ++i) suf[i] = i < nmax ? t[N - 1 - i] : 0;
 
-  // key = (match length << 32) | (end + 1); 0 = no match of length >= min_n
+  // key = (match length << 32) | (end + 1); 0 = no match of length >= min_n.
+  // End positions e run over [0, N - 2], one LDS tile at a time.
   uint64_t best = 0;
-  for (int e = N - 2 - tid; e >= 0; e -= kNgramThreads) {
-    int len = 0;
-    bool alive = true;
-#pragma unroll
-    for (int i = 0; i < kMaxNgram; ++i) {
-      if (alive) {
-        alive = i < nmax && i <= e && t[e - i] == suf[i];
-        len += alive;
+  for (int e0 = 0; e0 <= N - 2; e0 += kTile) {
+    const int lo = max(0, e0 - kHalo), hi = min(N - 1, e0 + kTile);  // tokens [lo, hi)
+    if (e0 > 0) __syncthreads();  // the previous tile is no longer read
+    const bool vec = ((reinterpret_cast<uintptr_t>(t + e0) & 15u) == 0);
+    if (vec) {  // 16-byte loads for the tile body, single loads for the rest
+      const int nv = (hi - e0) / 4;
+      const int4* v = reinterpret_cast<const int4*>(t + e0);
+      for (int i = tid; i < nv; i += kNgramThreads) {
+        const int4 x = v[i];
+        int32_t* d = lds + kHalo + 4 * i;
+        d[0] = x.x;
+        d[1] = x.y;
+        d[2] = x.z;
+        d[3] = x.w;
       }
+      for (int i = e0 + 4 * nv + tid; i < hi; i += kNgramThreads) lds[kHalo + i - e0] = t[i];
+    } else {
+      for (int i = e0 + tid; i < hi; i += kNgramThreads) lds[kHalo + i - e0] = t[i];
     }
-    if (len >= min_n) {
-      const uint64_t key = ((uint64_t)len << 32) | (uint32_t)(e + 1);
-      best = key > best ? key : best;
+    for (int i = lo + tid; i < e0; i += kNgramThreads) lds[kHalo + i - e0] = t[i];
+    __syncthreads();
+    const int e1 = min(N - 2, e0 + kTile - 1);
+    for (int e = e1 - tid; e >= e0; e -= kNgramThreads) {
+      int len = 0;
+      bool alive = true;
+#pragma unroll
+      for (int i = 0; i < kMaxNgram; ++i) {
+        if (alive) {
+          alive = i < nmax && i <= e && lds[kHalo + e - e0 - i] == suf[i];
+          len += alive;
+        }
+      }
+      if (len >= min_n) {
+        const uint64_t key = ((uint64_t)len << 32) | (uint32_t)(e + 1);
+        best = key > best ? key : best;
+      }
     }
   }
   best = wave_max_u64(best);
