@@ -1,5 +1,6 @@
-"""CPU oracle for the speculative-sampling verify step, the draft-token
-sampler and the n-gram prompt-lookup proposer that feed it.
+"""CPU oracle for the speculative-sampling verify step (rejection sampling,
+and typical acceptance), the draft-token sampler and the n-gram prompt-lookup
+proposer that feed it.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
 CPU-baseline leg of the benchmark may import this module.  The product path
@@ -74,6 +75,9 @@ def open_library(path: str):
     lib.svo_draft_sample.restype = u32
     lib.svo_ngram_propose.argtypes = [i32, P, i32, P, i32, i32, i32, i32, P, P]
     lib.svo_ngram_propose.restype = None
+    lib.svo_verify_typical.argtypes = [i32, i32, i32, i32, P, P, P, P, dbl, i32,
+                                       u64, u64, P, P, P, P, P]
+    lib.svo_verify_typical.restype = u32
     return lib
 
 
@@ -254,3 +258,28 @@ def ngram_propose(context, lens, *, min_n, max_n, k, max_model_len):
                               int(max_n), int(k), int(max_model_len),
                               _ptr(drafts), _ptr(num))
     return drafts, num
+
+
+def verify_typical(target, draft_ids, num_drafts, temperatures, *, eps, top_k=0,
+                   seed=0, offset=0, diagnostics=True):
+    """Typical acceptance on host arrays (target [B, K+1, V] float32 or bf16
+    bits).  Returns a dict with tokens, num_accepted, p (= p_j(x_j)),
+    margin_acc, margin_rec and flags, in the layout of verify()."""
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    ids = np.ascontiguousarray(draft_ids, dtype=np.int32).reshape(B, K)
+    nd = np.ascontiguousarray(num_drafts, dtype=np.int32).reshape(B)
+    temps = np.ascontiguousarray(temperatures, dtype=np.float32).reshape(B)
+    tokens = np.empty((B, K + 1), dtype=np.int32)
+    nacc = np.empty(B, dtype=np.int32)
+    p = np.empty((B, K), dtype=np.float64)
+    macc = np.empty((B, K), dtype=np.float64)
+    mrec = np.empty(B, dtype=np.float64)
+    d = diagnostics
+    flags = _load().svo_verify_typical(
+        B, K, V, _dtype_code(target), _ptr(target), _ptr(ids), _ptr(nd), _ptr(temps),
+        float(eps), int(top_k), int(seed), int(offset), _ptr(tokens), _ptr(nacc),
+        _ptr(p) if d else None, _ptr(macc) if d else None, _ptr(mrec) if d else None)
+    return dict(tokens=tokens, num_accepted=nacc, p=p, q=np.ones_like(p),
+                margin_acc=macc, margin_rec=mrec, flags=int(flags))

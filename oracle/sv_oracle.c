@@ -504,3 +504,95 @@ void svo_ngram_propose(int B, const int32_t *context, int stride,
     out_num[b] = count;
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Typical acceptance.  [P3] section 验收标准, Typical Acceptance: a draft    */
+/* token is accepted when its probability exceeds a hard threshold; the      */
+/* threshold can be relaxed through a top-k constraint; the tokens that form */
+/* the longest accepted run are kept and the rest discarded.                 */
+/*                                                                          */
+/* Readings: the probability is the target's p_j = softmax(l_j / T_b); x_j  */
+/* is accepted iff p_j(x_j) > eps or x_j ranks among the top_k of row j,    */
+/* i.e. #{i : l_i > l_x} < top_k (top_k = 0: the threshold alone; ties at   */
+/* the k-th value are all in); the walk stops at the first rejection; the    */
+/* token at that position, or the bonus token after n_b acceptances, is     */
+/* drawn from p itself with the verify step's draw uniform (no residual:    */
+/* there is no q); greedy requests keep the exact-match rule.               */
+/* Outputs as svo_verify; out_p[b][j] = p_j(x_j), margins: |p(x) - eps|     */
+/* (+inf when the rank decides, or for greedy requests).                     */
+/* ------------------------------------------------------------------------ */
+uint32_t svo_verify_typical(int B, int K, int V, int target_dtype,
+                            const void *target, const int32_t *draft_ids,
+                            const int32_t *num_drafts,
+                            const float *temperatures, double eps, int top_k,
+                            uint64_t seed, uint64_t offset, int32_t *out_tokens,
+                            int32_t *out_num_accepted, double *out_p,
+                            double *out_margin_acc, double *out_margin_rec) {
+  uint32_t flags = 0;
+  double *l = malloc(sizeof(double) * (size_t)V);
+  double *p = malloc(sizeof(double) * (size_t)V);
+  for (int b = 0; b < B; ++b) {
+    int n = num_drafts[b];
+    if (n < 0 || n > K) {
+      flags |= SVO_FLAG_BAD_NUM_DRAFTS;
+      n = n < 0 ? 0 : K;
+    }
+    const float T = temperatures[b];
+    const int sampling = svo_is_sampling(T);
+    const size_t row0 = (size_t)b * (K + 1);
+    for (int j = 0; j < K; ++j) {
+      if (out_p) out_p[(size_t)b * K + j] = NAN;
+      if (out_margin_acc) out_margin_acc[(size_t)b * K + j] = NAN;
+    }
+    int n_acc = 0;
+    for (int j = 0; j < n; ++j) {
+      const int x = draft_ids[(size_t)b * K + j];
+      const int valid = x >= 0 && x < V;
+      if (!valid) flags |= SVO_FLAG_BAD_DRAFT_ID;
+      load_row(target, target_dtype, row0 + j, V, l);
+      int accept;
+      double margin = INFINITY;
+      if (!sampling) {
+        accept = valid && l[x] == l[svo_argmax(l, V)];
+      } else {
+        svo_softmax(l, V, (double)T, p);
+        int above = 0;
+        if (valid)
+          for (int i = 0; i < V; ++i) above += l[i] > l[x];
+        const double px = valid ? p[x] : 0.0;
+        if (valid && above < top_k) {
+          accept = 1;
+        } else {
+          accept = valid && px > eps;
+          margin = fabs(px - eps);
+        }
+        if (out_p && valid) out_p[(size_t)b * K + j] = px;
+      }
+      if (out_margin_acc) out_margin_acc[(size_t)b * K + j] = margin;
+      if (!accept) break;
+      n_acc++;
+    }
+    int y;
+    double margin_rec = INFINITY;
+    load_row(target, target_dtype, row0 + n_acc, V, l);
+    if (!sampling) {
+      y = svo_argmax(l, V);
+    } else {
+      double ua, ur;
+      svo_uniforms(seed, offset, (uint64_t)b, (uint64_t)n_acc, &ua, &ur);
+      svo_softmax(l, V, (double)T, p);
+      y = svo_draw(p, V, ur, &margin_rec);
+    }
+    for (int j = 0; j < K + 1; ++j) {
+      int32_t tok = -1;
+      if (j < n_acc) tok = draft_ids[(size_t)b * K + j];
+      else if (j == n_acc) tok = y;
+      out_tokens[(size_t)b * (K + 1) + j] = tok;
+    }
+    out_num_accepted[b] = n_acc;
+    if (out_margin_rec) out_margin_rec[b] = margin_rec;
+  }
+  free(l);
+  free(p);
+  return flags;
+}

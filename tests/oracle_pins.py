@@ -505,6 +505,109 @@ def check_ngram_edge_cases():
     assert n[0] == 3 and d[0].tolist() == [6, 3, 1]
 
 
+# --------------------------------------------------------------------------
+# Typical acceptance
+# --------------------------------------------------------------------------
+def check_typical_golden():
+    ex = _golden("typical_acceptance_example.json")
+    t = np.log(np.array(ex["probs"], dtype=np.float64)).astype(np.float32)[None]
+    for case in ex["cases"]:
+        r = oracle.verify_typical(t, np.array([ex["draft_ids"]]), [2], [1.0],
+                                  eps=ex["eps"], top_k=case["top_k"])
+        assert r["num_accepted"][0] == case["num_accepted"], (case, r["num_accepted"])
+
+
+def _typical_case(rng, B, K, V):
+    t = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    ids = rng.integers(0, V, (B, K)).astype(np.int32)
+    top = np.argsort(-t[:, :K], axis=-1)[..., :3]  # some drafts among the top tokens
+    pick = rng.random((B, K)) < 0.6
+    ids = np.where(pick, np.take_along_axis(top, rng.integers(0, 3, (B, K, 1)), -1)[..., 0], ids)
+    nd = rng.integers(0, K + 1, B).astype(np.int32)
+    return t, ids.astype(np.int32), nd
+
+
+def check_typical_vs_library(cases=60, seed=91):
+    """Acceptances, the accepted prefix and the emitted token against numpy /
+    scipy: accept iff softmax(l/T)[x] > eps or #{l_i > l_x} < top_k; the
+    emitted token is searchsorted over p's cumulative sum (skipping draws
+    within 1e-9 of a boundary and decisions within 1e-12 of eps)."""
+    rng = np.random.default_rng(seed)
+    for c in range(cases):
+        B, K, V = int(rng.integers(1, 6)), int(rng.integers(1, 6)), int(rng.integers(2, 200))
+        t, ids, nd = _typical_case(rng, B, K, V)
+        temps = rng.choice([1.0, 0.6, 1.5, 0.0], B).astype(np.float32)
+        eps, top_k = float(rng.choice([0.0, 0.01, 0.05, 0.2, 1.0])), int(rng.integers(0, 4))
+        r = oracle.verify_typical(t, ids, nd, temps, eps=eps, top_k=top_k, seed=c, offset=c)
+        for b in range(B):
+            T = float(temps[b])
+            n_acc, ambiguous = 0, False
+            for j in range(int(nd[b])):
+                row, x = t[b, j].astype(np.float64), int(ids[b, j])
+                if T == 0.0:
+                    ok = row[x] == row.max()
+                else:
+                    p = scipy.special.softmax(row / T)
+                    ok = p[x] > eps or int(np.sum(row > row[x])) < top_k
+                    if abs(p[x] - eps) < 1e-12 and int(np.sum(row > row[x])) >= top_k:
+                        ambiguous = True
+                        break
+                if not ok:
+                    break
+                n_acc += 1
+            if ambiguous:
+                continue
+            assert r["num_accepted"][b] == n_acc, (c, b, r["num_accepted"][b], n_acc)
+            assert np.array_equal(r["tokens"][b, :n_acc], ids[b, :n_acc])
+            row = t[b, n_acc].astype(np.float64)
+            if T == 0.0:
+                y = int(np.argmax(row))
+            else:
+                p = scipy.special.softmax(row / T)
+                _, u = oracle.uniforms(c, c, b, n_acc)
+                cdf = np.cumsum(p)
+                y = int(np.searchsorted(cdf, u * cdf[-1], side="right"))
+                if r["margin_rec"][b] <= 1e-9:
+                    continue
+            assert r["tokens"][b, n_acc] == y, (c, b, r["tokens"][b], y)
+
+
+def check_typical_special_cases(seed=93):
+    """eps = 1 with top_k = 1 accepts exactly the drafts the greedy rule
+    accepts (x a row max); eps = 0 accepts every valid draft; eps = 1 with
+    top_k = 0 rejects at once and emits the plain temperature sample of row 0,
+    the token of the verify step with n_b = 0."""
+    rng = np.random.default_rng(seed)
+    B, K, V = 64, 4, 40
+    t, ids, nd = _typical_case(rng, B, K, V)
+    t = np.round(t)  # ties at the max
+    g = oracle.verify(t, None, ids, nd, np.zeros(B, np.float32))
+    r = oracle.verify_typical(t, ids, nd, np.ones(B, np.float32), eps=1.0, top_k=1)
+    assert np.array_equal(r["num_accepted"], g["num_accepted"])
+    r = oracle.verify_typical(t, ids, nd, np.full(B, 0.8, np.float32), eps=0.0)
+    assert np.array_equal(r["num_accepted"], nd)
+    r = oracle.verify_typical(t, ids, nd, np.full(B, 0.8, np.float32), eps=1.0, top_k=0,
+                              seed=4, offset=6)
+    assert np.all(r["num_accepted"] == 0)
+    plain = oracle.verify(t, None, ids, np.zeros(B, np.int32), np.full(B, 0.8, np.float32),
+                          seed=4, offset=6)
+    assert np.array_equal(r["tokens"][:, 0], plain["tokens"][:, 0])
+
+
+def check_typical_correction_law(B=1 << 17, V=6, T=0.9, seed=95):
+    """A draft that is always rejected: the emitted token follows p_0."""
+    rng = np.random.default_rng(seed)
+    row = rng.normal(0, 1, V).astype(np.float32)
+    t = np.broadcast_to(np.stack([row, row]), (B, 2, V)).copy()
+    x = int(np.argmin(row))
+    r = oracle.verify_typical(t, np.full((B, 1), x, np.int32), np.ones(B, np.int32),
+                              np.full(B, T, np.float32), eps=0.99, top_k=0, seed=seed,
+                              diagnostics=False)
+    assert np.all(r["num_accepted"] == 0)
+    p = scipy.special.softmax(row.astype(np.float64) / T)
+    assert _chisq_ok(np.bincount(r["tokens"][:, 0], minlength=V), p)
+
+
 ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_accept_example_philox, check_bpd_greedy_example,
              check_greedy_bruteforce, check_enumeration_law,
@@ -514,4 +617,6 @@ ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_certain_onehot_always_accepted, check_zero_mass_never_drawn,
              check_invariants, check_draft_uniform_mapping,
              check_draft_sample_vs_library, check_draft_sample_monte_carlo,
-             check_ngram_golden, check_ngram_vs_rfind, check_ngram_edge_cases]
+             check_ngram_golden, check_ngram_vs_rfind, check_ngram_edge_cases,
+             check_typical_golden, check_typical_vs_library, check_typical_special_cases,
+             check_typical_correction_law]

@@ -41,6 +41,11 @@ MUTANTS = {
                              "for (int n = min_n; n <= max_n && start < 0; ++n) {"),
     "ngram_self_match": ("for (int e = N - 2; e >= n - 1; --e) {", "for (int e = N - 1; e >= n - 1; --e) {"),
     "ngram_no_length_limit": ("if (count > max_model_len - N) count = max_model_len - N;", ""),
+    "typical_rank_off_by_one": ("if (valid && above < top_k) {", "if (valid && above <= top_k) {"),
+    "typical_threshold_on_logit": ("const double px = valid ? p[x] : 0.0;", "const double px = valid ? l[x] : 0.0;"),
+    "typical_no_stop": ("      if (!accept) break;\n      n_acc++;", "      if (accept) n_acc++;"),
+    "typical_draw_from_bonus_row": ("load_row(target, target_dtype, row0 + n_acc, V, l);",
+                                    "load_row(target, target_dtype, row0 + n, V, l);"),
 }
 
 
