@@ -518,8 +518,9 @@ void svo_ngram_propose(int B, const int32_t *context, int stride,
 /* token at that position, or the bonus token after n_b acceptances, is     */
 /* drawn from p itself with the verify step's draw uniform (no residual:    */
 /* there is no q); greedy requests keep the exact-match rule.               */
-/* Outputs as svo_verify; out_p[b][j] = p_j(x_j), margins: |p(x) - eps|     */
-/* (+inf when the rank decides, or for greedy requests).                     */
+/* Outputs as svo_verify; out_p[b][j] = p_j(x_j) for every drafted j of a    */
+/* sampling request; margins: |p(x) - eps| (+inf when the rank decides, or  */
+/* for greedy requests; NaN past the first rejection).                      */
 /* ------------------------------------------------------------------------ */
 uint32_t svo_verify_typical(int B, int K, int V, int target_dtype,
                             const void *target, const int32_t *draft_ids,
@@ -566,7 +567,6 @@ uint32_t svo_verify_typical(int B, int K, int V, int target_dtype,
           accept = valid && px > eps;
           margin = fabs(px - eps);
         }
-        if (out_p && valid) out_p[(size_t)b * K + j] = px;
       }
       if (out_margin_acc) out_margin_acc[(size_t)b * K + j] = margin;
       if (!accept) break;
@@ -591,6 +591,17 @@ uint32_t svo_verify_typical(int B, int K, int V, int target_dtype,
     }
     out_num_accepted[b] = n_acc;
     if (out_margin_rec) out_margin_rec[b] = margin_rec;
+
+    /* Diagnostics: p_j(x_j) for every drafted position, as in svo_verify. */
+    if (sampling && out_p) {
+      for (int j = 0; j < n; ++j) {
+        const int x = draft_ids[(size_t)b * K + j];
+        if (x < 0 || x >= V) continue;
+        load_row(target, target_dtype, row0 + j, V, l);
+        svo_softmax(l, V, (double)T, p);
+        out_p[(size_t)b * K + j] = p[x];
+      }
+    }
   }
   free(l);
   free(p);
