@@ -133,6 +133,35 @@ int spec_verify_run(spec_verify_t h, int32_t B, int32_t K,
                     int32_t *out_num_accepted, float *out_debug_probs,
                     void *stream);
 
+/* Enqueues a verify step with typical acceptance instead of rejection
+ * sampling.  Source: "投机采样" (razer666.cn), section 验收标准, Typical
+ * Acceptance: a draft token is accepted when its probability exceeds a hard
+ * threshold, the threshold may be relaxed through a top-k constraint, and
+ * the longest accepted run is kept.  The rule is lossy: outputs no longer
+ * follow p exactly.
+ *
+ * Readings: x_j is accepted iff p_j(x_j) > threshold or x_j ranks among the
+ * top_k tokens of target row j, i.e. #{i : l_i > l_x} < top_k (top_k = 0:
+ * the threshold alone); the walk stops at the first rejection; the token at
+ * that position, or the bonus token after n_b acceptances, is drawn from
+ * p itself with the draw uniform of spec_verify_run (word 1 of the block at
+ * counter (philox_offset, b, j, 0)); greedy requests keep exact matching.
+ * There are no draft rows: only ids.
+ *
+ * Arguments as spec_verify_run without draft_probs and draft_mode;
+ * threshold >= 0 and finite, top_k >= 0.  out_debug_probs holds
+ * (p_j(x_j), 1).  Returns SV_ERR_INVALID_ARG (bad threshold or top_k, null
+ * or misaligned pointer, B < 0, K < 0), SV_ERR_CAPACITY or SV_ERR_HIP. */
+int spec_verify_run_typical(spec_verify_t h, int32_t B, int32_t K,
+                            const void *target_logits,
+                            const int32_t *draft_ids,
+                            const int32_t *num_drafts_per_req,
+                            const float *temperatures, float threshold,
+                            int32_t top_k, uint64_t philox_seed,
+                            uint64_t philox_offset, int32_t *out_tokens,
+                            int32_t *out_num_accepted, float *out_debug_probs,
+                            void *stream);
+
 /* Enqueues the draft-token sampler: the step that produces the drafts the
  * verify step checks.  Sources: "深入推测解码：从概念到实现" (Exploring
  * Speculative Decoding), section 引言, the propose pseudo-code (each draft

@@ -12,4 +12,5 @@ from .binding import (SpecVerify, SpecVerifyError, load_library, sv_config,  # n
                       spec_verify_run, spec_verify_status_string,
                       spec_verify_timing_enable, spec_verify_timing_read,
                       spec_verify_chunk_elems, spec_draft_sample,
-                      spec_ngram_propose, ngram_propose, header_functions)
+                      spec_ngram_propose, ngram_propose, spec_verify_run_typical,
+                      header_functions)

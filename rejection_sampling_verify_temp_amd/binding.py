@@ -61,6 +61,9 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.spec_verify_run.argtypes = [P, i32, i32, P, P, P, P, P, P, u64, u64,
                                     P, P, P, P]
     lib.spec_verify_run.restype = ctypes.c_int
+    lib.spec_verify_run_typical.argtypes = [P, i32, i32, P, P, P, P, ctypes.c_float, i32,
+                                            u64, u64, P, P, P, P]
+    lib.spec_verify_run_typical.restype = ctypes.c_int
     lib.spec_draft_sample.argtypes = [P, i32, i32, P, P, P, u64, u64, P, P, P]
     lib.spec_draft_sample.restype = ctypes.c_int
     lib.spec_ngram_propose.argtypes = [i32, P, i32, P, i32, i32, i32, i32, P, P, P]
@@ -116,6 +119,17 @@ def spec_verify_run(h, B, K, target_logits, draft_probs, draft_mode, draft_ids,
     return load_library().spec_verify_run(
         h, int(B), int(K), target_logits, draft_probs, draft_mode, draft_ids,
         num_drafts_per_req, temperatures, int(philox_seed) & (2 ** 64 - 1),
+        int(philox_offset) & (2 ** 64 - 1), out_tokens, out_num_accepted,
+        out_debug_probs, stream)
+
+
+def spec_verify_run_typical(h, B, K, target_logits, draft_ids, num_drafts_per_req,
+                            temperatures, threshold, top_k, philox_seed, philox_offset,
+                            out_tokens, out_num_accepted, out_debug_probs, stream) -> int:
+    """Pointers are integers (device addresses); returns the status code."""
+    return load_library().spec_verify_run_typical(
+        h, int(B), int(K), target_logits, draft_ids, num_drafts_per_req, temperatures,
+        float(threshold), int(top_k), int(philox_seed) & (2 ** 64 - 1),
         int(philox_offset) & (2 ** 64 - 1), out_tokens, out_num_accepted,
         out_debug_probs, stream)
 
@@ -281,6 +295,47 @@ class SpecVerify:
                              stream.cuda_stream)
         if rc != SV_OK:
             raise SpecVerifyError("spec_verify_run", rc)
+        return out_tokens, out_num_accepted
+
+    def run_typical(self, target, draft_ids, num_drafts, temperatures, threshold,
+                    top_k=0, seed=0, offset=0, out_tokens=None, out_num_accepted=None,
+                    out_debug_probs=None, stream=None):
+        """Typical acceptance: target [B, K+1, V] logits, draft ids [B, K]."""
+        import torch
+        B, K1, V = target.shape
+        K = K1 - 1
+        if V != self.cfg.vocab:
+            raise ValueError(f"vocab {V} != handle vocab {self.cfg.vocab}")
+        if _dtype_code(target) != self.cfg.target_dtype:
+            raise TypeError("target dtype differs from the handle's")
+
+        def chk(t, shape, dtype=None):
+            if t is None:
+                return None
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("inputs must be contiguous device tensors")
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"shape {tuple(t.shape)} != {tuple(shape)}")
+            if dtype is not None and t.dtype != dtype:
+                raise TypeError(f"dtype {t.dtype} != {dtype}")
+            return t.data_ptr()
+
+        dev = target.device
+        if out_tokens is None:
+            out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        if out_num_accepted is None:
+            out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+        ptrs = [chk(target, (B, K + 1, V)), chk(draft_ids, (B, K), torch.int32),
+                chk(num_drafts, (B,), torch.int32), chk(temperatures, (B,), torch.float32)]
+        outs = [chk(out_tokens, (B, K + 1), torch.int32),
+                chk(out_num_accepted, (B,), torch.int32),
+                chk(out_debug_probs, (B, K, 2), torch.float32)]
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        rc = spec_verify_run_typical(self.handle, B, K, *ptrs, threshold, top_k, seed,
+                                     offset, *outs, stream.cuda_stream)
+        if rc != SV_OK:
+            raise SpecVerifyError("spec_verify_run_typical", rc)
         return out_tokens, out_num_accepted
 
     def sample(self, draft, num_drafts, temperatures, seed=0, offset=0,

@@ -1,6 +1,7 @@
 // Host side of the verify-step C ABI: argument checks, the workspace, and
 // the launches (see spec_verify.h for the contract).
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -233,6 +234,51 @@ int spec_verify_run(spec_verify_t h, int32_t B, int32_t K, const void* target_lo
   full.has_draft = draft_probs != nullptr;
   full.b_base = 0;
 
+  return enqueue(h, full, c.target_dtype, c.draft_dtype, stream);
+}
+
+int spec_verify_run_typical(spec_verify_t h, int32_t B, int32_t K, const void* target_logits,
+                            const int32_t* draft_ids, const int32_t* num_drafts_per_req,
+                            const float* temperatures, float threshold, int32_t top_k,
+                            uint64_t philox_seed, uint64_t philox_offset, int32_t* out_tokens,
+                            int32_t* out_num_accepted, float* out_debug_probs, void* stream) {
+  if (h == nullptr || B < 0 || K < 0 || !(threshold >= 0.f && threshold <= FLT_MAX) ||
+      top_k < 0)
+    return SV_ERR_INVALID_ARG;
+  if (B > h->cfg.max_batch || K > h->cfg.max_drafts) return SV_ERR_CAPACITY;
+  if (B == 0) return SV_OK;
+  const sv_config& c = h->cfg;
+  if (target_logits == nullptr || num_drafts_per_req == nullptr || temperatures == nullptr ||
+      out_tokens == nullptr || out_num_accepted == nullptr || (K > 0 && draft_ids == nullptr))
+    return SV_ERR_INVALID_ARG;
+  if (!aligned(target_logits, elt_bytes(c.target_dtype)) ||
+      (draft_ids != nullptr && !aligned(draft_ids, 4)) || !aligned(num_drafts_per_req, 4) ||
+      !aligned(temperatures, 4) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      (out_debug_probs != nullptr && !aligned(out_debug_probs, 4)))
+    return SV_ERR_INVALID_ARG;
+
+  sv::RunParams full{};
+  full.target = target_logits;
+  full.ids = draft_ids;
+  full.nd = num_drafts_per_req;
+  full.temps = temperatures;
+  full.out_tokens = out_tokens;
+  full.out_nacc = out_num_accepted;
+  full.out_dbg = out_debug_probs;
+  full.part = h->part;
+  full.desc = h->desc;
+  full.rsum = h->rsum;
+  full.flags = h->flags;
+  full.seed = philox_seed;
+  full.offset = philox_offset;
+  full.B = B;
+  full.K = K;
+  full.V = c.vocab;
+  full.chunk = h->chunk;
+  full.nchunk = h->nchunk;
+  full.typical = 1;
+  full.eps = threshold;
+  full.top_k = top_k;
   return enqueue(h, full, c.target_dtype, c.draft_dtype, stream);
 }
 

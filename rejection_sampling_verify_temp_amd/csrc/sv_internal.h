@@ -16,8 +16,9 @@ constexpr int kMaxVocab = kMaxChunks * kMaxChunkElems;
 constexpr int kMaxDrafts = 31;       // the 2K+1 row slots fit one wavefront
 
 // Per (row, vocabulary chunk) statistics.  Sampling rows: m = chunk max,
-// z = sum over the chunk of exp2(l_i * c + ref(m, c)).  Greedy rows: m =
-// chunk max, idx = lowest index attaining it.
+// z = sum over the chunk of exp2(l_i * c + ref(m, c)), idx = the count of
+// elements above the draft's logit under typical acceptance (else unused).
+// Greedy rows: m = chunk max, idx = lowest index attaining it.
 struct __align__(16) Partial {
   float m;
   int32_t idx;
@@ -75,6 +76,12 @@ struct RunParams {
   // buffer (passed as `target`, K = 0), drawn from softmax(l / T_b).
   int32_t sample_k;
   float* out_q;        // sampler: q(x) of each drawn token, or nullptr
+  // Typical acceptance (no draft rows): accept x_j iff p_j(x_j) > eps or
+  // #{i : l_i > l_x} < top_k; the statistics pass then also counts, per
+  // chunk, the elements above l_x (into Partial::idx).
+  int32_t typical;
+  float eps;
+  int32_t top_k;
 };
 
 constexpr int kNumKernels = 4;

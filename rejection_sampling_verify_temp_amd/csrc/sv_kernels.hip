@@ -267,6 +267,20 @@ __device__ double block_sum(double v, double* lds) {
 }
 
 template <int NT>
+__device__ int block_sum_int(int v, int* lds) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) lds[w] = v;
+  __syncthreads();
+  int r = lds[0];
+#pragma unroll
+  for (int k = 1; k < NT / 64; ++k) r += lds[k];
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
 __device__ void block_argmax(float& m, int& i, float* ldsm, int* ldsi) {
   wave_argmax(m, i);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -324,16 +338,19 @@ __device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
 // without rescaling, and no element needs a running-max test.  Vectors past
 // the chunk's end are neither loaded nor folded (the test is uniform in all
 // but one wave of a pass).
-template <int DT>
+// COUNT: also count the chunk's elements above lx (into *above).
+template <int DT, bool COUNT>
 __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int c1, float c,
                                                     float* ldsf, double* ldsd, float* m_out,
-                                                    double* z_out) {
+                                                    double* z_out, float lx = 0.f,
+                                                    int* ldsi = nullptr, int* above = nullptr) {
   using E = Elt<DT>;
   const Geo g = chunk_geo<DT>(row, c0, c1);
   const int tid = threadIdx.x;
   const u32x4* vp = reinterpret_cast<const u32x4*>(
       static_cast<const char*>(row) + (size_t)g.v0 * E::kBytes);
   float M = kNegInf, R = 0.f, S = 0.f;
+  int cnt = 0;
   for (int base = 0; base == 0 || base < g.nvec; base += kThreads * kUnroll) {
     const int v = base + tid;
     u32x4 d[kUnroll];
@@ -345,13 +362,17 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
     if (base == 0 && g.c0 + tid < g.v0) ht[0] = E::at(row, g.c0 + tid);
     if (base == 0 && g.t0 + tid < g.c1) ht[1] = E::at(row, g.t0 + tid);
     float t = fmaxf(ht[0], ht[1]);
+    if (COUNT) cnt += (ht[0] > lx) + (ht[1] > lx);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (v + u * kThreads < g.nvec) {
         float x[E::kVec];
         E::unpack(d[u], x);
 #pragma unroll
-        for (int k = 0; k < E::kVec; ++k) t = fmaxf(t, x[k]);
+        for (int k = 0; k < E::kVec; ++k) {
+          t = fmaxf(t, x[k]);
+          if (COUNT) cnt += x[k] > lx;
+        }
       }
     }
     const float pm = block_max<kThreads>(t, ldsf);
@@ -380,6 +401,7 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
   }
   *z_out = block_sum<kThreads>((double)S, ldsd);
   *m_out = M;
+  if (COUNT) *above = block_sum_int<kThreads>(cnt, ldsi);
 }
 
 template <int DT>
@@ -522,20 +544,24 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
   float r_ref = 0.f;  // sampling: exponent reference; greedy: row max
   double r_z = 0.0;   // sampling: row total relative to the reference
   int r_idx = 0;      // greedy: lowest index of the max
+  int rank = 0;       // typical acceptance: elements above the draft's logit
   if (lane < nslot && slot_needed(ri, lane, K)) {
     float m = kNegInf;
     int im = INT32_MAX;
+    const bool counts = p.typical && p.top_k > 0 && ri.sampling && lane < n;
     for (int k0 = 0; k0 < p.nchunk; k0 += kBatch) {
       if (k0 > 0) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) q[u] = pr[min(k0 + u, p.nchunk - 1)];
       }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
+      for (int u = 0; u < kBatch; ++u) {
         if (k0 + u < p.nchunk && q[u].m > m) {  // chunks ascend: first max wins
           m = q[u].m;
           im = q[u].idx;
         }
+        if (counts && k0 + u < p.nchunk) rank += q[u].idx;
+      }
     }
     if (ri.sampling) {
       r_ref = ref_of(m, c);
@@ -582,9 +608,13 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
       double ratio;
       if (qx > 0.0) ratio = px / qx;
       else ratio = px > 0.0 ? __builtin_inf() : 0.0;
-      double u_acc, u_rec;
-      uniforms(p.seed, p.offset, p.b_base + b, lane, &u_acc, &u_rec);
-      accept = u_acc < ratio;
+      if (p.typical) {  // threshold or top-k: no uniform
+        accept = px > (double)p.eps || rank < p.top_k;
+      } else {
+        double u_acc, u_rec;
+        uniforms(p.seed, p.offset, p.b_base + b, lane, &u_acc, &u_rec);
+        accept = u_acc < ratio;
+      }
       dbg_p = (float)px;
       dbg_q = (float)qx;
     }
@@ -633,7 +663,7 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
         d.u = u_rec;
       }
       d.kind = kDrawSingle;
-      if (je < n) {  // rejected at je
+      if (je < n && !p.typical) {  // rejected at je (typical: draw from p itself)
         d.x = (x >= 0 && x < V) ? x : -1;
         if (!ri.onehot) {
           d.kind = kDrawPair;
@@ -721,11 +751,22 @@ __device__ __forceinline__ void stats_item(const RunParams& p, int b, int s, int
   Partial out;
   if (ri.sampling) {
     const float c = temp_scale(ri.T);
-    if (is_target)
-      chunk_softmax_block<TDT>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z);
-    else
-      chunk_softmax_block<DDT>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z);
-    out.idx = -1;
+    if (p.typical && p.top_k > 0 && s < ri.n) {
+      // typical acceptance with a top-k clause: also count the elements
+      // above the draft's logit (an invalid id counts nothing)
+      const int x = p.ids[(size_t)b * p.K + s];
+      const float lx = (x >= 0 && x < p.V) ? load_elem(p.target, TDT, (size_t)b * (p.K + 1) + s, p.V, x)
+                                          : __builtin_inff();
+      int above = 0;
+      chunk_softmax_block<TDT, true>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z, lx, ldsi, &above);
+      out.idx = above;
+    } else if (is_target) {
+      chunk_softmax_block<TDT, false>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z);
+      out.idx = -1;
+    } else {
+      chunk_softmax_block<DDT, false>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z);
+      out.idx = -1;
+    }
   } else {  // greedy rows are target rows
     AmAcc a = chunk_argmax<TDT>(r, c0, c1);
     block_argmax<kThreads>(a.M, a.I, ldsf, ldsi);
