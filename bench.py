@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
     python bench.py --op draft_sample     # the draft-token sampler instead
     python bench.py --op ngram            # the n-gram prompt-lookup proposer
+    python bench.py --op typical          # verify with typical acceptance
 
 One step = one spec_verify_run over a whole batch: row statistics, decisions,
 residual sums of rejected probabilistic drafts, and the draws.  Inputs are
@@ -31,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified (req×pos×vocab) elems/s + achieved HBM GB/s vs peak, spec-verify step"
 METRIC_SAMPLE = "sampled (row×vocab) elems/s + achieved HBM GB/s vs peak, draft-token sampler"
+METRIC_TYPICAL = "verified (req×pos×vocab) elems/s + achieved HBM GB/s vs peak, typical acceptance"
 HBM_PEAK_GBPS = 8000.0
 DOMINANT = "stats"  # the kernel that streams every needed logits row
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", "sv_kernels.hip")
@@ -83,6 +85,31 @@ def cpu_baseline(w, seconds=12.0):
         t += time.perf_counter() - t0
         n = sub["num_drafts"].clip(0, w.K)
         elems += int((n + 1).sum()) * V
+        n_req += sl.stop - sl.start
+        start = sl.stop
+        if start >= w.B:
+            start, passes = 0, passes + 1
+    return dict(value=elems / t, unit="elems/s", cores=1, kind="oracle",
+                sample=f"{n_req} requests of the same batch (the batch cycled "
+                       f"with a new Philox offset per pass), {elems} verified "
+                       f"elems, {t:.1f} s of the single-threaded fp64 C oracle")
+
+
+def cpu_baseline_typical(w, eps, top_k, seconds=12.0):
+    """The CPU oracle's typical acceptance, as it stands, on slices of 8
+    requests of the same batch until about `seconds` of single-threaded work."""
+    import oracle
+    hs = w.host_arrays()
+    V = w.V
+    n_req, elems, t, passes, start = 0, 0, 0.0, 0, 0
+    while t < seconds and passes < 64:
+        sl = slice(start, min(w.B, start + 8))
+        t0 = time.perf_counter()
+        oracle.verify_typical(hs["target"][sl], hs["draft_ids"][sl], hs["num_drafts"][sl],
+                              hs["temperatures"][sl], eps=eps, top_k=top_k, seed=0,
+                              offset=passes, diagnostics=False)
+        t += time.perf_counter() - t0
+        elems += int((hs["num_drafts"][sl].clip(0, w.K) + 1).sum()) * V
         n_req += sl.stop - sl.start
         start = sl.stop
         if start >= w.B:
@@ -196,7 +223,11 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--op", choices=["verify", "draft_sample", "ngram"], default="verify")
+    ap.add_argument("--op", choices=["verify", "draft_sample", "ngram", "typical"],
+                    default="verify")
+    ap.add_argument("--threshold", type=float, default=0.05,
+                    help="--op typical: the probability threshold")
+    ap.add_argument("--top-k", type=int, default=2, help="--op typical: the top-k clause")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run one plain device copy of this "
@@ -228,6 +259,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     sample = args.op == "draft_sample"
+    typical = args.op == "typical"
     if sample and (w.draft is None or w.draft_is_probs):
         print("--op draft_sample needs a workload with draft logits", file=sys.stderr)
         sys.exit(2)
@@ -242,6 +274,10 @@ def main():
         if sample:
             h.sample(c.draft, nd_sample, c.temperatures, seed=0, offset=i,
                      out_ids=ids, stream=stream)
+        elif typical:
+            h.run_typical(c.target, c.draft_ids, c.num_drafts, c.temperatures,
+                          args.threshold, args.top_k, seed=0, offset=i, out_tokens=tok,
+                          out_num_accepted=nacc, stream=stream)
         else:
             h.run(c.target, c.draft, c.draft_mode, c.draft_ids, c.num_drafts,
                   c.temperatures, seed=0, offset=i, out_tokens=tok,
@@ -285,6 +321,9 @@ def main():
         n_rows = int(nd_sample.clamp(0, w.K).sum().item())
         elems = n_rows * w.V
         alg = n_rows * w.V * w.draft.element_size()  # each sampled row read once
+    elif typical:  # target rows 0..n_b only: no draft rows are read
+        elems = w.verified_elems()
+        alg = elems * w.elt()
     else:
         elems = w.verified_elems()
         alg = w.algorithmic_bytes()
@@ -300,10 +339,10 @@ def main():
     resid_bytes = pairs * w.V * (w.elt() + delt)
     stats_ms = kern_ms[DOMINANT]
     achieved = alg / (stats_ms * 1e-3) / 1e9
-    traffic = None if sample else read_traffic(args.workload)
+    traffic = None if (sample or typical) else read_traffic(args.workload)
     dt = {torch.bfloat16: "bf16", torch.float32: "f32"}[w.target.dtype]
     out = {
-        "metric": METRIC_SAMPLE if sample else METRIC,
+        "metric": METRIC_SAMPLE if sample else (METRIC_TYPICAL if typical else METRIC),
         "value": elems / (ms_step * 1e-3),
         "unit": "elems/s",
         "n_gpus": 1,
@@ -316,6 +355,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": (f"draft-token sampler, draft rows of {w.name}" if sample
+                                else f"typical acceptance (threshold {args.threshold}, "
+                                     f"top-k {args.top_k}), {w.name}" if typical
                                 else f"verify step, {w.name}"),
                    "B": w.B, "K": w.K, "V": w.V, "logits": dt,
                    ("sampled_elems" if sample else "verified_elems"): elems,
@@ -324,10 +365,12 @@ def main():
                    "chunk_elems": h.chunk_elems, "input_copies": len(copies),
                    "parallelism": "single GPU"},
         "step_hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
-        "resid_pairs": None if sample else pairs,
-        "resid_bytes": None if sample else resid_bytes,
+        "resid_pairs": None if (sample or typical) else pairs,
+        "resid_bytes": None if (sample or typical) else resid_bytes,
         "resid_gbps": (resid_bytes / (kern_ms["resid"] * 1e-3) / 1e9
-                       if "resid" in kern_ms and not sample else None),
+                       if "resid" in kern_ms and not (sample or typical) else None),
+        "accepted_per_proposed": (int(nacc.sum().item()) / max(1, int(n_b.sum()))
+                                  if not sample else None),
         "kernels_ms": kern_ms,
         "roofline": {"bound": "hbm", "kernel": DOMINANT,
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -335,7 +378,9 @@ def main():
                      "traffic": traffic},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_sample(w, nd_sample) if sample else cpu_baseline(w)
+        out["cpu_baseline"] = (cpu_baseline_sample(w, nd_sample) if sample else
+                               cpu_baseline_typical(w, args.threshold, args.top_k) if typical
+                               else cpu_baseline(w))
     h.close()
     print(json.dumps(out), flush=True)
 
