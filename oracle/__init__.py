@@ -1,6 +1,6 @@
 """CPU oracle for the speculative-sampling verify step (rejection sampling,
-and typical acceptance), the draft-token sampler and the n-gram prompt-lookup
-proposer that feed it.
+typical acceptance, token trees), the draft-token sampler and the n-gram
+prompt-lookup proposer that feed it.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
 CPU-baseline leg of the benchmark may import this module.  The product path
@@ -26,6 +26,7 @@ _LIB = os.path.join(_HERE, "libsvoracle.so")
 F32, BF16 = 0, 1
 MODE_PROB, MODE_ONEHOT = 0, 1
 FLAG_BAD_DRAFT_ID, FLAG_BAD_NUM_DRAFTS, FLAG_ZERO_RESIDUAL = 1, 2, 4
+FLAG_BAD_TREE = 16
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
@@ -78,6 +79,9 @@ def open_library(path: str):
     lib.svo_verify_typical.argtypes = [i32, i32, i32, i32, P, P, P, P, dbl, i32,
                                        u64, u64, P, P, P, P, P]
     lib.svo_verify_typical.restype = u32
+    lib.svo_verify_tree.argtypes = [i32, i32, i32, i32, P, i32, P, P, P, P, P, u64, u64,
+                                    P, P, P, P, P]
+    lib.svo_verify_tree.restype = u32
     return lib
 
 
@@ -283,3 +287,32 @@ def verify_typical(target, draft_ids, num_drafts, temperatures, *, eps, top_k=0,
         _ptr(p) if d else None, _ptr(macc) if d else None, _ptr(mrec) if d else None)
     return dict(tokens=tokens, num_accepted=nacc, p=p, q=np.ones_like(p),
                 margin_acc=macc, margin_rec=mrec, flags=int(flags))
+
+
+def verify_tree(target, draft, tokens, parents, num_nodes, temperatures, *, seed=0,
+                offset=0):
+    """Token-tree verification.  target [B, N, V] (float32 or bf16 bits),
+    draft [B, N, V] or None (one-hot tree), tokens / parents [B, N] int32,
+    num_nodes [B].  Returns a dict with tokens [B, N], num_accepted,
+    last_node, margin_acc, margin_rec and flags."""
+    target = np.ascontiguousarray(target)
+    B, N, V = target.shape
+    if draft is not None:
+        draft = np.ascontiguousarray(draft)
+        assert draft.shape == (B, N, V)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, N)
+    par = np.ascontiguousarray(parents, dtype=np.int32).reshape(B, N)
+    nn = np.ascontiguousarray(num_nodes, dtype=np.int32).reshape(B)
+    temps = np.ascontiguousarray(temperatures, dtype=np.float32).reshape(B)
+    out = np.empty((B, N), dtype=np.int32)
+    nacc = np.empty(B, dtype=np.int32)
+    last = np.empty(B, dtype=np.int32)
+    macc = np.empty(B, dtype=np.float64)
+    mrec = np.empty(B, dtype=np.float64)
+    flags = _load().svo_verify_tree(
+        B, N, V, _dtype_code(target), _ptr(target),
+        _dtype_code(draft) if draft is not None else F32, _ptr(draft), _ptr(tok), _ptr(par),
+        _ptr(nn), _ptr(temps), int(seed), int(offset), _ptr(out), _ptr(nacc), _ptr(last),
+        _ptr(macc), _ptr(mrec))
+    return dict(tokens=out, num_accepted=nacc, last_node=last, margin_acc=macc,
+                margin_rec=mrec, flags=int(flags))

@@ -607,3 +607,159 @@ uint32_t svo_verify_typical(int B, int K, int V, int target_dtype,
   free(p);
   return flags;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Token-tree verification.  [P3] section 验证阶段的策略 / 验证方案: draft     */
+/* sequences with shared prefixes are merged into a token tree (a trie),     */
+/* and the target scores every node in one pass (tree attention); SpecInfer  */
+/* and Spectr are named for the multi-branch rule, which the page does not   */
+/* give.                                                                     */
+/*                                                                          */
+/* Reading: the page's chain rule applied child by child, keeping the       */
+/* target law (multi-step speculative sampling).  At node v the children    */
+/* (nodes whose parent is v, in index order) are tested in turn; the k-th   */
+/* test uses the law left by the k earlier rejections:                      */
+/*   probabilistic tree: p'_k = max(0, p - c_k q) / Z_k, c_0 = 0, Z_0 = 1,   */
+/*     c_{k+1} = c_k + Z_k, Z_k = sum_i max(0, p_i - c_k q_i); child x is    */
+/*     accepted iff u < p'_k(x) / q(x)  (k = 0 is the chain's p(x)/q(x));    */
+/*   one-hot tree (no draft rows): p'_k = p with the rejected siblings'     */
+/*     tokens removed, renormalized; accepted iff u < p'_k(x);              */
+/*   greedy: the first child whose token attains the row maximum.           */
+/* An accepted child becomes v.  When every child is rejected, or v has     */
+/* none, one token is drawn at v from p'_k (from p at a leaf), the emitted  */
+/* token.  p at node i = softmax(target[i] / T_b), q = softmax(draft[i] /   */
+/* T_b), the law node i's children were drawn from.  Uniforms: the block at */
+/* counter (offset, b, i, 0) gives in word 0 the acceptance uniform of node */
+/* i + 1 and in word 1 the draw uniform at node i, so a chain-shaped tree   */
+/* (parent of i = i - 1) reproduces the verify step exactly.  A child with  */
+/* an id outside [0, V) is never accepted (counted as a rejection); nodes  */
+/* whose parent is not an earlier node are never visited; both are flagged. */
+/*                                                                          */
+/*   target [B][N][V], draft [B][N][V] or NULL; tokens, parents [B][N];     */
+/*   num_nodes [B] (clamped into [1, N]); out_tokens [B][N]: the accepted   */
+/*   path's tokens, the emitted token, then -1; out_num_accepted [B];       */
+/*   out_last_node [B]: the deepest accepted node (0 = root);               */
+/*   out_margin_acc [B]: smallest |u - ratio| of the sampling tests made    */
+/*   (+inf if none); out_margin_rec [B]: the draw margin (+inf greedy).     */
+/* ------------------------------------------------------------------------ */
+#define SVO_FLAG_BAD_TREE 16u
+
+uint32_t svo_verify_tree(int B, int N, int V, int target_dtype,
+                         const void *target, int draft_dtype, const void *draft,
+                         const int32_t *tokens, const int32_t *parents,
+                         const int32_t *num_nodes, const float *temperatures,
+                         uint64_t seed, uint64_t offset, int32_t *out_tokens,
+                         int32_t *out_num_accepted, int32_t *out_last_node,
+                         double *out_margin_acc, double *out_margin_rec) {
+  uint32_t flags = 0;
+  double *l = malloc(sizeof(double) * (size_t)V);
+  double *p = malloc(sizeof(double) * (size_t)V);
+  double *q = malloc(sizeof(double) * (size_t)V);
+  double *r = malloc(sizeof(double) * (size_t)V);
+  int *removed = malloc(sizeof(int) * (size_t)V);
+  for (int b = 0; b < B; ++b) {
+    int n = num_nodes[b];
+    if (n < 1 || n > N) {
+      flags |= SVO_FLAG_BAD_NUM_DRAFTS;
+      n = n < 1 ? 1 : N;
+    }
+    const int32_t *tok = tokens + (size_t)b * N, *par = parents + (size_t)b * N;
+    for (int i = 1; i < n; ++i)
+      if (par[i] < 0 || par[i] >= i) flags |= SVO_FLAG_BAD_TREE;
+    const float T = temperatures[b];
+    const int sampling = svo_is_sampling(T);
+    const int onehot = draft == NULL;
+    double margin_acc = INFINITY, margin_rec = INFINITY;
+    int v = 0, n_acc = 0, y = -1;
+    int32_t *out = out_tokens + (size_t)b * N;
+    for (int i = 0; i < N; ++i) out[i] = -1;
+    for (;;) {
+      load_row(target, target_dtype, (size_t)b * N + v, V, l);
+      if (sampling) svo_softmax(l, V, (double)T, p);
+      if (sampling && !onehot) {
+        load_row(draft, draft_dtype, (size_t)b * N + v, V, q);
+        svo_softmax(q, V, (double)T, q);
+      }
+      double ck = 0.0, Zk = 1.0;   /* probabilistic residual after k rejections */
+      int nrej = 0;
+      for (int i = 0; i < V; ++i) removed[i] = 0;
+      int next = -1;
+      for (int c = v + 1; c < n && next < 0; ++c) {
+        if (par[c] != v) continue;
+        const int x = tok[c];
+        const int valid = x >= 0 && x < V;
+        if (!valid) flags |= SVO_FLAG_BAD_DRAFT_ID;
+        int accept;
+        if (!sampling) {
+          accept = valid && l[x] == l[svo_argmax(l, V)];
+        } else {
+          double ua, ur, ratio = 0.0;
+          svo_uniforms(seed, offset, (uint64_t)b, (uint64_t)(c - 1), &ua, &ur);
+          if (valid && onehot) {
+            ratio = removed[x] ? 0.0 : p[x] / Zk;
+          } else if (valid) {
+            const double num = p[x] - ck * q[x];
+            ratio = svo_accept_ratio((num > 0.0 ? num : 0.0) / Zk, q[x]);
+          }
+          accept = ua < ratio;
+          const double m = fabs(ua - ratio);
+          if (m < margin_acc) margin_acc = m;
+        }
+        if (accept) {
+          next = c;
+          break;
+        }
+        nrej++;
+        if (sampling && onehot) {
+          if (valid && !removed[x]) {
+            removed[x] = 1;
+            Zk -= p[x];
+          }
+        } else if (sampling) {
+          ck += Zk;
+          for (int i = 0; i < V; ++i) {
+            const double d = p[i] - ck * q[i];
+            r[i] = d > 0.0 ? d : 0.0;
+          }
+          Zk = sum_compensated(r, V);
+        }
+      }
+      if (next >= 0) {
+        out[n_acc++] = tok[next];
+        v = next;
+        continue;
+      }
+      /* every child rejected, or a leaf: the emitted token is drawn at v */
+      if (!sampling) {
+        y = svo_argmax(l, V);
+      } else {
+        double ua, ur;
+        svo_uniforms(seed, offset, (uint64_t)b, (uint64_t)v, &ua, &ur);
+        if (onehot) {
+          for (int i = 0; i < V; ++i) r[i] = removed[i] ? 0.0 : p[i];
+        } else if (nrej > 0) {
+          for (int i = 0; i < V; ++i) {
+            const double d = p[i] - ck * q[i];
+            r[i] = d > 0.0 ? d : 0.0;
+          }
+        } else {
+          memcpy(r, p, sizeof(double) * (size_t)V);
+        }
+        y = svo_draw(r, V, ur, &margin_rec);
+        if (y < 0) { /* no residual mass: draw from p itself */
+          flags |= SVO_FLAG_ZERO_RESIDUAL;
+          y = svo_draw(p, V, ur, &margin_rec);
+          margin_rec = 0.0;
+        }
+      }
+      break;
+    }
+    out[n_acc] = y;
+    out_num_accepted[b] = n_acc;
+    out_last_node[b] = v;
+    if (out_margin_acc) out_margin_acc[b] = margin_acc;
+    if (out_margin_rec) out_margin_rec[b] = margin_rec;
+  }
+  free(l); free(p); free(q); free(r); free(removed);
+  return flags;
+}

@@ -608,6 +608,107 @@ def check_typical_correction_law(B=1 << 17, V=6, T=0.9, seed=95):
     assert _chisq_ok(np.bincount(r["tokens"][:, 0], minlength=V), p)
 
 
+# --------------------------------------------------------------------------
+# Token-tree verification
+# --------------------------------------------------------------------------
+def _chain_tree(t, d, ids, nd):
+    """The chain verify inputs laid out as a tree: node i = position i."""
+    B, K1, V = t.shape
+    N = K1
+    tokens = np.zeros((B, N), np.int32)
+    tokens[:, 1:] = ids
+    parents = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    dt = None
+    if d is not None:
+        dt = np.zeros((B, N, V), d.dtype)
+        dt[:, :N - 1] = d
+    return tokens, parents, dt, np.asarray(nd, np.int32) + 1
+
+
+def check_tree_chain_equals_verify(seed=101):
+    """A chain-shaped tree reproduces the verify step bit for bit: tokens,
+    counts and the smallest decision margin, for probabilistic, one-hot and
+    greedy requests."""
+    rng = np.random.default_rng(seed)
+    for c in range(12):
+        B, K, V = 24, int(rng.integers(1, 6)), int(rng.integers(2, 300))
+        t = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+        d = (t[:, :K] + rng.normal(0, 0.7, (B, K, V))).astype(np.float32)
+        ids = rng.integers(0, V, (B, K)).astype(np.int32)
+        am = np.argmax(d, -1)
+        ids = np.where(rng.random((B, K)) < 0.5, am, ids).astype(np.int32)
+        nd = rng.integers(0, K + 1, B).astype(np.int32)
+        temps = rng.choice([1.0, 0.7, 0.0, 1.4], B).astype(np.float32)
+        onehot = c % 3 == 2
+        dd = None if onehot else d
+        ref = oracle.verify(t, dd, ids, nd, temps, seed=c, offset=7 * c)
+        tok, par, dt, nn = _chain_tree(t, dd, ids, nd)
+        r = oracle.verify_tree(t, dt, tok, par, nn, temps, seed=c, offset=7 * c)
+        assert np.array_equal(r["num_accepted"], ref["num_accepted"]), c
+        assert np.array_equal(r["tokens"], ref["tokens"]), c
+        assert np.array_equal(r["last_node"], ref["num_accepted"]), c
+        for b in range(B):
+            m = ref["margin_acc"][b, :min(nd[b], ref["num_accepted"][b] + 1)]
+            m = m[np.isfinite(m)] if np.any(np.isfinite(m)) else np.array([np.inf])
+            assert r["margin_acc"][b] == m.min(), (c, b)
+            assert r["margin_rec"][b] == ref["margin_rec"][b], (c, b)
+
+
+def check_tree_lossless_monte_carlo(B=1 << 17, V=6, T=0.8, seed=103):
+    """Multi-step speculative sampling keeps the target law: three children
+    of the root drawn i.i.d. from q (duplicates allowed), and three fixed
+    distinct one-hot children; the first emitted token follows p_root."""
+    rng = np.random.default_rng(seed)
+    lp = rng.normal(0, 1, V).astype(np.float32)
+    lq = (lp + rng.normal(0, 1.2, V)).astype(np.float32)
+    p = scipy.special.softmax(lp.astype(np.float64) / T)
+    q = scipy.special.softmax(lq.astype(np.float64) / T)
+    N = 4
+    t = np.broadcast_to(lp, (B, N, V)).copy()
+    d = np.broadcast_to(lq, (B, N, V)).copy()
+    par = np.tile(np.array([-1, 0, 0, 0], np.int32), (B, 1))
+    tok = np.zeros((B, N), np.int32)
+    tok[:, 1:] = rng.choice(V, size=(B, 3), p=q)
+    temps = np.full(B, T, np.float32)
+    r = oracle.verify_tree(t, d, tok, par, np.full(B, N, np.int32), temps, seed=seed)
+    assert _chisq_ok(np.bincount(r["tokens"][:, 0], minlength=V), p)
+    tok[:, 1:] = [1, 4, 2]
+    r = oracle.verify_tree(t, None, tok, par, np.full(B, N, np.int32), temps, seed=seed + 1)
+    assert _chisq_ok(np.bincount(r["tokens"][:, 0], minlength=V), p)
+
+
+def check_tree_greedy_walk(cases=200, seed=105):
+    """Greedy trees against a walk written with numpy: follow the first
+    child (in index order) whose token attains its parent's row max; emit
+    the lowest argmax where none does."""
+    rng = np.random.default_rng(seed)
+    for c in range(cases):
+        N, V = int(rng.integers(1, 12)), int(rng.integers(2, 12))
+        t = np.round(rng.normal(0, 1.5, (1, N, V))).astype(np.float32)
+        par = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, N)], np.int32)
+        tok = rng.integers(0, V, N).astype(np.int32)
+        r = oracle.verify_tree(t, None, tok[None], par[None], [N], [0.0])
+        v, path = 0, []
+        while True:
+            kids = [i for i in range(v + 1, N) if par[i] == v and t[0, v, tok[i]] == t[0, v].max()]
+            if not kids:
+                break
+            v = kids[0]
+            path.append(int(tok[v]))
+        want = path + [int(np.argmax(t[0, v]))] + [-1] * (N - len(path) - 1)
+        assert r["tokens"][0].tolist() == want and r["last_node"][0] == v, (c, r, want)
+
+
+def check_tree_flags():
+    t = np.zeros((2, 3, 4), np.float32)
+    r = oracle.verify_tree(t, None, np.array([[0, 9, 1], [0, 1, 2]]),
+                           np.array([[-1, 0, 0], [-1, 2, 0]]), [3, 3], [1.0, 1.0])
+    assert r["flags"] & oracle.FLAG_BAD_DRAFT_ID and r["flags"] & oracle.FLAG_BAD_TREE
+    assert r["last_node"][1] in (0, 2)  # node 1 (parent 2 > 1) is never visited
+    r = oracle.verify_tree(t, None, np.zeros((2, 3)), np.full((2, 3), -1), [0, 7], [1.0, 1.0])
+    assert r["flags"] & oracle.FLAG_BAD_NUM_DRAFTS
+
+
 ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_accept_example_philox, check_bpd_greedy_example,
              check_greedy_bruteforce, check_enumeration_law,
@@ -619,4 +720,5 @@ ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_draft_sample_vs_library, check_draft_sample_monte_carlo,
              check_ngram_golden, check_ngram_vs_rfind, check_ngram_edge_cases,
              check_typical_golden, check_typical_vs_library, check_typical_special_cases,
-             check_typical_correction_law]
+             check_typical_correction_law, check_tree_chain_equals_verify,
+             check_tree_lossless_monte_carlo, check_tree_greedy_walk, check_tree_flags]

@@ -46,6 +46,11 @@ MUTANTS = {
     "typical_no_stop": ("      if (!accept) break;\n      n_acc++;", "      if (accept) n_acc++;"),
     "typical_draw_from_bonus_row": ("load_row(target, target_dtype, row0 + n_acc, V, l);",
                                     "load_row(target, target_dtype, row0 + n, V, l);"),
+    "tree_no_residual_update": ("          ck += Zk;\n", "          (void)ck;\n"),
+    "tree_onehot_no_renormalize": ("ratio = removed[x] ? 0.0 : p[x] / Zk;", "ratio = removed[x] ? 0.0 : p[x];"),
+    "tree_children_reversed": ("for (int c = v + 1; c < n && next < 0; ++c) {",
+                               "for (int c = n - 1; c > v && next < 0; --c) {"),
+    "tree_uniform_of_node": ("(uint64_t)(c - 1), &ua, &ur);", "(uint64_t)c, &ua, &ur);"),
 }
 
 
