@@ -79,7 +79,7 @@ def open_library(path: str):
     lib.svo_verify_typical.argtypes = [i32, i32, i32, i32, P, P, P, P, dbl, i32,
                                        u64, u64, P, P, P, P, P]
     lib.svo_verify_typical.restype = u32
-    lib.svo_verify_tree.argtypes = [i32, i32, i32, i32, P, i32, P, P, P, P, P, u64, u64,
+    lib.svo_verify_tree.argtypes = [i32, i32, i32, i32, P, i32, P, i32, P, P, P, P, u64, u64,
                                     P, P, P, P, P]
     lib.svo_verify_tree.restype = u32
     return lib
@@ -290,9 +290,10 @@ def verify_typical(target, draft_ids, num_drafts, temperatures, *, eps, top_k=0,
 
 
 def verify_tree(target, draft, tokens, parents, num_nodes, temperatures, *, seed=0,
-                offset=0):
+                offset=0, draft_is_probs=False):
     """Token-tree verification.  target [B, N, V] (float32 or bf16 bits),
-    draft [B, N, V] or None (one-hot tree), tokens / parents [B, N] int32,
+    draft [B, N, V] logits (normalized q with draft_is_probs) or None
+    (one-hot tree), tokens / parents [B, N] int32,
     num_nodes [B].  Returns a dict with tokens [B, N], num_accepted,
     last_node, margin_acc, margin_rec and flags."""
     target = np.ascontiguousarray(target)
@@ -311,7 +312,8 @@ def verify_tree(target, draft, tokens, parents, num_nodes, temperatures, *, seed
     mrec = np.empty(B, dtype=np.float64)
     flags = _load().svo_verify_tree(
         B, N, V, _dtype_code(target), _ptr(target),
-        _dtype_code(draft) if draft is not None else F32, _ptr(draft), _ptr(tok), _ptr(par),
+        _dtype_code(draft) if draft is not None else F32, _ptr(draft),
+        int(bool(draft_is_probs)), _ptr(tok), _ptr(par),
         _ptr(nn), _ptr(temps), int(seed), int(offset), _ptr(out), _ptr(nacc), _ptr(last),
         _ptr(macc), _ptr(mrec))
     return dict(tokens=out, num_accepted=nacc, last_node=last, margin_acc=macc,

@@ -169,3 +169,55 @@ def compare_draft(ref, ids, qx=None, *, band=1e-6, prob_rtol=1e-5,
             if not rel <= prob_rtol:
                 bad((b, j), f"q(x) {gq} vs {oq} rel {rel:.3g}")
     return rep
+
+
+def compare_tree(tokens_in, parents, num_nodes, V, ref, tokens, nacc, last, *, band=1e-6,
+                 max_report=20) -> ParityReport:
+    """Parity of token-tree verification.  tokens_in / parents [B, N] and
+    num_nodes [B]: the tree; ref: oracle.verify_tree's result; tokens [B, N],
+    nacc [B], last [B]: the implementation's.
+
+    A request is flagged when one of its sampling tests lay within ``band``
+    of its threshold or its draw within ``band`` of a CDF boundary.
+    Unflagged requests must match exactly (tokens, count, last node).  Every
+    output must be valid: the accepted path climbs from the last node to the
+    root through parents, its tokens are those nodes' tokens, then one token
+    in [0, V), then -1."""
+    tokens, nacc, last = np.asarray(tokens), np.asarray(nacc), np.asarray(last)
+    B, N = tokens.shape
+    rep = ParityReport(requests=B)
+
+    def bad(b, why):
+        rep.mismatches.append((b, why) if len(rep.mismatches) < max_report else (b, "..."))
+
+    for b in range(B):
+        n = int(np.clip(num_nodes[b], 1, N))
+        a, v = int(nacc[b]), int(last[b])
+        rep.accepted += a
+        path = []
+        node, ok = v, 0 <= v < n
+        while ok and node != 0:
+            path.append(node)
+            pn = int(parents[b, node])
+            ok = 0 <= pn < node
+            node = pn
+        path = path[::-1]
+        if not ok or len(path) != a:
+            bad(b, f"last node {v} is not {a} accepted steps below the root")
+            continue
+        if [int(tokens_in[b, i]) for i in path] != tokens[b, :a].tolist():
+            bad(b, "accepted tokens differ from the path's node tokens")
+        if not 0 <= int(tokens[b, a]) < V:
+            bad(b, f"emitted token {int(tokens[b, a])} outside [0, {V})")
+        if np.any(tokens[b, a + 1:] != -1):
+            bad(b, "padding after the emitted token is not -1")
+        if ref["margin_acc"][b] < band or ref["margin_rec"][b] < band:
+            rep.flagged += 1
+            rep.flagged_mismatch += int(not np.array_equal(tokens[b], ref["tokens"][b]))
+            continue
+        if a != int(ref["num_accepted"][b]) or v != int(ref["last_node"][b]):
+            bad(b, f"accepted {a} / last {v} != oracle {int(ref['num_accepted'][b])} / "
+                   f"{int(ref['last_node'][b])}")
+        elif not np.array_equal(tokens[b], ref["tokens"][b]):
+            bad(b, f"tokens {tokens[b].tolist()} != oracle {ref['tokens'][b].tolist()}")
+    return rep

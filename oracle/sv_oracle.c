@@ -635,7 +635,8 @@ uint32_t svo_verify_typical(int B, int K, int V, int target_dtype,
 /* an id outside [0, V) is never accepted (counted as a rejection); nodes  */
 /* whose parent is not an earlier node are never visited; both are flagged. */
 /*                                                                          */
-/*   target [B][N][V], draft [B][N][V] or NULL; tokens, parents [B][N];     */
+/*   target [B][N][V], draft [B][N][V] logits (or normalized q with         */
+/*   draft_is_probs) or NULL; tokens, parents [B][N];                       */
 /*   num_nodes [B] (clamped into [1, N]); out_tokens [B][N]: the accepted   */
 /*   path's tokens, the emitted token, then -1; out_num_accepted [B];       */
 /*   out_last_node [B]: the deepest accepted node (0 = root);               */
@@ -646,7 +647,8 @@ uint32_t svo_verify_typical(int B, int K, int V, int target_dtype,
 
 uint32_t svo_verify_tree(int B, int N, int V, int target_dtype,
                          const void *target, int draft_dtype, const void *draft,
-                         const int32_t *tokens, const int32_t *parents,
+                         int draft_is_probs, const int32_t *tokens,
+                         const int32_t *parents,
                          const int32_t *num_nodes, const float *temperatures,
                          uint64_t seed, uint64_t offset, int32_t *out_tokens,
                          int32_t *out_num_accepted, int32_t *out_last_node,
@@ -678,7 +680,7 @@ uint32_t svo_verify_tree(int B, int N, int V, int target_dtype,
       if (sampling) svo_softmax(l, V, (double)T, p);
       if (sampling && !onehot) {
         load_row(draft, draft_dtype, (size_t)b * N + v, V, q);
-        svo_softmax(q, V, (double)T, q);
+        if (!draft_is_probs) svo_softmax(q, V, (double)T, q);
       }
       double ck = 0.0, Zk = 1.0;   /* probabilistic residual after k rejections */
       int nrej = 0;
