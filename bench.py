@@ -35,13 +35,19 @@ METRIC_SAMPLE = "sampled (row×vocab) elems/s + achieved HBM GB/s vs peak, draft
 METRIC_TYPICAL = "verified (req×pos×vocab) elems/s + achieved HBM GB/s vs peak, typical acceptance"
 HBM_PEAK_GBPS = 8000.0
 DOMINANT = "stats"  # the kernel that streams every needed logits row
-KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", "sv_kernels.hip")
+# the sources the verify kernels are built from (the traffic summary is valid
+# only for the sources it was measured on)
+KERNEL_SRC = [os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", f)
+              for f in ("sv_kernels.hip", "sv_device.h", "sv_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_traffic_B256_K7_V152064_bf16.txt")
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload_idx):

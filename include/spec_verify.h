@@ -1,7 +1,7 @@
 /*
- * spec_verify.h -- C ABI of the speculative-sampling verify step, and of
- * the draft-token sampler and the n-gram proposer that feed it, on MI355X
- * (gfx950).
+ * spec_verify.h -- C ABI of the speculative-sampling verify step (chains,
+ * typical acceptance, token trees), and of the draft-token sampler and the
+ * n-gram proposer that feed it, on MI355X (gfx950).
  *
  * The operation (sources by page title and section):
  *   - "深入推测解码：从概念到实现" (Exploring Speculative Decoding), section
@@ -75,6 +75,8 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_DEVERR_DRAW_ROUNDING 8u  /* draw landed past a chunk's recomputed
                                        total (a rounding tie); nearest token
                                        with mass taken */
+#define SV_DEVERR_BAD_TREE 16u      /* a tree node whose parent is not an
+                                       earlier node: never visited */
 
 typedef struct {
   int32_t max_batch;      /* largest B of any run, >= 1 */
@@ -199,6 +201,60 @@ int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K,
                       const float *temperatures, uint64_t philox_seed,
                       uint64_t philox_offset, int32_t *out_ids, float *out_q,
                       void *stream);
+
+/* Most nodes (root included) of one request's tree in spec_verify_run_tree. */
+#define SPEC_TREE_MAX_NODES 256
+
+/* Enqueues token-tree verification.  Source: "投机采样" (razer666.cn),
+ * section 验证阶段的策略 / 验证方案: draft sequences with shared prefixes
+ * form a token tree (a trie) that the target scores in one pass (tree
+ * attention, each node seeing only its ancestors); SpecInfer and Spectr are
+ * named for the multi-branch rule, which the page does not give.
+ *
+ * Reading: the chain rule of spec_verify_run applied child by child, which
+ * keeps the target law (multi-step speculative sampling).  At node v (the
+ * walk starts at the root, node 0) the children (nodes whose parent is v, in
+ * index order) are tested in turn; after k rejections at v the law is
+ *   probabilistic tree: p'_k = max(0, p - c_k q) / Z_k, c_0 = 0, Z_0 = 1,
+ *     c_{k+1} = c_k + Z_k, Z_k = sum_i max(0, p_i - c_k q_i); child x is
+ *     accepted iff u < p'_k(x) / q(x);
+ *   one-hot tree (draft_logits NULL): p'_k = p without the rejected
+ *     siblings' tokens, renormalized; accepted iff u < p'_k(x);
+ *   greedy T_b: the first child whose token attains the row maximum.
+ * An accepted child becomes v; when every child of v is rejected, or v is a
+ * leaf, one token is drawn at v from p'_k (p at a leaf, the lowest argmax
+ * for greedy requests).  p at node i = softmax(target_logits[b][i] / T_b);
+ * q = softmax(draft_logits[b][i] / T_b) (or draft rows as given with
+ * draft_is_probs), the law node i's children were drawn from.  Uniforms: the
+ * Philox block at counter (philox_offset, b, i, 0) gives in word 0 the
+ * acceptance uniform of node i + 1 and in word 1 the draw uniform at node i,
+ * so a chain-shaped tree (parent of i = i - 1) reproduces spec_verify_run.
+ *
+ *   target_logits  device [B][N][V], cfg.target_dtype: the target's logits
+ *                  after each node (node 0: after the last committed token).
+ *   draft_logits   device [B][N][V], cfg.draft_dtype, or NULL (one-hot).
+ *   tokens         device [B][N] int32: the draft token of each node
+ *                  (node 0 unused); ids outside [0, V) are never accepted.
+ *   parents        device [B][N] int32: the parent of node i >= 1, an
+ *                  earlier node; other nodes are never visited (flagged).
+ *   num_nodes      device [B] int32: nodes in use, clamped into [1, N].
+ *   temperatures   device [B] float.
+ *   out_tokens     device [B][N] int32: the accepted path's tokens, the
+ *                  emitted token, then -1.
+ *   out_num_accepted device [B] int32; out_last_node device [B] int32: the
+ *                  deepest accepted node (0 = root).
+ *
+ * One workgroup per request walks its tree and reads only the rows of the
+ * nodes it visits.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
+ * B < 0, N outside [1, SPEC_TREE_MAX_NODES]), SV_ERR_CAPACITY (B >
+ * max_batch) or SV_ERR_HIP. */
+int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N,
+                         const void *target_logits, const void *draft_logits,
+                         const int32_t *tokens, const int32_t *parents,
+                         const int32_t *num_nodes, const float *temperatures,
+                         uint64_t philox_seed, uint64_t philox_offset,
+                         int32_t *out_tokens, int32_t *out_num_accepted,
+                         int32_t *out_last_node, void *stream);
 
 /* Longest n-gram spec_ngram_propose matches. */
 #define SPEC_NGRAM_MAX_N 32

@@ -13,4 +13,4 @@ from .binding import (SpecVerify, SpecVerifyError, load_library, sv_config,  # n
                       spec_verify_timing_enable, spec_verify_timing_read,
                       spec_verify_chunk_elems, spec_draft_sample,
                       spec_ngram_propose, ngram_propose, spec_verify_run_typical,
-                      header_functions)
+                      spec_verify_run_tree, header_functions)

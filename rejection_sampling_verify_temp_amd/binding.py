@@ -22,6 +22,7 @@ SV_DEVERR_BAD_DRAFT_ID = 1
 SV_DEVERR_BAD_NUM_DRAFTS = 2
 SV_DEVERR_ZERO_RESIDUAL = 4
 SV_DEVERR_DRAW_ROUNDING = 8
+SV_DEVERR_BAD_TREE = 16
 
 
 class sv_config(ctypes.Structure):
@@ -64,6 +65,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.spec_verify_run_typical.argtypes = [P, i32, i32, P, P, P, P, ctypes.c_float, i32,
                                             u64, u64, P, P, P, P]
     lib.spec_verify_run_typical.restype = ctypes.c_int
+    lib.spec_verify_run_tree.argtypes = [P, i32, i32, P, P, P, P, P, P, u64, u64, P, P, P, P]
+    lib.spec_verify_run_tree.restype = ctypes.c_int
     lib.spec_draft_sample.argtypes = [P, i32, i32, P, P, P, u64, u64, P, P, P]
     lib.spec_draft_sample.restype = ctypes.c_int
     lib.spec_ngram_propose.argtypes = [i32, P, i32, P, i32, i32, i32, i32, P, P, P]
@@ -132,6 +135,16 @@ def spec_verify_run_typical(h, B, K, target_logits, draft_ids, num_drafts_per_re
         float(threshold), int(top_k), int(philox_seed) & (2 ** 64 - 1),
         int(philox_offset) & (2 ** 64 - 1), out_tokens, out_num_accepted,
         out_debug_probs, stream)
+
+
+def spec_verify_run_tree(h, B, N, target_logits, draft_logits, tokens, parents, num_nodes,
+                         temperatures, philox_seed, philox_offset, out_tokens,
+                         out_num_accepted, out_last_node, stream) -> int:
+    """Pointers are integers (device addresses); returns the status code."""
+    return load_library().spec_verify_run_tree(
+        h, int(B), int(N), target_logits, draft_logits, tokens, parents, num_nodes,
+        temperatures, int(philox_seed) & (2 ** 64 - 1), int(philox_offset) & (2 ** 64 - 1),
+        out_tokens, out_num_accepted, out_last_node, stream)
 
 
 def spec_draft_sample(h, B, K, draft_logits, num_drafts_per_req, temperatures,
@@ -337,6 +350,46 @@ class SpecVerify:
         if rc != SV_OK:
             raise SpecVerifyError("spec_verify_run_typical", rc)
         return out_tokens, out_num_accepted
+
+    def run_tree(self, target, draft, tokens, parents, num_nodes, temperatures, seed=0,
+                 offset=0, stream=None):
+        """Token-tree verification: target [B, N, V] (and draft [B, N, V] or
+        None) logits, tokens / parents [B, N] int32, num_nodes [B] int32 ->
+        (tokens [B, N], num_accepted [B], last_node [B])."""
+        import torch
+        B, N, V = target.shape
+        if V != self.cfg.vocab:
+            raise ValueError(f"vocab {V} != handle vocab {self.cfg.vocab}")
+        if _dtype_code(target) != self.cfg.target_dtype:
+            raise TypeError("target dtype differs from the handle's")
+        if draft is not None and _dtype_code(draft) != self.cfg.draft_dtype:
+            raise TypeError("draft dtype differs from the handle's")
+
+        def chk(t, shape, dtype=None):
+            if t is None:
+                return None
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("inputs must be contiguous device tensors")
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"shape {tuple(t.shape)} != {tuple(shape)}")
+            if dtype is not None and t.dtype != dtype:
+                raise TypeError(f"dtype {t.dtype} != {dtype}")
+            return t.data_ptr()
+
+        dev = target.device
+        out = torch.empty((B, N), dtype=torch.int32, device=dev)
+        nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+        last = torch.empty((B,), dtype=torch.int32, device=dev)
+        ptrs = [chk(target, (B, N, V)), chk(draft, (B, N, V)),
+                chk(tokens, (B, N), torch.int32), chk(parents, (B, N), torch.int32),
+                chk(num_nodes, (B,), torch.int32), chk(temperatures, (B,), torch.float32)]
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        rc = spec_verify_run_tree(self.handle, B, N, *ptrs, seed, offset, out.data_ptr(),
+                                  nacc.data_ptr(), last.data_ptr(), stream.cuda_stream)
+        if rc != SV_OK:
+            raise SpecVerifyError("spec_verify_run_tree", rc)
+        return out, nacc, last
 
     def sample(self, draft, num_drafts, temperatures, seed=0, offset=0,
                out_ids=None, out_q=None, stream=None):

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libspecverify.so")
-SOURCES = ["sv_kernels.hip", "sv_api.hip", "sv_ngram.hip"]
+SOURCES = ["sv_kernels.hip", "sv_api.hip", "sv_ngram.hip", "sv_tree.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 

@@ -282,6 +282,52 @@ int spec_verify_run_typical(spec_verify_t h, int32_t B, int32_t K, const void* t
   return enqueue(h, full, c.target_dtype, c.draft_dtype, stream);
 }
 
+int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N, const void* target_logits,
+                         const void* draft_logits, const int32_t* tokens,
+                         const int32_t* parents, const int32_t* num_nodes,
+                         const float* temperatures, uint64_t philox_seed,
+                         uint64_t philox_offset, int32_t* out_tokens,
+                         int32_t* out_num_accepted, int32_t* out_last_node, void* stream) {
+  if (h == nullptr || B < 0 || N < 1 || N > SPEC_TREE_MAX_NODES) return SV_ERR_INVALID_ARG;
+  if (B > h->cfg.max_batch) return SV_ERR_CAPACITY;
+  if (B == 0) return SV_OK;
+  const sv_config& c = h->cfg;
+  if (target_logits == nullptr || tokens == nullptr || parents == nullptr ||
+      num_nodes == nullptr || temperatures == nullptr || out_tokens == nullptr ||
+      out_num_accepted == nullptr || out_last_node == nullptr)
+    return SV_ERR_INVALID_ARG;
+  if (!aligned(target_logits, elt_bytes(c.target_dtype)) ||
+      (draft_logits != nullptr && !aligned(draft_logits, elt_bytes(c.draft_dtype))) ||
+      !aligned(tokens, 4) || !aligned(parents, 4) || !aligned(num_nodes, 4) ||
+      !aligned(temperatures, 4) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      !aligned(out_last_node, 4))
+    return SV_ERR_INVALID_ARG;
+  sv::TreeParams tp{};
+  tp.target = target_logits;
+  tp.draft = draft_logits;
+  tp.tokens = tokens;
+  tp.parents = parents;
+  tp.nn = num_nodes;
+  tp.temps = temperatures;
+  tp.out_tokens = out_tokens;
+  tp.out_nacc = out_num_accepted;
+  tp.out_last = out_last_node;
+  tp.flags = h->flags;
+  tp.seed = philox_seed;
+  tp.offset = philox_offset;
+  tp.B = B;
+  tp.N = N;
+  tp.V = c.vocab;
+  tp.draft_is_probs = c.draft_is_probs;
+  DeviceGuard g(c.device);
+  if (!g.ok) return SV_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sv::launch_tree(tp, c.target_dtype, c.draft_dtype, s) != hipSuccess) return SV_ERR_HIP;
+  h->last_stream = s;
+  h->has_run = true;
+  return SV_OK;
+}
+
 int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K, const void* draft_logits,
                       const int32_t* num_drafts_per_req, const float* temperatures,
                       uint64_t philox_seed, uint64_t philox_offset, int32_t* out_ids,

@@ -93,4 +93,24 @@ hipError_t launch_kernel(int k, const RunParams& p, int target_dtype, int draft_
 
 const char* kernel_name(int i);
 
+// Token-tree verification of a batch (one workgroup per request).
+struct TreeParams {
+  const void* target;  // [B][N][V]
+  const void* draft;   // [B][N][V] or nullptr (one-hot tree)
+  const int32_t* tokens;
+  const int32_t* parents;
+  const int32_t* nn;
+  const float* temps;
+  int32_t* out_tokens;
+  int32_t* out_nacc;
+  int32_t* out_last;
+  uint32_t* flags;
+  uint64_t seed, offset;
+  int B, N, V;
+  int draft_is_probs;
+};
+
+hipError_t launch_tree(const TreeParams& p, int target_dtype, int draft_dtype,
+                       hipStream_t stream);
+
 }  // namespace sv

@@ -202,6 +202,101 @@ def make_contexts(B, N, V, *, seed=0, device="cpu", alpha=1.1, ragged=False,
     return ctx.to(torch.int32).contiguous(), lens.to(torch.int32)
 
 
+@dataclasses.dataclass
+class TreeWorkload:
+    """Inputs of token-tree verification (layout of spec_verify_run_tree)."""
+    name: str
+    target: torch.Tensor        # [B, N, V] logits after each node
+    draft: torch.Tensor | None  # [B, N, V] draft logits at each node, or None
+    tokens: torch.Tensor        # [B, N] int32, node 0 unused
+    parents: torch.Tensor       # [B, N] int32, node 0: -1
+    num_nodes: torch.Tensor     # [B] int32
+    temperatures: torch.Tensor  # [B] float32
+
+    @property
+    def B(self):
+        return self.target.shape[0]
+
+    @property
+    def N(self):
+        return self.target.shape[1]
+
+    @property
+    def V(self):
+        return self.target.shape[2]
+
+    def to(self, device):
+        f = lambda t: None if t is None else t.to(device)
+        return TreeWorkload(self.name, f(self.target), f(self.draft), f(self.tokens),
+                            f(self.parents), f(self.num_nodes), f(self.temperatures))
+
+    def host_arrays(self):
+        def np_of(t):
+            if t is None:
+                return None
+            t = t.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16)
+            return t.numpy()
+        return {k: np_of(getattr(self, k)) for k in
+                ("target", "draft", "tokens", "parents", "num_nodes", "temperatures")}
+
+
+def make_tree(B, N, V, *, dtype=torch.float32, draft_dtype=None, seed=0, device="cpu",
+              temps=(1.0,), onehot=False, corr=0.9, scale=2.0, ragged=True,
+              shape="random"):
+    """Seeded token trees.  Shape "random": node i's parent is uniform over the
+    earlier nodes (a random recursive tree); "chain": parent of i is i - 1;
+    "wide": the root has every other node as a child.  Draft logits at each
+    node are N(0, scale^2); target logits are corr * draft + noise.  Child
+    tokens are drawn from the parent's tempered draft law by Gumbel-max,
+    independently (siblings may repeat), or, for one-hot trees, half from the
+    parent's target top tokens and half uniformly; greedy requests take the
+    parent's draft argmax with random perturbations."""
+    device = torch.device(device)
+    g = _gen(device, seed)
+    draft_dtype = draft_dtype or dtype
+    D = _normal(g, (B, N, V), scale, device)
+    tgt = corr * D + math.sqrt(max(0.0, 1 - corr * corr)) * _normal(g, (B, N, V), scale, device)
+    target = tgt.to(dtype)
+    T = torch.tensor([temps[b % len(temps)] for b in range(B)], dtype=torch.float32,
+                     device=device)
+    par = torch.full((B, N), -1, dtype=torch.int64, device=device)
+    for i in range(1, N):
+        if shape == "chain":
+            par[:, i] = i - 1
+        elif shape == "wide":
+            par[:, i] = 0
+        else:
+            par[:, i] = torch.randint(0, i, (B,), generator=g, device=device)
+    tok = torch.zeros((B, N), dtype=torch.int64, device=device)
+    base = D.to(draft_dtype).float()
+    tq = torch.where(T > 0, T, torch.ones_like(T)).view(-1, 1, 1)
+    pg = torch.gather(base, 1, par.clamp_min(0).unsqueeze(-1).expand(B, N, V))
+    if onehot:
+        pt = torch.gather(target.float(), 1, par.clamp_min(0).unsqueeze(-1).expand(B, N, V))
+        top = torch.topk(pt, 3, dim=-1).indices
+        pick = torch.randint(0, 3, (B, N, 1), generator=g, device=device)
+        tok_top = torch.gather(top, 2, pick)[..., 0]
+        tok_rnd = torch.randint(0, V, (B, N), generator=g, device=device)
+        tok = torch.where(torch.rand((B, N), generator=g, device=device) < 0.5, tok_top, tok_rnd)
+    else:
+        tok = _gumbel_argmax(pg / tq, g)
+        am = torch.argmax(pg, -1)
+        greedy = (T <= 0).view(-1, 1)
+        tok = torch.where(greedy & (torch.rand((B, N), generator=g, device=device) < 0.7), am, tok)
+    tok[:, 0] = 0
+    if ragged:
+        nn = torch.randint(1, N + 1, (B,), generator=g, device=device)
+    else:
+        nn = torch.full((B,), N, device=device)
+    return TreeWorkload(f"tree B={B} N={N} V={V} {shape}{' one-hot' if onehot else ''}",
+                        target.contiguous(),
+                        None if onehot else D.to(draft_dtype).contiguous(),
+                        tok.to(torch.int32).contiguous(), par.to(torch.int32).contiguous(),
+                        nn.to(torch.int32), T)
+
+
 def make_config(idx: int, device="cpu", seed: int | None = None) -> Workload:
     """The five verify workloads (shapes, value laws and draft structure)."""
     device = torch.device(device)

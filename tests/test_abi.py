@@ -12,7 +12,7 @@ def test_library_exports_header_functions():
     names = sv.header_functions()
     assert "spec_verify_run" in names and "spec_verify_create" in names
     assert "spec_draft_sample" in names and "spec_ngram_propose" in names
-    assert "spec_verify_run_typical" in names
+    assert "spec_verify_run_typical" in names and "spec_verify_run_tree" in names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -60,6 +60,8 @@ def test_run_and_queries_reject_null_handle():
         binding.SV_ERR_INVALID_ARG
     assert sv.spec_verify_run_typical(None, 1, 1, 1, 1, 1, 1, 0.1, 0, 0, 0, 1, 1, 0,
                                       None) == binding.SV_ERR_INVALID_ARG
+    assert sv.spec_verify_run_tree(None, 1, 4, 1, 0, 1, 1, 1, 1, 0, 0, 1, 1, 1, None) == \
+        binding.SV_ERR_INVALID_ARG
 
 
 def test_ngram_rejects_bad_arguments_without_device():

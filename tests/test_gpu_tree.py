@@ -1,0 +1,122 @@
+"""GPU parity of token-tree verification (spec_verify_run_tree) against the
+CPU oracle (oracle.verify_tree), with oracle.parity.compare_tree: accepted
+paths, counts, last nodes and emitted tokens bit-exact outside the 1e-6
+decision and draw bands, every output a valid walk of its tree."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.parity import compare_tree
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def svlib():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import rejection_sampling_verify_temp_amd as m
+    m.load_library()
+    return m
+
+
+def check(svlib, w, seed=0, offset=0, draft_is_probs=False, expect_flags=0):
+    say(f"[gpu] tree {w.name} seed={seed} offset={offset}")
+    w = w.to("cuda")
+    h = svlib.SpecVerify(w.B, 1, w.V, w.target.dtype,
+                         draft_dtype=w.draft.dtype if w.draft is not None else None,
+                         draft_is_probs=draft_is_probs)
+    tokens, nacc, last = h.run_tree(w.target, w.draft, w.tokens, w.parents, w.num_nodes,
+                                    w.temperatures, seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    flags = h.device_errors(clear=True)
+    h.close()
+    hs = w.host_arrays()
+    ref = oracle.verify_tree(hs["target"], hs["draft"], hs["tokens"], hs["parents"],
+                             hs["num_nodes"], hs["temperatures"], seed=seed, offset=offset,
+                             draft_is_probs=draft_is_probs)
+    rep = compare_tree(hs["tokens"], hs["parents"], hs["num_nodes"], w.V, ref,
+                       tokens.cpu().numpy(), nacc.cpu().numpy(), last.cpu().numpy())
+    say(f"      requests={rep.requests} flagged={rep.flagged} (differing "
+        f"{rep.flagged_mismatch}) accepted={rep.accepted} flags={flags}")
+    assert rep.ok(), rep.mismatches
+    assert flags & ~8 == expect_flags, (flags, expect_flags)
+    assert ref["flags"] == expect_flags
+    return rep, ref
+
+
+CASES = {
+    "f32_V1001_random": dict(B=32, N=12, V=1001, temps=(1.0, 0.0, 0.6)),
+    "bf16_V4099_random": dict(B=32, N=16, V=4099, dtype=torch.bfloat16, temps=(0.8, 1.3)),
+    "bf16_wide": dict(B=24, N=9, V=3000, dtype=torch.bfloat16, temps=(1.0,), shape="wide"),
+    "chain": dict(B=24, N=8, V=2051, temps=(1.0, 0.0, 0.7), shape="chain"),
+    "onehot_random": dict(B=32, N=12, V=777, temps=(1.0, 0.5, 0.0), onehot=True),
+    "onehot_wide": dict(B=24, N=7, V=500, temps=(0.9,), onehot=True, shape="wide"),
+    "mixed_dtypes": dict(B=16, N=10, V=2000, dtype=torch.bfloat16, draft_dtype=torch.float32,
+                         temps=(1.1,)),
+    "V2": dict(B=64, N=6, V=2, temps=(1.0, 0.5, 0.0)),
+    "V1": dict(B=8, N=4, V=1, temps=(1.0, 0.0)),
+    "N1_root_only": dict(B=16, N=1, V=300, temps=(1.0, 0.0)),
+    "low_corr": dict(B=32, N=14, V=1500, temps=(1.0,), corr=0.2),
+    "tiny_T": dict(B=16, N=8, V=300, temps=(1e-3, 0.05)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_random_trees(svlib, name):
+    for seed in (0, 1):
+        w = synth.make_tree(seed=seed, **CASES[name])
+        check(svlib, w, seed=seed, offset=5 * seed)
+
+
+def test_chain_tree_equals_verify(svlib):
+    """A chain-shaped tree on the GPU gives the verify step's outputs."""
+    w = synth.make_random(32, 5, 3000, dtype=torch.bfloat16, temps=(1.0, 0.7, 0.0),
+                          n_mode="ragged", seed=6, nan_padding=False)
+    B, K, V = w.B, w.K, w.V
+    N = K + 1
+    tokens = torch.zeros((B, N), dtype=torch.int32)
+    tokens[:, 1:] = w.draft_ids
+    parents = torch.arange(-1, N - 1, dtype=torch.int32).repeat(B, 1)
+    draft = torch.zeros((B, N, V), dtype=w.draft.dtype)
+    draft[:, :K] = w.draft
+    t = synth.TreeWorkload("chain of a verify batch", w.target, draft, tokens, parents,
+                           w.num_drafts + 1, w.temperatures)
+    rep, ref = check(svlib, t, seed=2, offset=3)
+    hs = w.host_arrays()
+    chain = oracle.verify(hs["target"], hs["draft"], hs["draft_ids"], hs["num_drafts"],
+                          hs["temperatures"], seed=2, offset=3)
+    assert np.array_equal(ref["tokens"], chain["tokens"])
+
+
+def test_probability_drafts(svlib):
+    w = synth.make_tree(24, 10, 1200, temps=(1.0, 0.8), seed=3)
+    w.draft = torch.softmax(w.draft.float(), -1)
+    check(svlib, w, seed=1, draft_is_probs=True)
+
+
+def test_malformed_trees_are_flagged(svlib):
+    w = synth.make_tree(8, 6, 300, temps=(1.0, 0.0), seed=4, ragged=False)
+    w.parents[0, 3] = 5      # parent after the node: never visited
+    w.tokens[1, 1] = -4      # bad id: never accepted
+    w.tokens[2, 2] = 300
+    w.num_nodes[3] = 0       # clamped into [1, N]
+    w.num_nodes[4] = 9
+    check(svlib, w, expect_flags=16 | 1 | 2)
+
+
+def test_realistic_size(svlib):
+    """64 requests, trees of 16 nodes over a 32000-token vocabulary."""
+    w = synth.make_tree(64, 16, 32000, dtype=torch.bfloat16, temps=(1.0, 0.6, 0.0), seed=8,
+                        corr=0.95, device="cuda")
+    rep, _ = check(svlib, w, seed=9, offset=1)
+    assert rep.accepted > 0
