@@ -4,6 +4,7 @@
     python bench.py --op draft_sample     # the draft-token sampler instead
     python bench.py --op ngram            # the n-gram prompt-lookup proposer
     python bench.py --op typical          # verify with typical acceptance
+    python bench.py --op tree             # token-tree verification
 
 One step = one spec_verify_run over a whole batch: row statistics, decisions,
 residual sums of rejected probabilistic drafts, and the draws.  Inputs are
@@ -220,6 +221,91 @@ def bench_ngram(args):
     print(json.dumps(out), flush=True)
 
 
+METRIC_TREE = "tree elems/s (req×node×vocab) + achieved HBM GB/s vs peak, token-tree verification"
+TREE = dict(B=256, N=16, V=152064)
+
+
+def bench_tree(args):
+    """Token-tree verification: 256 requests, random recursive trees of 16
+    nodes over V = 152064 (bf16 target and draft logits, child tokens drawn
+    from the parent's draft law, per-request T in {0.6, 1.0, 0.0, 0.8}).  A
+    step is one spec_verify_run_tree over the batch."""
+    import torch
+    import synth
+    import rejection_sampling_verify_temp_amd as sv
+    c = TREE
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copies = [synth.make_tree(c["B"], c["N"], c["V"], dtype=torch.bfloat16, seed=31 + i,
+                              temps=(0.6, 1.0, 0.0, 0.8), corr=0.95, ragged=False, device=dev)
+              for i in range(args.rotate)]
+    w = copies[0]
+    h = sv.SpecVerify(w.B, 1, w.V, torch.bfloat16, draft_dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+    outs = []
+
+    def step(i):
+        t = copies[i % len(copies)]
+        outs.append(h.run_tree(t.target, t.draft, t.tokens, t.parents, t.num_nodes,
+                               t.temperatures, seed=0, offset=i, stream=stream))
+        del outs[:-len(copies)]
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    assert h.device_errors() & ~8 == 0
+    # bytes of the visited nodes' rows (target and draft), from the last
+    # steps' walks: the least the walk must read
+    row = c["V"] * 2
+    visited, accepted = 0, 0
+    for k in range(len(copies)):
+        _, nacc, _ = outs[k]
+        visited += int((nacc + 1).sum().item())
+        accepted += int(nacc.sum().item())
+    visited /= len(copies)
+    alg = visited * 2 * row
+    elems = sum(int(t.num_nodes.sum().item()) for t in copies) / len(copies) * c["V"]
+    out = {
+        "metric": METRIC_TREE,
+        "value": elems / (ms_step * 1e-3),
+        "unit": "elems/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "token-tree verification, B=256 random trees of 16 nodes, "
+                               "V=152064 bf16",
+                   **c, "input_copies": len(copies), "visited_rows_per_step": visited,
+                   "accepted_per_request": accepted / len(copies) / c["B"],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "tree", "achieved": alg / (ms_step * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        hs = w.host_arrays()
+        t0, n_req = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 12.0 and n_req < c["B"]:
+            sl = slice(n_req, n_req + 4)
+            oracle.verify_tree(hs["target"][sl], hs["draft"][sl], hs["tokens"][sl],
+                               hs["parents"][sl], hs["num_nodes"][sl], hs["temperatures"][sl])
+            n_req += 4
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(value=n_req * c["N"] * c["V"] / dt, unit="elems/s", cores=1,
+                                   kind="oracle",
+                                   sample=f"{n_req} requests of the same batch, {dt:.1f} s of "
+                                          "the single-threaded fp64 C oracle")
+    h.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,7 +315,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--op", choices=["verify", "draft_sample", "ngram", "typical"],
+    ap.add_argument("--op", choices=["verify", "draft_sample", "ngram", "typical", "tree"],
                     default="verify")
     ap.add_argument("--threshold", type=float, default=0.05,
                     help="--op typical: the probability threshold")
@@ -245,6 +331,8 @@ def main():
         sys.exit(2)
     if args.op == "ngram":
         return bench_ngram(args)
+    if args.op == "tree":
+        return bench_tree(args)
 
     import torch
     import synth

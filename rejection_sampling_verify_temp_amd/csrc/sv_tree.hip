@@ -13,9 +13,11 @@
 //   - the children of v are tested in index order; after k rejections the
 //     law is max(0, p - c_k q) / Z_k, and each further sibling test needs
 //     Z_k, one more pass over the row pair;
-//   - where the walk stops, the emitted token is drawn by inverse CDF:
-//     every thread sums a contiguous segment, a workgroup scan finds the
-//     segment holding u * S, and its thread walks it.
+//   - where the walk stops, the emitted token is drawn by inverse CDF: each
+//     wavefront sums its 64-vector slot of every strided pass, a workgroup
+//     scan over the slot sums finds the slot holding u * S, and one
+//     wavefront re-reads that slot to find the element.
+// All row passes use 16-byte loads, four per thread in flight.
 // The walk is sequential per request; requests run in parallel.
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -45,32 +47,53 @@ struct RowStats {
   int arg;     // lowest index of the max (greedy)
 };
 
-// Statistics of one row (whole workgroup; strided, 8 loads in flight).
+// A row is a scalar head [0, v0) up to the first 16-byte boundary, nvec
+// vectors from v0 and a scalar tail [t0, V) (chunk_geo over the whole row).
+// Vectors are strided over the workgroup, 4 per thread in flight.
+constexpr int kTreeUnroll = 4;
+
+__device__ __forceinline__ const u32x4* vec_base(const void* row, const Geo& g, int bytes) {
+  return reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + (size_t)g.v0 * bytes);
+}
+
+// Statistics of one row (whole workgroup).  Each thread visits its elements
+// in increasing index order (head, its vectors, tail), so the first max it
+// meets is its lowest.
 template <int DT>
 __device__ RowStats row_stats(const void* row, int V, bool sampling, float c, float* ldsf,
                               double* ldsd, int* ldsi) {
+  using E = Elt<DT>;
   const int tid = threadIdx.x;
+  const Geo g = chunk_geo<DT>(row, 0, V);
+  const u32x4* vp = vec_base(row, g, E::kBytes);
   float m = kNegInf, R = 0.f, S = 0.f;
   int arg = INT32_MAX;
-  for (int i0 = tid; i0 < V; i0 += 8 * kTreeThreads) {
-    float x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * kTreeThreads;
-      x[u] = i < V ? Elt<DT>::at(row, i) : kNegInf;
+  auto visit = [&](float x, int i) {
+    if (sampling) {
+      sm_add(x, c, m, R, S);
+    } else if (x > m) {
+      m = x;
+      arg = i;
     }
+  };
+  if (tid < g.v0) visit(E::at(row, tid), tid);
+  for (int v = tid; v < g.nvec; v += kTreeUnroll * kTreeThreads) {
+    u32x4 d[kTreeUnroll];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * kTreeThreads;
-      if (i >= V) continue;
-      if (sampling) {
-        sm_add(x[u], c, m, R, S);
-      } else if (x[u] > m) {  // indices ascend per thread: first max wins
-        m = x[u];
-        arg = i;
+    for (int u = 0; u < kTreeUnroll; ++u)
+      if (v + u * kTreeThreads < g.nvec) d[u] = vp[v + u * kTreeThreads];
+#pragma unroll
+    for (int u = 0; u < kTreeUnroll; ++u) {
+      const int vi = v + u * kTreeThreads;
+      if (vi < g.nvec) {
+        float x[E::kVec];
+        E::unpack(d[u], x);
+#pragma unroll
+        for (int k = 0; k < E::kVec; ++k) visit(x[k], g.v0 + vi * E::kVec + k);
       }
     }
   }
+  if (g.t0 + tid < V) visit(E::at(row, g.t0 + tid), g.t0 + tid);
   RowStats st;
   if (sampling) {
     st.m = block_max<kTreeThreads>(m, ldsf);
@@ -99,30 +122,73 @@ struct Law {
   bool probs;
 };
 
-template <int TDT, int DDT>
-__device__ __forceinline__ float law_at(const Law& L, const void* prow, const void* qrow, int i) {
-  const float pt = fast_exp2(fmaf(Elt<TDT>::at(prow, i), L.c, L.ref_p));
+__device__ __forceinline__ float law_of(const Law& L, float lp, float lq) {
+  const float pt = fast_exp2(fmaf(lp, L.c, L.ref_p));
   if (!L.pair) return pt;
-  const float lq = Elt<DDT>::at(qrow, i);
   const float qt = L.probs ? lq : fast_exp2(fmaf(lq, L.c, L.ref_q));
   float r = fmaf(-qt, L.kap_hi, pt);
   r = fmaf(-qt, L.kap_lo, r);
   return r > 0.f ? r : 0.f;
 }
 
+template <int TDT, int DDT>
+__device__ __forceinline__ float law_at(const Law& L, const void* prow, const void* qrow, int i) {
+  return law_of(L, Elt<TDT>::at(prow, i), L.pair ? Elt<DDT>::at(qrow, i) : 0.f);
+}
+
+// The law at the kVec elements of target vector vi.  The draft row's
+// elements come by one vector load when both rows have the same element
+// type and alignment (qvec), else element by element.
+template <int TDT, int DDT>
+__device__ __forceinline__ void law_vec(const Law& L, const void* prow, const void* qrow,
+                                        const Geo& g, int vi, bool qvec, float* r) {
+  using EP = Elt<TDT>;
+  float lp[EP::kVec], lq[EP::kVec];
+  EP::unpack(vec_base(prow, g, EP::kBytes)[vi], lp);
+  if (L.pair) {
+    if constexpr (TDT == DDT) {
+      if (qvec) {
+        EP::unpack(vec_base(qrow, g, EP::kBytes)[vi], lq);
+      } else {
+#pragma unroll
+        for (int k = 0; k < EP::kVec; ++k) lq[k] = Elt<DDT>::at(qrow, g.v0 + vi * EP::kVec + k);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < EP::kVec; ++k) lq[k] = Elt<DDT>::at(qrow, g.v0 + vi * EP::kVec + k);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < EP::kVec; ++k) r[k] = law_of(L, lp[k], L.pair ? lq[k] : 0.f);
+}
+
+__device__ __forceinline__ bool same_alignment(const void* a, const void* b) {
+  return ((reinterpret_cast<uintptr_t>(a) ^ reinterpret_cast<uintptr_t>(b)) & 15u) == 0;
+}
+
 // Sum of the law over the row (whole workgroup, fp64 across threads).
 template <int TDT, int DDT>
 __device__ double law_sum(const Law& L, const void* prow, const void* qrow, int V, double* ldsd) {
+  using EP = Elt<TDT>;
+  const int tid = threadIdx.x;
+  const Geo g = chunk_geo<TDT>(prow, 0, V);
+  const bool qvec = L.pair && same_alignment(prow, qrow);
   double acc = 0.0;
-  for (int i0 = threadIdx.x; i0 < V; i0 += 8 * kTreeThreads) {
-    float r[8];
+  if (tid < g.v0) acc += (double)law_at<TDT, DDT>(L, prow, qrow, tid);
+  for (int v = tid; v < g.nvec; v += kTreeUnroll * kTreeThreads) {
+    float s[kTreeUnroll];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * kTreeThreads;
-      r[u] = i < V ? law_at<TDT, DDT>(L, prow, qrow, i) : 0.f;
+    for (int u = 0; u < kTreeUnroll; ++u) {
+      s[u] = 0.f;
+      if (v + u * kTreeThreads < g.nvec) {
+        float r[EP::kVec];
+        law_vec<TDT, DDT>(L, prow, qrow, g, v + u * kTreeThreads, qvec, r);
+        s[u] = pairwise_sum(r);
+      }
     }
-    acc += (double)pairwise_sum(r);
+    acc += (double)pairwise_sum(s);
   }
+  if (g.t0 + tid < V) acc += (double)law_at<TDT, DDT>(L, prow, qrow, g.t0 + tid);
   return block_sum<kTreeThreads>(acc, ldsd);
 }
 
@@ -132,73 +198,164 @@ __device__ __forceinline__ bool excluded(const int* ex, int nex, int i) {
   return false;
 }
 
-// Inverse-CDF draw from the law with uniform u (whole workgroup).  The
-// tokens in ex[0..nex) are removed.  Returns the token; *rounding is set if
-// u * S fell past the recomputed total.
+// Inverse-CDF draw from the law with uniform u (whole workgroup); the tokens
+// in ex[0..nex) are removed.  The row is cut into slots: 0 = the head, then
+// one slot per 64 vectors (one wavefront's share of one strided iteration,
+// summed by that wavefront), then the tail.  A workgroup scan over the slot
+// sums finds the slot holding u * S, and wavefront 0 re-reads only that slot
+// (one vector per lane) to find the element.  Returns the token; *rounding
+// is set if u * S fell past the recomputed total, *empty if the law is 0.
 template <int TDT, int DDT>
 __device__ int law_draw(const Law& L, const void* prow, const void* qrow, int V, const int* ex,
-                        int nex, double u, double* s_woff, int* s_y, int* s_lastseg,
-                        bool* rounding, bool* empty) {
+                        int nex, double u, double* s_slot, double* s_woff, int* s_sel,
+                        double* s_th, bool* rounding, bool* empty) {
+  using EP = Elt<TDT>;
+  constexpr int KV = EP::kVec;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int seglen = (V + kTreeThreads - 1) / kTreeThreads;
-  const int i0 = min(V, tid * seglen), i1 = min(V, i0 + seglen);
-  double seg = 0.0;
-  for (int i = i0; i < i1; ++i) seg += (double)law_at<TDT, DDT>(L, prow, qrow, i);
-  for (int k = 0; k < nex; ++k)  // removed tokens: their owner takes them out
-    if (ex[k] >= i0 && ex[k] < i1 && !excluded(ex, k, ex[k]))
-      seg -= (double)law_at<TDT, DDT>(L, prow, qrow, ex[k]);
-  if (!(seg > 0.0)) seg = 0.0;
-  // exclusive scan of the segment sums
-  const double incl = wave_incl_scan(seg, lane);
+  const Geo g = chunk_geo<TDT>(prow, 0, V);
+  const bool qvec = L.pair && same_alignment(prow, qrow);
+  const int npieces = (g.nvec + 63) / 64, nslot = npieces + 2;
+
+  // (1) slot sums
+  for (int j = 0; j * kTreeThreads < g.nvec; ++j) {
+    const int vi = j * kTreeThreads + tid;
+    float sv = 0.f;
+    if (vi < g.nvec) {
+      float r[KV];
+      law_vec<TDT, DDT>(L, prow, qrow, g, vi, qvec, r);
+      sv = pairwise_sum(r);
+    }
+    const double ws = wave_sum((double)sv);
+    if (lane == 0 && j * kTreeWaves + w < npieces) s_slot[1 + j * kTreeWaves + w] = ws;
+  }
+  if (w == 0) {
+    const double h = wave_sum(lane < g.v0 ? (double)law_at<TDT, DDT>(L, prow, qrow, lane) : 0.0);
+    const double t =
+        wave_sum(g.t0 + lane < V ? (double)law_at<TDT, DDT>(L, prow, qrow, g.t0 + lane) : 0.0);
+    if (lane == 0) {
+      s_slot[0] = h;
+      s_slot[nslot - 1] = t;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {  // removed tokens leave their slots
+    for (int k = 0; k < nex; ++k) {
+      const int e = ex[k];
+      const int sl = e < g.v0 ? 0 : (e >= g.t0 ? nslot - 1 : 1 + (e - g.v0) / KV / 64);
+      s_slot[sl] -= (double)law_at<TDT, DDT>(L, prow, qrow, e);
+    }
+    for (int k = 0; k < nex; ++k) {  // rounding can leave a tiny negative
+      const int e = ex[k];
+      const int sl = e < g.v0 ? 0 : (e >= g.t0 ? nslot - 1 : 1 + (e - g.v0) / KV / 64);
+      if (!(s_slot[sl] > 0.0)) s_slot[sl] = 0.0;
+    }
+    *s_sel = -1;
+  }
+  __syncthreads();
+
+  // (2) scan of the slot sums: thread t takes slots [t sp, t sp + sp)
+  const int sp = (nslot + kTreeThreads - 1) / kTreeThreads;
+  const int k0 = min(nslot, tid * sp), k1 = min(nslot, k0 + sp);
+  double loc = 0.0;
+  int lastpos = -1;
+  for (int k = k0; k < k1; ++k) {
+    loc += s_slot[k];
+    if (s_slot[k] > 0.0) lastpos = k;
+  }
+  const double incl = wave_incl_scan(loc, lane);
   if (lane == 63) s_woff[w] = incl;
   double q = __shfl_up(incl, 1, 64);
   if (lane == 0) q = 0.0;
-  if (tid == 0) {
-    *s_y = INT32_MAX;
-    *s_lastseg = -1;
-  }
   __syncthreads();
-  if (seg > 0.0) atomicMax(s_lastseg, tid);
   double total = 0.0;
   for (int k = 0; k < kTreeWaves; ++k) {
     if (k < w) q += s_woff[k];
     total += s_woff[k];
   }
-  __syncthreads();
   *empty = !(total > 0.0);
-  if (*empty) return -1;
+  if (*empty) {
+    __syncthreads();
+    return -1;
+  }
   const double theta = u * total;
-  const bool mine = seg > 0.0 && q <= theta && theta < q + seg;
-  const bool past = *s_lastseg == tid && !(theta < q + seg);
-  int ymine = INT32_MAX;
-  if (mine || past) {
+  if (loc > 0.0 && q <= theta && theta < q + loc) {
     double acc = q;
-    int y = -1, lp = -1;
-    for (int i = i0; i < i1; ++i) {
-      float r = law_at<TDT, DDT>(L, prow, qrow, i);
-      if (nex > 0 && excluded(ex, nex, i)) r = 0.f;
-      acc += (double)r;
-      if (r > 0.f) {
-        if (y < 0 && mine && acc > theta) y = i;
-        lp = i;
+    for (int k = k0; k < k1; ++k) {
+      if (s_slot[k] > 0.0 && theta < acc + s_slot[k]) {
+        *s_sel = k;
+        *s_th = theta - acc;
+        break;
       }
+      acc += s_slot[k];
     }
-    ymine = y >= 0 ? y : lp;
-    if (ymine < 0) ymine = INT32_MAX;
-    if (mine) atomicMin(s_y, ymine);
   }
   __syncthreads();
-  int y = *s_y;
   *rounding = false;
-  if (y == INT32_MAX) {  // theta past the recomputed total: last positive element
+  if (*s_sel < 0) {  // theta at or past the total: the last slot with mass
     *rounding = true;
     __syncthreads();
-    if (past && ymine != INT32_MAX) *s_y = ymine;
+    if (lastpos >= 0) atomicMax(s_sel, lastpos);
+    if (tid == 0) *s_th = __builtin_inf();
     __syncthreads();
-    y = *s_y;
-    if (y == INT32_MAX) y = 0;
   }
-  return y;
+  const int sel = *s_sel;
+  const double th = *s_th;
+
+  // (3) wavefront 0 finds the element inside slot sel
+  if (w == 0) {
+    float r[KV];
+    int base;  // index of r[0]
+    int cnt;   // valid elements in r
+    if (sel == 0 || sel == nslot - 1) {
+      base = sel == 0 ? lane : g.t0 + lane;
+      cnt = (sel == 0 ? lane < g.v0 : g.t0 + lane < V) ? 1 : 0;
+      r[0] = cnt ? law_at<TDT, DDT>(L, prow, qrow, base) : 0.f;
+#pragma unroll
+      for (int k = 1; k < KV; ++k) r[k] = 0.f;
+    } else {
+      const int vi = (sel - 1) * 64 + lane;
+      base = g.v0 + vi * KV;
+      cnt = vi < g.nvec ? KV : 0;
+      if (cnt) {
+        law_vec<TDT, DDT>(L, prow, qrow, g, vi, qvec, r);
+      } else {
+#pragma unroll
+        for (int k = 0; k < KV; ++k) r[k] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KV; ++k)
+      if (k >= cnt || (nex > 0 && excluded(ex, nex, base + k))) r[k] = 0.f;
+    double ls = 0.0;
+#pragma unroll
+    for (int k = 0; k < KV; ++k) ls += (double)r[k];
+    const double li = wave_incl_scan(ls, lane);
+    double before = __shfl_up(li, 1, 64);
+    if (lane == 0) before = 0.0;
+    const uint64_t hit = __ballot(ls > 0.0 && before <= th && th < li);
+    const uint64_t has = __ballot(ls > 0.0);
+    const int src = hit ? (int)__builtin_ctzll(hit) : (has ? 63 - (int)__builtin_clzll(has) : 0);
+    if (lane == src) {
+      double a = before;
+      int y = -1, lp = -1;
+#pragma unroll
+      for (int k = 0; k < KV; ++k) {
+        a += (double)r[k];
+        if (r[k] > 0.f) {
+          if (y < 0 && a > th) y = base + k;
+          lp = base + k;
+        }
+      }
+      if (!hit) *rounding = true;
+      *s_sel = y >= 0 ? y : (lp >= 0 ? lp : base);
+      if (!hit || y < 0) *s_th = -1.0;  // marks a rounding fallback
+    }
+  }
+  __syncthreads();
+  const int token = *s_sel;
+  if (*s_th == -1.0) *rounding = true;
+  __syncthreads();
+  return token;
 }
 
 template <int TDT, int DDT, bool HAS_DRAFT>
@@ -208,7 +365,9 @@ __global__ __launch_bounds__(kTreeThreads) void k_tree(const TreeParams p) {
   __shared__ double ldsd[kTreeWaves];
   __shared__ int ldsi[kTreeWaves];
   __shared__ double s_woff[kTreeWaves];
-  __shared__ int s_y, s_lastseg;
+  __shared__ double s_slot[kMaxVocab / 256 + 2];  // draw slots: 64 vectors each
+  __shared__ int s_sel;
+  __shared__ double s_th;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int N = p.N, V = p.V;
   int n = p.nn[b];
@@ -314,12 +473,12 @@ __global__ __launch_bounds__(kTreeThreads) void k_tree(const TreeParams p) {
         L.kap_lo = (float)(kap - (double)L.kap_hi);
       }
       bool rounding = false, empty = false;
-      y = law_draw<TDT, DDT>(L, prow, qrow, V, s_ex, nex, u_rec, s_woff, &s_y, &s_lastseg,
+      y = law_draw<TDT, DDT>(L, prow, qrow, V, s_ex, nex, u_rec, s_slot, s_woff, &s_sel, &s_th,
                              &rounding, &empty);
       if (empty) {  // no residual mass: draw from p itself
         fl |= SV_DEVERR_ZERO_RESIDUAL;
         L.pair = false;
-        y = law_draw<TDT, DDT>(L, prow, qrow, V, s_ex, 0, u_rec, s_woff, &s_y, &s_lastseg,
+        y = law_draw<TDT, DDT>(L, prow, qrow, V, s_ex, 0, u_rec, s_slot, s_woff, &s_sel, &s_th,
                                &rounding, &empty);
       }
       if (rounding) fl |= SV_DEVERR_DRAW_ROUNDING;
