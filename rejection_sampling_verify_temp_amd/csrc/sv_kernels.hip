@@ -564,50 +564,70 @@ __device__ __forceinline__ void unpack8(const Raw8<DT>& r, float* x) {
   }
 }
 
-// Sum over [c0, c1) of max(0, p~ - kappa q~), token x excluded.
+// Groups of 8 elements per thread per round: enough for one round over a
+// default chunk (15360 bf16 or 8192 fp32 elements) within 128 VGPRs.
+template <int TDT, int DDT>
+constexpr int resid_groups() {
+  return (TDT == SV_F32 || DDT == SV_F32) ? 4 : 8;
+}
+
+// Sum over [c0, c1) of max(0, p~ - kappa q~), token x excluded.  All loads of
+// a round (resid_groups() groups of eight elements of both rows per thread)
+// are issued before any is used; validity is tested per group, and the
+// excluded token's residual is subtracted once from its own loads.
 template <int TDT, int DDT>
 __device__ __forceinline__ double pair_chunk_sum(const void* prow, const void* qrow, int c0,
                                                  int c1, const DrawDesc& d, bool probs,
                                                  double* ldsd) {
-  // groups of eight elements per thread per step
-  constexpr int kGroups = 4;
+  constexpr int kResidGroups = resid_groups<TDT, DDT>();
   const int tid = threadIdx.x;
-  float acc = 0.f;
+  double acc = 0.0;
+  // the excluded token's elements, loaded with the rest
+  const bool has_x = tid == 0 && d.x >= c0 && d.x < c1;
+  float xp = 0.f, xq = 0.f;
+  if (has_x) {
+    xp = Elt<TDT>::at(prow, d.x);
+    xq = Elt<DDT>::at(qrow, d.x);
+  }
   const uintptr_t pa = reinterpret_cast<uintptr_t>(prow) + (uintptr_t)c0 * Elt<TDT>::kBytes;
   const uintptr_t qa = reinterpret_cast<uintptr_t>(qrow) + (uintptr_t)c0 * Elt<DDT>::kBytes;
   int done = c0;
   if (((pa | qa) & 15u) == 0) {
     const int ngrp = (c1 - c0) / 8;
-    for (int g = tid; g < ngrp; g += kThreads * kGroups) {
-      Raw8<TDT> rp[kGroups];
-      Raw8<DDT> rq[kGroups];
+    for (int g = tid; g < ngrp; g += kThreads * kResidGroups) {
+      Raw8<TDT> rp[kResidGroups];
+      Raw8<DDT> rq[kResidGroups];
 #pragma unroll
-      for (int u = 0; u < kGroups; ++u) {
+      for (int u = 0; u < kResidGroups; ++u) {
         const int gi = g + u * kThreads;
         if (gi < ngrp) {
           rp[u] = load8<TDT>(prow, c0 + gi * 8);
           rq[u] = load8<DDT>(qrow, c0 + gi * 8);
         }
       }
+      float s[kResidGroups];
 #pragma unroll
-      for (int u = 0; u < kGroups; ++u) {
-        const int gi = g + u * kThreads;
-        float lp[8], lq[8], e[8];
-        unpack8<TDT>(rp[u], lp);
-        unpack8<DDT>(rq[u], lq);
+      for (int u = 0; u < kResidGroups; ++u) {
+        s[u] = 0.f;
+        if (g + u * kThreads < ngrp) {
+          float lp[8], lq[8], e[8];
+          unpack8<TDT>(rp[u], lp);
+          unpack8<DDT>(rq[u], lq);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int i = c0 + gi * 8 + k;
-          e[k] = (gi < ngrp && i != d.x) ? pair_resid(lp[k], lq[k], d, probs) : 0.f;
+          for (int k = 0; k < 8; ++k) e[k] = pair_resid(lp[k], lq[k], d, probs);
+          s[u] = pairwise_sum(e);
         }
-        acc += pairwise_sum(e);
       }
+      acc += (double)pairwise_sum(s);
     }
     done = c0 + ngrp * 8;
   }
+  float tail = 0.f;
   for (int i = done + tid; i < c1; i += kThreads)
-    if (i != d.x) acc += pair_resid(Elt<TDT>::at(prow, i), Elt<DDT>::at(qrow, i), d, probs);
-  return block_sum<kThreads>((double)acc, ldsd);
+    tail += pair_resid(Elt<TDT>::at(prow, i), Elt<DDT>::at(qrow, i), d, probs);
+  acc += (double)tail;
+  if (has_x) acc -= (double)pair_resid(xp, xq, d, probs);
+  return block_sum<kThreads>(acc, ldsd);
 }
 
 // ---------------------------------------------------------------------------
