@@ -13,12 +13,15 @@
 //   - the children of v are tested in index order; after k rejections the
 //     law is max(0, p - c_k q) / Z_k, and each further sibling test needs
 //     Z_k, one more pass over the row pair;
-//   - where the walk stops, the emitted token is drawn by inverse CDF: each
-//     wavefront sums its 64-vector slot of every strided pass, a workgroup
-//     scan over the slot sums finds the slot holding u * S, and one
-//     wavefront re-reads that slot to find the element.
-// All row passes use 16-byte loads, four per thread in flight.
-// The walk is sequential per request; requests run in parallel.
+//   - where the walk stops, the emitted token is drawn by inverse CDF: one
+//     pass sums the law per slot of 64 vectors, a workgroup scan over the
+//     slot sums finds the slot holding u * S, and one wavefront re-reads that
+//     slot to find the element.
+// Row passes issue 160-224 KiB of 16-byte loads per workgroup before using any
+// (one round trip per round), through buffer resources, so the loads of a
+// round cost no address registers and no branches, and no round waits at a
+// workgroup barrier.  The walk is sequential per request; requests run in
+// parallel, one per compute unit at the usual batch sizes.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -29,17 +32,6 @@ constexpr int kTreeThreads = 1024;
 constexpr int kTreeWaves = kTreeThreads / 64;
 constexpr int kMaxNodes = SPEC_TREE_MAX_NODES;
 
-// Online softmax of the elements a thread visits (in increasing order).
-__device__ __forceinline__ void sm_add(float x, float c, float& m, float& R, float& S) {
-  if (x > m) {
-    const float rn = ref_of(x, c);
-    S = (m == kNegInf) ? 0.f : S * fast_exp2(rn - R);
-    R = rn;
-    m = x;
-  }
-  S += fast_exp2(fmaf(x, c, R));
-}
-
 struct RowStats {
   float m;     // row max
   float ref;   // exponent reference ref_of(m, c)
@@ -49,66 +41,175 @@ struct RowStats {
 
 // A row is a scalar head [0, v0) up to the first 16-byte boundary, nvec
 // vectors from v0 and a scalar tail [t0, V) (chunk_geo over the whole row).
-// Vectors are strided over the workgroup, 4 per thread in flight.
-constexpr int kTreeUnroll = 4;
+// A pass takes the vectors in rounds: every thread issues all its loads of a
+// round (vectors b0 + u * 1024 + tid) before it uses any, so one round trip
+// to memory covers kRowVecs * 16 KiB of a single row (160 KiB), or kPairVecs
+// * 16 KiB of each row of a pair (224 KiB).  The 10 or 14 vectors take 40 or
+// 56 of the 128 registers a thread of a 1024-thread workgroup has; the
+// walk's own state takes most of the rest.
+constexpr int kRowVecs = 10;
+constexpr int kPairVecs = 7;
+constexpr int kRound = kTreeThreads;  // vectors per unroll step of a round
+
+// Draw slots: slot 0 is the head, slot 1 + k the 64 vectors [64 k, 64 k + 64)
+// (one wavefront's share of one unroll step), the last slot the tail.
+__device__ __forceinline__ int num_slots(const Geo& g) { return (g.nvec + 63) / 64 + 2; }
 
 __device__ __forceinline__ const u32x4* vec_base(const void* row, const Geo& g, int bytes) {
   return reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + (size_t)g.v0 * bytes);
 }
 
-// Statistics of one row (whole workgroup).  Each thread visits its elements
-// in increasing index order (head, its vectors, tail), so the first max it
-// meets is its lowest.
+// The vectors of a row as a buffer resource: base and size in bytes.  The
+// hardware checks each load's offset register against the size and returns 0
+// past it without touching memory, so a round issues all its loads with no
+// branch, and the vectors past the row are then padded in registers.  The
+// row pointer is the same for the whole workgroup: readfirstlane states it.
+struct VecBuf {
+  __amdgpu_buffer_rsrc_t r;
+};
+
+__device__ __forceinline__ VecBuf vec_buf(const void* row, const Geo& g, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(vec_base(row, g, bytes));
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  // word 3: 32-bit data format, as the gfx9 family takes for raw loads
+  return VecBuf{__builtin_amdgcn_make_buffer_rsrc(base, 0, g.nvec * 16, 0x00020000)};
+}
+
+// Vector b0 + tid + u * kRound of the row, or 0 past its end.  The whole
+// offset is in the checked register (the scalar offset is not checked).
+__device__ __forceinline__ u32x4 vec_load(const VecBuf& vb, int b0, int u, int tid) {
+  return __builtin_amdgcn_raw_buffer_load_b128(vb.r, (uint32_t)(b0 + u * kRound + tid) * 16u,
+                                               0u, 0);
+}
+
+// The thread index, hidden from loop-invariant code motion: each pass
+// recomputes what it derives from it (per-vector masks, slot indices) rather
+// than the compiler hoisting all of them out of the walk, where they would
+// hold registers through every pass.
+__device__ __forceinline__ int pass_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__device__ __forceinline__ u32x4 select_vec(bool keep, u32x4 a, u32x4 b) {
+  return u32x4{keep ? a.x : b.x, keep ? a.y : b.y, keep ? a.z : b.z, keep ? a.w : b.w};
+}
+
+// 2^(r - rw) for floats r <= rw: the difference is exact in double; its
+// integer part goes to the exponent and v_exp_f32 takes the fraction, so the
+// factor is as accurate as the element exponentials themselves.
+__device__ __forceinline__ double exp2_diff(float r, float rw) {
+  const double d = (double)r - (double)rw;
+  const double n = floor(d);
+  return ldexp((double)fast_exp2((float)(d - n)), (int)n);
+}
+
+// Statistics of one row (whole workgroup).  Sampling rows take each round in
+// two phases per wavefront: the wavefront's max of the round first, which
+// fixes one exponent reference for its 64 lanes, then the sums of
+// exp2(l c + ref) with no per-element max test.  A later round that raises a
+// wavefront's max rescales its sums once.  No round needs a workgroup
+// barrier, so the wavefronts drift apart and one's loads overlap another's
+// arithmetic; the wavefronts' sums meet once, at the row's reference.
+// Greedy rows keep the max and its lowest index.
 template <int DT>
-__device__ RowStats row_stats(const void* row, int V, bool sampling, float c, float* ldsf,
-                              double* ldsd, int* ldsi) {
+__device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampling, float c,
+                                              float* ldsf, double* ldsd, int* ldsi) {
   using E = Elt<DT>;
-  const int tid = threadIdx.x;
+  constexpr int U = kRowVecs;
+  const int tid = pass_tid();
   const Geo g = chunk_geo<DT>(row, 0, V);
-  const u32x4* vp = vec_base(row, g, E::kBytes);
-  float m = kNegInf, R = 0.f, S = 0.f;
-  int arg = INT32_MAX;
-  auto visit = [&](float x, int i) {
-    if (sampling) {
-      sm_add(x, c, m, R, S);
-    } else if (x > m) {
-      m = x;
-      arg = i;
+  const VecBuf vb = vec_buf(row, g, E::kBytes);
+  // each thread's scalar elements: one of the head, one of the tail
+  const bool has_h = tid < g.v0, has_t = g.t0 + tid < V;
+  const float hx = has_h ? E::at(row, tid) : kNegInf;
+  const float tx = has_t ? E::at(row, g.t0 + tid) : kNegInf;
+  RowStats st;
+  if (!sampling) {
+    AmAcc a{kNegInf, INT32_MAX};
+    if (has_h) {
+      const float x[1] = {hx};
+      const int ix[1] = {tid};
+      am_tile(a, x, ix);
     }
-  };
-  if (tid < g.v0) visit(E::at(row, tid), tid);
-  for (int v = tid; v < g.nvec; v += kTreeUnroll * kTreeThreads) {
-    u32x4 d[kTreeUnroll];
+    for (int b0 = 0; b0 < g.nvec; b0 += U * kRound) {
+      u32x4 d[U];
 #pragma unroll
-    for (int u = 0; u < kTreeUnroll; ++u)
-      if (v + u * kTreeThreads < g.nvec) d[u] = vp[v + u * kTreeThreads];
+      for (int u = 0; u < U; ++u)
+        if (b0 + u * kRound + tid < g.nvec) d[u] = vec_load(vb, b0, u, tid);
 #pragma unroll
-    for (int u = 0; u < kTreeUnroll; ++u) {
-      const int vi = v + u * kTreeThreads;
-      if (vi < g.nvec) {
-        float x[E::kVec];
-        E::unpack(d[u], x);
+      for (int u = 0; u < U; ++u) {
+        const int vi = b0 + u * kRound + tid;
+        if (vi < g.nvec) {
+          float x[E::kVec];
+          int ix[E::kVec];
+          E::unpack(d[u], x);
 #pragma unroll
-        for (int k = 0; k < E::kVec; ++k) visit(x[k], g.v0 + vi * E::kVec + k);
+          for (int k = 0; k < E::kVec; ++k) ix[k] = g.v0 + vi * E::kVec + k;
+          am_tile(a, x, ix);
+        }
       }
     }
-  }
-  if (g.t0 + tid < V) visit(E::at(row, g.t0 + tid), g.t0 + tid);
-  RowStats st;
-  if (sampling) {
-    st.m = block_max<kTreeThreads>(m, ldsf);
-    st.ref = ref_of(st.m, c);
-    double contrib = 0.0;
-    if (S != 0.f && st.m != kNegInf) contrib = (double)S * exp2((double)st.ref - (double)R);
-    st.z = block_sum<kTreeThreads>(contrib, ldsd);
-    st.arg = 0;
-  } else {
-    block_argmax<kTreeThreads>(m, arg, ldsf, ldsi);
-    st.m = m;
-    st.arg = arg == INT32_MAX ? 0 : arg;
+    if (has_t) {
+      const float x[1] = {tx};
+      const int ix[1] = {g.t0 + tid};
+      am_tile(a, x, ix);
+    }
+    block_argmax<kTreeThreads>(a.M, a.I, ldsf, ldsi);
+    st.m = a.M;
+    st.arg = a.I == INT32_MAX ? 0 : a.I;
     st.ref = 0.f;
     st.z = 0.0;
+    return st;
   }
+  float Mw = kNegInf, Rw = 0.f;  // the wavefront's max and reference so far
+  double S = 0.0;                // this thread's sum, relative to Rw
+  for (int b0 = 0; b0 == 0 || b0 < g.nvec; b0 += U * kRound) {
+    u32x4 d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[u] = vec_load(vb, b0, u, tid);
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[u] = select_vec(b0 + u * kRound + tid < g.nvec, d[u], E::neg_inf());
+    float t = b0 == 0 ? fmaxf(hx, tx) : kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[E::kVec];
+      E::unpack(d[u], x);
+#pragma unroll
+      for (int k = 0; k < E::kVec; ++k) t = fmaxf(t, x[k]);
+    }
+    const float wm = wave_max(t);
+    if (wm > Mw) {  // uniform across the wavefront
+      const float rn = ref_of(wm, c);
+      if (Mw != kNegInf) S *= (double)fast_exp2(rn - Rw);
+      Rw = rn;
+      Mw = wm;
+    }
+    if (b0 == 0) S += (double)fast_exp2(fmaf(hx, c, Rw)) + (double)fast_exp2(fmaf(tx, c, Rw));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // unpack again rather than keep the floats live: the empty asm hides
+      // the first unpack from common-subexpression elimination
+      u32x4 wv = d[u];
+      asm volatile("" : "+v"(wv));
+      float e[E::kVec];
+      E::unpack(wv, e);
+#pragma unroll
+      for (int k = 0; k < E::kVec; ++k) e[k] = fast_exp2(fmaf(e[k], c, Rw));
+      S += (double)pairwise_sum(e);  // 0 for padding
+      asm volatile("" : "+v"(S));    // fold in order: no sums wait in registers
+    }
+  }
+  const float M = block_max<kTreeThreads>(Mw, ldsf);
+  const float R = ref_of(M, c);
+  const double f = Mw == kNegInf ? 0.0 : (Mw == M ? 1.0 : exp2_diff(R, Rw));
+  st.m = M;
+  st.ref = R;
+  st.z = block_sum<kTreeThreads>(S * f, ldsd);
+  st.arg = 0;
   return st;
 }
 
@@ -166,68 +267,99 @@ __device__ __forceinline__ bool same_alignment(const void* a, const void* b) {
   return ((reinterpret_cast<uintptr_t>(a) ^ reinterpret_cast<uintptr_t>(b)) & 15u) == 0;
 }
 
-// Sum of the law over the row (whole workgroup, fp64 across threads).
-template <int TDT, int DDT>
-__device__ double law_sum(const Law& L, const void* prow, const void* qrow, int V, double* ldsd) {
+// One pass over the law of a row (and, for a pair, of its draft row): calls
+// f(b, s) once per unroll step of every round, convergently, with s the
+// thread's fp32 sum of the law over its vector b + tid (0 past the vectors).
+// When the draft row has the target's element type and 16-byte alignment,
+// both rows' vectors of a round are loaded together, kPairVecs each (or
+// kRowVecs of a single row); otherwise the draft elements are loaded one by
+// one, a vector of the target at a time.
+template <int TDT, int DDT, typename F>
+__device__ __forceinline__ void law_pass(const Law& L, const void* prow, const void* qrow,
+                                         const Geo& g, F&& f) {
   using EP = Elt<TDT>;
-  const int tid = threadIdx.x;
-  const Geo g = chunk_geo<TDT>(prow, 0, V);
-  const bool qvec = L.pair && same_alignment(prow, qrow);
-  double acc = 0.0;
-  if (tid < g.v0) acc += (double)law_at<TDT, DDT>(L, prow, qrow, tid);
-  for (int v = tid; v < g.nvec; v += kTreeUnroll * kTreeThreads) {
-    float s[kTreeUnroll];
+  constexpr int KV = EP::kVec;
+  const int tid = pass_tid();
+  const VecBuf pb = vec_buf(prow, g, EP::kBytes);
+  if (!L.pair) {
+    for (int b0 = 0; b0 < g.nvec; b0 += kRowVecs * kRound) {
+      u32x4 d[kRowVecs];
 #pragma unroll
-    for (int u = 0; u < kTreeUnroll; ++u) {
-      s[u] = 0.f;
-      if (v + u * kTreeThreads < g.nvec) {
-        float r[EP::kVec];
-        law_vec<TDT, DDT>(L, prow, qrow, g, v + u * kTreeThreads, qvec, r);
-        s[u] = pairwise_sum(r);
+      for (int u = 0; u < kRowVecs; ++u) d[u] = vec_load(pb, b0, u, tid);
+#pragma unroll
+      for (int u = 0; u < kRowVecs; ++u) {
+        float r[KV];
+        EP::unpack(d[u], r);
+#pragma unroll
+        for (int k = 0; k < KV; ++k) r[k] = law_of(L, r[k], 0.f);
+        const float sv = pairwise_sum(r);
+        f(b0 + u * kRound, b0 + u * kRound + tid < g.nvec ? sv : 0.f);
       }
     }
-    acc += (double)pairwise_sum(s);
+    return;
   }
+  if constexpr (TDT == DDT) {
+    if (same_alignment(prow, qrow)) {
+      const VecBuf qb = vec_buf(qrow, g, EP::kBytes);
+      for (int b0 = 0; b0 < g.nvec; b0 += kPairVecs * kRound) {
+        u32x4 dp[kPairVecs], dq[kPairVecs];
+#pragma unroll
+        for (int u = 0; u < kPairVecs; ++u) {
+          dp[u] = vec_load(pb, b0, u, tid);
+          dq[u] = vec_load(qb, b0, u, tid);
+        }
+#pragma unroll
+        for (int u = 0; u < kPairVecs; ++u) {
+          float lp[KV], lq[KV], r[KV];
+          EP::unpack(dp[u], lp);
+          EP::unpack(dq[u], lq);
+#pragma unroll
+          for (int k = 0; k < KV; ++k) r[k] = law_of(L, lp[k], lq[k]);
+          const float sv = pairwise_sum(r);
+          f(b0 + u * kRound, b0 + u * kRound + tid < g.nvec ? sv : 0.f);
+        }
+      }
+      return;
+    }
+  }
+  for (int b0 = 0; b0 < g.nvec; b0 += kRound) {
+    float sv = 0.f;
+    if (b0 + tid < g.nvec) {
+      float r[KV];
+      law_vec<TDT, DDT>(L, prow, qrow, g, b0 + tid, false, r);
+      sv = pairwise_sum(r);
+    }
+    f(b0, sv);
+  }
+}
+
+// Sum of the law over the row (whole workgroup, fp64 across vectors).
+template <int TDT, int DDT>
+__device__ __forceinline__ double law_sum(const Law& L, const void* prow, const void* qrow, int V, double* ldsd) {
+  const int tid = pass_tid();
+  const Geo g = chunk_geo<TDT>(prow, 0, V);
+  double acc = 0.0;
+  if (tid < g.v0) acc += (double)law_at<TDT, DDT>(L, prow, qrow, tid);
+  law_pass<TDT, DDT>(L, prow, qrow, g, [&](int, float sv) {
+    acc += (double)sv;
+    asm volatile("" : "+v"(acc));  // fold in order: no sums wait in registers
+  });
   if (g.t0 + tid < V) acc += (double)law_at<TDT, DDT>(L, prow, qrow, g.t0 + tid);
   return block_sum<kTreeThreads>(acc, ldsd);
 }
 
-__device__ __forceinline__ bool excluded(const int* ex, int nex, int i) {
-  for (int k = 0; k < nex; ++k)
-    if (ex[k] == i) return true;
-  return false;
-}
-
-// Inverse-CDF draw from the law with uniform u (whole workgroup); the tokens
-// in ex[0..nex) are removed.  The row is cut into slots: 0 = the head, then
-// one slot per 64 vectors (one wavefront's share of one strided iteration,
-// summed by that wavefront), then the tail.  A workgroup scan over the slot
-// sums finds the slot holding u * S, and wavefront 0 re-reads only that slot
-// (one vector per lane) to find the element.  Returns the token; *rounding
-// is set if u * S fell past the recomputed total, *empty if the law is 0.
+// The law's sums per draw slot, by one pass over the row (or row pair).
 template <int TDT, int DDT>
-__device__ int law_draw(const Law& L, const void* prow, const void* qrow, int V, const int* ex,
-                        int nex, double u, double* s_slot, double* s_woff, int* s_sel,
-                        double* s_th, bool* rounding, bool* empty) {
-  using EP = Elt<TDT>;
-  constexpr int KV = EP::kVec;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__device__ __forceinline__ void slot_pass(const Law& L, const void* prow, const void* qrow, int V,
+                          double* s_slot) {
+  const int tid = pass_tid(), lane = tid & 63, w = tid >> 6;
   const Geo g = chunk_geo<TDT>(prow, 0, V);
-  const bool qvec = L.pair && same_alignment(prow, qrow);
   const int npieces = (g.nvec + 63) / 64, nslot = npieces + 2;
-
-  // (1) slot sums
-  for (int j = 0; j * kTreeThreads < g.nvec; ++j) {
-    const int vi = j * kTreeThreads + tid;
-    float sv = 0.f;
-    if (vi < g.nvec) {
-      float r[KV];
-      law_vec<TDT, DDT>(L, prow, qrow, g, vi, qvec, r);
-      sv = pairwise_sum(r);
-    }
+  law_pass<TDT, DDT>(L, prow, qrow, g, [&](int b, float sv) {
+    const int piece = b / 64 + w;
     const double ws = wave_sum((double)sv);
-    if (lane == 0 && j * kTreeWaves + w < npieces) s_slot[1 + j * kTreeWaves + w] = ws;
-  }
+    if (lane == 0 && piece < npieces) s_slot[1 + piece] = ws;
+  });
   if (w == 0) {
     const double h = wave_sum(lane < g.v0 ? (double)law_at<TDT, DDT>(L, prow, qrow, lane) : 0.0);
     const double t =
@@ -237,6 +369,31 @@ __device__ int law_draw(const Law& L, const void* prow, const void* qrow, int V,
       s_slot[nslot - 1] = t;
     }
   }
+}
+
+__device__ __forceinline__ bool excluded(const int* ex, int nex, int i) {
+  for (int k = 0; k < nex; ++k)
+    if (ex[k] == i) return true;
+  return false;
+}
+
+// Inverse-CDF draw from the law with uniform u (whole workgroup), given its
+// sums per draw slot in s_slot (written by slot_pass); the
+// tokens in ex[0..nex) are removed.  A workgroup scan over the slot sums
+// finds the slot holding u * S, and wavefront 0 re-reads only that slot (one
+// vector per lane) to find the element.  Returns the token; *rounding is set
+// if u * S fell past the recomputed total, *empty if the law is 0.  The slot
+// sums of removed tokens are reduced in place.
+template <int TDT, int DDT>
+__device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, const void* qrow, int V,
+                               const int* ex, int nex, double u, double* s_slot, double* s_woff,
+                               int* s_sel, double* s_th, bool* rounding, bool* empty) {
+  using EP = Elt<TDT>;
+  constexpr int KV = EP::kVec;
+  const int tid = pass_tid(), lane = tid & 63, w = tid >> 6;
+  const Geo g = chunk_geo<TDT>(prow, 0, V);
+  const bool qvec = L.pair && same_alignment(prow, qrow);
+  const int nslot = num_slots(g);
   __syncthreads();
   if (tid == 0) {  // removed tokens leave their slots
     for (int k = 0; k < nex; ++k) {
@@ -323,9 +480,15 @@ __device__ int law_draw(const Law& L, const void* prow, const void* qrow, int V,
         for (int k = 0; k < KV; ++k) r[k] = 0.f;
       }
     }
+    // removed tokens: a uniform loop over the list with a select per
+    // element (no per-lane search with an early exit)
+    for (int e = 0; e < nex; ++e) {
+      const int t = ex[e];
 #pragma unroll
-    for (int k = 0; k < KV; ++k)
-      if (k >= cnt || (nex > 0 && excluded(ex, nex, base + k))) r[k] = 0.f;
+      for (int k = 0; k < KV; ++k) r[k] = t == base + k ? 0.f : r[k];
+    }
+#pragma unroll
+    for (int k = 0; k < KV; ++k) r[k] = k < cnt ? r[k] : 0.f;
     double ls = 0.0;
 #pragma unroll
     for (int k = 0; k < KV; ++k) ls += (double)r[k];
@@ -356,6 +519,41 @@ __device__ int law_draw(const Law& L, const void* prow, const void* qrow, int V,
   if (*s_th == -1.0) *rounding = true;
   __syncthreads();
   return token;
+}
+
+// The walk's per-child scalar math (fp64 exponentials, Philox).  Every lane
+// computes the same value.
+struct Odds {
+  double px;     // p(x)
+  double ratio;  // acceptance ratio of x under the current law
+};
+
+// mode 0: one-hot drafts (ratio p(x) / Zk, 0 for a removed token); 1: draft
+// logits; 2: draft probabilities.
+__device__ __forceinline__ Odds child_odds(float lp, float lq, float c, float pref, double pz,
+                                        float qref, double qz, double ck, double Zk, int mode,
+                                        bool removed) {
+  Odds o;
+  o.px = exp2((double)lp * (double)c + (double)pref) / pz;
+  if (mode == 0) {
+    o.ratio = removed ? 0.0 : o.px / Zk;
+  } else {
+    const double qx = mode == 2 ? (double)lq : exp2((double)lq * (double)c + (double)qref) / qz;
+    double num = o.px - ck * qx;
+    num = num > 0.0 ? num / Zk : 0.0;
+    o.ratio = qx > 0.0 ? num / qx : (num > 0.0 ? __builtin_inf() : 0.0);
+  }
+  return o;
+}
+
+struct Uniforms {
+  double acc, rec;
+};
+
+__device__ __forceinline__ Uniforms tree_uniforms(uint64_t seed, uint64_t offset, int b, int i) {
+  Uniforms u;
+  uniforms(seed, offset, b, i, &u.acc, &u.rec);
+  return u;
 }
 
 template <int TDT, int DDT, bool HAS_DRAFT>
@@ -411,20 +609,15 @@ __global__ __launch_bounds__(kTreeThreads) void k_tree(const TreeParams p) {
       } else {
         double ratio = 0.0, px = 0.0;
         if (valid) {
-          px = exp2((double)Elt<TDT>::at(prow, x) * (double)c + (double)ps.ref) / ps.z;
-          if (!HAS_DRAFT) {
-            ratio = excluded(s_ex, nex, x) ? 0.0 : px / Zk;
-          } else {
-            const double lq = (double)Elt<DDT>::at(qrow, x);
-            const double qx = probs ? lq : exp2(lq * (double)c + (double)qs.ref) / qs.z;
-            double num = px - ck * qx;
-            num = num > 0.0 ? num / Zk : 0.0;
-            ratio = qx > 0.0 ? num / qx : (num > 0.0 ? __builtin_inf() : 0.0);
-          }
+          const float lq = HAS_DRAFT ? Elt<DDT>::at(qrow, x) : 0.f;
+          const Odds o = child_odds(Elt<TDT>::at(prow, x), lq, c, ps.ref, ps.z, qs.ref, qs.z, ck,
+                                    Zk, !HAS_DRAFT ? 0 : (probs ? 2 : 1),
+                                    !HAS_DRAFT && excluded(s_ex, nex, x));
+          px = o.px;
+          ratio = o.ratio;
         }
-        double u_acc, u_rec;
-        uniforms(p.seed, p.offset, b, ch - 1, &u_acc, &u_rec);
-        accept = u_acc < ratio;
+        const Uniforms un = tree_uniforms(p.seed, p.offset, b, ch - 1);
+        accept = un.acc < ratio;
         // one-hot: a rejected token leaves the law, which is renormalized
         if (!accept && !HAS_DRAFT && valid && !excluded(s_ex, nex, x)) Zk -= px;
       }
@@ -463,8 +656,7 @@ __global__ __launch_bounds__(kTreeThreads) void k_tree(const TreeParams p) {
     if (!sampling) {
       y = ps.arg;
     } else {
-      double u_acc, u_rec;
-      uniforms(p.seed, p.offset, b, v, &u_acc, &u_rec);
+      const double u_rec = tree_uniforms(p.seed, p.offset, b, v).rec;
       Law L{false, c, ps.ref, qs.ref, 0.f, 0.f, probs};
       if (HAS_DRAFT && nrej > 0) {
         L.pair = true;
@@ -472,14 +664,16 @@ __global__ __launch_bounds__(kTreeThreads) void k_tree(const TreeParams p) {
         L.kap_hi = (float)kap;
         L.kap_lo = (float)(kap - (double)L.kap_hi);
       }
+      slot_pass<TDT, DDT>(L, prow, qrow, V, s_slot);
       bool rounding = false, empty = false;
-      y = law_draw<TDT, DDT>(L, prow, qrow, V, s_ex, nex, u_rec, s_slot, s_woff, &s_sel, &s_th,
-                             &rounding, &empty);
-      if (empty) {  // no residual mass: draw from p itself
+      y = draw_from_slots<TDT, DDT>(L, prow, qrow, V, s_ex, nex, u_rec, s_slot, s_woff, &s_sel,
+                                    &s_th, &rounding, &empty);
+      if (empty) {  // no mass left: draw from p itself
         fl |= SV_DEVERR_ZERO_RESIDUAL;
         L.pair = false;
-        y = law_draw<TDT, DDT>(L, prow, qrow, V, s_ex, 0, u_rec, s_slot, s_woff, &s_sel, &s_th,
-                               &rounding, &empty);
+        slot_pass<TDT, DDT>(L, prow, qrow, V, s_slot);
+        y = draw_from_slots<TDT, DDT>(L, prow, qrow, V, s_ex, 0, u_rec, s_slot, s_woff, &s_sel,
+                                      &s_th, &rounding, &empty);
       }
       if (rounding) fl |= SV_DEVERR_DRAW_ROUNDING;
     }
