@@ -1,7 +1,8 @@
 // Device helpers shared by the HIP sources of the library: the temperature
 // scale and exponent references, Philox4x64-10 and the uniform layouts, the
 // element formats (bf16 as the top half of a float), chunk geometry,
-// per-thread accumulators and the wavefront / workgroup reductions.  Each
+// buffer-resource loads, per-thread accumulators and the wavefront /
+// workgroup reductions.  Each
 // source that includes it gets its own internal copies.
 #pragma once
 
@@ -157,6 +158,32 @@ __device__ __forceinline__ Geo chunk_geo(const void* row, int c0, int c1) {
   g.nvec = (c1 - g.v0) / Elt<DT>::kVec;
   g.t0 = g.v0 + g.nvec * Elt<DT>::kVec;
   return g;
+}
+
+// A run of 16-byte vectors as a buffer resource: base address and size in
+// bytes.  The hardware checks each load's offset register against the size
+// and returns 0 past it without touching memory, so a round of loads needs
+// no branches, and one offset register per load replaces a 64-bit address.
+// (The scalar offset operand is not checked: offsets go in the register.)
+// The base is the same for the whole workgroup; readfirstlane states it.
+struct VecBuf {
+  __amdgpu_buffer_rsrc_t r;
+};
+
+__device__ __forceinline__ VecBuf make_vec_buf(const void* base16, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base16);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  // word 3: 32-bit data format, as the gfx9 family takes for raw loads
+  return VecBuf{__builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000)};
+}
+
+// The vector at byte offset off, or 0 past the end; NT marks it nontemporal
+// (read once: streamed past the caches).
+template <bool NT>
+__device__ __forceinline__ u32x4 buf_load(const VecBuf& b, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(b.r, off, 0u, NT ? 2 : 0);
 }
 
 // ---------------------------------------------------------------------------

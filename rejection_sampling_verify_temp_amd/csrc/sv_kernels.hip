@@ -43,6 +43,7 @@ namespace {
 #endif
 constexpr int kUnroll = SV_LOADS_IN_FLIGHT;  // 16-byte loads in flight per thread
 
+
 // Streaming 16-byte load; rows are read once per step.
 __device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
 #if SV_STREAM_NT
@@ -57,8 +58,10 @@ __device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
 // together); the workgroup takes the max of the pass first, moves the shared
 // exponent reference R = ref_of(M, c) if the max grew, and only then sums
 // exp2(l * c + R).  With one reference for the workgroup the thread sums add
-// without rescaling, and no element needs a running-max test.  Vectors past
-// the chunk's end are neither loaded nor folded (the test is uniform in all
+// without rescaling, and no element needs a running-max test.  The loads go
+// through a buffer resource over the chunk's vectors: a round issues all of
+// them with no branch, and past the chunk the hardware returns 0 without
+// touching memory; those vectors are not folded (the test is uniform in all
 // but one wave of a pass).
 // COUNT: also count the chunk's elements above lx (into *above).
 template <int DT, bool COUNT>
@@ -71,6 +74,7 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
   const int tid = threadIdx.x;
   const u32x4* vp = reinterpret_cast<const u32x4*>(
       static_cast<const char*>(row) + (size_t)g.v0 * E::kBytes);
+  const VecBuf vb = make_vec_buf(vp, (uint32_t)g.nvec * 16u);
   float M = kNegInf, R = 0.f, S = 0.f;
   int cnt = 0;
   for (int base = 0; base == 0 || base < g.nvec; base += kThreads * kUnroll) {
@@ -78,7 +82,7 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
     u32x4 d[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (v + u * kThreads < g.nvec) d[u] = stream_load(vp + v + u * kThreads);
+      d[u] = buf_load<SV_STREAM_NT != 0>(vb, (uint32_t)(v + u * kThreads) * 16u);
     // head and tail (each under one vector) ride along with the first pass
     float ht[2] = {kNegInf, kNegInf};
     if (base == 0 && g.c0 + tid < g.v0) ht[0] = E::at(row, g.c0 + tid);
@@ -544,15 +548,6 @@ struct Raw8 {
   u32x4 w[DT == SV_BF16 ? 1 : 2];
 };
 
-template <int DT>
-__device__ __forceinline__ Raw8<DT> load8(const void* row, int i) {
-  const u32x4* v = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
-                                                  (size_t)i * Elt<DT>::kBytes);
-  Raw8<DT> r;
-  r.w[0] = stream_load(v);
-  if (DT == SV_F32) r.w[DT == SV_BF16 ? 0 : 1] = stream_load(v + 1);
-  return r;
-}
 
 template <int DT>
 __device__ __forceinline__ void unpack8(const Raw8<DT>& r, float* x) {
@@ -594,29 +589,32 @@ __device__ __forceinline__ double pair_chunk_sum(const void* prow, const void* q
   int done = c0;
   if (((pa | qa) & 15u) == 0) {
     const int ngrp = (c1 - c0) / 8;
+    // buffer loads: every load of a round is issued unconditionally (past the
+    // groups the hardware returns 0) with one offset register each
+    constexpr int kPB = 8 * Elt<TDT>::kBytes, kQB = 8 * Elt<DDT>::kBytes;  // bytes per group
+    const VecBuf pb = make_vec_buf(reinterpret_cast<const void*>(pa), (uint32_t)ngrp * kPB);
+    const VecBuf qb = make_vec_buf(reinterpret_cast<const void*>(qa), (uint32_t)ngrp * kQB);
     for (int g = tid; g < ngrp; g += kThreads * kResidGroups) {
       Raw8<TDT> rp[kResidGroups];
       Raw8<DDT> rq[kResidGroups];
 #pragma unroll
       for (int u = 0; u < kResidGroups; ++u) {
         const int gi = g + u * kThreads;
-        if (gi < ngrp) {
-          rp[u] = load8<TDT>(prow, c0 + gi * 8);
-          rq[u] = load8<DDT>(qrow, c0 + gi * 8);
-        }
+#pragma unroll
+        for (int h = 0; h < kPB / 16; ++h) rp[u].w[h] = buf_load<true>(pb, (uint32_t)gi * kPB + 16 * h);
+#pragma unroll
+        for (int h = 0; h < kQB / 16; ++h) rq[u].w[h] = buf_load<true>(qb, (uint32_t)gi * kQB + 16 * h);
       }
       float s[kResidGroups];
 #pragma unroll
       for (int u = 0; u < kResidGroups; ++u) {
-        s[u] = 0.f;
-        if (g + u * kThreads < ngrp) {
-          float lp[8], lq[8], e[8];
-          unpack8<TDT>(rp[u], lp);
-          unpack8<DDT>(rq[u], lq);
+        float lp[8], lq[8], e[8];
+        unpack8<TDT>(rp[u], lp);
+        unpack8<DDT>(rq[u], lq);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) e[k] = pair_resid(lp[k], lq[k], d, probs);
-          s[u] = pairwise_sum(e);
-        }
+        for (int k = 0; k < 8; ++k) e[k] = pair_resid(lp[k], lq[k], d, probs);
+        const float sg = pairwise_sum(e);
+        s[u] = g + u * kThreads < ngrp ? sg : 0.f;
       }
       acc += (double)pairwise_sum(s);
     }

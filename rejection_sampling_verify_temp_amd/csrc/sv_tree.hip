@@ -59,29 +59,14 @@ __device__ __forceinline__ const u32x4* vec_base(const void* row, const Geo& g, 
   return reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + (size_t)g.v0 * bytes);
 }
 
-// The vectors of a row as a buffer resource: base and size in bytes.  The
-// hardware checks each load's offset register against the size and returns 0
-// past it without touching memory, so a round issues all its loads with no
-// branch, and the vectors past the row are then padded in registers.  The
-// row pointer is the same for the whole workgroup: readfirstlane states it.
-struct VecBuf {
-  __amdgpu_buffer_rsrc_t r;
-};
-
+// The vectors of a row as a buffer resource (loads past the row return 0).
 __device__ __forceinline__ VecBuf vec_buf(const void* row, const Geo& g, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(vec_base(row, g, bytes));
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  // word 3: 32-bit data format, as the gfx9 family takes for raw loads
-  return VecBuf{__builtin_amdgcn_make_buffer_rsrc(base, 0, g.nvec * 16, 0x00020000)};
+  return make_vec_buf(vec_base(row, g, bytes), (uint32_t)g.nvec * 16u);
 }
 
-// Vector b0 + tid + u * kRound of the row, or 0 past its end.  The whole
-// offset is in the checked register (the scalar offset is not checked).
+// Vector b0 + tid + u * kRound of the row, or 0 past its end.
 __device__ __forceinline__ u32x4 vec_load(const VecBuf& vb, int b0, int u, int tid) {
-  return __builtin_amdgcn_raw_buffer_load_b128(vb.r, (uint32_t)(b0 + u * kRound + tid) * 16u,
-                                               0u, 0);
+  return buf_load<false>(vb, (uint32_t)(b0 + u * kRound + tid) * 16u);
 }
 
 // The thread index, hidden from loop-invariant code motion: each pass
