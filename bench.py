@@ -102,6 +102,73 @@ def cpu_baseline(w, seconds=12.0):
                        f"elems, {t:.1f} s of the single-threaded fp64 C oracle")
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads():
+    """Worker threads for the all-cores leg: the CPUs this process may run on,
+    at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline_threads(w, seconds=6.0):
+    """The same oracle on all the host cores this process may use: each
+    worker thread runs slices of 8 requests (the C oracle releases the
+    interpreter lock), cycling through the batch with a new Philox offset per
+    pass, until about `seconds` of wall time; requests are independent, so
+    this is the oracle as it stands, only run side by side."""
+    import threading
+    import oracle
+    hs = w.host_arrays()
+    V, B, K = w.V, w.B, w.K
+    nthreads = cpu_threads()
+    lock = threading.Lock()
+    state = {"next": 0, "elems": 0, "req": 0}
+    stop = time.perf_counter() + seconds
+
+    def worker():
+        while time.perf_counter() < stop:
+            with lock:
+                k = state["next"]
+                state["next"] += 1
+            start = (k * 8) % B
+            sl = slice(start, min(B, start + 8))
+            sub = {kk: (v[sl] if hasattr(v, "shape") and v.shape[:1] == (B,) else v)
+                   for kk, v in hs.items()}
+            oracle.verify(sub["target"], sub["draft"], sub["draft_ids"], sub["num_drafts"],
+                          sub["temperatures"], draft_mode=sub["draft_mode"],
+                          draft_is_probs=sub["draft_is_probs"], seed=0,
+                          offset=(k * 8) // B, diagnostics=False)
+            n = sub["num_drafts"].clip(0, K)
+            with lock:
+                state["elems"] += int((n + 1).sum()) * V
+                state["req"] += sl.stop - sl.start
+
+    t0 = time.perf_counter()
+    threads = [threading.Thread(target=worker) for _ in range(nthreads)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    dt = time.perf_counter() - t0
+    return dict(value=state["elems"] / dt, unit="elems/s", cores=nthreads, kind="oracle",
+                cpu=cpu_model(),
+                sample=f"{state['req']} requests of the same batch on {nthreads} threads "
+                       f"(slices of 8, a new Philox offset per pass over the batch), "
+                       f"{state['elems']} verified elems, {dt:.1f} s wall time")
+
+
 def cpu_baseline_typical(w, eps, top_k, seconds=12.0):
     """The CPU oracle's typical acceptance, as it stands, on slices of 8
     requests of the same batch until about `seconds` of single-threaded work."""
@@ -475,6 +542,9 @@ def main():
         out["cpu_baseline"] = (cpu_baseline_sample(w, nd_sample) if sample else
                                cpu_baseline_typical(w, args.threshold, args.top_k) if typical
                                else cpu_baseline(w))
+        out["cpu_baseline"]["cpu"] = cpu_model()
+        if not sample and not typical:
+            out["cpu_baseline_threads"] = cpu_baseline_threads(w)
     h.close()
     print(json.dumps(out), flush=True)
 
