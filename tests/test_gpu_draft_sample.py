@@ -193,3 +193,15 @@ def test_empty_and_unsupported(svlib):
     hp = svlib.SpecVerify(4, 2, 100, torch.float32, draft_is_probs=True)
     assert svlib.spec_draft_sample(hp.handle, 4, 2, 1, 0, 1, 0, 0, 1, 0, None) == -2
     hp.close()
+
+
+def test_max_vocab_and_drafts(svlib):
+    """The largest sizes a handle takes: V = 983040 (64 chunks) and K = 31."""
+    l = _rows(3, 2, 983040, torch.bfloat16, 11)
+    temps = torch.tensor([1.0, 0.0, 0.7])
+    nd = torch.tensor([2, 2, 1], dtype=torch.int32)
+    check(svlib, "max vocab", l, nd, temps, seed=1, offset=5)
+    l = _rows(6, 31, 2000, torch.float32, 12)
+    temps = torch.tensor([1.0, 0.0, 0.7, 1.5, 0.3, 1.0])
+    nd = torch.tensor([31, 30, 0, 17, 31, 1], dtype=torch.int32)
+    check(svlib, "max drafts", l, nd, temps, seed=2, offset=6)

@@ -199,3 +199,23 @@ def test_empty_batch_is_noop(svlib):
               torch.zeros(5, dtype=torch.int32, device="cuda"),
               torch.ones(5, device="cuda"))
     h.close()
+
+
+# ---------------------------------------------------------------------------
+# The largest sizes a handle takes
+# ---------------------------------------------------------------------------
+def test_max_vocab(svlib):
+    """V = 983040: 64 chunks of 15360, one decide lane per chunk.  bf16 and
+    fp32 rows; sampling, greedy and one-hot requests, ragged counts."""
+    for dtype, seed in ((torch.bfloat16, 0), (torch.float32, 1)):
+        w = synth.make_random(6, 2, 983040, dtype=dtype, temps=(1.0, 0.0, 0.7),
+                              n_mode="ragged", onehot_frac=0.3, seed=seed, device="cuda")
+        check(svlib, w, seed=seed, offset=4)
+
+
+def test_max_drafts(svlib):
+    """K = 31: 2K + 1 = 63 row slots, one wavefront lane each in the decision."""
+    w = synth.make_random(16, 31, 3000, dtype=torch.bfloat16, temps=(1.0, 0.0, 0.8),
+                          n_mode="ragged", onehot_frac=0.25, corr=0.97, seed=5, device="cuda")
+    rep = check(svlib, w, seed=2, offset=7)
+    assert rep.accepted > 0

@@ -111,3 +111,10 @@ def test_chunk_sizes(svlib):
                           n_mode="ragged", seed=9)
     for chunk in (256, 1024, 15360):
         check(svlib, w, 0.002, 3, chunk=chunk)
+
+
+def test_max_vocab(svlib):
+    """V = 983040 (64 chunks): rank counts summed over every chunk."""
+    w = synth.make_random(6, 3, 983040, dtype=torch.bfloat16, temps=(1.0, 0.0, 0.6),
+                          n_mode="ragged", corr=0.97, seed=3, device="cuda")
+    check(svlib, w, 1e-6, 3, seed=2, offset=1)
