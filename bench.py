@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -43,11 +44,21 @@ KERNEL_SRC = [os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", f
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_traffic_B256_K7_V152064_bf16.txt")
 
 
+def _code_only(text):
+    """The source with comments removed and whitespace collapsed, so that an
+    edit to a comment keeps a measurement that the compiled kernel still
+    matches.  (Comment markers inside string literals do not occur in these
+    sources.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for path in KERNEL_SRC:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -35,6 +35,9 @@ namespace {
 // ---------------------------------------------------------------------------
 // Chunk streaming
 // ---------------------------------------------------------------------------
+// Build-time tuning knobs (-D on the compiler line).  The defaults are the
+// fastest measured on MI355X for the bf16 verify step: 8 loads in flight per
+// thread (12 was 6% slower) and nontemporal loads (temporal ones 14% slower).
 #ifndef SV_LOADS_IN_FLIGHT
 #define SV_LOADS_IN_FLIGHT 8
 #endif
@@ -42,7 +45,6 @@ namespace {
 #define SV_STREAM_NT 1
 #endif
 constexpr int kUnroll = SV_LOADS_IN_FLIGHT;  // 16-byte loads in flight per thread
-
 
 // Streaming 16-byte load; rows are read once per step.
 __device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
@@ -504,6 +506,8 @@ __device__ __forceinline__ void stats_item(const RunParams& p, int b, int s, int
     p.part[((size_t)b * (2 * p.K + 1) + s) * p.nchunk + chunk] = out;
 }
 
+// Tuning knob: a minimum-waves-per-SIMD hint for the stats kernel (1 = none;
+// 8, which caps it at 64 registers, measured no faster).
 #ifndef SV_STATS_WAVES_PER_EU
 #define SV_STATS_WAVES_PER_EU 1
 #endif
@@ -1055,10 +1059,10 @@ __global__ __launch_bounds__(NT) void k_sample(const RunParams p) {
   locate<DT, DT, false, NT>(p, b, s_d);
 }
 
+// Tuning knob: batches of at most this many draws use 1024-thread draws.
 #ifndef SV_LOC_WIDE_MAX_DRAWS
 #define SV_LOC_WIDE_MAX_DRAWS 384
 #endif
-// Batches of at most this many draws use 1024-thread draws.
 constexpr int kLocWideMaxDraws = SV_LOC_WIDE_MAX_DRAWS;
 
 template <int TDT, int DDT, bool PAIR>
