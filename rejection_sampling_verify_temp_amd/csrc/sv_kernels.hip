@@ -508,6 +508,15 @@ __device__ __forceinline__ void stats_item(const RunParams& p, int b, int s, int
 
 // Tuning knob: a minimum-waves-per-SIMD hint for the stats kernel (1 = none;
 // 8, which caps it at 64 registers, measured no faster).
+// Row slots in the stats grid per request: target rows 0..K, and draft rows
+// only when some request may need a draft softmax.  Typical acceptance, runs
+// without draft rows and probability drafts never do; the host knows that
+// without reading device data, and the grid then has no draft slots to skip
+// (an empty workgroup still costs its launch: 4 us at B=512 K=3).
+__host__ __device__ __forceinline__ int stats_slots(const RunParams& p) {
+  return (p.typical || !p.has_draft || p.draft_is_probs) ? p.K + 1 : 2 * p.K + 1;
+}
+
 #ifndef SV_STATS_WAVES_PER_EU
 #define SV_STATS_WAVES_PER_EU 1
 #endif
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(kThreads, SV_STATS_WAVES_PER_EU) void k_stats(const
   __shared__ float ldsf[kThreads / 64];
   __shared__ double ldsd[kThreads / 64];
   __shared__ int ldsi[kThreads / 64];
-  const int nslot = 2 * p.K + 1;
+  const int nslot = stats_slots(p);
   const int bid = blockIdx.x;
   const int row = bid / p.nchunk, chunk = bid - row * p.nchunk;
   const int b = row / nslot, s = row - b * nslot;
@@ -1077,7 +1086,7 @@ template <int TDT, int DDT>
 void launch_one(int k, const RunParams& p, hipStream_t s) {
   switch (k) {
     case kKernelStats: {
-      const uint64_t g = (uint64_t)p.B * (2 * p.K + 1) * p.nchunk;
+      const uint64_t g = (uint64_t)p.B * stats_slots(p) * p.nchunk;
       hipLaunchKernelGGL((k_stats<TDT, DDT>), dim3((unsigned)g), dim3(kThreads), 0, s, p);
       break;
     }
