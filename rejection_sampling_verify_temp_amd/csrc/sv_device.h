@@ -226,28 +226,101 @@ __device__ __forceinline__ void am_tile(AmAcc& a, const float (&x)[N],
 // Wavefront / workgroup reductions (fixed butterfly order: every lane ends
 // with the same bits, results are reproducible run to run)
 // ---------------------------------------------------------------------------
+// Wavefront max and sum by DPP lane moves, which stay in the register file
+// (a few cycles each) where a shuffle goes through the LDS crossbar: row_shr
+// 1, 2, 4 and 8 leave each 16-lane row's total in its lane 15; row_bcast:15
+// adds row 0's into row 1 and row 2's into row 3; row_bcast:31 adds lane
+// 31's into rows 2 and 3; lane 63 then holds the total, read back for every
+// lane.  A lane whose source is out of range keeps a neutral value.  The
+// whole wavefront must be active.
+template <int CTRL, int ROWS, int BANKS = 0xf>
+__device__ __forceinline__ int dpp_move(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, BANKS, false);
+}
+
+// A double moved by DPP, 0 where the lane is masked or its source is out of
+// range.
+template <int CTRL, int ROWS, int BANKS = 0xf>
+__device__ __forceinline__ double dpp_move_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)dpp_move<CTRL, ROWS, BANKS>(0, (int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)dpp_move<CTRL, ROWS, BANKS>(0, (int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const int b = __float_as_int(v);
+  return fmaxf(v, __int_as_float(dpp_move<CTRL, ROWS>(b, b)));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_sum_step(double v) {
+  return v + dpp_move_f64<CTRL, ROWS>(v);
+}
+
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr3 = 0x113, kDppShr4 = 0x114,
+              kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  v = dpp_max_step<kDppShr1, 0xf>(v);
+  v = dpp_max_step<kDppShr2, 0xf>(v);
+  v = dpp_max_step<kDppShr4, 0xf>(v);
+  v = dpp_max_step<kDppShr8, 0xf>(v);
+  v = dpp_max_step<kDppBcast15, 0xa>(v);
+  v = dpp_max_step<kDppBcast31, 0xc>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v = dpp_sum_step<kDppShr1, 0xf>(v);
+  v = dpp_sum_step<kDppShr2, 0xf>(v);
+  v = dpp_sum_step<kDppShr4, 0xf>(v);
+  v = dpp_sum_step<kDppShr8, 0xf>(v);
+  v = dpp_sum_step<kDppBcast15, 0xa>(v);
+  v = dpp_sum_step<kDppBcast31, 0xc>(v);
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-__device__ __forceinline__ void wave_argmax(float& m, int& i) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float om = __shfl_xor(m, off, 64);
-    const int oi = __shfl_xor(i, off, 64);
-    if (om > m || (om == m && oi < i)) {
-      m = om;
-      i = oi;
-    }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void dpp_argmax_step(float& m, int& i) {
+  const float om = __int_as_float(dpp_move<CTRL, ROWS>(__float_as_int(m), __float_as_int(m)));
+  const int oi = dpp_move<CTRL, ROWS>(i, i);
+  if (om > m || (om == m && oi < i)) {
+    m = om;
+    i = oi;
   }
+}
+
+// The max and the lowest index attaining it, for every lane (DPP as above).
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+  dpp_argmax_step<kDppShr1, 0xf>(m, i);
+  dpp_argmax_step<kDppShr2, 0xf>(m, i);
+  dpp_argmax_step<kDppShr4, 0xf>(m, i);
+  dpp_argmax_step<kDppShr8, 0xf>(m, i);
+  dpp_argmax_step<kDppBcast15, 0xa>(m, i);
+  dpp_argmax_step<kDppBcast31, 0xc>(m, i);
+  m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_isum_step(int v) {
+  return v + dpp_move<CTRL, ROWS>(0, v);
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+  v = dpp_isum_step<kDppShr1, 0xf>(v);
+  v = dpp_isum_step<kDppShr2, 0xf>(v);
+  v = dpp_isum_step<kDppShr4, 0xf>(v);
+  v = dpp_isum_step<kDppShr8, 0xf>(v);
+  v = dpp_isum_step<kDppBcast15, 0xa>(v);
+  v = dpp_isum_step<kDppBcast31, 0xc>(v);
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 template <int NT>
@@ -278,8 +351,7 @@ __device__ double block_sum(double v, double* lds) {
 
 template <int NT>
 __device__ int block_sum_int(int v, int* lds) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  v = wave_sum_int(v);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (lane == 0) lds[w] = v;
   __syncthreads();
@@ -311,12 +383,39 @@ __device__ void block_argmax(float& m, int& i, float* ldsm, int* ldsi) {
 }
 
 
+// Value of lane src, for a src the same in every lane (a register read
+// instead of a shuffle through the LDS crossbar).
+__device__ __forceinline__ int lane_i32(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ float lane_f32(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+__device__ __forceinline__ double lane_f64(double v, int src) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// The previous lane's value (0 in lane 0): DPP wave_shr:1.
+constexpr int kDppWaveShr1 = 0x138;
+__device__ __forceinline__ double lane_before(double v) {
+  return dpp_move_f64<kDppWaveShr1, 0xf>(v);
+}
+
+// Inclusive prefix sum over the wavefront by DPP: the lane's own value plus
+// the three before it in its row, then row_shr 4 into banks 1-3 and row_shr 8
+// into banks 2-3 complete each row's scan; row_bcast:15 and row_bcast:31
+// carry the row totals forward.  The whole wavefront must be active.
 __device__ __forceinline__ double wave_incl_scan(double v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+  (void)lane;
+  const double x = v;
+  v += dpp_move_f64<kDppShr1, 0xf>(x);
+  v += dpp_move_f64<kDppShr2, 0xf>(x);
+  v += dpp_move_f64<kDppShr3, 0xf>(x);
+  v += dpp_move_f64<kDppShr4, 0xf, 0xe>(v);
+  v += dpp_move_f64<kDppShr8, 0xf, 0xc>(v);
+  v += dpp_move_f64<kDppBcast15, 0xa>(v);
+  v += dpp_move_f64<kDppBcast31, 0xc>(v);
   return v;
 }
 

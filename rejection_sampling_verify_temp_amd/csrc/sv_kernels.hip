@@ -55,6 +55,20 @@ __device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
 #endif
 }
 
+// Raw bits of element i of a row, and their value.
+template <int DT>
+__device__ __forceinline__ uint32_t raw_elem(const void* row, int i) {
+  if constexpr (DT == SV_BF16)
+    return static_cast<const uint16_t*>(row)[i];
+  else
+    return static_cast<const uint32_t*>(row)[i];
+}
+
+template <int DT>
+__device__ __forceinline__ float raw_to_float(uint32_t w) {
+  return __uint_as_float(DT == SV_BF16 ? w << 16 : w);
+}
+
 // Softmax statistics of one chunk, by the whole workgroup.  A pass holds
 // kUnroll 16-byte vectors per thread in registers (all loads in flight
 // together); the workgroup takes the max of the pass first, moves the shared
@@ -81,14 +95,26 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
   int cnt = 0;
   for (int base = 0; base == 0 || base < g.nvec; base += kThreads * kUnroll) {
     const int v = base + tid;
+    // head and tail (each under one vector) ride along with the first pass.
+    // Their loads go first and every lane makes them, at an index clamped
+    // into the chunk: loads complete in issue order for the wait counter, so
+    // waiting for them then does not wait for the vectors (each vector is
+    // folded as it arrives), and no branch makes the compiler wait at its end.
+    uint32_t h = 0, tl = 0;  // raw element bits
+    if (base == 0) {  // uniform
+      h = raw_elem<DT>(row, min(g.c0 + tid, g.c1 - 1));
+      tl = raw_elem<DT>(row, min(g.t0 + tid, g.c1 - 1));
+    }
     u32x4 d[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
       d[u] = buf_load<SV_STREAM_NT != 0>(vb, (uint32_t)(v + u * kThreads) * 16u);
-    // head and tail (each under one vector) ride along with the first pass
-    float ht[2] = {kNegInf, kNegInf};
-    if (base == 0 && g.c0 + tid < g.v0) ht[0] = E::at(row, g.c0 + tid);
-    if (base == 0 && g.t0 + tid < g.c1) ht[1] = E::at(row, g.t0 + tid);
+    // the head and tail bits are first used past this point, after every
+    // load of the pass is issued (the clobber keeps the loads above it)
+    asm volatile("" : "+v"(h), "+v"(tl) : : "memory");
+    float ht[2];
+    ht[0] = base == 0 && g.c0 + tid < g.v0 ? raw_to_float<DT>(h) : kNegInf;
+    ht[1] = base == 0 && g.t0 + tid < g.c1 ? raw_to_float<DT>(tl) : kNegInf;
     float t = fmaxf(ht[0], ht[1]);
     if (COUNT) cnt += (ht[0] > lx) + (ht[1] > lx);
 #pragma unroll
@@ -413,12 +439,12 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
   // a single-row draw (from p, less an excluded one-hot draft) is placed in
   // its chunk here, one lane per chunk: chunk masses are the row's partials
   // rescaled to ref_p, the values the fold above summed
-  if (__shfl(d.kind, n_acc, 64) == kDrawSingle) {
+  if (lane_i32(d.kind, n_acc) == kDrawSingle) {
     const int je = n_acc;
-    const float dc = __shfl(d.c, je, 64), dref = __shfl(d.ref_p, je, 64);
-    const double du = __shfl(d.u, je, 64);
-    int excl = __shfl(d.x, je, 64);
-    const float lx = __shfl(lt, je, 64);
+    const float dc = lane_f32(d.c, je), dref = lane_f32(d.ref_p, je);
+    const double du = lane_f64(d.u, je);
+    int excl = lane_i32(d.x, je);
+    const float lx = lane_f32(lt, je);
     double mass = 0.0, px = 0.0;
     if (lane < p.nchunk) {
       const Partial q = p.part[((size_t)b * nslot + je) * p.nchunk + lane];
@@ -428,23 +454,23 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
     double mx = mass - px;
     if (!(mx > 0.0)) mx = 0.0;
     double incl = wave_incl_scan(mx, lane);
-    double S = __shfl(incl, 63, 64);
+    double S = lane_f64(incl, 63);
     if (!(S > 0.0) && excl >= 0) {  // no residual mass: draw from p itself
       if (outputs && lane == 0) atomicOr(p.flags, SV_DEVERR_ZERO_RESIDUAL);
       excl = -1;
       mx = mass > 0.0 ? mass : 0.0;
       incl = wave_incl_scan(mx, lane);
-      S = __shfl(incl, 63, 64);
+      S = lane_f64(incl, 63);
     }
     const double theta = du * S;
-    double before = __shfl_up(incl, 1, 64);
+    double before = lane_before(incl);
     if (lane == 0) before = 0.0;
     const uint64_t hits = __ballot(mx > 0.0 && before <= theta && theta < incl);
     int cstar;
     double th;
     if (hits) {
       cstar = (int)__builtin_ctzll(hits);
-      th = theta - __shfl(before, cstar, 64);
+      th = theta - lane_f64(before, cstar);
     } else {  // rounding left theta at or past the total: last chunk with mass
       const uint64_t has = __ballot(mx > 0.0);
       cstar = has ? 63 - (int)__builtin_clzll(has) : 0;
@@ -843,7 +869,7 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
         if (!(mass > 0.0)) mass = 0.0;
       }
       const double incl = wave_incl_scan(mass, lane);
-      const double S = __shfl(incl, 63, 64);
+      const double S = lane_f64(incl, 63);
       if (!(S > 0.0) && attempt == 0) {  // no residual mass: draw from p
         if (lane == 0) atomicOr(p.flags, SV_DEVERR_ZERO_RESIDUAL);
         kind = kDrawSingle;
@@ -851,7 +877,7 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
         continue;
       }
       const double theta = d.u * S;
-      double before = __shfl_up(incl, 1, 64);
+      double before = lane_before(incl);
       if (lane == 0) before = 0.0;
       const bool hit = mass > 0.0 && before <= theta && theta < incl;
       const uint64_t hits = __ballot(hit);
@@ -860,7 +886,7 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
       if (hits) {
         const int src = (int)__builtin_ctzll(hits);
         cstar = src;
-        th = theta - __shfl(before, src, 64);
+        th = theta - lane_f64(before, src);
       } else {  // rounding left theta at or past the total: last chunk with mass
         const uint64_t has = __ballot(mass > 0.0);
         cstar = has ? 63 - (int)__builtin_clzll(has) : 0;
@@ -909,7 +935,7 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
   // (c) exclusive scan of the segment sums
   const double incl = wave_incl_scan(seg, lane);
   if (lane == 63) s_woff[w] = incl;
-  double q = __shfl_up(incl, 1, 64);
+  double q = lane_before(incl);
   if (lane == 0) q = 0.0;
   if (seg > 0.0) atomicMax(&s_lastseg, tid);
   __syncthreads();
@@ -1031,17 +1057,17 @@ __global__ __launch_bounds__(NT) void k_sample(const RunParams p) {
       double mass = 0.0;
       if (lane < p.nchunk && q.z != 0.0) mass = q.z * exp2((double)ref - (double)ref_of(q.m, c));
       const double incl = wave_incl_scan(mass, lane);
-      const double S = __shfl(incl, 63, 64);
+      const double S = lane_f64(incl, 63);
       const double u = draft_uniform(p.seed, p.offset, p.b_base + ri.rb, ri.rj);
       const double theta = u * S;
-      double before = __shfl_up(incl, 1, 64);
+      double before = lane_before(incl);
       if (lane == 0) before = 0.0;
       const uint64_t hits = __ballot(mass > 0.0 && before <= theta && theta < incl);
       int cstar;
       double th;
       if (hits) {
         cstar = (int)__builtin_ctzll(hits);
-        th = theta - __shfl(before, cstar, 64);
+        th = theta - lane_f64(before, cstar);
       } else {  // rounding left theta at or past the total: last chunk with mass
         const uint64_t has = __ballot(mass > 0.0);
         cstar = has ? 63 - (int)__builtin_clzll(has) : 0;

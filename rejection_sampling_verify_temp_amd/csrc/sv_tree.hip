@@ -406,7 +406,7 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
   }
   const double incl = wave_incl_scan(loc, lane);
   if (lane == 63) s_woff[w] = incl;
-  double q = __shfl_up(incl, 1, 64);
+  double q = lane_before(incl);
   if (lane == 0) q = 0.0;
   __syncthreads();
   double total = 0.0;
@@ -478,7 +478,7 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
 #pragma unroll
     for (int k = 0; k < KV; ++k) ls += (double)r[k];
     const double li = wave_incl_scan(ls, lane);
-    double before = __shfl_up(li, 1, 64);
+    double before = lane_before(li);
     if (lane == 0) before = 0.0;
     const uint64_t hit = __ballot(ls > 0.0 && before <= th && th < li);
     const uint64_t has = __ballot(ls > 0.0);
