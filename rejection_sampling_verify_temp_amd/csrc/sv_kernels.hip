@@ -1099,11 +1099,20 @@ __global__ __launch_bounds__(NT) void k_sample(const RunParams p) {
 #define SV_LOC_WIDE_MAX_DRAWS 384
 #endif
 constexpr int kLocWideMaxDraws = SV_LOC_WIDE_MAX_DRAWS;
+// Tuning knob: batches of at most this many draws (and more than the above)
+// use 512-thread draws; larger ones 256.  At 512 draws the middle size took
+// the draw kernel from 19.9 to 16.0 us; at 962 it was even, above 1024 slower.
+#ifndef SV_LOC_MID_MAX_DRAWS
+#define SV_LOC_MID_MAX_DRAWS 768
+#endif
+constexpr int kLocMidMaxDraws = SV_LOC_MID_MAX_DRAWS;
 
 template <int TDT, int DDT, bool PAIR>
 void launch_locate(const RunParams& p, hipStream_t s) {
   if (p.B <= kLocWideMaxDraws)
     hipLaunchKernelGGL((k_locate<TDT, DDT, PAIR, 1024>), dim3(p.B), dim3(1024), 0, s, p);
+  else if (p.B <= kLocMidMaxDraws)
+    hipLaunchKernelGGL((k_locate<TDT, DDT, PAIR, 512>), dim3(p.B), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((k_locate<TDT, DDT, PAIR, 256>), dim3(p.B), dim3(256), 0, s, p);
 }
@@ -1128,6 +1137,8 @@ void launch_one(int k, const RunParams& p, hipStream_t s) {
       if (p.sample_k > 0) {
         if (p.B <= kLocWideMaxDraws)
           hipLaunchKernelGGL((k_sample<TDT, 1024>), dim3(p.B), dim3(1024), 0, s, p);
+        else if (p.B <= kLocMidMaxDraws)
+          hipLaunchKernelGGL((k_sample<TDT, 512>), dim3(p.B), dim3(512), 0, s, p);
         else
           hipLaunchKernelGGL((k_sample<TDT, 256>), dim3(p.B), dim3(256), 0, s, p);
       } else if (p.has_draft) {

@@ -219,3 +219,12 @@ def test_max_drafts(svlib):
                           n_mode="ragged", onehot_frac=0.25, corr=0.97, seed=5, device="cuda")
     rep = check(svlib, w, seed=2, offset=7)
     assert rep.accepted > 0
+
+
+def test_draw_sizes(svlib):
+    """Batches whose draw count selects each draw workgroup size: up to 384
+    draws take 1024 threads, up to 768 take 512, more take 256."""
+    for B in (384, 500, 769):
+        w = synth.make_random(B, 3, 2000, dtype=torch.bfloat16, temps=(1.0, 0.7, 0.0),
+                              n_mode="ragged", onehot_frac=0.2, seed=B, device="cuda")
+        check(svlib, w, seed=1, offset=B)

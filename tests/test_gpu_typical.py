@@ -118,3 +118,11 @@ def test_max_vocab(svlib):
     w = synth.make_random(6, 3, 983040, dtype=torch.bfloat16, temps=(1.0, 0.0, 0.6),
                           n_mode="ragged", corr=0.97, seed=3, device="cuda")
     check(svlib, w, 1e-6, 3, seed=2, offset=1)
+
+
+def test_draw_sizes(svlib):
+    """Batches whose draw count selects each draw workgroup size."""
+    for B in (300, 600, 800):
+        w = synth.make_random(B, 2, 1500, dtype=torch.bfloat16, temps=(1.0, 0.0, 0.8),
+                              n_mode="ragged", corr=0.97, seed=B, device="cuda")
+        check(svlib, w, 0.02, 2, seed=2, offset=B)
