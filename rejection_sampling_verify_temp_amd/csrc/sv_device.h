@@ -75,7 +75,7 @@ __device__ void uniforms(uint64_t seed, uint64_t offset, int b, int j,
 
 // The draft sampler's uniform for row j of request b: word 0 of the block at
 // counter (offset, b, j, 1); the verify step's counters have word 3 = 0.
-__device__ double draft_uniform(uint64_t seed, uint64_t offset, int b, int j) {
+[[maybe_unused]] __device__ double draft_uniform(uint64_t seed, uint64_t offset, int b, int j) {
   uint64_t ctr[4] = {offset, (uint64_t)b, (uint64_t)j, 1};
   philox4x64_10(ctr, seed, 0);
   return (double)(ctr[0] >> 40) * 0x1p-24;

@@ -256,10 +256,6 @@ __device__ __forceinline__ bool slot_needed(const ReqInfo& r, int s, int K) {
   return r.active && (s <= K ? s <= r.n : (s - K - 1 < r.n && r.draft_stats));
 }
 
-__device__ __forceinline__ int rows_needed(const ReqInfo& r) {
-  return r.n + 1 + (r.draft_stats ? r.n : 0);
-}
-
 // ---------------------------------------------------------------------------
 // Decisions of one request (one wavefront)
 // ---------------------------------------------------------------------------
@@ -670,16 +666,10 @@ __device__ __forceinline__ double pair_chunk_sum(const void* prow, const void* q
 // ---------------------------------------------------------------------------
 // Inverse-CDF draw of the emitted token (one workgroup)
 // ---------------------------------------------------------------------------
-// Residual of element i from its loaded logits (lp target, lq draft).
-__device__ __forceinline__ float resid_of(float lp, float lq, int kind, int i, int excl,
-                                          const DrawDesc& d, bool probs) {
-  const float r = kind == kDrawPair ? pair_resid(lp, lq, d, probs) : single_resid(lp, d);
-  return i == excl ? 0.f : r;
-}
-
 // The draw of one request runs NT threads, each owning 16384 / NT
 // consecutive elements of the chosen chunk.  Few draws take 1024 threads
-// (short per-thread work); many draws take 256 (more draws resident per CU).
+// (short per-thread work), more take 512, many take 256 (more draws
+// resident per CU).
 template <int NT>
 constexpr int seg_len() { return 16384 / NT; }
 static_assert(seg_len<1024>() * 1024 >= kMaxChunkElems, "a chunk must fit the segments");

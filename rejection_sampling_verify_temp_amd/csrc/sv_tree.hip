@@ -673,8 +673,6 @@ __global__ __launch_bounds__(kTreeThreads) void k_tree(const TreeParams p) {
   }
 }
 
-bool aligned(const void* ptr, int a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
-
 }  // namespace
 
 hipError_t launch_tree(const TreeParams& p, int tdt, int ddt, hipStream_t s) {
