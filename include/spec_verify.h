@@ -293,6 +293,17 @@ int spec_ngram_propose(int32_t B, const int32_t *context, int32_t stride,
                        int32_t *out_drafts, int32_t *out_num_drafts,
                        void *stream);
 
+/* Global index of the handle's request 0, for a batch split into shards
+ * (across GPUs, or across calls).  Every later run on the handle draws its
+ * Philox counters for request b at request index base + b, in place of b:
+ * in spec_verify_run, spec_verify_run_typical, spec_verify_run_tree, and
+ * in spec_draft_sample, where b is the request (row / K).  A shard
+ * [base, base + B_s) of a batch, run with that base and the batch's seed and
+ * offset, therefore gives exactly the rows the whole batch gives in one
+ * call.  Default 0.  Host-only; takes effect for runs enqueued after it.
+ * Returns SV_ERR_INVALID_ARG for a null handle or base < 0. */
+int spec_verify_set_request_base(spec_verify_t h, int32_t base);
+
 /* Waits for the handle's last run, copies the sticky SV_DEVERR_* bitmask to
  * *host_flags and, if clear != 0, resets it.  Synchronizing call. */
 int spec_verify_get_device_errors(spec_verify_t h, uint32_t *host_flags,

@@ -73,6 +73,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.spec_ngram_propose.restype = ctypes.c_int
     lib.spec_verify_get_device_errors.argtypes = [P, ctypes.POINTER(u32), i32]
     lib.spec_verify_get_device_errors.restype = ctypes.c_int
+    lib.spec_verify_set_request_base.argtypes = [P, i32]
+    lib.spec_verify_set_request_base.restype = ctypes.c_int
     lib.spec_verify_timing_enable.argtypes = [P, i32]
     lib.spec_verify_timing_enable.restype = ctypes.c_int
     lib.spec_verify_timing_read.argtypes = [P, ctypes.POINTER(ctypes.c_float),
@@ -191,6 +193,12 @@ def ngram_propose(context, context_lens, *, min_n, max_n, k, max_model_len,
     if rc != SV_OK:
         raise SpecVerifyError("spec_ngram_propose", rc)
     return out_drafts, out_num
+
+
+def spec_verify_set_request_base(h, base: int) -> None:
+    rc = load_library().spec_verify_set_request_base(h, int(base))
+    if rc != SV_OK:
+        raise SpecVerifyError("spec_verify_set_request_base", rc)
 
 
 def spec_verify_get_device_errors(h, clear: bool = False) -> int:
@@ -429,3 +437,7 @@ class SpecVerify:
 
     def device_errors(self, clear=False):
         return spec_verify_get_device_errors(self.handle, clear)
+
+    def set_request_base(self, base):
+        """Global index of request 0 for later runs (a shard of a batch)."""
+        spec_verify_set_request_base(self.handle, base)

@@ -61,6 +61,7 @@ struct spec_verify_s {
   uint32_t* flags = nullptr;
   hipStream_t last_stream = nullptr;
   bool has_run = false;
+  int32_t b_base = 0;  // global index of request 0 (spec_verify_set_request_base)
   // timing: per run, one start/stop pair per kernel
   bool timing = false;
   hipEvent_t ev[kTimingSlots][kEventsPerRun] = {};
@@ -232,7 +233,7 @@ int spec_verify_run(spec_verify_t h, int32_t B, int32_t K, const void* target_lo
   full.nchunk = h->nchunk;
   full.draft_is_probs = c.draft_is_probs;
   full.has_draft = draft_probs != nullptr;
-  full.b_base = 0;
+  full.b_base = h->b_base;
 
   return enqueue(h, full, c.target_dtype, c.draft_dtype, stream);
 }
@@ -279,6 +280,7 @@ int spec_verify_run_typical(spec_verify_t h, int32_t B, int32_t K, const void* t
   full.typical = 1;
   full.eps = threshold;
   full.top_k = top_k;
+  full.b_base = h->b_base;
   return enqueue(h, full, c.target_dtype, c.draft_dtype, stream);
 }
 
@@ -319,12 +321,19 @@ int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N, const void* targ
   tp.N = N;
   tp.V = c.vocab;
   tp.draft_is_probs = c.draft_is_probs;
+  tp.b_base = h->b_base;
   DeviceGuard g(c.device);
   if (!g.ok) return SV_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (sv::launch_tree(tp, c.target_dtype, c.draft_dtype, s) != hipSuccess) return SV_ERR_HIP;
   h->last_stream = s;
   h->has_run = true;
+  return SV_OK;
+}
+
+int spec_verify_set_request_base(spec_verify_t h, int32_t base) {
+  if (h == nullptr || base < 0) return SV_ERR_INVALID_ARG;
+  h->b_base = base;
   return SV_OK;
 }
 
@@ -363,6 +372,7 @@ int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K, const void* draft_l
   full.chunk = h->chunk;
   full.nchunk = h->nchunk;
   full.sample_k = K;
+  full.b_base = h->b_base;
   return enqueue(h, full, c.draft_dtype, c.draft_dtype, stream);
 }
 

@@ -108,6 +108,7 @@ struct TreeParams {
   uint64_t seed, offset;
   int B, N, V;
   int draft_is_probs;
+  int b_base;  // global index of request 0 (Philox counters use b_base + b)
 };
 
 hipError_t launch_tree(const TreeParams& p, int target_dtype, int draft_dtype,

@@ -601,7 +601,7 @@ __global__ __launch_bounds__(kTreeThreads) void k_tree(const TreeParams p) {
           px = o.px;
           ratio = o.ratio;
         }
-        const Uniforms un = tree_uniforms(p.seed, p.offset, b, ch - 1);
+        const Uniforms un = tree_uniforms(p.seed, p.offset, p.b_base + b, ch - 1);
         accept = un.acc < ratio;
         // one-hot: a rejected token leaves the law, which is renormalized
         if (!accept && !HAS_DRAFT && valid && !excluded(s_ex, nex, x)) Zk -= px;
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kTreeThreads) void k_tree(const TreeParams p) {
     if (!sampling) {
       y = ps.arg;
     } else {
-      const double u_rec = tree_uniforms(p.seed, p.offset, b, v).rec;
+      const double u_rec = tree_uniforms(p.seed, p.offset, p.b_base + b, v).rec;
       Law L{false, c, ps.ref, qs.ref, 0.f, 0.f, probs};
       if (HAS_DRAFT && nrej > 0) {
         L.pair = true;
