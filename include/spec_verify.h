@@ -313,7 +313,9 @@ int spec_verify_get_device_errors(spec_verify_t h, uint32_t *host_flags,
  * enable != 0 starts recording (and resets the totals); each later run adds
  * the duration of each of its kernels.  spec_verify_timing_read waits for
  * the last run and writes up to n totals in milliseconds (kernel order as
- * spec_verify_kernel_name) and the number of timed runs. */
+ * spec_verify_kernel_name) and the number of timed runs.  A kernel a run
+ * does not launch (the decision kernel of the draft sampler, the residual
+ * kernel of runs without draft rows) adds nothing to its total. */
 int spec_verify_timing_enable(spec_verify_t h, int32_t enable);
 int spec_verify_timing_read(spec_verify_t h, float *total_ms, int32_t n,
                             int32_t *runs);

@@ -65,6 +65,7 @@ struct spec_verify_s {
   // timing: per run, one start/stop pair per kernel
   bool timing = false;
   hipEvent_t ev[kTimingSlots][kEventsPerRun] = {};
+  uint32_t ev_launched[kTimingSlots] = {};  // per event set: the kernels it timed
   int ev_pending = 0;  // event sets recorded and not yet read
   int ev_next = 0;     // next ring slot
   double tot_ms[sv::kNumKernels] = {};
@@ -87,6 +88,7 @@ void free_all(spec_verify_s* h) {
 hipError_t drain_one(spec_verify_s* h) {
   const int slot = (h->ev_next - h->ev_pending + kTimingSlots) % kTimingSlots;
   for (int k = 0; k < sv::kNumKernels; ++k) {
+    if (!(h->ev_launched[slot] & (1u << k))) continue;  // not launched in that run
     hipEvent_t* e = &h->ev[slot][2 * k];
     hipError_t err = hipEventSynchronize(e[1]);
     if (err != hipSuccess) return err;
@@ -112,7 +114,10 @@ int enqueue(spec_verify_s* h, const sv::RunParams& p, int tdt, int ddt, void* st
     ev = h->ev[h->ev_next];
   }
   bool ok = true;
+  uint32_t launched = 0;
   for (int k = 0; ok && k < sv::kNumKernels; ++k) {
+    if (!sv::kernel_launched(k, p)) continue;
+    launched |= 1u << k;
     hipEvent_t* e = ev ? &ev[2 * k] : nullptr;
     ok = (!e || hipEventRecord(e[0], s) == hipSuccess) &&
          sv::launch_kernel(k, p, tdt, ddt, s) == hipSuccess &&
@@ -120,6 +125,7 @@ int enqueue(spec_verify_s* h, const sv::RunParams& p, int tdt, int ddt, void* st
   }
   if (!ok) return SV_ERR_HIP;
   if (h->timing) {
+    h->ev_launched[h->ev_next] = launched;
     h->ev_next = (h->ev_next + 1) % kTimingSlots;
     h->ev_pending++;
   }

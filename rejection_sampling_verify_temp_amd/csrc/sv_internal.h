@@ -93,6 +93,10 @@ hipError_t launch_kernel(int k, const RunParams& p, int target_dtype, int draft_
 
 const char* kernel_name(int i);
 
+// Whether launch_kernel(k, p, ...) launches anything for these parameters
+// (the draft sampler has no decisions; runs without draft rows no residual).
+bool kernel_launched(int k, const RunParams& p);
+
 // Token-tree verification of a batch (one workgroup per request).
 struct TreeParams {
   const void* target;  // [B][N][V]

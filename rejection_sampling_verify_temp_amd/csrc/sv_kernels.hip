@@ -1107,6 +1107,16 @@ void launch_locate(const RunParams& p, hipStream_t s) {
     hipLaunchKernelGGL((k_locate<TDT, DDT, PAIR, 256>), dim3(p.B), dim3(256), 0, s, p);
 }
 
+}  // namespace
+
+bool kernel_launched(int k, const RunParams& p) {
+  if (k == kKernelDecide) return p.sample_k == 0;
+  if (k == kKernelResid) return p.has_draft != 0;
+  return true;
+}
+
+namespace {
+
 template <int TDT, int DDT>
 void launch_one(int k, const RunParams& p, hipStream_t s) {
   switch (k) {
@@ -1115,13 +1125,12 @@ void launch_one(int k, const RunParams& p, hipStream_t s) {
       hipLaunchKernelGGL((k_stats<TDT, DDT>), dim3((unsigned)g), dim3(kThreads), 0, s, p);
       break;
     }
-    case kKernelDecide:  // the draft sampler has no decisions
-      if (p.sample_k == 0) hipLaunchKernelGGL((k_decide<TDT, DDT>), dim3(p.B), dim3(64), 0, s, p);
+    case kKernelDecide:
+      hipLaunchKernelGGL((k_decide<TDT, DDT>), dim3(p.B), dim3(64), 0, s, p);
       break;
     case kKernelResid:
-      if (p.has_draft)
-        hipLaunchKernelGGL((k_resid<TDT, DDT>), dim3((unsigned)((uint64_t)p.B * p.nchunk)),
-                           dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((k_resid<TDT, DDT>), dim3((unsigned)((uint64_t)p.B * p.nchunk)),
+                         dim3(kThreads), 0, s, p);
       break;
     default:
       if (p.sample_k > 0) {
@@ -1143,6 +1152,7 @@ void launch_one(int k, const RunParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_kernel(int k, const RunParams& p, int tdt, int ddt, hipStream_t s) {
+  if (!kernel_launched(k, p)) return hipSuccess;
   if (tdt == SV_F32 && ddt == SV_F32) launch_one<SV_F32, SV_F32>(k, p, s);
   else if (tdt == SV_F32 && ddt == SV_BF16) launch_one<SV_F32, SV_BF16>(k, p, s);
   else if (tdt == SV_BF16 && ddt == SV_F32) launch_one<SV_BF16, SV_F32>(k, p, s);
