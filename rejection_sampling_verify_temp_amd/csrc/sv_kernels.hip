@@ -927,7 +927,9 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
   if (lane == 63) s_woff[w] = incl;
   double q = lane_before(incl);
   if (lane == 0) q = 0.0;
-  if (seg > 0.0) atomicMax(&s_lastseg, tid);
+  // the last segment with mass: one atomic per wavefront, not per thread
+  const uint64_t has = __ballot(seg > 0.0);
+  if (lane == 0 && has != 0) atomicMax(&s_lastseg, w * 64 + 63 - (int)__builtin_clzll(has));
   __syncthreads();
   for (int k = 0; k < w; ++k) q += s_woff[k];
 
