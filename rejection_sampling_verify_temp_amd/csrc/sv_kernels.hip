@@ -282,6 +282,13 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
   int x = -1;
   if (lane < n) x = p.ids[(size_t)b * K + lane];
 
+  // lanes 0..n draw their Philox blocks once, while the loads are in flight:
+  // word 0 decides position j, word 1 is the draw uniform if the walk stops
+  // there
+  double u_acc = 0.0, u_rec = 0.0;
+  if (ri.sampling && p.sample_k == 0 && lane <= n)
+    uniforms(p.seed, p.offset, p.b_base + b, lane, &u_acc, &u_rec);
+
   // values of the drafted tokens
   float lt = __builtin_nanf(""), ld = __builtin_nanf("");
   if (lane < n && x >= 0 && x < V) {
@@ -358,13 +365,10 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
       double ratio;
       if (qx > 0.0) ratio = px / qx;
       else ratio = px > 0.0 ? __builtin_inf() : 0.0;
-      if (p.typical) {  // threshold or top-k: no uniform
+      if (p.typical)  // threshold or top-k: no uniform
         accept = px > (double)p.eps || rank < p.top_k;
-      } else {
-        double u_acc, u_rec;
-        uniforms(p.seed, p.offset, p.b_base + b, lane, &u_acc, &u_rec);
+      else
         accept = u_acc < ratio;
-      }
       dbg_p = (float)px;
       dbg_q = (float)qx;
     }
@@ -405,13 +409,10 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
       d.c = c;
       d.ref_p = t_ref;
       d.z_p = t_z;
-      if (p.sample_k > 0) {
+      if (p.sample_k > 0)
         d.u = draft_uniform(p.seed, p.offset, p.b_base + ri.rb, ri.rj);
-      } else {
-        double u_acc, u_rec;
-        uniforms(p.seed, p.offset, p.b_base + b, je, &u_acc, &u_rec);
-        d.u = u_rec;
-      }
+      else
+        d.u = u_rec;  // this lane is je = n_acc <= n
       d.kind = kDrawSingle;
       if (je < n && !p.typical) {  // rejected at je (typical: draw from p itself)
         d.x = (x >= 0 && x < V) ? x : -1;
