@@ -62,6 +62,7 @@ struct spec_verify_s {
   hipStream_t last_stream = nullptr;
   bool has_run = false;
   int32_t b_base = 0;  // global index of request 0 (spec_verify_set_request_base)
+  int lds_per_cu = 0;  // bytes of LDS per compute unit (0: unknown, stats launches uncapped)
   // timing: per run, one start/stop pair per kernel
   bool timing = false;
   hipEvent_t ev[kTimingSlots][kEventsPerRun] = {};
@@ -120,7 +121,7 @@ int enqueue(spec_verify_s* h, const sv::RunParams& p, int tdt, int ddt, void* st
     launched |= 1u << k;
     hipEvent_t* e = ev ? &ev[2 * k] : nullptr;
     ok = (!e || hipEventRecord(e[0], s) == hipSuccess) &&
-         sv::launch_kernel(k, p, tdt, ddt, s) == hipSuccess &&
+         sv::launch_kernel(k, p, tdt, ddt, h->lds_per_cu, s) == hipSuccess &&
          (!e || hipEventRecord(e[1], s) == hipSuccess);
   }
   if (!ok) return SV_ERR_HIP;
@@ -179,6 +180,11 @@ int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
   h->cfg = c;
   h->chunk = chunk;
   h->nchunk = nchunk;
+  if (hipDeviceGetAttribute(&h->lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                            c.device) != hipSuccess) {
+    h->lds_per_cu = 0;
+    (void)hipGetLastError();  // not reported by a later launch
+  }
   const size_t rows = (size_t)c.max_batch * (2 * (size_t)c.max_drafts + 1);
   bool ok = hipMalloc(&h->part, rows * nchunk * sizeof(sv::Partial)) == hipSuccess &&
             hipMalloc(&h->desc, (size_t)c.max_batch * (c.max_drafts > 1 ? c.max_drafts : 1) *

@@ -88,8 +88,10 @@ constexpr int kNumKernels = 4;
 enum KernelId { kKernelStats = 0, kKernelDecide = 1, kKernelResid = 2, kKernelLocate = 3 };
 
 // Enqueue kernel k of a step (for the requests p describes) on `stream`.
+// lds_per_cu (bytes of LDS per compute unit, 0 if unknown) sets the stats
+// kernel's occupancy cap.
 hipError_t launch_kernel(int k, const RunParams& p, int target_dtype, int draft_dtype,
-                         hipStream_t stream);
+                         int lds_per_cu, hipStream_t stream);
 
 const char* kernel_name(int i);
 

@@ -228,24 +228,36 @@ struct ReqInfo {
 
 __device__ __forceinline__ ReqInfo req_info(const RunParams& p, int b) {
   ReqInfo r;
-  if (p.sample_k > 0) {
-    r.rb = b / p.sample_k;
-    r.rj = b - r.rb * p.sample_k;
-    const int nb = p.nd != nullptr ? p.nd[r.rb] : p.sample_k;
+  const bool sampler = p.sample_k > 0;
+  r.rb = sampler ? b / p.sample_k : b;
+  r.rj = b - r.rb * (sampler ? p.sample_k : 1);
+  // the per-request loads go out together as scalar loads, so a workgroup
+  // knows after one round trip whether its row slot is needed.  A missing
+  // count array reads the temperature's address instead (that value is
+  // unused); the mode byte comes from its aligned word, which lies in the
+  // byte's own page.
+  const float* tp = p.temps + r.rb;
+  const int32_t* np = p.nd != nullptr ? p.nd + r.rb : reinterpret_cast<const int32_t*>(tp);
+  const int nv = *np;
+  r.T = *tp;
+  uint32_t mv = 0;
+  if (p.mode != nullptr) {
+    const uint8_t* m = p.mode + r.rb;
+    const uint32_t sh = reinterpret_cast<uintptr_t>(m) & 3u;
+    mv = (*reinterpret_cast<const uint32_t*>(m - sh) >> (8 * sh)) & 0xffu;
+  }
+  asm volatile("" ::"s"(nv), "s"(r.T), "s"(mv));  // no load waits for another
+  if (sampler) {
+    const int nb = p.nd != nullptr ? nv : p.sample_k;
     r.bad_n = nb < 0 || nb > p.sample_k;
     r.active = r.rj < clamp_drafts(nb, p.sample_k);
     r.n = 0;
-    r.T = p.temps[r.rb];
     r.onehot = true;
   } else {
-    r.rb = b;
-    r.rj = 0;
-    const int nb = p.nd[b];
-    r.n = clamp_drafts(nb, p.K);
-    r.bad_n = nb != r.n;
+    r.n = clamp_drafts(nv, p.K);
+    r.bad_n = nv != r.n;
     r.active = true;
-    r.T = p.temps[b];
-    r.onehot = !p.has_draft || (p.mode != nullptr && p.mode[b] != 0);
+    r.onehot = !p.has_draft || (p.mode != nullptr && mv != 0);
   }
   r.sampling = is_sampling(r.T);
   r.draft_stats = r.sampling && !r.onehot && !p.draft_is_probs;
@@ -542,6 +554,18 @@ __host__ __device__ __forceinline__ int stats_slots(const RunParams& p) {
 
 #ifndef SV_STATS_WAVES_PER_EU
 #define SV_STATS_WAVES_PER_EU 1
+#endif
+// Tuning knobs: stats workgroups resident per compute unit.  The kernel
+// streams rows at the memory system's limit, and once that is saturated more
+// resident workgroups only lengthen the memory queues.  Best measured on
+// MI355X: 6 for bf16 target rows and 4 for fp32 ones (half the arithmetic per
+// byte); 0 (no cap) when typical acceptance also counts elements, which adds
+// arithmetic per byte.  The limit without a cap is 8 (the kernel's registers).
+#ifndef SV_STATS_WG_CAP_BF16
+#define SV_STATS_WG_CAP_BF16 6
+#endif
+#ifndef SV_STATS_WG_CAP_F32
+#define SV_STATS_WG_CAP_F32 4
 #endif
 // One workgroup per (request, row slot, chunk); unneeded slots exit at once.
 template <int TDT, int DDT>
@@ -1120,12 +1144,25 @@ bool kernel_launched(int k, const RunParams& p) {
 
 namespace {
 
+// Dynamic LDS of a stats launch: a request that lets at most the cap's
+// number of workgroups share a compute unit's LDS (1 KB is left for the
+// kernel's static LDS and the allocation granularity).  0 means no cap.
+size_t stats_lds_bytes(const RunParams& p, int tdt, int lds_per_cu) {
+  const int cap = (p.typical && p.top_k > 0) ? 0
+                  : tdt == SV_F32            ? SV_STATS_WG_CAP_F32
+                                             : SV_STATS_WG_CAP_BF16;
+  if (cap <= 0 || lds_per_cu <= 0) return 0;
+  const int bytes = lds_per_cu / cap - 1024;
+  return bytes > lds_per_cu / (cap + 1) ? (size_t)bytes : 0;
+}
+
 template <int TDT, int DDT>
-void launch_one(int k, const RunParams& p, hipStream_t s) {
+void launch_one(int k, const RunParams& p, int lds_per_cu, hipStream_t s) {
   switch (k) {
     case kKernelStats: {
       const uint64_t g = (uint64_t)p.B * stats_slots(p) * p.nchunk;
-      hipLaunchKernelGGL((k_stats<TDT, DDT>), dim3((unsigned)g), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((k_stats<TDT, DDT>), dim3((unsigned)g), dim3(kThreads),
+                         stats_lds_bytes(p, TDT, lds_per_cu), s, p);
       break;
     }
     case kKernelDecide:
@@ -1154,12 +1191,13 @@ void launch_one(int k, const RunParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_kernel(int k, const RunParams& p, int tdt, int ddt, hipStream_t s) {
+hipError_t launch_kernel(int k, const RunParams& p, int tdt, int ddt, int lds_per_cu,
+                         hipStream_t s) {
   if (!kernel_launched(k, p)) return hipSuccess;
-  if (tdt == SV_F32 && ddt == SV_F32) launch_one<SV_F32, SV_F32>(k, p, s);
-  else if (tdt == SV_F32 && ddt == SV_BF16) launch_one<SV_F32, SV_BF16>(k, p, s);
-  else if (tdt == SV_BF16 && ddt == SV_F32) launch_one<SV_BF16, SV_F32>(k, p, s);
-  else launch_one<SV_BF16, SV_BF16>(k, p, s);
+  if (tdt == SV_F32 && ddt == SV_F32) launch_one<SV_F32, SV_F32>(k, p, lds_per_cu, s);
+  else if (tdt == SV_F32 && ddt == SV_BF16) launch_one<SV_F32, SV_BF16>(k, p, lds_per_cu, s);
+  else if (tdt == SV_BF16 && ddt == SV_F32) launch_one<SV_BF16, SV_F32>(k, p, lds_per_cu, s);
+  else launch_one<SV_BF16, SV_BF16>(k, p, lds_per_cu, s);
   return hipGetLastError();
 }
 
