@@ -189,7 +189,7 @@ int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
   bool ok = hipMalloc(&h->part, rows * nchunk * sizeof(sv::Partial)) == hipSuccess &&
             hipMalloc(&h->desc, (size_t)c.max_batch * (c.max_drafts > 1 ? c.max_drafts : 1) *
                                     sizeof(sv::DrawDesc)) == hipSuccess &&
-            hipMalloc(&h->rsum, (size_t)c.max_batch * nchunk * sizeof(double)) == hipSuccess &&
+            hipMalloc(&h->rsum, (size_t)c.max_batch * nchunk * sv::kResidSplitMax * sizeof(double)) == hipSuccess &&
             hipMalloc(&h->flags, sizeof(uint32_t)) == hipSuccess &&
             hipMemset(h->flags, 0, sizeof(uint32_t)) == hipSuccess;
   if (!ok) {

@@ -12,6 +12,17 @@ constexpr int kThreads = 256;        // every workgroup: four wavefronts
 constexpr int kMaxChunkElems = 15360; // the draw stages one chunk of floats in LDS
 constexpr int kMinChunkElems = 256;
 constexpr int kMaxChunks = 64;     // one lane per chunk when a request is combined
+// Tuning knobs: workgroups that share one chunk of a residual pair, each
+// summing a contiguous part of it, for bf16 rows and for pairs with an fp32
+// row.  The residual sums hold kResidSplitMax values per chunk.
+#ifndef SV_RESID_SPLIT_BF16
+#define SV_RESID_SPLIT_BF16 2
+#endif
+#ifndef SV_RESID_SPLIT_F32
+#define SV_RESID_SPLIT_F32 4
+#endif
+constexpr int kResidSplitMax =
+    SV_RESID_SPLIT_BF16 > SV_RESID_SPLIT_F32 ? SV_RESID_SPLIT_BF16 : SV_RESID_SPLIT_F32;
 constexpr int kMaxVocab = kMaxChunks * kMaxChunkElems;
 constexpr int kMaxDrafts = 31;       // the 2K+1 row slots fit one wavefront
 

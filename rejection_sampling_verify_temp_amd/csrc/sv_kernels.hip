@@ -621,9 +621,18 @@ __device__ __forceinline__ void unpack8(const Raw8<DT>& r, float* x) {
 
 // Groups of 8 elements per thread per round: enough for one round over a
 // default chunk (15360 bf16 or 8192 fp32 elements) within 128 VGPRs.
+// Parts per chunk of a residual pair (the residual pass runs one workgroup
+// per part).
+template <int TDT, int DDT>
+constexpr int resid_split() {
+  return (TDT == SV_F32 || DDT == SV_F32) ? SV_RESID_SPLIT_F32 : SV_RESID_SPLIT_BF16;
+}
+static_assert(SV_RESID_SPLIT_BF16 >= 1 && SV_RESID_SPLIT_F32 >= 1, "a chunk has one part or more");
+
 template <int TDT, int DDT>
 constexpr int resid_groups() {
-  return (TDT == SV_F32 || DDT == SV_F32) ? 4 : 8;
+  constexpr int g = ((TDT == SV_F32 || DDT == SV_F32) ? 4 : 8) / resid_split<TDT, DDT>();
+  return g > 0 ? g : 1;
 }
 
 // Sum over [c0, c1) of max(0, p~ - kappa q~), token x excluded.  All loads of
@@ -874,7 +883,11 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
       double mass = 0.0;
       if (lane < p.nchunk) {
         if (kind == kDrawPair) {
-          mass = p.rsum[(size_t)b * p.nchunk + lane];
+          constexpr int kSplit = resid_split<TDT, DDT>();
+          const double* rs = p.rsum + ((size_t)b * p.nchunk + lane) * kSplit;
+          mass = rs[0];
+#pragma unroll
+          for (int h = 1; h < kSplit; ++h) mass += rs[h];
         } else {
           const Partial q = p.part[((size_t)b * (2 * K + 1) + d.j) * p.nchunk + lane];
           if (q.z != 0.0) mass = q.z * exp2((double)d.ref_p - (double)ref_of(q.m, d.c));
@@ -1015,17 +1028,23 @@ template <int TDT, int DDT>
 __global__ __launch_bounds__(kThreads) void k_resid(
     const RunParams p) {
   __shared__ double ldsd[kThreads / 64];
+  constexpr int kSplit = resid_split<TDT, DDT>();
   const int bid = blockIdx.x;
-  const int rb = bid / p.nchunk, chunk = bid - rb * p.nchunk;
+  const int rb = bid / (p.nchunk * kSplit), part = bid - rb * (p.nchunk * kSplit);
+  const int chunk = part / kSplit, h = part - chunk * kSplit;
   const int b = p.B - 1 - rb;  // the most recently streamed requests first
   const DrawDesc d = p.desc[b];
   if (d.kind != kDrawPair) return;
   const int K = p.K, V = p.V;
   const void* prow = row_ptr(p.target, TDT, (size_t)b * (K + 1) + d.j, V);
   const void* qrow = row_ptr(p.draft, DDT, (size_t)b * K + d.j, V);
-  const int c0 = chunk * p.chunk, c1 = min(V, c0 + p.chunk);
+  // part h of the chunk: a multiple of 64 elements, so every part starts on
+  // a 16-byte boundary when the chunk does
+  const int ch0 = chunk * p.chunk, ch1 = min(V, ch0 + p.chunk);
+  const int plen = ((ch1 - ch0 + kSplit - 1) / kSplit + 63) & ~63;
+  const int c0 = min(ch1, ch0 + h * plen), c1 = min(ch1, c0 + plen);
   const double s = pair_chunk_sum<TDT, DDT>(prow, qrow, c0, c1, d, p.draft_is_probs != 0, ldsd);
-  if (threadIdx.x == 0) p.rsum[(size_t)b * p.nchunk + chunk] = s;
+  if (threadIdx.x == 0) p.rsum[((size_t)b * p.nchunk + chunk) * kSplit + h] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -1169,8 +1188,10 @@ void launch_one(int k, const RunParams& p, int lds_per_cu, hipStream_t s) {
       hipLaunchKernelGGL((k_decide<TDT, DDT>), dim3(p.B), dim3(64), 0, s, p);
       break;
     case kKernelResid:
-      hipLaunchKernelGGL((k_resid<TDT, DDT>), dim3((unsigned)((uint64_t)p.B * p.nchunk)),
-                         dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((k_resid<TDT, DDT>),
+                         dim3((unsigned)((uint64_t)p.B * p.nchunk * resid_split<TDT, DDT>())),
+                         dim3(kThreads),
+                         0, s, p);
       break;
     default:
       if (p.sample_k > 0) {
