@@ -856,7 +856,7 @@ __device__ __forceinline__ int seg_walk(const SegWords<TDT, SEG>& P,
 template <int TDT, int DDT, bool PAIR, int NT>
 __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
   constexpr int SEG = seg_len<NT>();
-  __shared__ int s_cstar, s_kind, s_excl, s_y, s_lastseg;
+  __shared__ int s_r0, s_rlen, s_kind, s_excl, s_y, s_lastseg;
   __shared__ double s_theta;
   __shared__ double s_woff[NT / 64];
   const int K = p.K, V = p.V, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -865,12 +865,14 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
   const void* qrow = d.kind == kDrawPair ? row_ptr(p.draft, DDT, (size_t)b * K + d.j, V) : nullptr;
   const bool probs = p.draft_is_probs != 0;
 
-  // (a) the chunk holding u * S.  Single-row draws were placed by the
-  // decision kernel; pair draws scan the residual chunk sums here
-  // (wavefront 0, lane = chunk).
+  // (a) the range holding u * S: a chunk, or for a pair draw the part of a
+  // chunk that one residual workgroup summed.  Single-row draws were placed
+  // in their chunk by the decision kernel; pair draws scan the residual sums
+  // here (wavefront 0, lane = chunk).
   if (d.cstar >= 0) {
     if (tid == 0) {
-      s_cstar = d.cstar;
+      s_r0 = d.cstar * p.chunk;
+      s_rlen = min(V, s_r0 + p.chunk) - s_r0;
       s_theta = d.th;
       s_kind = d.kind;
       s_excl = d.x;
@@ -878,16 +880,21 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
       s_lastseg = -1;
     }
   } else if (w == 0) {
+    constexpr int kSplit = resid_split<TDT, DDT>();
     int kind = d.kind, excl = d.x;
     for (int attempt = 0; attempt < 2; ++attempt) {
       double mass = 0.0;
+      double part[kSplit];  // a pair's part sums of chunk `lane`
+#pragma unroll
+      for (int h = 0; h < kSplit; ++h) part[h] = 0.0;
       if (lane < p.nchunk) {
         if (kind == kDrawPair) {
-          constexpr int kSplit = resid_split<TDT, DDT>();
           const double* rs = p.rsum + ((size_t)b * p.nchunk + lane) * kSplit;
-          mass = rs[0];
 #pragma unroll
-          for (int h = 1; h < kSplit; ++h) mass += rs[h];
+          for (int h = 0; h < kSplit; ++h) part[h] = rs[h];
+          mass = part[0];
+#pragma unroll
+          for (int h = 1; h < kSplit; ++h) mass += part[h];
         } else {
           const Partial q = p.part[((size_t)b * (2 * K + 1) + d.j) * p.nchunk + lane];
           if (q.z != 0.0) mass = q.z * exp2((double)d.ref_p - (double)ref_of(q.m, d.c));
@@ -921,8 +928,37 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
         th = __builtin_inf();
         if (lane == 0) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
       }
+      int r0 = cstar * p.chunk, rlen = min(V, r0 + p.chunk) - r0;
+      if (kind == kDrawPair && kSplit > 1) {
+        // the part: running sums in the order that gave the chunk's mass, so
+        // the last one equals it; the parts' bounds are the residual pass's
+        const int plen = ((rlen + kSplit - 1) / kSplit + 63) & ~63;
+        int hs = -1, hlast = 0;
+        double c = 0.0, c_before = 0.0;
+#pragma unroll
+        for (int h = 0; h < kSplit; ++h) {
+          const double v = lane_f64(part[h], cstar);
+          const double cn = h == 0 ? v : c + v;
+          if (v > 0.0) hlast = h;
+          if (hs < 0 && th < cn) {
+            hs = h;
+            c_before = c;
+          }
+          c = cn;
+        }
+        if (hs < 0) {  // theta at or past the chunk's last running sum
+          hs = hlast;
+          if (th != __builtin_inf() && lane == 0) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
+          th = __builtin_inf();
+        } else {
+          th -= c_before;
+        }
+        r0 += min(rlen, hs * plen);
+        rlen = min(plen, max(0, rlen - hs * plen));
+      }
       if (lane == 0) {
-        s_cstar = cstar;
+        s_r0 = r0;
+        s_rlen = rlen;
         s_theta = th;
         s_kind = kind;
         s_excl = excl;
@@ -934,11 +970,10 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
   }
   __syncthreads();
 
-  // (b) thread t owns chunk elements [t SEG, t SEG + SEG): their raw words
+  // (b) thread t owns range elements [t SEG, t SEG + SEG): their raw words
   // stay in registers, the residual sum is taken in fp64
   const int kind = s_kind, excl = s_excl;
-  const int c0 = s_cstar * p.chunk;
-  const int len = min(V, c0 + p.chunk) - c0;
+  const int c0 = s_r0, len = s_rlen;
   const int i0 = tid * SEG;
   const int nseg = max(0, min(SEG, len - i0));
   const bool pair = PAIR && kind == kDrawPair;
