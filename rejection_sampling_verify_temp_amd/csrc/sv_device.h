@@ -26,6 +26,17 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; tiny results flush to 0
 }
 
+// 2^(r - rw) for finite floats r <= rw, the factor that moves a sum of
+// exponentials from reference rw to reference r: the difference is exact in
+// double; its integer part goes to the exponent and v_exp_f32 takes the
+// fraction, so the factor is as accurate as the element exponentials that
+// the sum holds, at a fraction of a double exp2's cost.
+__device__ __forceinline__ double exp2_diff(float r, float rw) {
+  const double d = (double)r - (double)rw;
+  const double n = floor(d);
+  return ldexp((double)fast_exp2((float)(d - n)), (int)n);
+}
+
 // Sampling iff T is a positive, normal, finite float (NaN compares false).
 __device__ __forceinline__ bool is_sampling(float T) {
   return T >= FLT_MIN && T <= FLT_MAX;

@@ -342,7 +342,7 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
           if (k0 + u < p.nchunk && q[u].z != 0.0)
-            r_z += q[u].z * exp2((double)r_ref - (double)ref_of(q[u].m, c));
+            r_z += q[u].z * exp2_diff(r_ref, ref_of(q[u].m, c));
       }
     } else {
       r_ref = m;
@@ -457,7 +457,7 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
     double mass = 0.0, px = 0.0;
     if (lane < p.nchunk) {
       const Partial q = p.part[((size_t)b * nslot + je) * p.nchunk + lane];
-      if (q.z != 0.0) mass = q.z * exp2((double)dref - (double)ref_of(q.m, dc));
+      if (q.z != 0.0) mass = q.z * exp2_diff(dref, ref_of(q.m, dc));
       if (excl >= 0 && excl / p.chunk == lane) px = exp2((double)lx * (double)dc + (double)dref);
     }
     double mx = mass - px;
@@ -897,7 +897,7 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
           for (int h = 1; h < kSplit; ++h) mass += part[h];
         } else {
           const Partial q = p.part[((size_t)b * (2 * K + 1) + d.j) * p.nchunk + lane];
-          if (q.z != 0.0) mass = q.z * exp2((double)d.ref_p - (double)ref_of(q.m, d.c));
+          if (q.z != 0.0) mass = q.z * exp2_diff(d.ref_p, ref_of(q.m, d.c));
           if (excl >= 0 && excl / p.chunk == lane)
             mass -= exp2((double)Elt<TDT>::at(prow, excl) * (double)d.c + (double)d.ref_p);
         }
@@ -1126,7 +1126,7 @@ __global__ __launch_bounds__(NT) void k_sample(const RunParams p) {
       const float c = temp_scale(ri.T);
       const float ref = ref_of(wave_max(q.m), c);
       double mass = 0.0;
-      if (lane < p.nchunk && q.z != 0.0) mass = q.z * exp2((double)ref - (double)ref_of(q.m, c));
+      if (lane < p.nchunk && q.z != 0.0) mass = q.z * exp2_diff(ref, ref_of(q.m, c));
       const double incl = wave_incl_scan(mass, lane);
       const double S = lane_f64(incl, 63);
       const double u = draft_uniform(p.seed, p.offset, p.b_base + ri.rb, ri.rj);

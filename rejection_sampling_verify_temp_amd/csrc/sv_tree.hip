@@ -83,15 +83,6 @@ __device__ __forceinline__ u32x4 select_vec(bool keep, u32x4 a, u32x4 b) {
   return u32x4{keep ? a.x : b.x, keep ? a.y : b.y, keep ? a.z : b.z, keep ? a.w : b.w};
 }
 
-// 2^(r - rw) for floats r <= rw: the difference is exact in double; its
-// integer part goes to the exponent and v_exp_f32 takes the fraction, so the
-// factor is as accurate as the element exponentials themselves.
-__device__ __forceinline__ double exp2_diff(float r, float rw) {
-  const double d = (double)r - (double)rw;
-  const double n = floor(d);
-  return ldexp((double)fast_exp2((float)(d - n)), (int)n);
-}
-
 // Statistics of one row (whole workgroup).  Sampling rows take each round in
 // two phases per wavefront: the wavefront's max of the round first, which
 // fixes one exponent reference for its 64 lanes, then the sums of
