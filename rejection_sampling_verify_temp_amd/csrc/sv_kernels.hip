@@ -853,9 +853,19 @@ __device__ __forceinline__ int seg_walk(const SegWords<TDT, SEG>& P,
 }
 
 // PAIR = false: a batch with no draft rows (no residual pairs).
+// A pair draw's residual part sums (wavefront 0, lane = chunk): their
+// addresses need only the request, so the draw kernel loads them with the
+// descriptor.
+template <int TDT, int DDT>
+struct ResidParts {
+  double v[resid_split<TDT, DDT>()];
+};
+
 template <int TDT, int DDT, bool PAIR, int NT>
-__device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
+__device__ __forceinline__ void locate(const RunParams& p, int b, const DrawDesc& d,
+                                       const ResidParts<TDT, DDT>& pre) {
   constexpr int SEG = seg_len<NT>();
+  constexpr int kSplit = resid_split<TDT, DDT>();
   __shared__ int s_r0, s_rlen, s_kind, s_excl, s_y, s_lastseg;
   __shared__ double s_theta;
   __shared__ double s_woff[NT / 64];
@@ -880,7 +890,6 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
       s_lastseg = -1;
     }
   } else if (w == 0) {
-    constexpr int kSplit = resid_split<TDT, DDT>();
     int kind = d.kind, excl = d.x;
     for (int attempt = 0; attempt < 2; ++attempt) {
       double mass = 0.0;
@@ -889,9 +898,8 @@ __device__ void locate(const RunParams& p, int b, const DrawDesc& d) {
       for (int h = 0; h < kSplit; ++h) part[h] = 0.0;
       if (lane < p.nchunk) {
         if (kind == kDrawPair) {
-          const double* rs = p.rsum + ((size_t)b * p.nchunk + lane) * kSplit;
 #pragma unroll
-          for (int h = 0; h < kSplit; ++h) part[h] = rs[h];
+          for (int h = 0; h < kSplit; ++h) part[h] = pre.v[h];
           mass = part[0];
 #pragma unroll
           for (int h = 1; h < kSplit; ++h) mass += part[h];
@@ -1087,10 +1095,19 @@ __global__ __launch_bounds__(kThreads) void k_resid(
 // ---------------------------------------------------------------------------
 template <int TDT, int DDT, bool PAIR, int NT>
 __global__ __launch_bounds__(NT) void k_locate(const RunParams p) {
-  const int b = blockIdx.x;
+  constexpr int kSplit = resid_split<TDT, DDT>();
+  const int b = blockIdx.x, tid = threadIdx.x;
   const DrawDesc d = p.desc[b];
-  if (d.kind == kDrawNone) return;
-  locate<TDT, DDT, PAIR, NT>(p, b, d);
+  ResidParts<TDT, DDT> pre;
+#pragma unroll
+  for (int h = 0; h < kSplit; ++h) pre.v[h] = 0.0;
+  if (PAIR && tid < 64 && tid < p.nchunk) {  // read by pair draws only
+    const double* rs = p.rsum + ((size_t)b * p.nchunk + tid) * kSplit;
+#pragma unroll
+    for (int h = 0; h < kSplit; ++h) pre.v[h] = rs[h];
+  }
+  if (d.kind == kDrawNone) return;  // uniform
+  locate<TDT, DDT, PAIR, NT>(p, b, d, pre);
 }
 
 // Draft sampler: the draw of one row without a decision kernel.  Wavefront 0
@@ -1162,7 +1179,7 @@ __global__ __launch_bounds__(NT) void k_sample(const RunParams p) {
   }
   if (!ri.sampling) return;  // uniform across the workgroup
   __syncthreads();
-  locate<DT, DT, false, NT>(p, b, s_d);
+  locate<DT, DT, false, NT>(p, b, s_d, ResidParts<DT, DT>{});
 }
 
 // Tuning knob: batches of at most this many draws use 1024-thread draws.
