@@ -92,7 +92,7 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
       static_cast<const char*>(row) + (size_t)g.v0 * E::kBytes);
   const VecBuf vb = make_vec_buf(vp, (uint32_t)g.nvec * 16u);
   float M = kNegInf, R = 0.f, S = 0.f;
-  int cnt = 0;
+  int cnt = 0;  // COUNT: elements above lx seen by this wavefront (uniform)
   for (int base = 0; base == 0 || base < g.nvec; base += kThreads * kUnroll) {
     const int v = base + tid;
     // head and tail (each under one vector) ride along with the first pass.
@@ -116,7 +116,9 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
     ht[0] = base == 0 && g.c0 + tid < g.v0 ? raw_to_float<DT>(h) : kNegInf;
     ht[1] = base == 0 && g.t0 + tid < g.c1 ? raw_to_float<DT>(tl) : kNegInf;
     float t = fmaxf(ht[0], ht[1]);
-    if (COUNT) cnt += (ht[0] > lx) + (ht[1] > lx);
+    // a compare per element, counted across the wavefront by a scalar
+    // popcount of its lane mask instead of a per-lane add
+    if (COUNT) cnt += __popcll(__ballot(ht[0] > lx)) + __popcll(__ballot(ht[1] > lx));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (v + u * kThreads < g.nvec) {
@@ -125,7 +127,7 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
 #pragma unroll
         for (int k = 0; k < E::kVec; ++k) {
           t = fmaxf(t, x[k]);
-          if (COUNT) cnt += x[k] > lx;
+          if (COUNT) cnt += __popcll(__ballot(x[k] > lx));
         }
       }
     }
@@ -155,7 +157,7 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
   }
   *z_out = block_sum<kThreads>((double)S, ldsd);
   *m_out = M;
-  if (COUNT) *above = block_sum_int<kThreads>(cnt, ldsi);
+  if (COUNT) *above = block_sum_int<kThreads>((tid & 63) == 0 ? cnt : 0, ldsi);
 }
 
 template <int DT>
