@@ -4,18 +4,22 @@
 //   1. stats   streams every needed logits row once, split into vocabulary
 //              chunks: per chunk the max and the sum of exp2(l * c + ref)
 //              (sampling rows) or the max and its lowest index (greedy rows).
-//              HBM-bound; this is the hot loop.
+//              HBM-bound; this is the hot loop.  A dynamic LDS request caps
+//              its resident workgroups per CU (more only lengthen the queues).
 //   2. decide  one wavefront per request: lane s folds the chunk partials
 //              of row slot s; then lane j draws the Philox uniforms of
 //              position j, forms p(x)/q(x) in fp64, a ballot of the accept
 //              bits gives the first rejection by count-trailing-zeros, and
 //              the outputs and a draw descriptor are written.
-//   3. resid   requests rejected on a probabilistic draft: per chunk the sum
-//              of max(0, p - q) over that row pair.
+//   3. resid   requests rejected on a probabilistic draft: the sum of
+//              max(0, p - q) over each part of each chunk of that row pair
+//              (2 parts per chunk for bf16 rows, 4 with an fp32 row).
 //   4. locate  one workgroup per sampling request: a prefix over the chunk
-//              sums finds the chunk holding u * S; each of 1024 threads
-//              takes 16 consecutive residuals of it in registers, and a
-//              workgroup scan of the segment sums finds the token.
+//              sums finds the chunk holding u * S (and, for a pair, the
+//              part); each of its 1024, 512 or 256 threads takes
+//              16384 / threads consecutive residuals of that range in
+//              registers, and a workgroup scan of the segment sums finds
+//              the token.
 //
 // Method (page title, section): "深入推测解码：从概念到实现" 保证原始分布
 // (accept with min(1, p/q), resample from max(0, p - q)); "RTP-LLM
@@ -543,8 +547,6 @@ __device__ __forceinline__ void stats_item(const RunParams& p, int b, int s, int
     p.part[((size_t)b * (2 * p.K + 1) + s) * p.nchunk + chunk] = out;
 }
 
-// Tuning knob: a minimum-waves-per-SIMD hint for the stats kernel (1 = none;
-// 8, which caps it at 64 registers, measured no faster).
 // Row slots in the stats grid per request: target rows 0..K, and draft rows
 // only when some request may need a draft softmax.  Typical acceptance, runs
 // without draft rows and probability drafts never do; the host knows that
@@ -554,6 +556,8 @@ __host__ __device__ __forceinline__ int stats_slots(const RunParams& p) {
   return (p.typical || !p.has_draft || p.draft_is_probs) ? p.K + 1 : 2 * p.K + 1;
 }
 
+// Tuning knob: a minimum-waves-per-SIMD hint for the stats kernel (1 = none;
+// 8, which caps it at 64 registers, measured no faster).
 #ifndef SV_STATS_WAVES_PER_EU
 #define SV_STATS_WAVES_PER_EU 1
 #endif
