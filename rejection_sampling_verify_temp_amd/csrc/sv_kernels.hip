@@ -1189,15 +1189,17 @@ __global__ __launch_bounds__(NT) void k_sample(const RunParams p) {
 }
 
 // Tuning knob: batches of at most this many draws use 1024-thread draws.
+// Verify draws at 512 requests: 11.5 us against 12.5 for 512 threads; the
+// sampler's whole-chunk draws at 768 rows: even.
 #ifndef SV_LOC_WIDE_MAX_DRAWS
-#define SV_LOC_WIDE_MAX_DRAWS 384
+#define SV_LOC_WIDE_MAX_DRAWS 768
 #endif
 constexpr int kLocWideMaxDraws = SV_LOC_WIDE_MAX_DRAWS;
 // Tuning knob: batches of at most this many draws (and more than the above)
-// use 512-thread draws; larger ones 256.  At 512 draws the middle size took
-// the draw kernel from 19.9 to 16.0 us; at 962 it was even, above 1024 slower.
+// use 512-thread draws; larger ones 256.  At 962 sampler rows 256 threads
+// take 17.1 us, 512 about the same and 1024 20.7 us.
 #ifndef SV_LOC_MID_MAX_DRAWS
-#define SV_LOC_MID_MAX_DRAWS 768
+#define SV_LOC_MID_MAX_DRAWS 896
 #endif
 constexpr int kLocMidMaxDraws = SV_LOC_MID_MAX_DRAWS;
 

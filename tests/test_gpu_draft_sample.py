@@ -209,8 +209,8 @@ def test_max_vocab_and_drafts(svlib):
 
 def test_draw_sizes(svlib):
     """Row counts on each side of the draw workgroup sizes (1024 threads up to
-    384 rows, 512 up to 768, 256 above)."""
-    for B, K in ((96, 4), (100, 5), (154, 5)):
+    768 rows, 512 up to 896, 256 above)."""
+    for B, K in ((192, 4), (160, 5), (180, 5)):
         l = _rows(B, K, 3000, torch.bfloat16, 20 + B)
         temps = torch.tensor([(1.0, 0.0, 0.6)[b % 3] for b in range(B)])
         check(svlib, f"{B * K} rows", l, None, temps, seed=3, offset=B)

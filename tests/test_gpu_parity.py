@@ -222,9 +222,9 @@ def test_max_drafts(svlib):
 
 
 def test_draw_sizes(svlib):
-    """Batches whose draw count selects each draw workgroup size: up to 384
-    draws take 1024 threads, up to 768 take 512, more take 256."""
-    for B in (384, 500, 769):
+    """Batches whose size selects each draw workgroup size: up to 768
+    requests take 1024 threads, up to 896 take 512, more take 256."""
+    for B in (768, 800, 900):
         w = synth.make_random(B, 3, 2000, dtype=torch.bfloat16, temps=(1.0, 0.7, 0.0),
                               n_mode="ragged", onehot_frac=0.2, seed=B, device="cuda")
         check(svlib, w, seed=1, offset=B)

@@ -122,7 +122,7 @@ def test_max_vocab(svlib):
 
 def test_draw_sizes(svlib):
     """Batches whose draw count selects each draw workgroup size."""
-    for B in (300, 600, 800):
+    for B in (700, 800, 900):
         w = synth.make_random(B, 2, 1500, dtype=torch.bfloat16, temps=(1.0, 0.0, 0.8),
                               n_mode="ragged", corr=0.97, seed=B, device="cuda")
         check(svlib, w, 0.02, 2, seed=2, offset=B)
