@@ -556,6 +556,11 @@ def main():
         out["cpu_baseline"]["cpu"] = cpu_model()
         if not sample and not typical:
             out["cpu_baseline_threads"] = cpu_baseline_threads(w)
+        # the same rates as bytes of input read once (the step's algorithmic
+        # bytes per element), for comparison with the GPU's GB/s
+        for key in ("cpu_baseline", "cpu_baseline_threads"):
+            if key in out:
+                out[key]["algorithmic_gbps"] = out[key]["value"] * alg / elems / 1e9
     h.close()
     print(json.dumps(out), flush=True)
 
