@@ -1081,7 +1081,7 @@ __global__ __launch_bounds__(kThreads) void k_resid(
   const int bid = blockIdx.x;
   const int rb = bid / (p.nchunk * kSplit), part = bid - rb * (p.nchunk * kSplit);
   const int chunk = part / kSplit, h = part - chunk * kSplit;
-  const int b = p.B - 1 - rb;  // the most recently streamed requests first
+  const int b = p.B - 1 - rb;  // last request first (measured the same as first first)
   const DrawDesc d = p.desc[b];
   if (d.kind != kDrawPair) return;
   const int K = p.K, V = p.V;
