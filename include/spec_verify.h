@@ -109,7 +109,11 @@ int spec_verify_create(const sv_config *cfg, spec_verify_t *out);
  *                      are never read.  NULL: every request is one-hot.
  *   draft_mode         device [B] uint8: 0 probabilistic, nonzero one-hot.
  *                      NULL: every request is probabilistic (if draft_probs
- *                      is given).
+ *                      is given).  The kernels read each byte through the
+ *                      aligned 4-byte word that holds it, so the bytes of
+ *                      those words next to the array must be readable memory
+ *                      (as in any device allocation; their values are not
+ *                      used).
  *   draft_ids          device [B][K] int32: the drafted tokens x_j.
  *   num_drafts_per_req device [B] int32: n_b, expected in [0, K].
  *   temperatures       device [B] float: T_b (see Conventions).
