@@ -46,6 +46,10 @@
  *     clamped or rejected and recorded in a sticky bitmask that
  *     spec_verify_get_device_errors returns.
  *   - The same inputs and (seed, offset) give bit-identical outputs.
+ *   - The rows a step reads are expected to hold finite logits (-inf counts
+ *     as probability 0) or, with draft_is_probs, probabilities.  NaN or +inf
+ *     there gives unspecified tokens, but never a fault or an access outside
+ *     the buffers.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
