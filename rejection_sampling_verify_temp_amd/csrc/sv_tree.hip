@@ -147,15 +147,17 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
     u32x4 d[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) d[u] = vec_load(vb, b0, u, tid);
-#pragma unroll
-    for (int u = 0; u < U; ++u) d[u] = select_vec(b0 + u * kRound + tid < g.nvec, d[u], E::neg_inf());
+    // vectors past the row are skipped by a test that is uniform in all but
+    // one wavefront of the row (the loads there returned 0)
     float t = b0 == 0 ? fmaxf(hx, tx) : kNegInf;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float x[E::kVec];
-      E::unpack(d[u], x);
+      if (b0 + u * kRound + tid < g.nvec) {
+        float x[E::kVec];
+        E::unpack(d[u], x);
 #pragma unroll
-      for (int k = 0; k < E::kVec; ++k) t = fmaxf(t, x[k]);
+        for (int k = 0; k < E::kVec; ++k) t = fmaxf(t, x[k]);
+      }
     }
     const float wm = wave_max(t);
     if (wm > Mw) {  // uniform across the wavefront
@@ -164,20 +166,24 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
       Rw = rn;
       Mw = wm;
     }
-    if (b0 == 0) S += (double)fast_exp2(fmaf(hx, c, Rw)) + (double)fast_exp2(fmaf(tx, c, Rw));
+    // the round's sum in fp32, added to the fp64 total once
+    float sr = b0 == 0 ? fast_exp2(fmaf(hx, c, Rw)) + fast_exp2(fmaf(tx, c, Rw)) : 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      // unpack again rather than keep the floats live: the empty asm hides
-      // the first unpack from common-subexpression elimination
-      u32x4 wv = d[u];
-      asm volatile("" : "+v"(wv));
-      float e[E::kVec];
-      E::unpack(wv, e);
+      if (b0 + u * kRound + tid < g.nvec) {
+        // unpack again rather than keep the floats live: the empty asm hides
+        // the first unpack from common-subexpression elimination
+        u32x4 wv = d[u];
+        asm volatile("" : "+v"(wv));
+        float e[E::kVec];
+        E::unpack(wv, e);
 #pragma unroll
-      for (int k = 0; k < E::kVec; ++k) e[k] = fast_exp2(fmaf(e[k], c, Rw));
-      S += (double)pairwise_sum(e);  // 0 for padding
-      asm volatile("" : "+v"(S));    // fold in order: no sums wait in registers
+        for (int k = 0; k < E::kVec; ++k) e[k] = fast_exp2(fmaf(e[k], c, Rw));
+        sr += pairwise_sum(e);
+        asm volatile("" : "+v"(sr));  // fold in order: no sums wait in registers
+      }
     }
+    S += (double)sr;
   }
   const float M = block_max<kTreeThreads>(Mw, ldsf);
   const float R = ref_of(M, c);
