@@ -284,6 +284,22 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_sum_step_f32(float v) {
+  const int b = __float_as_int(v);
+  return v + __int_as_float(dpp_move<CTRL, ROWS>(0, b));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = dpp_sum_step_f32<kDppShr1, 0xf>(v);
+  v = dpp_sum_step_f32<kDppShr2, 0xf>(v);
+  v = dpp_sum_step_f32<kDppShr4, 0xf>(v);
+  v = dpp_sum_step_f32<kDppShr8, 0xf>(v);
+  v = dpp_sum_step_f32<kDppBcast15, 0xa>(v);
+  v = dpp_sum_step_f32<kDppBcast31, 0xc>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
   v = dpp_sum_step<kDppShr1, 0xf>(v);
   v = dpp_sum_step<kDppShr2, 0xf>(v);

@@ -270,12 +270,15 @@ __device__ __forceinline__ void law_pass(const Law& L, const void* prow, const v
       for (int u = 0; u < kRowVecs; ++u) d[u] = vec_load(pb, b0, u, tid);
 #pragma unroll
       for (int u = 0; u < kRowVecs; ++u) {
-        float r[KV];
-        EP::unpack(d[u], r);
+        float sv = 0.f;  // vectors past the row: a test uniform in all but one wavefront
+        if (b0 + u * kRound + tid < g.nvec) {
+          float r[KV];
+          EP::unpack(d[u], r);
 #pragma unroll
-        for (int k = 0; k < KV; ++k) r[k] = law_of(L, r[k], 0.f);
-        const float sv = pairwise_sum(r);
-        f(b0 + u * kRound, b0 + u * kRound + tid < g.nvec ? sv : 0.f);
+          for (int k = 0; k < KV; ++k) r[k] = law_of(L, r[k], 0.f);
+          sv = pairwise_sum(r);
+        }
+        f(b0 + u * kRound, sv);
       }
     }
     return;
@@ -292,13 +295,16 @@ __device__ __forceinline__ void law_pass(const Law& L, const void* prow, const v
         }
 #pragma unroll
         for (int u = 0; u < kPairVecs; ++u) {
-          float lp[KV], lq[KV], r[KV];
-          EP::unpack(dp[u], lp);
-          EP::unpack(dq[u], lq);
+          float sv = 0.f;
+          if (b0 + u * kRound + tid < g.nvec) {
+            float lp[KV], lq[KV], r[KV];
+            EP::unpack(dp[u], lp);
+            EP::unpack(dq[u], lq);
 #pragma unroll
-          for (int k = 0; k < KV; ++k) r[k] = law_of(L, lp[k], lq[k]);
-          const float sv = pairwise_sum(r);
-          f(b0 + u * kRound, b0 + u * kRound + tid < g.nvec ? sv : 0.f);
+            for (int k = 0; k < KV; ++k) r[k] = law_of(L, lp[k], lq[k]);
+            sv = pairwise_sum(r);
+          }
+          f(b0 + u * kRound, sv);
         }
       }
       return;
@@ -322,10 +328,20 @@ __device__ __forceinline__ double law_sum(const Law& L, const void* prow, const 
   const Geo g = chunk_geo<TDT>(prow, 0, V);
   double acc = 0.0;
   if (tid < g.v0) acc += (double)law_at<TDT, DDT>(L, prow, qrow, tid);
+  // eight vector sums in fp32, then one fp64 add (every thread makes the
+  // same number of calls, so the flush is uniform)
+  float part = 0.f;
+  int nv = 0;
   law_pass<TDT, DDT>(L, prow, qrow, g, [&](int, float sv) {
-    acc += (double)sv;
-    asm volatile("" : "+v"(acc));  // fold in order: no sums wait in registers
+    part += sv;
+    asm volatile("" : "+v"(part));  // fold in order: no sums wait in registers
+    if (++nv == 8) {
+      acc += (double)part;
+      part = 0.f;
+      nv = 0;
+    }
   });
+  acc += (double)part;
   if (g.t0 + tid < V) acc += (double)law_at<TDT, DDT>(L, prow, qrow, g.t0 + tid);
   return block_sum<kTreeThreads>(acc, ldsd);
 }
@@ -339,7 +355,7 @@ __device__ __forceinline__ void slot_pass(const Law& L, const void* prow, const 
   const int npieces = (g.nvec + 63) / 64, nslot = npieces + 2;
   law_pass<TDT, DDT>(L, prow, qrow, g, [&](int b, float sv) {
     const int piece = b / 64 + w;
-    const double ws = wave_sum((double)sv);
+    const double ws = (double)wave_sum_f32(sv);  // 64 vector sums: fp32 is ample
     if (lane == 0 && piece < npieces) s_slot[1 + piece] = ws;
   });
   if (w == 0) {
