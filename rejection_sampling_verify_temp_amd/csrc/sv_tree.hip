@@ -79,10 +79,6 @@ __device__ __forceinline__ int pass_tid() {
   return t;
 }
 
-__device__ __forceinline__ u32x4 select_vec(bool keep, u32x4 a, u32x4 b) {
-  return u32x4{keep ? a.x : b.x, keep ? a.y : b.y, keep ? a.z : b.z, keep ? a.w : b.w};
-}
-
 // Statistics of one row (whole workgroup).  Sampling rows take each round in
 // two phases per wavefront: the wavefront's max of the round first, which
 // fixes one exponent reference for its 64 lanes, then the sums of
