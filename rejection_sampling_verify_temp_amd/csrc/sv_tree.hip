@@ -21,7 +21,10 @@
 // (one round trip per round), through buffer resources, so the loads of a
 // round cost no address registers and no branches, and no round waits at a
 // workgroup barrier.  The walk is sequential per request; requests run in
-// parallel, one per compute unit at the usual batch sizes.
+// parallel, one per compute unit at the usual batch sizes.  A walk left
+// running alone is bound by its compute unit's arithmetic (~6 VALU slots per
+// element) more than by memory, so the inner loops keep per-element work to
+// the minimum: uniform tests for the row's end, fp32 sums per round.
 #include "sv_device.h"
 #include "sv_internal.h"
 
