@@ -88,6 +88,14 @@ def test_config_parity(svlib, cfg):
         check(svlib, w, seed=12345, offset=7)
 
 
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_config_second_stream(svlib, cfg):
+    """The two largest workloads again at another (seed, offset): other
+    uniforms, so other rejection positions and draws."""
+    w = synth.make_config(cfg, device="cuda")
+    check(svlib, w, seed=777, offset=11)
+
+
 @pytest.mark.parametrize("offset", range(12))
 def test_config0_many_offsets(svlib, offset):
     w = synth.make_config(0)
