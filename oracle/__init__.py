@@ -29,14 +29,15 @@ FLAG_BAD_DRAFT_ID, FLAG_BAD_NUM_DRAFTS, FLAG_ZERO_RESIDUAL = 1, 2, 4
 FLAG_BAD_TREE = 16
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+def build(force: bool = True, src: str = _SRC, out: str = _LIB, flags=()) -> str:
     """Compile the oracle's C source into a shared library with gcc
-    (-O2, no fast-math)."""
+    (-O2, no fast-math); `flags` are extra gcc options (the tests build
+    sanitizer and planted-mistake copies this way)."""
     if force or not os.path.exists(out):
         tmp = out + ".tmp%d" % os.getpid()
         subprocess.check_call(
             ["gcc", "-std=gnu11", "-O2", "-fPIC", "-shared", "-Wall",
-             "-Werror", src, "-o", tmp, "-lm"])
+             "-Werror", *flags, src, "-o", tmp, "-lm"])
         os.replace(tmp, out)
     return out
 
@@ -64,6 +65,17 @@ def open_library(path: str):
     lib.svo_residual.restype = None
     lib.svo_draw.argtypes = [P, i32, dbl, P]
     lib.svo_draw.restype = i32
+    lib.svo_draw_interval.argtypes = [P, i32, i32, P, P]
+    lib.svo_draw_interval.restype = dbl
+    lib.svo_verify_path.argtypes = [i32, i32, i32, P, i32, P, i32, i32, P, i32, flt, P, P,
+                                    i32, i32, P, P, P, P, P]
+    lib.svo_verify_path.restype = u32
+    lib.svo_verify_typical_path.argtypes = [i32, i32, i32, P, P, i32, flt, dbl, i32, P, i32,
+                                            i32, P, P, P, P, P]
+    lib.svo_verify_typical_path.restype = u32
+    lib.svo_verify_tree_path.argtypes = [i32, i32, i32, P, i32, P, i32, P, P, i32, flt, P, P,
+                                         i32, P, i32, P, P, P, P, P]
+    lib.svo_verify_tree_path.restype = u32
     common = [i32, i32, i32, i32, P, i32, P, i32, P, P, P, P]
     lib.svo_verify_with_uniforms.argtypes = common + [P, P] + [P] * 6
     lib.svo_verify_with_uniforms.restype = u32
@@ -165,6 +177,25 @@ def draw(r, u):
     return int(y), m.value
 
 
+def draw_interval(r, y):
+    """(lo, hi, mass) of token y in the inverse CDF of the unnormalized law
+    r: u selects y iff lo <= u < hi; mass = r_y / sum(r)."""
+    r = np.ascontiguousarray(r, dtype=np.float64)
+    lo, hi = ctypes.c_double(), ctypes.c_double()
+    m = _load().svo_draw_interval(_ptr(r), r.size, int(y), ctypes.byref(lo),
+                                  ctypes.byref(hi))
+    return lo.value, hi.value, float(m)
+
+
+def row_f64(a, idx):
+    """Row idx (a tuple of leading indices) of a float32 or bf16-bits array
+    as float64: the input conversion the oracle makes."""
+    row = np.asarray(a[idx])
+    if row.dtype == np.uint16:
+        row = (row.astype(np.uint32) << 16).view(np.float32)
+    return row.astype(np.float64)
+
+
 def _dtype_code(a):
     if a.dtype == np.float32:
         return F32
@@ -217,9 +248,14 @@ def verify(target, draft, draft_ids, num_drafts, temperatures, *,
         ur = np.ascontiguousarray(u_rec, dtype=np.float64).reshape(B, K + 1)
         flags = lib.svo_verify_with_uniforms(*head, _ptr(ua), _ptr(ur), *tail)
     else:
+        ua = ur = None
         flags = lib.svo_verify(*head, int(seed), int(offset), *tail)
+    call = dict(kind="verify", target=target, draft=draft, draft_ids=ids,
+                num_drafts=nd, temperatures=temps, draft_mode=mode,
+                draft_is_probs=bool(draft_is_probs), seed=int(seed),
+                offset=int(offset), u_acc=ua, u_rec=ur)
     return dict(tokens=tokens, num_accepted=nacc, p=p, q=q, margin_acc=macc,
-                margin_rec=mrec, flags=int(flags))
+                margin_rec=mrec, flags=int(flags), call=call)
 
 
 def draft_uniform(seed, offset, b, j):
@@ -247,7 +283,9 @@ def draft_sample(draft, num_drafts, temperatures, *, seed=0, offset=0,
         B, K, V, _dtype_code(draft), _ptr(draft), _ptr(nd), _ptr(temps),
         int(seed), int(offset), _ptr(ids),
         _ptr(q) if diagnostics else None, _ptr(margin) if diagnostics else None)
-    return dict(ids=ids, q=q, margin=margin, flags=int(flags))
+    call = dict(kind="draft_sample", draft=draft, num_drafts=nd,
+                temperatures=temps, seed=int(seed), offset=int(offset))
+    return dict(ids=ids, q=q, margin=margin, flags=int(flags), call=call)
 
 
 def ngram_propose(context, lens, *, min_n, max_n, k, max_model_len):
@@ -285,8 +323,11 @@ def verify_typical(target, draft_ids, num_drafts, temperatures, *, eps, top_k=0,
         B, K, V, _dtype_code(target), _ptr(target), _ptr(ids), _ptr(nd), _ptr(temps),
         float(eps), int(top_k), int(seed), int(offset), _ptr(tokens), _ptr(nacc),
         _ptr(p) if d else None, _ptr(macc) if d else None, _ptr(mrec) if d else None)
+    call = dict(kind="typical", target=target, draft_ids=ids, num_drafts=nd,
+                temperatures=temps, eps=float(eps), top_k=int(top_k),
+                seed=int(seed), offset=int(offset))
     return dict(tokens=tokens, num_accepted=nacc, p=p, q=np.ones_like(p),
-                margin_acc=macc, margin_rec=mrec, flags=int(flags))
+                margin_acc=macc, margin_rec=mrec, flags=int(flags), call=call)
 
 
 def verify_tree(target, draft, tokens, parents, num_nodes, temperatures, *, seed=0,
@@ -316,5 +357,111 @@ def verify_tree(target, draft, tokens, parents, num_nodes, temperatures, *, seed
         int(bool(draft_is_probs)), _ptr(tok), _ptr(par),
         _ptr(nn), _ptr(temps), int(seed), int(offset), _ptr(out), _ptr(nacc), _ptr(last),
         _ptr(macc), _ptr(mrec))
+    call = dict(kind="tree", target=target, draft=draft, tokens=tok, parents=par,
+                num_nodes=nn, temperatures=temps, draft_is_probs=bool(draft_is_probs),
+                seed=int(seed), offset=int(offset))
     return dict(tokens=out, num_accepted=nacc, last_node=last, margin_acc=macc,
-                margin_rec=mrec, flags=int(flags))
+                margin_rec=mrec, flags=int(flags), call=call)
+
+
+# --------------------------------------------------------------------------
+# Evaluation along a given path (checks of flagged requests)
+# --------------------------------------------------------------------------
+def _request_uniforms(call, b, n):
+    """u_acc, u_rec [n] of request b of a recorded call."""
+    if call.get("u_acc") is not None:
+        return (np.ascontiguousarray(call["u_acc"][b], dtype=np.float64),
+                np.ascontiguousarray(call["u_rec"][b], dtype=np.float64))
+    ua, ur = np.empty(n), np.empty(n)
+    for j in range(n):
+        ua[j], ur[j] = uniforms(call["seed"], call["offset"], b, j)
+    return ua, ur
+
+
+def _path_result(acc, margin, tok, mrec, out_y, flags):
+    return dict(accept=acc, margin=margin, token=int(tok.value),
+                margin_rec=float(mrec.value), lo=float(out_y[0]), hi=float(out_y[1]),
+                mass=float(out_y[2]), u=float(out_y[3]), flags=int(flags))
+
+
+def verify_path(ref, b, n_path, y):
+    """Request b of an oracle.verify() (or verify_typical()) result
+    evaluated along the path "n_path drafts accepted, then token y emitted
+    at position n_path".  Returns a dict: accept / margin [K] (the oracle's
+    decision and |u - threshold| at every position the path decides, NaN
+    elsewhere), token / margin_rec (the oracle's own emitted token at n_path
+    and its draw margin), lo / hi / mass / u (where y sits in that draw's
+    law: u selects y iff lo <= u < hi) and flags."""
+    c = ref["call"]
+    if c["kind"] == "typical":
+        return verify_typical_path(ref, b, n_path, y)
+    t = np.ascontiguousarray(c["target"][b])
+    K = t.shape[0] - 1
+    V = t.shape[1]
+    d = None if c["draft"] is None else np.ascontiguousarray(c["draft"][b])
+    onehot = c["draft_mode"] is not None and int(c["draft_mode"][b]) != 0
+    ua, ur = _request_uniforms(c, b, K + 1)
+    ids = np.ascontiguousarray(c["draft_ids"][b], dtype=np.int32)
+    acc, margin = np.empty(K), np.empty(K)
+    tok, mrec, out_y = ctypes.c_int32(), ctypes.c_double(), np.empty(4)
+    flags = _load().svo_verify_path(
+        K, V, _dtype_code(t), _ptr(t), _dtype_code(d) if d is not None else F32, _ptr(d),
+        int(c["draft_is_probs"]), int(onehot), _ptr(ids), int(c["num_drafts"][b]),
+        float(c["temperatures"][b]), _ptr(ua), _ptr(ur), int(n_path), int(y), _ptr(acc),
+        _ptr(margin), ctypes.byref(tok), ctypes.byref(mrec), _ptr(out_y))
+    return _path_result(acc, margin, tok, mrec, out_y, flags)
+
+
+def verify_typical_path(ref, b, n_path, y):
+    """verify_path for a verify_typical() result (margin = |p(x) - eps|, or
+    +inf where the rank decides)."""
+    c = ref["call"]
+    t = np.ascontiguousarray(c["target"][b])
+    K = t.shape[0] - 1
+    V = t.shape[1]
+    _, ur = _request_uniforms(c, b, K + 1)
+    ids = np.ascontiguousarray(c["draft_ids"][b], dtype=np.int32)
+    acc, margin = np.empty(K), np.empty(K)
+    tok, mrec, out_y = ctypes.c_int32(), ctypes.c_double(), np.empty(4)
+    flags = _load().svo_verify_typical_path(
+        K, V, _dtype_code(t), _ptr(t), _ptr(ids), int(c["num_drafts"][b]),
+        float(c["temperatures"][b]), c["eps"], c["top_k"], _ptr(ur), int(n_path), int(y),
+        _ptr(acc), _ptr(margin), ctypes.byref(tok), ctypes.byref(mrec), _ptr(out_y))
+    return _path_result(acc, margin, tok, mrec, out_y, flags)
+
+
+def verify_tree_path(ref, b, path, y):
+    """Request b of an oracle.verify_tree() result evaluated along the walk
+    `path` (node 0 first, then the accepted nodes in order) with token y
+    emitted at its last node.  Returns a dict: tests [k, 4] (child tested,
+    the walk's outcome 1/0, the oracle's decision 1/0, |u - ratio|; None if
+    the path is not a walk of the tree), token / margin_rec / lo / hi / mass
+    / u as in verify_path, and flags."""
+    c = ref["call"]
+    t = np.ascontiguousarray(c["target"][b])
+    N, V = t.shape
+    d = None if c["draft"] is None else np.ascontiguousarray(c["draft"][b])
+    ua, ur = _request_uniforms(c, b, N)
+    path = np.ascontiguousarray(path, dtype=np.int32)
+    tests = np.empty((N, 4))
+    nt = ctypes.c_int()
+    tok, mrec, out_y = ctypes.c_int32(), ctypes.c_double(), np.empty(4)
+    flags = _load().svo_verify_tree_path(
+        N, V, _dtype_code(t), _ptr(t), _dtype_code(d) if d is not None else F32, _ptr(d),
+        int(c["draft_is_probs"]), _ptr(c["tokens"][b]), _ptr(c["parents"][b]),
+        int(c["num_nodes"][b]), float(c["temperatures"][b]), _ptr(ua), _ptr(ur),
+        len(path) - 1, _ptr(path), int(y), _ptr(tests), ctypes.byref(nt), ctypes.byref(tok),
+        ctypes.byref(mrec), _ptr(out_y))
+    res = _path_result(None, None, tok, mrec, out_y, flags)
+    del res["accept"], res["margin"]
+    res["tests"] = None if nt.value < 0 else tests[:nt.value].copy()
+    return res
+
+
+def draft_sample_interval(ref, b, j, y):
+    """Where token y sits in the law of row (b, j) of an oracle.draft_sample()
+    result: (lo, hi, mass, u), u selecting y iff lo <= u < hi."""
+    c = ref["call"]
+    q = softmax(row_f64(c["draft"], (b, j)), float(c["temperatures"][b]))
+    lo, hi, mass = draw_interval(q, y)
+    return lo, hi, mass, draft_uniform(c["seed"], c["offset"], b, j)

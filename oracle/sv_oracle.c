@@ -208,6 +208,23 @@ int svo_draw(const double *r, int V, double u, double *margin) {
   return y;
 }
 
+/* Where token y sits in the inverse CDF of svo_draw: with the same running
+ * sums C and total S, *lo = C_{y-1} / S and *hi = C_y / S, so a uniform u
+ * selects y iff lo <= u < hi (u * S against C).  Returns r_y / S; for y
+ * outside [0, V) or S not positive returns 0 and sets lo = hi = NaN. */
+double svo_draw_interval(const double *r, int V, int y, double *lo,
+                         double *hi) {
+  double S = sum_compensated(r, V);
+  *lo = NAN;
+  *hi = NAN;
+  if (!(S > 0.0) || y < 0 || y >= V) return 0.0;
+  double C = 0.0;
+  for (int i = 0; i < y; ++i) C += r[i];
+  *lo = C / S;
+  *hi = (C + r[y]) / S;
+  return r[y] / S;
+}
+
 /* ------------------------------------------------------------------------ */
 /* The verify step, driven by explicit uniforms.                              */
 /*                                                                          */
@@ -762,6 +779,334 @@ uint32_t svo_verify_tree(int B, int N, int V, int target_dtype,
     if (out_margin_acc) out_margin_acc[b] = margin_acc;
     if (out_margin_rec) out_margin_rec[b] = margin_rec;
   }
+  free(l); free(p); free(q); free(r); free(removed);
+  return flags;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Outputs along a given path.  A decision whose uniform lies within        */
+/* rounding of its threshold, or a draw within rounding of a CDF boundary,  */
+/* may go the other way in an implementation that rounds differently.  Its  */
+/* output then follows another path through the same method: the functions  */
+/* below evaluate the method along a path the caller names, with the same   */
+/* arithmetic as the walks above, so that every step of that output can be  */
+/* checked (each step either agrees with this arithmetic or lies within the */
+/* caller's band of its threshold).  They decide nothing themselves.        */
+/* ------------------------------------------------------------------------ */
+
+/* Shared output of a path's emitted token: the oracle's own token there and
+ * its draw margin, and where a given token y sits in that draw's law. */
+static void path_emit(const double *r, int V, double u, int y, int32_t *tok,
+                      double *margin_rec, double *out_y) {
+  double m = 0.0;
+  *tok = svo_draw(r, V, u, &m);
+  *margin_rec = m;
+  double lo, hi;
+  const double mass = svo_draw_interval(r, V, y, &lo, &hi);
+  out_y[0] = lo;
+  out_y[1] = hi;
+  out_y[2] = mass;
+  out_y[3] = u;
+}
+
+/* The verify step of one request along the path "the first n_path drafts
+ * accepted, then the token at position n_path emitted": the correction
+ * drawn after a rejection at n_path when n_path < n_b, else the bonus token.
+ *
+ *   target [K+1][V], draft [K][V] or NULL (one-hot; also when onehot != 0),
+ *   draft_ids [K], num_drafts (clamped into [0, K]), T, u_acc / u_rec [K+1]
+ *   as in svo_verify_with_uniforms; 0 <= n_path <= n_b.
+ *   out_accept[j], out_margin[j], j < K: for every position the path
+ *     decides (j <= n_path and j < n_b) the oracle's decision there (1
+ *     accept, 0 reject) and |u - ratio| (+inf for greedy); NaN elsewhere.
+ *   *out_tok, *out_margin_rec: the oracle's emitted token at n_path and its
+ *     draw margin (greedy: the lowest argmax, +inf).
+ *   out_y[4] for token y: (lo, hi, mass, u) of y in that draw's law (see
+ *     svo_draw_interval) and the draw uniform; greedy: NaN.
+ * Returns the SVO_FLAG_* conditions met on the path. */
+uint32_t svo_verify_path(int K, int V, int target_dtype, const void *target,
+                         int draft_dtype, const void *draft,
+                         int draft_is_probs, int onehot,
+                         const int32_t *draft_ids, int num_drafts, float T,
+                         const double *u_acc, const double *u_rec, int n_path,
+                         int y, double *out_accept, double *out_margin,
+                         int32_t *out_tok, double *out_margin_rec,
+                         double *out_y) {
+  uint32_t flags = 0;
+  int n = num_drafts;
+  if (n < 0 || n > K) {
+    flags |= SVO_FLAG_BAD_NUM_DRAFTS;
+    n = n < 0 ? 0 : K;
+  }
+  const int sampling = svo_is_sampling(T);
+  const int mode = (draft == NULL || onehot) ? SVO_MODE_ONEHOT : SVO_MODE_PROB;
+  for (int j = 0; j < K; ++j) out_accept[j] = out_margin[j] = NAN;
+  for (int i = 0; i < 4; ++i) out_y[i] = NAN;
+  *out_tok = -1;
+  *out_margin_rec = NAN;
+  if (n_path < 0 || n_path > n) return flags;
+  double *tl = malloc(sizeof(double) * (size_t)V);
+  double *dl = malloc(sizeof(double) * (size_t)V);
+  double *p = malloc(sizeof(double) * (size_t)V);
+  double *q = malloc(sizeof(double) * (size_t)V);
+  double *r = malloc(sizeof(double) * (size_t)V);
+
+  /* every decision the path makes: accepts at 0..n_path-1, the stop at n_path */
+  for (int j = 0; j <= n_path && j < n; ++j) {
+    const int x = draft_ids[j];
+    const int valid = x >= 0 && x < V;
+    if (!valid) flags |= SVO_FLAG_BAD_DRAFT_ID;
+    load_row(target, target_dtype, (size_t)j, V, tl);
+    if (!sampling) {
+      out_accept[j] = valid && tl[x] == tl[svo_argmax(tl, V)];
+      out_margin[j] = INFINITY;
+      continue;
+    }
+    svo_softmax(tl, V, (double)T, p);
+    double px = valid ? p[x] : 0.0, qx = 1.0;
+    if (mode == SVO_MODE_PROB) {
+      load_row(draft, draft_dtype, (size_t)j, V, dl);
+      if (draft_is_probs)
+        memcpy(q, dl, sizeof(double) * (size_t)V);
+      else
+        svo_softmax(dl, V, (double)T, q);
+      qx = valid ? q[x] : 0.0;
+    }
+    const double ratio = valid ? svo_accept_ratio(px, qx) : 0.0;
+    out_accept[j] = u_acc[j] < ratio;
+    out_margin[j] = fabs(u_acc[j] - ratio);
+  }
+
+  /* the emitted token at n_path */
+  load_row(target, target_dtype, (size_t)n_path, V, tl);
+  if (!sampling) {
+    *out_tok = svo_argmax(tl, V);
+    *out_margin_rec = INFINITY;
+  } else {
+    svo_softmax(tl, V, (double)T, p);
+    if (n_path < n) {
+      if (mode == SVO_MODE_PROB) {
+        load_row(draft, draft_dtype, (size_t)n_path, V, dl);
+        if (draft_is_probs)
+          memcpy(q, dl, sizeof(double) * (size_t)V);
+        else
+          svo_softmax(dl, V, (double)T, q);
+      }
+      svo_residual(p, q, mode, draft_ids[n_path], V, r);
+    } else {
+      memcpy(r, p, sizeof(double) * (size_t)V);
+    }
+    if (!(sum_compensated(r, V) > 0.0)) { /* no residual mass: from p */
+      flags |= SVO_FLAG_ZERO_RESIDUAL;
+      memcpy(r, p, sizeof(double) * (size_t)V);
+      path_emit(r, V, u_rec[n_path], y, out_tok, out_margin_rec, out_y);
+      *out_margin_rec = 0.0;
+    } else {
+      path_emit(r, V, u_rec[n_path], y, out_tok, out_margin_rec, out_y);
+    }
+  }
+  free(tl); free(dl); free(p); free(q); free(r);
+  return flags;
+}
+
+/* Typical acceptance of one request along the path "n_path drafts
+ * accepted, then the token at n_path drawn from p_{n_path}" (see
+ * svo_verify_typical for the rule).  Arguments and outputs as in
+ * svo_verify_path, without draft rows; out_margin[j] is |p(x) - eps|, or
+ * +inf where the rank decides or the request is greedy. */
+uint32_t svo_verify_typical_path(int K, int V, int target_dtype,
+                                 const void *target, const int32_t *draft_ids,
+                                 int num_drafts, float T, double eps,
+                                 int top_k, const double *u_rec, int n_path,
+                                 int y, double *out_accept, double *out_margin,
+                                 int32_t *out_tok, double *out_margin_rec,
+                                 double *out_y) {
+  uint32_t flags = 0;
+  int n = num_drafts;
+  if (n < 0 || n > K) {
+    flags |= SVO_FLAG_BAD_NUM_DRAFTS;
+    n = n < 0 ? 0 : K;
+  }
+  const int sampling = svo_is_sampling(T);
+  for (int j = 0; j < K; ++j) out_accept[j] = out_margin[j] = NAN;
+  for (int i = 0; i < 4; ++i) out_y[i] = NAN;
+  *out_tok = -1;
+  *out_margin_rec = NAN;
+  if (n_path < 0 || n_path > n) return flags;
+  double *l = malloc(sizeof(double) * (size_t)V);
+  double *p = malloc(sizeof(double) * (size_t)V);
+  for (int j = 0; j <= n_path && j < n; ++j) {
+    const int x = draft_ids[j];
+    const int valid = x >= 0 && x < V;
+    if (!valid) flags |= SVO_FLAG_BAD_DRAFT_ID;
+    load_row(target, target_dtype, (size_t)j, V, l);
+    double margin = INFINITY;
+    int accept;
+    if (!sampling) {
+      accept = valid && l[x] == l[svo_argmax(l, V)];
+    } else {
+      svo_softmax(l, V, (double)T, p);
+      int above = 0;
+      if (valid)
+        for (int i = 0; i < V; ++i) above += l[i] > l[x];
+      const double px = valid ? p[x] : 0.0;
+      if (valid && above < top_k) {
+        accept = 1;
+      } else {
+        accept = valid && px > eps;
+        margin = fabs(px - eps);
+      }
+    }
+    out_accept[j] = accept;
+    out_margin[j] = margin;
+  }
+  load_row(target, target_dtype, (size_t)n_path, V, l);
+  if (!sampling) {
+    *out_tok = svo_argmax(l, V);
+    *out_margin_rec = INFINITY;
+  } else {
+    svo_softmax(l, V, (double)T, p);
+    path_emit(p, V, u_rec[n_path], y, out_tok, out_margin_rec, out_y);
+  }
+  free(l);
+  free(p);
+  return flags;
+}
+
+/* Token-tree verification of one request along a given walk: path[0] = 0
+ * (the root), path[1..a] the accepted nodes in order (each a child of the
+ * one before), and the emitted token drawn at path[a] after every child of
+ * path[a] was rejected.  At each path node the children are tested in index
+ * order as in svo_verify_tree: those before the next path node are
+ * rejected, the next path node is accepted, and at the last node all are
+ * rejected; the law after each rejection is updated as there.
+ *
+ *   target [N][V], draft [N][V] or NULL, tokens / parents [N], num_nodes
+ *   (clamped into [1, N]), T; ua[i] / ur[i] = words 0 / 1 of the Philox
+ *   block of node index i (ua[c - 1] tests child c, ur[v] draws at v).
+ *   out_tests[4 k + 0..3] for the k-th test on the walk: the child tested,
+ *     the walk's outcome there (1 accepted, 0 rejected), the oracle's
+ *     decision, and |u - ratio| (+inf for greedy); *n_tests = k.
+ *   *out_tok, *out_margin_rec, out_y[4]: as in svo_verify_path, for the
+ *     draw at path[a].
+ * Returns the SVO_FLAG_* conditions met on the walk, and -1 in *n_tests
+ * for a path that is not a walk of this tree. */
+uint32_t svo_verify_tree_path(int N, int V, int target_dtype,
+                              const void *target, int draft_dtype,
+                              const void *draft, int draft_is_probs,
+                              const int32_t *tokens, const int32_t *parents,
+                              int num_nodes, float T, const double *ua,
+                              const double *ur, int a, const int32_t *path,
+                              int y, double *out_tests, int *n_tests,
+                              int32_t *out_tok, double *out_margin_rec,
+                              double *out_y) {
+  uint32_t flags = 0;
+  int n = num_nodes;
+  if (n < 1 || n > N) {
+    flags |= SVO_FLAG_BAD_NUM_DRAFTS;
+    n = n < 1 ? 1 : N;
+  }
+  *n_tests = 0;
+  *out_tok = -1;
+  *out_margin_rec = NAN;
+  for (int i = 0; i < 4; ++i) out_y[i] = NAN;
+  if (a < 0 || a >= n || path[0] != 0) {
+    *n_tests = -1;
+    return flags;
+  }
+  for (int k = 1; k <= a; ++k)
+    if (path[k] <= path[k - 1] || path[k] >= n || parents[path[k]] != path[k - 1]) {
+      *n_tests = -1;
+      return flags;
+    }
+  const int sampling = svo_is_sampling(T);
+  const int onehot = draft == NULL;
+  double *l = malloc(sizeof(double) * (size_t)V);
+  double *p = malloc(sizeof(double) * (size_t)V);
+  double *q = malloc(sizeof(double) * (size_t)V);
+  double *r = malloc(sizeof(double) * (size_t)V);
+  int *removed = malloc(sizeof(int) * (size_t)V);
+  int nt = 0;
+  for (int k = 0; k <= a; ++k) {
+    const int v = path[k];
+    const int next = k < a ? path[k + 1] : -1;
+    load_row(target, target_dtype, (size_t)v, V, l);
+    if (sampling) svo_softmax(l, V, (double)T, p);
+    if (sampling && !onehot) {
+      load_row(draft, draft_dtype, (size_t)v, V, q);
+      if (!draft_is_probs) svo_softmax(q, V, (double)T, q);
+    }
+    double ck = 0.0, Zk = 1.0;
+    int nrej = 0;
+    for (int i = 0; i < V; ++i) removed[i] = 0;
+    for (int c = v + 1; c < n; ++c) {
+      if (parents[c] != v) continue;
+      const int x = tokens[c];
+      const int valid = x >= 0 && x < V;
+      if (!valid) flags |= SVO_FLAG_BAD_DRAFT_ID;
+      int accept;
+      double m = INFINITY;
+      if (!sampling) {
+        accept = valid && l[x] == l[svo_argmax(l, V)];
+      } else {
+        double ratio = 0.0;
+        if (valid && onehot) {
+          ratio = removed[x] ? 0.0 : p[x] / Zk;
+        } else if (valid) {
+          const double num = p[x] - ck * q[x];
+          ratio = svo_accept_ratio((num > 0.0 ? num : 0.0) / Zk, q[x]);
+        }
+        accept = ua[c - 1] < ratio;
+        m = fabs(ua[c - 1] - ratio);
+      }
+      out_tests[4 * nt + 0] = c;
+      out_tests[4 * nt + 1] = c == next;
+      out_tests[4 * nt + 2] = accept;
+      out_tests[4 * nt + 3] = m;
+      nt++;
+      if (c == next) break; /* the walk moves on to the next path node */
+      nrej++;
+      if (sampling && onehot) {
+        if (valid && !removed[x]) {
+          removed[x] = 1;
+          Zk -= p[x];
+        }
+      } else if (sampling) {
+        ck += Zk;
+        for (int i = 0; i < V; ++i) {
+          const double d = p[i] - ck * q[i];
+          r[i] = d > 0.0 ? d : 0.0;
+        }
+        Zk = sum_compensated(r, V);
+      }
+    }
+    if (k < a) continue;
+    /* the draw at the last node */
+    if (!sampling) {
+      *out_tok = svo_argmax(l, V);
+      *out_margin_rec = INFINITY;
+    } else {
+      if (onehot) {
+        for (int i = 0; i < V; ++i) r[i] = removed[i] ? 0.0 : p[i];
+      } else if (nrej > 0) {
+        for (int i = 0; i < V; ++i) {
+          const double d = p[i] - ck * q[i];
+          r[i] = d > 0.0 ? d : 0.0;
+        }
+      } else {
+        memcpy(r, p, sizeof(double) * (size_t)V);
+      }
+      if (!(sum_compensated(r, V) > 0.0)) { /* no residual mass: from p */
+        flags |= SVO_FLAG_ZERO_RESIDUAL;
+        memcpy(r, p, sizeof(double) * (size_t)V);
+        path_emit(r, V, ur[v], y, out_tok, out_margin_rec, out_y);
+        *out_margin_rec = 0.0;
+      } else {
+        path_emit(r, V, ur[v], y, out_tok, out_margin_rec, out_y);
+      }
+    }
+  }
+  *n_tests = nt;
   free(l); free(p); free(q); free(r); free(removed);
   return flags;
 }

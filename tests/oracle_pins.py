@@ -250,7 +250,7 @@ def _chisq_ok(counts, probs, alpha=1e-3):
     return scipy.stats.chisquare(obs, ex).pvalue > alpha
 
 
-def check_monte_carlo(B=1 << 19, V=8, T=0.7, seed=21):
+def check_monte_carlo(B=1 << 20, V=8, T=0.7, seed=21):
     rng = np.random.default_rng(seed)
     K = 2
     lt = rng.normal(0, 2, (K + 1, V)).astype(np.float32)
@@ -709,6 +709,375 @@ def check_tree_flags():
     assert r["flags"] & oracle.FLAG_BAD_NUM_DRAFTS
 
 
+# --------------------------------------------------------------------------
+# Margins: the distance of each decision's uniform to its threshold and of
+# each draw's u * S to the chosen token's CDF boundaries, recomputed with
+# numpy / scipy.  They decide which requests the parity rule lets differ,
+# so they are pinned against an independent computation, not only used.
+# --------------------------------------------------------------------------
+def _np_draw(r, u):
+    """numpy's inverse CDF of the unnormalized law r: the token
+    searchsorted(cumsum(r), u * S, 'right') picks, the distance of u * S to
+    its nearer boundary over S, and its boundaries (C_{y-1}, C_y) over S.
+    Past the end (rounding): the last token with mass, margin 0."""
+    C = np.cumsum(r)
+    S = C[-1]
+    theta = u * S
+    y = int(np.searchsorted(C, theta, side="right"))
+    if y >= len(r):
+        y = int(np.flatnonzero(r > 0)[-1])
+        return y, 0.0, (C[y - 1] if y else 0.0) / S, C[y] / S
+    lo = C[y - 1] if y else 0.0
+    return y, min(theta - lo, C[y] - theta) / S, lo / S, C[y] / S
+
+
+def check_draw_margin_vs_library(cases=400, seed=111):
+    """svo_draw's token and margin, and svo_draw_interval's (lo, hi, mass),
+    against numpy's cumulative sum and searchsorted on random laws with
+    zeros and totals far from 1."""
+    rng = np.random.default_rng(seed)
+    for c in range(cases):
+        V = int(rng.integers(1, 60))
+        r = rng.random(V) * (rng.random(V) < 0.7) * float(rng.choice([1e-3, 0.3, 1.0, 40.0]))
+        if not r.sum() > 0:
+            r[int(rng.integers(V))] = 0.25
+        u = float(rng.integers(0, 1 << 24)) / 2.0 ** 24
+        y, m = oracle.draw(r, u)
+        yn, mn, lo, hi = _np_draw(r, u)
+        if mn > 1e-12:
+            assert y == yn, (c, y, yn)
+        assert abs(m - mn) <= 1e-12, (c, m, mn)
+        lo_o, hi_o, mass = oracle.draw_interval(r, yn)
+        assert abs(lo_o - lo) <= 1e-12 and abs(hi_o - hi) <= 1e-12, (c, lo_o, lo, hi_o, hi)
+        assert abs(mass - r[yn] / r.sum()) <= 1e-12, (c, mass)
+        z = int(rng.integers(V))
+        lo_z, hi_z, mass_z = oracle.draw_interval(r, z)
+        C = np.cumsum(r)
+        assert abs(lo_z - (C[z - 1] if z else 0.0) / C[-1]) <= 1e-12
+        assert abs(hi_z - C[z] / C[-1]) <= 1e-12 and abs(mass_z - r[z] / C[-1]) <= 1e-12
+    lo, hi, m = oracle.draw_interval(np.array([0.5, 0.5]), 2)
+    assert m == 0.0 and np.isnan(lo) and np.isnan(hi)
+
+
+def _np_uniforms(seed, offset, b, j):
+    w = _numpy_block([offset, b, j, 0], [seed, 0])
+    return (int(w[0]) >> 40) / 2.0 ** 24, (int(w[1]) >> 40) / 2.0 ** 24
+
+
+def _np_laws(h, b, j, T, need_q=True):
+    """scipy's p_j and q_j of request b (q None for one-hot, or when not
+    needed), from the raw input rows."""
+    p = scipy.special.softmax(oracle.row_f64(h["target"], (b, j)) / T)
+    onehot = h["draft"] is None or (h["draft_mode"] is not None and h["draft_mode"][b] != 0)
+    if onehot or not need_q:
+        return p, None
+    d = oracle.row_f64(h["draft"], (b, j))
+    return p, (d if h["draft_is_probs"] else scipy.special.softmax(d / T))
+
+
+def _np_request(h, b, seed, offset, n_path=None):
+    """The verify step of one sampling request with numpy / scipy: the
+    decisions [(accept, |u - ratio|)] of the walk (to the first rejection, or
+    along the path with n_path accepts) and the emitted draw (token, margin,
+    lo, hi, law) at its end; None where a value lies within 1e-12 of a
+    threshold (rounding could take either side)."""
+    K = h["target"].shape[1] - 1
+    T = float(np.float32(h["temperatures"][b]))
+    n = int(np.clip(h["num_drafts"][b], 0, K))
+    dec, j = [], 0
+    while j < n:
+        p, q = _np_laws(h, b, j, T)
+        x = int(h["draft_ids"][b, j])
+        ua, _ = _np_uniforms(seed, offset, b, j)
+        if not 0 <= x < p.size:
+            ratio = 0.0
+        elif q is None:
+            ratio = p[x]
+        else:
+            ratio = p[x] / q[x] if q[x] > 0 else (np.inf if p[x] > 0 else 0.0)
+        m = abs(ua - ratio)
+        if m < 1e-12:
+            return None
+        dec.append((ua < ratio, m))
+        stop = (not ua < ratio) if n_path is None else j == n_path
+        if stop:
+            break
+        j += 1
+    if n_path is not None:
+        j = n_path
+    p, q = _np_laws(h, b, j, T, need_q=j < n)
+    if j < n:
+        x = int(h["draft_ids"][b, j])
+        if q is None:
+            r = p.copy()
+            if 0 <= x < p.size:
+                r[x] = 0.0
+        else:
+            r = np.maximum(p - q, 0.0)
+    else:
+        r = p
+    if not r.sum() > 0:
+        return None
+    _, ur = _np_uniforms(seed, offset, b, j)
+    y, m, lo, hi = _np_draw(r, ur)
+    if m < 1e-11:
+        return None
+    return dec, (y, m, lo, hi, r)
+
+
+def _margin_batches(seed):
+    import torch
+    import synth
+    kws = [dict(temps=(1.0, 0.6, 1.5), n_mode="ragged", corr=0.8),
+           dict(temps=(0.8,), onehot_frac=0.5, n_mode="ragged"),
+           dict(temps=(1.2, 0.9), dtype=torch.bfloat16, corr=0.95),
+           dict(temps=(0.9, 1.1), draft_is_probs=True, n_mode="ragged", corr=0.7)]
+    for i, kw in enumerate(kws):
+        yield i, synth.make_random(24, 4, 120, seed=seed + i, **kw).host_arrays()
+
+
+def check_margins_vs_library(seed=121):
+    """Every decision margin |u - p(x)/q(x)| the oracle reports and its
+    draw margin, against scipy's softmax, numpy's Philox and numpy's
+    inverse CDF (probabilistic, one-hot, probability and bf16 drafts)."""
+    checked = 0
+    for i, h in _margin_batches(seed):
+        r = oracle.verify(h["target"], h["draft"], h["draft_ids"], h["num_drafts"],
+                          h["temperatures"], draft_mode=h["draft_mode"],
+                          draft_is_probs=h["draft_is_probs"], seed=i, offset=5 + i)
+        for b in range(h["target"].shape[0]):
+            got = _np_request(h, b, i, 5 + i)
+            if got is None:
+                continue
+            dec, (y, m, lo, hi, _) = got
+            for j, (acc, mj) in enumerate(dec):
+                mo = r["margin_acc"][b, j]
+                assert abs(mo - mj) <= 1e-12 * max(1.0, mj), (i, b, j, mo, mj)
+            assert np.all(np.isnan(r["margin_acc"][b, len(dec):])), (i, b)
+            assert int(r["num_accepted"][b]) == sum(a for a, _ in dec), (i, b)
+            a = int(r["num_accepted"][b])
+            assert int(r["tokens"][b, a]) == y, (i, b, r["tokens"][b], y)
+            assert abs(r["margin_rec"][b] - m) <= 1e-11, (i, b, r["margin_rec"][b], m)
+            checked += 1
+    assert checked > 60, checked
+
+
+def check_forced_path_vs_library(seed=131):
+    """oracle.verify_path along paths the walk did not take (any count of
+    accepts up to n_b): the decisions and margins on the path, the emitted
+    draw there, and where another token sits in that draw's law, against
+    scipy / numpy."""
+    rng = np.random.default_rng(seed)
+    checked = 0
+    for i, h in _margin_batches(seed):
+        K = h["target"].shape[1] - 1
+        r = oracle.verify(h["target"], h["draft"], h["draft_ids"], h["num_drafts"],
+                          h["temperatures"], draft_mode=h["draft_mode"],
+                          draft_is_probs=h["draft_is_probs"], seed=i, offset=9)
+        for b in range(h["target"].shape[0]):
+            n = int(np.clip(h["num_drafts"][b], 0, K))
+            n_path = int(rng.integers(0, n + 1))
+            z = int(rng.integers(0, h["target"].shape[2]))
+            ev = oracle.verify_path(r, b, n_path, z)
+            got = _np_request(h, b, i, 9, n_path=n_path)
+            if got is None:
+                continue
+            dec, (y, m, lo, hi, law) = got
+            assert len(dec) == min(n_path + 1, n), (i, b)
+            for j, (acc, mj) in enumerate(dec):
+                assert ev["accept"][j] == acc, (i, b, j)
+                assert abs(ev["margin"][j] - mj) <= 1e-12 * max(1.0, mj), (i, b, j)
+            assert np.all(np.isnan(ev["accept"][len(dec):]))
+            assert ev["token"] == y and abs(ev["margin_rec"] - m) <= 1e-11, (i, b, ev, y, m)
+            C = np.cumsum(law)
+            assert abs(ev["lo"] - (C[z - 1] if z else 0.0) / C[-1]) <= 1e-12, (i, b)
+            assert abs(ev["hi"] - C[z] / C[-1]) <= 1e-12, (i, b)
+            assert abs(ev["mass"] - law[z] / C[-1]) <= 1e-12, (i, b)
+            checked += 1
+    assert checked > 60, checked
+
+
+def check_typical_path_vs_library(cases=40, seed=141):
+    """oracle.verify_typical_path along any path: decisions by scipy's
+    softmax and numpy's ranks, the draw from p at the stop by numpy."""
+    rng = np.random.default_rng(seed)
+    for c in range(cases):
+        B, K, V = 3, int(rng.integers(1, 5)), int(rng.integers(2, 150))
+        t, ids, nd = _typical_case(rng, B, K, V)
+        temps = rng.choice([1.0, 0.6, 0.0], B).astype(np.float32)
+        eps, top_k = float(rng.choice([0.01, 0.05, 0.2])), int(rng.integers(0, 3))
+        r = oracle.verify_typical(t, ids, nd, temps, eps=eps, top_k=top_k, seed=c, offset=1)
+        for b in range(B):
+            n = int(nd[b])
+            n_path = int(rng.integers(0, n + 1))
+            z = int(rng.integers(0, V))
+            ev = oracle.verify_path(r, b, n_path, z)
+            T = float(temps[b])
+            for j in range(min(n_path + 1, n)):
+                row, x = t[b, j].astype(np.float64), int(ids[b, j])
+                if T == 0.0:
+                    assert ev["accept"][j] == (row[x] == row.max()) and np.isinf(ev["margin"][j])
+                    continue
+                p = scipy.special.softmax(row / T)
+                rank_ok = int(np.sum(row > row[x])) < top_k
+                assert ev["accept"][j] == (rank_ok or p[x] > eps), (c, b, j)
+                if not rank_ok:
+                    assert abs(ev["margin"][j] - abs(p[x] - eps)) <= 1e-12, (c, b, j)
+            row = t[b, n_path].astype(np.float64)
+            if T == 0.0:
+                assert ev["token"] == int(np.argmax(row))
+                continue
+            p = scipy.special.softmax(row / T)
+            _, u = _np_uniforms(c, 1, b, n_path)
+            y, m, lo, hi = _np_draw(p, u)
+            if m > 1e-11:
+                assert ev["token"] == y and abs(ev["margin_rec"] - m) <= 1e-11, (c, b)
+            C = np.cumsum(p)
+            assert abs(ev["lo"] - (C[z - 1] if z else 0.0) / C[-1]) <= 1e-12
+            assert abs(ev["hi"] - C[z] / C[-1]) <= 1e-12
+
+
+def check_tree_chain_probs_equals_verify(seed=151):
+    """The tree's probability-draft branch: a chain-shaped tree whose draft
+    rows are normalized q (draft_is_probs) reproduces the verify step with
+    draft_is_probs bit for bit, tokens, counts and margins."""
+    rng = np.random.default_rng(seed)
+    for c in range(6):
+        B, K, V = 16, int(rng.integers(1, 5)), int(rng.integers(2, 200))
+        t = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+        dl = t[:, :K] + rng.normal(0, 0.8, (B, K, V))
+        d = scipy.special.softmax(dl / 0.9, axis=-1).astype(np.float32)
+        ids = np.array([[rng.choice(V, p=d[b, j] / d[b, j].sum()) for j in range(K)]
+                        for b in range(B)], np.int32)
+        nd = rng.integers(0, K + 1, B).astype(np.int32)
+        temps = rng.choice([1.0, 0.7, 1.3], B).astype(np.float32)
+        ref = oracle.verify(t, d, ids, nd, temps, draft_is_probs=True, seed=c, offset=3)
+        tok, par, dt, nn = _chain_tree(t, d, ids, nd)
+        r = oracle.verify_tree(t, dt, tok, par, nn, temps, seed=c, offset=3, draft_is_probs=True)
+        assert np.array_equal(r["tokens"], ref["tokens"]), c
+        assert np.array_equal(r["num_accepted"], ref["num_accepted"]), c
+        for b in range(B):
+            m = ref["margin_acc"][b, :min(nd[b], ref["num_accepted"][b] + 1)]
+            assert r["margin_acc"][b] == (m.min() if m.size else np.inf), (c, b)
+            assert r["margin_rec"][b] == ref["margin_rec"][b], (c, b)
+
+
+def check_tree_path_chain_equals_verify_path(seed=161):
+    """oracle.verify_tree_path on a chain-shaped tree equals
+    oracle.verify_path (pinned above against scipy / numpy) for every
+    forced count of accepts: the same decisions, margins and draw."""
+    rng = np.random.default_rng(seed)
+    for c in range(4):
+        B, K, V = 8, int(rng.integers(1, 5)), int(rng.integers(2, 120))
+        t = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+        d = (t[:, :K] + rng.normal(0, 0.7, (B, K, V))).astype(np.float32)
+        ids = rng.integers(0, V, (B, K)).astype(np.int32)
+        nd = rng.integers(0, K + 1, B).astype(np.int32)
+        temps = rng.choice([1.0, 0.7, 0.0], B).astype(np.float32)
+        dd = None if c == 3 else d
+        ref = oracle.verify(t, dd, ids, nd, temps, seed=c, offset=2)
+        tok, par, dt, nn = _chain_tree(t, dd, ids, nd)
+        rt = oracle.verify_tree(t, dt, tok, par, nn, temps, seed=c, offset=2)
+        for b in range(B):
+            for n_path in range(int(nd[b]) + 1):
+                z = int(rng.integers(0, V))
+                ev = oracle.verify_path(ref, b, n_path, z)
+                et = oracle.verify_tree_path(rt, b, list(range(n_path + 1)), z)
+                tests = et["tests"]
+                assert tests is not None and len(tests) == min(n_path + 1, int(nd[b])), (c, b)
+                for j, (child, walk, orc, m) in enumerate(tests):
+                    assert child == j + 1 and walk == (j < n_path), (c, b, j)
+                    assert orc == ev["accept"][j] and (m == ev["margin"][j]), (c, b, j)
+                for key in ("token", "margin_rec", "lo", "hi", "mass", "u"):
+                    a1, a2 = et[key], ev[key]
+                    assert a1 == a2 or (np.isnan(a1) and np.isnan(a2)), (c, b, key, a1, a2)
+
+
+# --------------------------------------------------------------------------
+# Long statistical pins (run once, not for every planted mistake)
+# --------------------------------------------------------------------------
+def check_config0_chi_square(total=1 << 20, batch=4096, seed=171, threads=8):
+    """The distribution claim at the size the task states, on the B=1, K=4,
+    V=1000 workload's own rows: 2^20 verify steps, each with fresh drafts
+    x_j ~ q_j drawn by numpy, over distinct Philox counters (one offset per
+    batch of requests).  The first emitted token follows p_0 and, given an
+    acceptance at position 0, the second follows p_1 (chi-square, p > 1e-3);
+    the acceptance rate at position 0 equals sum_x min(p_0, q_0) within 4
+    sigma."""
+    from concurrent.futures import ThreadPoolExecutor
+    import synth
+    w = synth.make_config(0)
+    h = w.host_arrays()
+    K, V = w.K, w.V
+    T = float(h["temperatures"][0])
+    p = [scipy.special.softmax(h["target"][0, j].astype(np.float64) / T) for j in range(K + 1)]
+    q = [scipy.special.softmax(h["draft"][0, j].astype(np.float64) / T) for j in range(K)]
+    tgt = np.broadcast_to(h["target"][0], (batch, K + 1, V)).copy()
+    dft = np.broadcast_to(h["draft"][0], (batch, K, V)).copy()
+
+    def run(i):
+        rng = np.random.default_rng([seed, i])
+        ids = np.stack([rng.choice(V, batch, p=q[j]) for j in range(K)], 1).astype(np.int32)
+        r = oracle.verify(tgt, dft, ids, np.full(batch, K), np.full(batch, T, np.float32),
+                          seed=seed, offset=i, diagnostics=False)
+        acc0 = r["num_accepted"] >= 1
+        return (np.bincount(r["tokens"][:, 0], minlength=V),
+                np.bincount(r["tokens"][acc0, 1], minlength=V), int(acc0.sum()))
+
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(run, range(total // batch)))
+    first = sum(x[0] for x in parts)
+    second = sum(x[1] for x in parts)
+    n_acc0 = sum(x[2] for x in parts)
+    assert first.sum() == total
+    assert _chisq_ok(first, p[0]), "first emitted token vs p_0"
+    assert _chisq_ok(second, p[1]), "second emitted token vs p_1"
+    pa = np.minimum(p[0], q[0]).sum()
+    assert abs(n_acc0 / total - pa) < 4 * np.sqrt(pa * (1 - pa) / total), (n_acc0 / total, pa)
+
+
+def check_grid_one_decision_full(seed=181, chunk=1 << 21):
+    """One decision and its recovery draw over the whole 2^24 grid of
+    uniforms, through the full verify entry (V = 4, T = 0.8, a draft x with
+    p(x) < q(x)).  Acceptances: #{k : k / 2^24 < p(x)/q(x)}, within 1 of
+    ratio * 2^24 with the ratio from scipy.  Recovery (the decision forced to
+    reject): the count of grid points drawing token i is r_i / S * 2^24
+    within 1, r = max(0, p - q) from scipy."""
+    rng = np.random.default_rng(seed)
+    V, T, G = 4, 0.8, 1 << 24
+    while True:
+        lt = rng.normal(0, 1.5, (2, V)).astype(np.float32)
+        ld = (lt[:1] + rng.normal(0, 1.2, (1, V))).astype(np.float32)
+        p = scipy.special.softmax(lt[0].astype(np.float64) / T)
+        q = scipy.special.softmax(ld[0].astype(np.float64) / T)
+        x = int(np.argmin(p / q))
+        if p[x] / q[x] < 0.9 and np.count_nonzero(p > q) >= 2:
+            break
+    ratio = p[x] / q[x]
+    r = np.maximum(p - q, 0.0)
+    tgt = np.broadcast_to(lt, (chunk, 2, V)).copy()
+    dft = np.broadcast_to(ld, (chunk, 1, V)).copy()
+    ids = np.full((chunk, 1), x, np.int32)
+    accepted, hist = 0, np.zeros(V, np.int64)
+    for start in range(0, G, chunk):
+        grid = (start + np.arange(chunk)) / G
+        ua = np.zeros((chunk, 2))
+        ua[:, 0] = grid
+        res = oracle.verify(tgt, dft, ids, np.ones(chunk), np.full(chunk, T), u_acc=ua,
+                            u_rec=np.full((chunk, 2), 0.5), diagnostics=False)
+        accepted += int(res["num_accepted"].sum())
+        ua[:, 0] = 1.0 - 2.0 ** -24
+        ur = np.zeros((chunk, 2))
+        ur[:, 0] = grid
+        res = oracle.verify(tgt, dft, ids, np.ones(chunk), np.full(chunk, T), u_acc=ua,
+                            u_rec=ur, diagnostics=False)
+        assert np.all(res["num_accepted"] == 0)
+        hist += np.bincount(res["tokens"][:, 0], minlength=V)
+    assert abs(accepted - ratio * G) <= 1.0, (accepted, ratio * G)
+    assert hist[x] == 0 and np.all(hist[r == 0] == 0), hist
+    assert np.all(np.abs(hist - r / r.sum() * G) <= 1.0), (hist, r / r.sum() * G)
+
+
 ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_accept_example_philox, check_bpd_greedy_example,
              check_greedy_bruteforce, check_enumeration_law,
@@ -721,4 +1090,7 @@ ALL_QUICK = [check_philox_known_answers, check_uniform_mapping,
              check_ngram_golden, check_ngram_vs_rfind, check_ngram_edge_cases,
              check_typical_golden, check_typical_vs_library, check_typical_special_cases,
              check_typical_correction_law, check_tree_chain_equals_verify,
-             check_tree_lossless_monte_carlo, check_tree_greedy_walk, check_tree_flags]
+             check_tree_lossless_monte_carlo, check_tree_greedy_walk, check_tree_flags,
+             check_draw_margin_vs_library, check_margins_vs_library,
+             check_forced_path_vs_library, check_typical_path_vs_library,
+             check_tree_chain_probs_equals_verify, check_tree_path_chain_equals_verify_path]

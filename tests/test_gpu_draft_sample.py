@@ -71,6 +71,9 @@ def check(svlib, name, draft, nd, temps, seed=0, offset=0, chunk=0, expect_flags
         f"{rep.flagged_mismatch}) q_max_rel={rep.prob_max_rel:.2e} flags={flags}")
     assert rep.ok(), rep.mismatches
     assert flags & ~8 == expect_flags, (flags, expect_flags)
+    # a draw on a rounding tie at a chunk boundary (device flag 8) is a draw
+    # within the band of a CDF boundary: only a batch the oracle flags has one
+    assert not flags & 8 or rep.flagged > 0, (flags, rep.flagged)
     assert ref["flags"] == expect_flags
     return ids, ref
 
@@ -180,7 +183,11 @@ def test_sampler_and_verify_share_a_handle(svlib):
                         hs["temperatures"], seed=4, offset=1)
     rep = compare(hs, ref, tokens.cpu().numpy(), nacc.cpu().numpy())
     assert rep.ok(), rep.mismatches
-    assert h.device_errors(clear=True) & ~8 == 0
+    flags = h.device_errors(clear=True)
+    assert flags & ~8 == 0
+    # a draw on a rounding tie at a chunk boundary (device flag 8) is a draw
+    # within the band of a CDF boundary: only a batch the oracle flags has one
+    assert not flags & 8 or rep.flagged > 0, (flags, rep.flagged)
     h.close()
 
 

@@ -125,5 +125,9 @@ def test_proposals_feed_the_verify_step(svlib):
                         hs["temperatures"], seed=9, offset=2)
     rep = compare(hs, ref, tokens.cpu().numpy(), nacc.cpu().numpy())
     assert rep.ok(), rep.mismatches
-    assert h.device_errors(clear=True) & ~8 == 0
+    flags = h.device_errors(clear=True)
+    assert flags & ~8 == 0
+    # a draw on a rounding tie at a chunk boundary (device flag 8) is a draw
+    # within the band of a CDF boundary: only a batch the oracle flags has one
+    assert not flags & 8 or rep.flagged > 0, (flags, rep.flagged)
     h.close()
