@@ -16,10 +16,23 @@ the library launches on.  A second loop of the same length times each kernel
 with the library's own HIP events (spec_verify_timing_*), which gives the
 dominant kernel's duration for the roofline.
 
+Before the warm-up, untimed steps run for --ramp-ms of GPU time so that the
+clocks have ramped up (reported as clock_ramp); the warm-up and timed steps
+are then exactly --warmup and --steps.
+
 Prints ONE JSON line.  value = verified (request x position x vocabulary)
 elements per second = sum_b (n_b + 1) * V / step time.  With --op
 draft_sample a step is one spec_draft_sample over the workload's draft rows
 (j < n_b) and value = sampled elements per second = sum_b n_b * V / step time.
+roofline.frac is the dominant (row statistics) kernel's algorithmic GB/s over
+the 8 TB/s peak; roofline.step_frac is the same bytes over the whole step.
+With --op verify the other large workloads (--also, default B=64 and B=512)
+are measured the same way afterwards and reported under "workloads".
+
+The CPU leg (skipped with --no-cpu-baseline) runs the fp64 oracle twice: once,
+untimed, on the exact inputs of the last timed step of each workload, whose
+outputs it checks by the parity rule ("parity"), and once timed on a bounded
+sample ("cpu_baseline").
 """
 import argparse
 import hashlib
@@ -256,6 +269,7 @@ def bench_ngram(args):
         ctx, lens = copies[i % len(copies)]
         sv.ngram_propose(ctx, lens, out_drafts=drafts, out_num=num, stream=stream, **kw)
 
+    ramp = clock_ramp(step, args.ramp_ms, first=1 << 20)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -280,6 +294,7 @@ def bench_ngram(args):
                                "V=129280, n in [2, 5], k=3",
                    **c, "input_copies": len(copies), "requests_with_drafts": proposals,
                    "parallelism": "single GPU"},
+        "clock_ramp": {"steps": ramp[0], "ms": round(ramp[1], 1)},
         "roofline": {"bound": "hbm", "kernel": "ngram", "achieved": alg / (ms_step * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None},
@@ -328,6 +343,7 @@ def bench_tree(args):
                                t.temperatures, seed=0, offset=i, stream=stream))
         del outs[:-len(copies)]
 
+    ramp = clock_ramp(step, args.ramp_ms, first=1 << 40)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -356,12 +372,13 @@ def bench_tree(args):
         "unit": "elems/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "token-tree verification, B=256 random trees of 16 nodes, "
                                "V=152064 bf16",
                    **c, "input_copies": len(copies), "visited_rows_per_step": visited,
                    "accepted_per_request": accepted / len(copies) / c["B"],
                    "parallelism": "single GPU"},
+        "clock_ramp": {"steps": ramp[0], "ms": round(ramp[1], 1)},
         "roofline": {"bound": "hbm", "kernel": "tree", "achieved": alg / (ms_step * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None},
@@ -384,13 +401,162 @@ def bench_tree(args):
     print(json.dumps(out), flush=True)
 
 
+def clock_ramp(step, ms, first):
+    """Untimed steps until about `ms` of GPU time has passed, so the clocks
+    have ramped up before the warm-up and the timed steps (offsets start at
+    `first`, away from the timed ones).  Returns (steps, wall ms)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step(first + n)
+            n += 1
+        torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+def measure(args, widx, op):
+    """Ramp, warm-up and timed steps of one workload.  Returns the numbers
+    and the context the parity check of the CPU leg needs."""
+    import torch
+    import synth
+    import rejection_sampling_verify_temp_amd as sv
+
+    dev = torch.device("cuda:0")
+    base = synth.make_config(widx, device=dev)
+    copies = [base] + [base.clone() for _ in range(max(0, args.rotate - 1))]
+    torch.cuda.synchronize()
+    w = base
+    h = sv.SpecVerify(w.B, w.K, w.V, w.target.dtype,
+                      draft_dtype=w.draft.dtype if w.draft is not None else None,
+                      draft_is_probs=w.draft_is_probs, device=0,
+                      chunk_elems=args.chunk)
+    tok = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
+    nacc = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    ids = torch.empty((w.B, w.K), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sample, typical = op == "draft_sample", op == "typical"
+    # the sampler draws the draft rows that hold logits: rows j < n_b of the
+    # probabilistic requests (one-hot requests have no draft distribution)
+    nd_sample = w.num_drafts if w.draft_mode is None else torch.where(
+        w.draft_mode == 0, w.num_drafts, torch.zeros_like(w.num_drafts))
+
+    def step(i):
+        c = copies[i % len(copies)]
+        if sample:
+            h.sample(c.draft, nd_sample, c.temperatures, seed=0, offset=i,
+                     out_ids=ids, stream=stream)
+        elif typical:
+            h.run_typical(c.target, c.draft_ids, c.num_drafts, c.temperatures,
+                          args.threshold, args.top_k, seed=0, offset=i, out_tokens=tok,
+                          out_num_accepted=nacc, stream=stream)
+        else:
+            h.run(c.target, c.draft, c.draft_mode, c.draft_ids, c.num_drafts,
+                  c.temperatures, seed=0, offset=i, out_tokens=tok,
+                  out_num_accepted=nacc, stream=stream)
+
+    ramp_steps, ramp_ms = clock_ramp(step, args.ramp_ms, first=1 << 40)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel timing (library events on the same stream), separate loop
+    # over the same steps: its last step leaves the outputs of the last timed
+    # step (same inputs, same offset)
+    sv.spec_verify_timing_enable(h.handle, True)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    nk = 0
+    while sv.spec_verify_kernel_name(nk) is not None:
+        nk += 1
+    tot, runs = sv.spec_verify_timing_read(h.handle, nk)
+    sv.spec_verify_timing_enable(h.handle, False)
+    torch.cuda.synchronize()
+    kern_ms = {sv.spec_verify_kernel_name(k): tot[k] / runs for k in range(nk) if tot[k] > 0}
+    # bit 8: a draw met a rounding tie at a chunk boundary (a valid token is
+    # taken); any other bit would be bad input data
+    dev_flags = h.device_errors()
+    assert dev_flags & ~8 == 0, dev_flags
+
+    if sample:
+        n_rows = int(nd_sample.clamp(0, w.K).sum().item())
+        elems = n_rows * w.V
+        alg = n_rows * w.V * w.draft.element_size()  # each sampled row read once
+    elif typical:  # target rows 0..n_b only: no draft rows are read
+        elems = w.verified_elems()
+        alg = elems * w.elt()
+    else:
+        elems = w.verified_elems()
+        alg = w.algorithmic_bytes()
+    last = args.warmup + args.steps - 1
+    ctx = dict(w=w, copy=copies[last % len(copies)], offset=last, tok=tok, nacc=nacc,
+               ids=ids, nd_sample=nd_sample)
+    res = dict(ms_step=ms_step, kern_ms=kern_ms, elems=elems, alg=alg, h=h,
+               ramp=dict(steps=ramp_steps, ms=round(ramp_ms, 1)), dev_flags=dev_flags)
+    return res, ctx
+
+
+def cpu_parity(ctx, op, args):
+    """Part of the CPU leg: the oracle on the exact inputs of the last timed
+    step (whole batch, same seed and offset), compared with the GPU's outputs
+    of that step by the parity rule.  Untimed."""
+    import oracle
+    from oracle.parity import compare, compare_draft
+    t0 = time.perf_counter()
+    c = ctx["copy"]
+    hs = c.host_arrays()
+    if op == "draft_sample":
+        ref = oracle.draft_sample(hs["draft"], ctx["nd_sample"].cpu().numpy(),
+                                  hs["temperatures"], seed=0, offset=ctx["offset"])
+        rep = compare_draft(ref, ctx["ids"].cpu().numpy())
+    elif op == "typical":
+        ref = oracle.verify_typical(hs["target"], hs["draft_ids"], hs["num_drafts"],
+                                    hs["temperatures"], eps=args.threshold, top_k=args.top_k,
+                                    seed=0, offset=ctx["offset"])
+        rep = compare(hs, ref, ctx["tok"].cpu().numpy(), ctx["nacc"].cpu().numpy())
+    else:
+        ref = oracle.verify(hs["target"], hs["draft"], hs["draft_ids"], hs["num_drafts"],
+                            hs["temperatures"], draft_mode=hs["draft_mode"],
+                            draft_is_probs=hs["draft_is_probs"], seed=0,
+                            offset=ctx["offset"])
+        rep = compare(hs, ref, ctx["tok"].cpu().numpy(), ctx["nacc"].cpu().numpy())
+    return {"status": "ok" if rep.ok() else "FAIL", "checked": rep.requests,
+            "flagged": rep.flagged, "flagged_differing": rep.flagged_mismatch,
+            "mismatches": len(rep.mismatches), "first_mismatches": [str(m) for m in
+                                                                   rep.mismatches[:3]],
+            "what": f"the whole batch of the last timed step (Philox offset {ctx['offset']}) "
+                    f"against the fp64 C oracle, {time.perf_counter() - t0:.1f} s"}
+
+
+def step_fractions(res):
+    """Achieved HBM GB/s of the dominant kernel and of the whole step."""
+    k_ms = res["kern_ms"][DOMINANT]
+    return (res["alg"] / (k_ms * 1e-3) / 1e9, res["alg"] / (res["ms_step"] * 1e-3) / 1e9)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # the GPU clocks take ~10 ms of load to ramp up: warm up for ~30 ms
     ap.add_argument("--warmup", type=int, default=200)
+    # the GPU clocks take ~10 ms of load to ramp up: untimed steps before the
+    # warm-up, reported in the output
+    ap.add_argument("--ramp-ms", type=float, default=40.0)
     ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--also", default="2,4",
+                    help="--op verify: other workloads measured after the main one "
+                         "and reported under 'workloads' (comma list, '' for none)")
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--op", choices=["verify", "draft_sample", "ngram", "typical", "tree"],
@@ -413,74 +579,16 @@ def main():
         return bench_tree(args)
 
     import torch
-    import synth
-    import rejection_sampling_verify_temp_amd as sv
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    base = synth.make_config(args.workload, device=dev)
-    copies = [base] + [base.clone() for _ in range(max(0, args.rotate - 1))]
-    torch.cuda.synchronize()
-    w = base
-    h = sv.SpecVerify(w.B, w.K, w.V, w.target.dtype,
-                      draft_dtype=w.draft.dtype if w.draft is not None else None,
-                      draft_is_probs=w.draft_is_probs, device=0,
-                      chunk_elems=args.chunk)
-    tok = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
-    nacc = torch.empty((w.B,), dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    sample = args.op == "draft_sample"
-    typical = args.op == "typical"
+    op = args.op
+    sample, typical = op == "draft_sample", op == "typical"
+    res, ctx = measure(args, args.workload, op)
+    w = ctx["w"]
     if sample and (w.draft is None or w.draft_is_probs):
         print("--op draft_sample needs a workload with draft logits", file=sys.stderr)
         sys.exit(2)
-    ids = torch.empty((w.B, w.K), dtype=torch.int32, device=dev)
-    # the sampler draws the draft rows that hold logits: rows j < n_b of the
-    # probabilistic requests (one-hot requests have no draft distribution)
-    nd_sample = w.num_drafts if w.draft_mode is None else torch.where(
-        w.draft_mode == 0, w.num_drafts, torch.zeros_like(w.num_drafts))
-
-    def step(i):
-        c = copies[i % len(copies)]
-        if sample:
-            h.sample(c.draft, nd_sample, c.temperatures, seed=0, offset=i,
-                     out_ids=ids, stream=stream)
-        elif typical:
-            h.run_typical(c.target, c.draft_ids, c.num_drafts, c.temperatures,
-                          args.threshold, args.top_k, seed=0, offset=i, out_tokens=tok,
-                          out_num_accepted=nacc, stream=stream)
-        else:
-            h.run(c.target, c.draft, c.draft_mode, c.draft_ids, c.num_drafts,
-                  c.temperatures, seed=0, offset=i, out_tokens=tok,
-                  out_num_accepted=nacc, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # whole-step timing
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-
-    # per-kernel timing (library events on the same stream), separate loop
-    sv.spec_verify_timing_enable(h.handle, True)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    nk = 0
-    while sv.spec_verify_kernel_name(nk) is not None:
-        nk += 1
-    tot, runs = sv.spec_verify_timing_read(h.handle, nk)
-    sv.spec_verify_timing_enable(h.handle, False)
-    torch.cuda.synchronize()
-    kern_ms = {sv.spec_verify_kernel_name(k): tot[k] / runs for k in range(nk)}
-    assert h.device_errors() == 0
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -489,16 +597,7 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    if sample:
-        n_rows = int(nd_sample.clamp(0, w.K).sum().item())
-        elems = n_rows * w.V
-        alg = n_rows * w.V * w.draft.element_size()  # each sampled row read once
-    elif typical:  # target rows 0..n_b only: no draft rows are read
-        elems = w.verified_elems()
-        alg = elems * w.elt()
-    else:
-        elems = w.verified_elems()
-        alg = w.algorithmic_bytes()
+    nacc = ctx["nacc"]
     # bytes the residual pass re-reads: the rejected row pair of every
     # probabilistic sampling request (from the last step's outputs)
     n_b = w.num_drafts.clamp(0, w.K).cpu()
@@ -509,8 +608,8 @@ def main():
     pairs = int(((nacc.cpu() < n_b) & samp & prob).sum())
     delt = w.draft.element_size() if w.draft is not None else 0
     resid_bytes = pairs * w.V * (w.elt() + delt)
-    stats_ms = kern_ms[DOMINANT]
-    achieved = alg / (stats_ms * 1e-3) / 1e9
+    ms_step, kern_ms, elems, alg = res["ms_step"], res["kern_ms"], res["elems"], res["alg"]
+    achieved, step_gbps = step_fractions(res)
     traffic = None if (sample or typical) else read_traffic(args.workload)
     dt = {torch.bfloat16: "bf16", torch.float32: "f32"}[w.target.dtype]
     out = {
@@ -524,7 +623,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dt,
         "data": "synthetic",
         "config": {"workload": (f"draft-token sampler, draft rows of {w.name}" if sample
                                 else f"typical acceptance (threshold {args.threshold}, "
@@ -534,23 +633,54 @@ def main():
                    ("sampled_elems" if sample else "verified_elems"): elems,
                    "algorithmic_bytes": alg,
                    "nominal_bytes": w.nominal_bytes(),
-                   "chunk_elems": h.chunk_elems, "input_copies": len(copies),
+                   "chunk_elems": res["h"].chunk_elems, "input_copies": args.rotate,
                    "parallelism": "single GPU"},
-        "step_hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
+        "clock_ramp": res["ramp"],
+        "step_hbm_gbps": step_gbps,
         "resid_pairs": None if (sample or typical) else pairs,
         "resid_bytes": None if (sample or typical) else resid_bytes,
         "resid_gbps": (resid_bytes / (kern_ms["resid"] * 1e-3) / 1e9
                        if "resid" in kern_ms and not (sample or typical) else None),
         "accepted_per_proposed": (int(nacc.sum().item()) / max(1, int(n_b.sum()))
                                   if not sample else None),
+        "emitted_per_request": (float((nacc.cpu() + 1).float().mean()) if not sample
+                                else None),
+        "device_flags": res["dev_flags"],
         "kernels_ms": kern_ms,
         "roofline": {"bound": "hbm", "kernel": DOMINANT,
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "step_achieved": step_gbps,
+                     "step_frac": step_gbps / HBM_PEAK_GBPS},
     }
+    res["h"].close()
+    extra = {}
+    also = [int(x) for x in args.also.split(",") if x.strip()] if op == "verify" else []
+    for k in also:
+        if k == args.workload:
+            continue
+        r2, c2 = measure(args, k, op)
+        a2, s2 = step_fractions(r2)
+        extra[str(k)] = {"workload": f"verify step, {c2['w'].name}",
+                         "ms_per_step": r2["ms_step"],
+                         "value": r2["elems"] / (r2["ms_step"] * 1e-3),
+                         "algorithmic_bytes": r2["alg"],
+                         "kernels_ms": r2["kern_ms"],
+                         "stats_frac": a2 / HBM_PEAK_GBPS,
+                         "step_frac": s2 / HBM_PEAK_GBPS,
+                         "emitted_per_request": float((c2["nacc"].cpu() + 1).float().mean()),
+                         "clock_ramp": r2["ramp"], "device_flags": r2["dev_flags"]}
+        if not args.no_cpu_baseline:
+            extra[str(k)]["parity"] = cpu_parity(c2, op, args)
+        r2["h"].close()
+        del c2
+        torch.cuda.empty_cache()
+    if extra:
+        out["workloads"] = extra
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (cpu_baseline_sample(w, nd_sample) if sample else
+        out["parity"] = cpu_parity(ctx, op, args)
+        out["cpu_baseline"] = (cpu_baseline_sample(w, ctx["nd_sample"]) if sample else
                                cpu_baseline_typical(w, args.threshold, args.top_k) if typical
                                else cpu_baseline(w))
         out["cpu_baseline"]["cpu"] = cpu_model()
@@ -561,7 +691,6 @@ def main():
         for key in ("cpu_baseline", "cpu_baseline_threads"):
             if key in out:
                 out[key]["algorithmic_gbps"] = out[key]["value"] * alg / elems / 1e9
-    h.close()
     print(json.dumps(out), flush=True)
 
 
