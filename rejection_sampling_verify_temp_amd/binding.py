@@ -242,6 +242,20 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
 
 
+def chk(t, shape, dtype=None):
+    """The device address of a contiguous device tensor of the given shape
+    (and dtype), None for None; raises otherwise."""
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("inputs must be contiguous device tensors")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"shape {tuple(t.shape)} != {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"dtype {t.dtype} != {dtype}")
+    return t.data_ptr()
+
+
 class SpecVerify:
     """A handle bound to one device; run() takes torch device tensors."""
 
@@ -282,17 +296,6 @@ class SpecVerify:
         if V != self.cfg.vocab:
             raise ValueError(f"vocab {V} != handle vocab {self.cfg.vocab}")
 
-        def chk(t, shape, dtype=None):
-            if t is None:
-                return None
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError("inputs must be contiguous device tensors")
-            if tuple(t.shape) != tuple(shape):
-                raise ValueError(f"shape {tuple(t.shape)} != {tuple(shape)}")
-            if dtype is not None and t.dtype != dtype:
-                raise TypeError(f"dtype {t.dtype} != {dtype}")
-            return t.data_ptr()
-
         if _dtype_code(target) != self.cfg.target_dtype:
             raise TypeError("target dtype differs from the handle's")
         if draft is not None and _dtype_code(draft) != self.cfg.draft_dtype:
@@ -330,17 +333,6 @@ class SpecVerify:
         if _dtype_code(target) != self.cfg.target_dtype:
             raise TypeError("target dtype differs from the handle's")
 
-        def chk(t, shape, dtype=None):
-            if t is None:
-                return None
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError("inputs must be contiguous device tensors")
-            if tuple(t.shape) != tuple(shape):
-                raise ValueError(f"shape {tuple(t.shape)} != {tuple(shape)}")
-            if dtype is not None and t.dtype != dtype:
-                raise TypeError(f"dtype {t.dtype} != {dtype}")
-            return t.data_ptr()
-
         dev = target.device
         if out_tokens is None:
             out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
@@ -373,17 +365,6 @@ class SpecVerify:
         if draft is not None and _dtype_code(draft) != self.cfg.draft_dtype:
             raise TypeError("draft dtype differs from the handle's")
 
-        def chk(t, shape, dtype=None):
-            if t is None:
-                return None
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError("inputs must be contiguous device tensors")
-            if tuple(t.shape) != tuple(shape):
-                raise ValueError(f"shape {tuple(t.shape)} != {tuple(shape)}")
-            if dtype is not None and t.dtype != dtype:
-                raise TypeError(f"dtype {t.dtype} != {dtype}")
-            return t.data_ptr()
-
         dev = target.device
         out = torch.empty((B, N), dtype=torch.int32, device=dev)
         nacc = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -412,17 +393,6 @@ class SpecVerify:
         dev = draft.device
         if out_ids is None:
             out_ids = torch.empty((B, K), dtype=torch.int32, device=dev)
-
-        def chk(t, shape, dtype=None):
-            if t is None:
-                return None
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError("inputs must be contiguous device tensors")
-            if tuple(t.shape) != tuple(shape):
-                raise ValueError(f"shape {tuple(t.shape)} != {tuple(shape)}")
-            if dtype is not None and t.dtype != dtype:
-                raise TypeError(f"dtype {t.dtype} != {dtype}")
-            return t.data_ptr()
 
         ptrs = [chk(draft, (B, K, V)), chk(num_drafts, (B,), torch.int32),
                 chk(temperatures, (B,), torch.float32)]
