@@ -143,6 +143,48 @@ int spec_verify_run(spec_verify_t h, int32_t B, int32_t K,
                     int32_t *out_num_accepted, float *out_debug_probs,
                     void *stream);
 
+/* Bytes of the fixed device array spec_verify_run_noalloc works in (one per
+ * GPU). */
+#define SPEC_VERIFY_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* spec_verify_run for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * There is no handle and nothing is allocated.  The step's workspace lives
+ * in one fixed array of SPEC_VERIFY_NOALLOC_SCRATCH_BYTES of device memory
+ * per GPU, the library's own, held until the process ends: chunk partials,
+ * draw descriptors, residual sums and a flag word.  The kernels and the
+ * outputs are those of spec_verify_run with the same configuration (request
+ * base 0).
+ *
+ *   cfg              as for spec_verify_create (checked the same way); B <=
+ *                    cfg->max_batch and K <= cfg->max_drafts.
+ *   other arguments  as for spec_verify_run.
+ *   out_device_flags device uint32 receiving the step's SV_DEVERR_* bits
+ *                    (zeroed by the step itself, so not sticky across
+ *                    calls), or NULL to leave them in the array.
+ *
+ * Limit: with nchunk = ceil(V / chunk) (the chunk spec_verify_chunk_elems
+ * reports for a handle of the same cfg), the step needs 256 +
+ * a(B (2K+1) nchunk 16) + a(B 64) + a(B nchunk 32) bytes, a() rounding up to
+ * 256; above the array's size the call returns SV_ERR_CAPACITY and enqueues
+ * nothing.  V = 152064 (10 chunks) with B = 256, K = 7 needs 0.7 MB.
+ *
+ * Every call on one GPU shares that GPU's array, and a call leaves it
+ * holding its own step.  Calls ordered on one stream are safe; calls that
+ * overlap on one GPU (two streams, two host threads) race and give wrong
+ * outputs.  The first call on a device looks up the array's address
+ * (hipGetSymbolAddress); later calls only enqueue.  Returns the status codes
+ * of spec_verify_run, SV_ERR_CAPACITY as above, SV_ERR_HIP if the array's
+ * address cannot be found. */
+int spec_verify_run_noalloc(const sv_config *cfg, int32_t B, int32_t K,
+                            const void *target_logits, const void *draft_probs,
+                            const uint8_t *draft_mode, const int32_t *draft_ids,
+                            const int32_t *num_drafts_per_req,
+                            const float *temperatures, uint64_t philox_seed,
+                            uint64_t philox_offset, int32_t *out_tokens,
+                            int32_t *out_num_accepted, float *out_debug_probs,
+                            uint32_t *out_device_flags, void *stream);
+
 /* Enqueues a verify step with typical acceptance instead of rejection
  * sampling.  Source: "投机采样" (razer666.cn), section 验收标准, Typical
  * Acceptance: a draft token is accepted when its probability exceeds a hard

@@ -62,6 +62,9 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.spec_verify_run.argtypes = [P, i32, i32, P, P, P, P, P, P, u64, u64,
                                     P, P, P, P]
     lib.spec_verify_run.restype = ctypes.c_int
+    lib.spec_verify_run_noalloc.argtypes = [ctypes.POINTER(sv_config), i32, i32, P, P, P, P,
+                                            P, P, u64, u64, P, P, P, P, P]
+    lib.spec_verify_run_noalloc.restype = ctypes.c_int
     lib.spec_verify_run_typical.argtypes = [P, i32, i32, P, P, P, P, ctypes.c_float, i32,
                                             u64, u64, P, P, P, P]
     lib.spec_verify_run_typical.restype = ctypes.c_int
@@ -126,6 +129,18 @@ def spec_verify_run(h, B, K, target_logits, draft_probs, draft_mode, draft_ids,
         num_drafts_per_req, temperatures, int(philox_seed) & (2 ** 64 - 1),
         int(philox_offset) & (2 ** 64 - 1), out_tokens, out_num_accepted,
         out_debug_probs, stream)
+
+
+def spec_verify_run_noalloc(cfg: sv_config, B, K, target_logits, draft_probs, draft_mode,
+                            draft_ids, num_drafts_per_req, temperatures, philox_seed,
+                            philox_offset, out_tokens, out_num_accepted, out_debug_probs,
+                            out_device_flags, stream) -> int:
+    """Pointers are integers (device addresses); returns the status code."""
+    return load_library().spec_verify_run_noalloc(
+        ctypes.byref(cfg), int(B), int(K), target_logits, draft_probs, draft_mode, draft_ids,
+        num_drafts_per_req, temperatures, int(philox_seed) & (2 ** 64 - 1),
+        int(philox_offset) & (2 ** 64 - 1), out_tokens, out_num_accepted, out_debug_probs,
+        out_device_flags, stream)
 
 
 def spec_verify_run_typical(h, B, K, target_logits, draft_ids, num_drafts_per_req,

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "sv_internal.h"
@@ -47,6 +48,74 @@ int pick_chunk(const sv_config& c) {
   if (ch < sv::kMinChunkElems) ch = sv::kMinChunkElems;
   if (ch > sv::kMaxChunkElems) ch = sv::kMaxChunkElems;
   return ch;
+}
+
+// The checks spec_verify_create makes on a configuration (status code).
+int check_config(const sv_config& c) {
+  if (c.max_batch < 1 || c.max_drafts < 0 || c.max_drafts > sv::kMaxDrafts ||
+      c.vocab < 1 || c.vocab > sv::kMaxVocab || c.device < 0)
+    return SV_ERR_INVALID_ARG;
+  if ((c.target_dtype != SV_F32 && c.target_dtype != SV_BF16) ||
+      (c.draft_dtype != SV_F32 && c.draft_dtype != SV_BF16) ||
+      (c.draft_is_probs != 0 && c.draft_is_probs != 1))
+    return SV_ERR_UNSUPPORTED;
+  if (c.chunk_elems != 0 &&
+      (c.chunk_elems % 64 != 0 || c.chunk_elems < sv::kMinChunkElems ||
+       c.chunk_elems > sv::kMaxChunkElems))
+    return SV_ERR_INVALID_ARG;
+  return SV_OK;
+}
+
+// The argument checks of a verify step (status code; SV_OK for B == 0 too).
+int check_run_args(const sv_config& c, int32_t B, int32_t K, const void* target_logits,
+                   const void* draft_probs, const int32_t* draft_ids,
+                   const int32_t* num_drafts_per_req, const float* temperatures,
+                   const int32_t* out_tokens, const int32_t* out_num_accepted,
+                   const float* out_debug_probs) {
+  if (B < 0 || K < 0) return SV_ERR_INVALID_ARG;
+  if (B > c.max_batch || K > c.max_drafts) return SV_ERR_CAPACITY;
+  if (B == 0) return SV_OK;
+  if (target_logits == nullptr || num_drafts_per_req == nullptr ||
+      temperatures == nullptr || out_tokens == nullptr || out_num_accepted == nullptr ||
+      (K > 0 && draft_ids == nullptr))
+    return SV_ERR_INVALID_ARG;
+  if (!aligned(target_logits, elt_bytes(c.target_dtype)) ||
+      (draft_probs != nullptr && !aligned(draft_probs, elt_bytes(c.draft_dtype))) ||
+      (draft_ids != nullptr && !aligned(draft_ids, 4)) || !aligned(num_drafts_per_req, 4) ||
+      !aligned(temperatures, 4) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      (out_debug_probs != nullptr && !aligned(out_debug_probs, 4)))
+    return SV_ERR_INVALID_ARG;
+  return SV_OK;
+}
+
+// Parameters of a verify step (the workspace pointers are left to the caller).
+sv::RunParams verify_params(const sv_config& c, int chunk, int nchunk, int32_t B, int32_t K,
+                            const void* target_logits, const void* draft_probs,
+                            const uint8_t* draft_mode, const int32_t* draft_ids,
+                            const int32_t* num_drafts_per_req, const float* temperatures,
+                            uint64_t philox_seed, uint64_t philox_offset,
+                            int32_t* out_tokens, int32_t* out_num_accepted,
+                            float* out_debug_probs) {
+  sv::RunParams p{};
+  p.target = target_logits;
+  p.draft = draft_probs;
+  p.mode = draft_mode;
+  p.ids = draft_ids;
+  p.nd = num_drafts_per_req;
+  p.temps = temperatures;
+  p.out_tokens = out_tokens;
+  p.out_nacc = out_num_accepted;
+  p.out_dbg = out_debug_probs;
+  p.seed = philox_seed;
+  p.offset = philox_offset;
+  p.B = B;
+  p.K = K;
+  p.V = c.vocab;
+  p.chunk = chunk;
+  p.nchunk = nchunk;
+  p.draft_is_probs = c.draft_is_probs;
+  p.has_draft = draft_probs != nullptr;
+  return p;
 }
 
 }  // namespace
@@ -157,17 +226,8 @@ int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
   *out = nullptr;
   if (cfg == nullptr) return SV_ERR_INVALID_ARG;
   const sv_config c = *cfg;
-  if (c.max_batch < 1 || c.max_drafts < 0 || c.max_drafts > sv::kMaxDrafts ||
-      c.vocab < 1 || c.vocab > sv::kMaxVocab || c.device < 0)
-    return SV_ERR_INVALID_ARG;
-  if ((c.target_dtype != SV_F32 && c.target_dtype != SV_BF16) ||
-      (c.draft_dtype != SV_F32 && c.draft_dtype != SV_BF16) ||
-      (c.draft_is_probs != 0 && c.draft_is_probs != 1))
-    return SV_ERR_UNSUPPORTED;
-  if (c.chunk_elems != 0 &&
-      (c.chunk_elems % 64 != 0 || c.chunk_elems < sv::kMinChunkElems ||
-       c.chunk_elems > sv::kMaxChunkElems))
-    return SV_ERR_INVALID_ARG;
+  const int rc = check_config(c);
+  if (rc != SV_OK) return rc;
 
   DeviceGuard g(c.device);
   if (!g.ok) return SV_ERR_HIP;
@@ -207,44 +267,20 @@ int spec_verify_run(spec_verify_t h, int32_t B, int32_t K, const void* target_lo
                     const float* temperatures, uint64_t philox_seed,
                     uint64_t philox_offset, int32_t* out_tokens,
                     int32_t* out_num_accepted, float* out_debug_probs, void* stream) {
-  if (h == nullptr || B < 0 || K < 0) return SV_ERR_INVALID_ARG;
-  if (B > h->cfg.max_batch || K > h->cfg.max_drafts) return SV_ERR_CAPACITY;
-  if (B == 0) return SV_OK;
+  if (h == nullptr) return SV_ERR_INVALID_ARG;
   const sv_config& c = h->cfg;
-  if (target_logits == nullptr || num_drafts_per_req == nullptr ||
-      temperatures == nullptr || out_tokens == nullptr || out_num_accepted == nullptr ||
-      (K > 0 && draft_ids == nullptr))
-    return SV_ERR_INVALID_ARG;
-  if (!aligned(target_logits, elt_bytes(c.target_dtype)) ||
-      (draft_probs != nullptr && !aligned(draft_probs, elt_bytes(c.draft_dtype))) ||
-      (draft_ids != nullptr && !aligned(draft_ids, 4)) || !aligned(num_drafts_per_req, 4) ||
-      !aligned(temperatures, 4) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
-      (out_debug_probs != nullptr && !aligned(out_debug_probs, 4)))
-    return SV_ERR_INVALID_ARG;
-
-  sv::RunParams full{};
-  full.target = target_logits;
-  full.draft = draft_probs;
-  full.mode = draft_mode;
-  full.ids = draft_ids;
-  full.nd = num_drafts_per_req;
-  full.temps = temperatures;
-  full.out_tokens = out_tokens;
-  full.out_nacc = out_num_accepted;
-  full.out_dbg = out_debug_probs;
+  const int rc = check_run_args(c, B, K, target_logits, draft_probs, draft_ids,
+                                num_drafts_per_req, temperatures, out_tokens,
+                                out_num_accepted, out_debug_probs);
+  if (rc != SV_OK || B == 0) return rc;
+  sv::RunParams full = verify_params(c, h->chunk, h->nchunk, B, K, target_logits, draft_probs,
+                                     draft_mode, draft_ids, num_drafts_per_req, temperatures,
+                                     philox_seed, philox_offset, out_tokens, out_num_accepted,
+                                     out_debug_probs);
   full.part = h->part;
   full.desc = h->desc;
   full.rsum = h->rsum;
   full.flags = h->flags;
-  full.seed = philox_seed;
-  full.offset = philox_offset;
-  full.B = B;
-  full.K = K;
-  full.V = c.vocab;
-  full.chunk = h->chunk;
-  full.nchunk = h->nchunk;
-  full.draft_is_probs = c.draft_is_probs;
-  full.has_draft = draft_probs != nullptr;
   full.b_base = h->b_base;
 
   return enqueue(h, full, c.target_dtype, c.draft_dtype, stream);
@@ -439,6 +475,119 @@ int spec_verify_destroy(spec_verify_t h) {
   }
   delete h;
   return rc;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// spec_verify_run_noalloc: the verify step with its workspace in a fixed
+// device array instead of a handle's allocation.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Bytes of the array: the chunk partials, draw descriptors, residual sums and
+// a flag word of one step.  Each GPU that runs the entry point holds its own
+// copy until the process ends.
+constexpr size_t kScratchBytes = SPEC_VERIFY_NOALLOC_SCRATCH_BYTES;
+constexpr int kScratchDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Per device: the array's device address (from hipGetSymbolAddress; the
+// name `scratch` in host code is only a host-side stand-in) and the bytes of
+// LDS per compute unit.  Filled once, on the device's first call.
+struct ScratchDev {
+  void* ptr = nullptr;
+  int lds_per_cu = 0;
+};
+ScratchDev g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Layout of one step in the array: flag word, partials, descriptors,
+// residual sums (each region 256-byte aligned).
+struct ScratchLayout {
+  size_t part, desc, rsum, total;
+};
+
+ScratchLayout scratch_layout(int32_t B, int32_t K, int nchunk) {
+  ScratchLayout l;
+  l.part = 256;
+  l.desc = l.part + align256((size_t)B * (2 * (size_t)K + 1) * nchunk * sizeof(sv::Partial));
+  l.rsum = l.desc + align256((size_t)B * sizeof(sv::DrawDesc));
+  l.total = l.rsum + align256((size_t)B * nchunk * sv::kResidSplitMax * sizeof(double));
+  return l;
+}
+
+// The array's address on `device` (the current device), looked up on its
+// first use.  nullptr if the lookup fails.
+const ScratchDev* scratch_on(int device) {
+  if (device < 0 || device >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchDev& d = g_scratch[device];
+  if (d.ptr == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    int lds = 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              device) != hipSuccess) {
+      lds = 0;
+      (void)hipGetLastError();
+    }
+    d.lds_per_cu = lds;
+    d.ptr = ptr;
+  }
+  return &d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_run_noalloc(const sv_config* cfg, int32_t B, int32_t K,
+                            const void* target_logits, const void* draft_probs,
+                            const uint8_t* draft_mode, const int32_t* draft_ids,
+                            const int32_t* num_drafts_per_req, const float* temperatures,
+                            uint64_t philox_seed, uint64_t philox_offset, int32_t* out_tokens,
+                            int32_t* out_num_accepted, float* out_debug_probs,
+                            uint32_t* out_device_flags, void* stream) {
+  if (cfg == nullptr) return SV_ERR_INVALID_ARG;
+  const sv_config c = *cfg;
+  int rc = check_config(c);
+  if (rc != SV_OK) return rc;
+  rc = check_run_args(c, B, K, target_logits, draft_probs, draft_ids, num_drafts_per_req,
+                      temperatures, out_tokens, out_num_accepted, out_debug_probs);
+  if (rc != SV_OK || B == 0) return rc;
+  if (out_device_flags != nullptr && !aligned(out_device_flags, 4)) return SV_ERR_INVALID_ARG;
+  const int chunk = pick_chunk(c);
+  const int nchunk = (c.vocab + chunk - 1) / chunk;
+  if (nchunk > sv::kMaxChunks) return SV_ERR_UNSUPPORTED;
+  const ScratchLayout lay = scratch_layout(B, K, nchunk);
+  if (lay.total > kScratchBytes) return SV_ERR_CAPACITY;
+
+  DeviceGuard g(c.device);
+  if (!g.ok) return SV_ERR_HIP;
+  const ScratchDev* sd = scratch_on(c.device);
+  if (sd == nullptr) return SV_ERR_HIP;
+  unsigned char* base = static_cast<unsigned char*>(sd->ptr);
+  sv::RunParams p = verify_params(c, chunk, nchunk, B, K, target_logits, draft_probs,
+                                  draft_mode, draft_ids, num_drafts_per_req, temperatures,
+                                  philox_seed, philox_offset, out_tokens, out_num_accepted,
+                                  out_debug_probs);
+  p.part = reinterpret_cast<sv::Partial*>(base + lay.part);
+  p.desc = reinterpret_cast<sv::DrawDesc*>(base + lay.desc);
+  p.rsum = reinterpret_cast<double*>(base + lay.rsum);
+  p.flags = out_device_flags != nullptr ? out_device_flags : reinterpret_cast<uint32_t*>(base);
+  p.clear_flags = 1;  // the step's first kernel zeroes the flag word
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int k = 0; k < sv::kNumKernels; ++k)
+    if (sv::launch_kernel(k, p, c.target_dtype, c.draft_dtype, sd->lds_per_cu, s) != hipSuccess)
+      return SV_ERR_HIP;
+  return SV_OK;
 }
 
 }  // extern "C"

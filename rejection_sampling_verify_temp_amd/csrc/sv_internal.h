@@ -93,6 +93,9 @@ struct RunParams {
   int32_t typical;
   float eps;
   int32_t top_k;
+  // Nonzero: the statistics kernel zeroes *flags before any kernel of the
+  // step can set a bit (a step that owns no sticky flag word).
+  int32_t clear_flags;
 };
 
 constexpr int kNumKernels = 4;

@@ -581,6 +581,8 @@ __global__ __launch_bounds__(kThreads, SV_STATS_WAVES_PER_EU) void k_stats(const
   __shared__ int ldsi[kThreads / 64];
   const int nslot = stats_slots(p);
   const int bid = blockIdx.x;
+  // kernels of the step that set flags run after this one on the stream
+  if (p.clear_flags && bid == 0 && threadIdx.x == 0) *p.flags = 0u;
   const int row = bid / p.nchunk, chunk = bid - row * p.nchunk;
   const int b = row / nslot, s = row - b * nslot;
   const ReqInfo ri = req_info(p, b);

@@ -82,3 +82,27 @@ def test_ngram_rejects_bad_arguments_without_device():
     assert lib.spec_verify_chunk_elems(None) == 0
     assert lib.spec_verify_set_request_base(None, 0) == binding.SV_ERR_INVALID_ARG
     assert lib.spec_verify_destroy(None) == 0
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    """The no-alloc entry point checks its configuration, arguments and the
+    size of its fixed workspace on the host: a null configuration, a bad
+    field and a step too large for the array are rejected with no device
+    call (this machine has no GPU)."""
+    assert "spec_verify_run_noalloc" in sv.header_functions()
+    lib = sv.load_library()
+    P = 256  # an aligned stand-in address: nothing is dereferenced on these paths
+    args = lambda B, K: [B, K, P, P, None, P, P, P, 0, 0, P, P, None, None, None]
+    assert lib.spec_verify_run_noalloc(None, *args(1, 1)) == binding.SV_ERR_INVALID_ARG
+    f = dict(max_batch=512, max_drafts=31, vocab=983040, target_dtype=1, draft_dtype=1,
+             draft_is_probs=0, device=0, chunk_elems=0)
+    cfg = binding.sv_config(**f)
+    # 512 requests x 63 row slots x 64 chunks of partials alone are 33 MB
+    assert lib.spec_verify_run_noalloc(ctypes.byref(cfg), *args(512, 31)) == \
+        binding.SV_ERR_CAPACITY
+    assert lib.spec_verify_run_noalloc(ctypes.byref(cfg), *args(513, 1)) == \
+        binding.SV_ERR_CAPACITY  # above cfg.max_batch
+    bad = binding.sv_config(**dict(f, vocab=0))
+    assert lib.spec_verify_run_noalloc(ctypes.byref(bad), *args(1, 1)) == \
+        binding.SV_ERR_INVALID_ARG
+    assert lib.spec_verify_run_noalloc(ctypes.byref(cfg), *args(0, 1)) == binding.SV_OK
