@@ -73,6 +73,23 @@ __device__ __forceinline__ float raw_to_float(uint32_t w) {
   return __uint_as_float(DT == SV_BF16 ? w << 16 : w);
 }
 
+// The raw bits of element k of a 16-byte vector replaced by -inf, which
+// takes the element out of a chunk's max and sums.
+template <int DT>
+__device__ __forceinline__ u32x4 mask_elem(u32x4 d, int k) {
+  uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == SV_BF16) {
+      const uint32_t lo = (w[i] & 0xffff0000u) | 0xff80u, hi = (w[i] & 0xffffu) | 0xff800000u;
+      w[i] = k == 2 * i ? lo : (k == 2 * i + 1 ? hi : w[i]);
+    } else {
+      w[i] = k == i ? 0xff800000u : w[i];
+    }
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // Softmax statistics of one chunk, by the whole workgroup.  A pass holds
 // kUnroll 16-byte vectors per thread in registers (all loads in flight
 // together); the workgroup takes the max of the pass first, moves the shared
@@ -84,11 +101,15 @@ __device__ __forceinline__ float raw_to_float(uint32_t w) {
 // touching memory; those vectors are not folded (the test is uniform in all
 // but one wave of a pass).
 // COUNT: also count the chunk's elements above lx (into *above).
-template <int DT, bool COUNT>
+// EXCL: element xi of the chunk is left out of the sums (the draft of a
+// one-hot row: a correction draws from the chunk without it); the max and
+// so the reference still include it.
+template <int DT, bool COUNT, bool EXCL = false>
 __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int c1, float c,
                                                     float* ldsf, double* ldsd, float* m_out,
                                                     double* z_out, float lx = 0.f,
-                                                    int* ldsi = nullptr, int* above = nullptr) {
+                                                    int* ldsi = nullptr, int* above = nullptr,
+                                                    int xi = -1) {
   using E = Elt<DT>;
   const Geo g = chunk_geo<DT>(row, c0, c1);
   const int tid = threadIdx.x;
@@ -142,6 +163,11 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
       R = rn;
       M = pm;
     }
+    // EXCL: xi stays in the max (the chunk's reference may include it) but
+    // leaves the sums: its bits become -inf in the sum phase's copy of the
+    // one vector or scalar that holds it
+    if (EXCL && base == 0 && xi < g.v0 && g.c0 + tid == xi) ht[0] = kNegInf;
+    if (EXCL && base == 0 && xi >= g.t0 && g.t0 + tid == xi) ht[1] = kNegInf;
     float s = fast_exp2(fmaf(ht[0], c, R)) + fast_exp2(fmaf(ht[1], c, R));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -150,6 +176,8 @@ __device__ __forceinline__ void chunk_softmax_block(const void* row, int c0, int
         // the first unpack from common-subexpression elimination
         u32x4 w = d[u];
         asm volatile("" : "+v"(w));
+        if (EXCL && xi >= g.v0 && xi < g.t0 && v + u * kThreads == (xi - g.v0) / E::kVec)
+          w = mask_elem<DT>(w, (xi - g.v0) % E::kVec);
         float e[E::kVec];
         E::unpack(w, e);
 #pragma unroll
@@ -274,6 +302,15 @@ __device__ __forceinline__ bool slot_needed(const ReqInfo& r, int s, int K) {
   return r.active && (s <= K ? s <= r.n : (s - K - 1 < r.n && r.draft_stats));
 }
 
+// Whether target row j's statistics leave out its draft x (= xid): a one-hot
+// sampling request's drafted rows.  A correction at j then draws from the
+// row's partials as they are, and the decision adds x's share back to the
+// row total in fp64.  The same test is made on both sides of the hand-off.
+__device__ __forceinline__ bool excl_draft(const RunParams& p, const ReqInfo& r, int j, int xid) {
+  return p.sample_k == 0 && !p.typical && r.sampling && r.onehot && j < r.n && xid >= 0 &&
+         xid < p.V;
+}
+
 // ---------------------------------------------------------------------------
 // Decisions of one request (one wavefront)
 // ---------------------------------------------------------------------------
@@ -338,6 +375,9 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
         if (counts && k0 + u < p.nchunk) rank += q[u].idx;
       }
     }
+    // a one-hot row's chunk sums leave out its draft (its max keeps it): the
+    // row total takes x back, exactly (lt is x's logit)
+    const bool excl = excl_draft(p, ri, lane, x);
     if (ri.sampling) {
       r_ref = ref_of(m, c);
       for (int k0 = 0; k0 < p.nchunk; k0 += kBatch) {
@@ -350,6 +390,7 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
           if (k0 + u < p.nchunk && q[u].z != 0.0)
             r_z += q[u].z * exp2_diff(r_ref, ref_of(q[u].m, c));
       }
+      if (excl) r_z += exp2((double)lt * (double)c + (double)r_ref);
     } else {
       r_ref = m;
       r_idx = im == INT32_MAX ? 0 : im;
@@ -460,20 +501,20 @@ __device__ void decide_request(const RunParams& p, int b, const ReqInfo& ri, boo
     const double du = lane_f64(d.u, je);
     int excl = lane_i32(d.x, je);
     const float lx = lane_f32(lt, je);
-    double mass = 0.0, px = 0.0;
+    // chunk masses: the row's partials at ref_p (a one-hot row's already
+    // leave out its draft x, so a correction needs no subtraction)
+    double mass = 0.0;
     if (lane < p.nchunk) {
       const Partial q = p.part[((size_t)b * nslot + je) * p.nchunk + lane];
       if (q.z != 0.0) mass = q.z * exp2_diff(dref, ref_of(q.m, dc));
-      if (excl >= 0 && excl / p.chunk == lane) px = exp2((double)lx * (double)dc + (double)dref);
     }
-    double mx = mass - px;
-    if (!(mx > 0.0)) mx = 0.0;
+    double mx = mass > 0.0 ? mass : 0.0;
     double incl = wave_incl_scan(mx, lane);
     double S = lane_f64(incl, 63);
-    if (!(S > 0.0) && excl >= 0) {  // no residual mass: draw from p itself
+    if (!(S > 0.0) && excl >= 0) {  // no mass without x: draw from p itself
       if (outputs && lane == 0) atomicOr(p.flags, SV_DEVERR_ZERO_RESIDUAL);
+      if (excl / p.chunk == lane) mx += exp2((double)lx * (double)dc + (double)dref);
       excl = -1;
-      mx = mass > 0.0 ? mass : 0.0;
       incl = wave_incl_scan(mx, lane);
       S = lane_f64(incl, 63);
     }
@@ -529,6 +570,13 @@ __device__ __forceinline__ void stats_item(const RunParams& p, int b, int s, int
       int above = 0;
       chunk_softmax_block<TDT, true>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z, lx, ldsi, &above);
       out.idx = above;
+    } else if (is_target && excl_draft(p, ri, s, 0) &&
+               excl_draft(p, ri, s, p.ids[(size_t)b * p.K + s]) &&
+               p.ids[(size_t)b * p.K + s] >= c0 && p.ids[(size_t)b * p.K + s] < c1) {
+      // a one-hot row's draft (loaded only here) leaves its chunk's sums
+      chunk_softmax_block<TDT, false, true>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z, 0.f,
+                                            nullptr, nullptr, p.ids[(size_t)b * p.K + s]);
+      out.idx = -1;
     } else if (is_target) {
       chunk_softmax_block<TDT, false>(r, c0, c1, c, ldsf, ldsd, &out.m, &out.z);
       out.idx = -1;
@@ -768,33 +816,39 @@ __device__ __forceinline__ float seg_resid(const SegWords<TDT, SEG>& P,
   return IS_PAIR ? pair_resid(P.at(k), Q.at(k), d, probs) : single_resid(P.at(k), d);
 }
 
-// Residual sum of a whole segment, excluded token included (fp32 within
-// groups of 8, fp64 across them).
+// Residual sum of a whole segment with element ex (the excluded token, or
+// -1) set to 0 before it is summed (fp32 within groups of 8, fp64 across
+// them): the sum is exact to the rounding of the elements that remain, even
+// when the excluded one held nearly all of the chunk.
 template <bool IS_PAIR, int TDT, int DDT, int SEG>
 __device__ __forceinline__ double seg_sum(const SegWords<TDT, SEG>& P,
                                           const SegWords<DDT, SEG>& Q, const DrawDesc& d,
-                                          bool probs) {
+                                          bool probs, int ex) {
   double seg = 0.0;
 #pragma unroll
   for (int g = 0; g < SEG; g += 8) {
     float r[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = seg_resid<IS_PAIR>(P, Q, d, probs, g + k);
+    for (int k = 0; k < 8; ++k) {
+      r[k] = seg_resid<IS_PAIR>(P, Q, d, probs, g + k);
+      r[k] = g + k == ex ? 0.f : r[k];
+    }
     seg += (double)pairwise_sum(r);
   }
   return seg;
 }
 
-// Walk of a segment (q = mass before it, ex = excluded offset or -1, rx
-// its residual): the offset of the first element whose running sum passes
-// theta, else of the last element with positive residual (-1 if none).  Two
-// levels keep the serial fp64 chain short: the group sums of seg_sum
-// (recomputed bit for bit) find the group, then that group's 8 elements are
-// walked.  *logit receives the target logit of the chosen element.
+// Walk of a segment (q = mass before it, ex = excluded offset or -1): the
+// offset of the first element whose running sum passes theta, else of the
+// last element with positive residual (-1 if none).  Two levels keep the
+// serial fp64 chain short: the group sums of seg_sum (recomputed bit for
+// bit, the excluded element zeroed alike) find the group, then that group's
+// 8 elements are walked.  *logit receives the target logit of the chosen
+// element.
 template <bool IS_PAIR, int TDT, int DDT, int SEG>
 __device__ __forceinline__ int seg_walk(const SegWords<TDT, SEG>& P,
                                         const SegWords<DDT, SEG>& Q, const DrawDesc& d,
-                                        bool probs, int ex, float rx, double q, double theta,
+                                        bool probs, int ex, double q, double theta,
                                         float* logit) {
   constexpr int NG = SEG / 8;
   // (1) the group holding theta, else the last group with mass
@@ -805,9 +859,11 @@ __device__ __forceinline__ int seg_walk(const SegWords<TDT, SEG>& P,
   for (int g = 0; g < NG; ++g) {
     float r[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = seg_resid<IS_PAIR>(P, Q, d, probs, 8 * g + k);
-    double sg = (double)pairwise_sum(r);
-    if (ex >= 8 * g && ex < 8 * g + 8) sg -= (double)rx;
+    for (int k = 0; k < 8; ++k) {
+      r[k] = seg_resid<IS_PAIR>(P, Q, d, probs, 8 * g + k);
+      r[k] = 8 * g + k == ex ? 0.f : r[k];
+    }
+    const double sg = (double)pairwise_sum(r);
     const bool has = sg > 0.0;
     const bool hit = gstar < 0 && has && L + sg > theta;
     Lstar = hit ? L : Lstar;
@@ -911,11 +967,9 @@ __device__ __forceinline__ void locate(const RunParams& p, int b, const DrawDesc
           mass = part[0];
 #pragma unroll
           for (int h = 1; h < kSplit; ++h) mass += part[h];
-        } else {
+        } else {  // a pair draw's retry from p (single draws arrive placed)
           const Partial q = p.part[((size_t)b * (2 * K + 1) + d.j) * p.nchunk + lane];
           if (q.z != 0.0) mass = q.z * exp2_diff(d.ref_p, ref_of(q.m, d.c));
-          if (excl >= 0 && excl / p.chunk == lane)
-            mass -= exp2((double)Elt<TDT>::at(prow, excl) * (double)d.c + (double)d.ref_p);
         }
         if (!(mass > 0.0)) mass = 0.0;
       }
@@ -1002,13 +1056,7 @@ __device__ __forceinline__ void locate(const RunParams& p, int b, const DrawDesc
   if (pair) load_words<DDT>(qrow, c0 + min(i0, len), nseg, pad_q, Q);
   int ex = excl >= 0 ? excl - c0 - i0 : -1;  // excluded token in the segment
   if (ex >= nseg) ex = -1;
-  float rx = 0.f;  // its residual, from its own loads
-  if (ex >= 0) {
-    const float lp = Elt<TDT>::at(prow, excl);
-    rx = pair ? pair_resid(lp, Elt<DDT>::at(qrow, excl), d, probs) : single_resid(lp, d);
-  }
-  double seg = pair ? seg_sum<true>(P, Q, d, probs) : seg_sum<false>(P, Q, d, probs);
-  seg -= (double)rx;
+  double seg = pair ? seg_sum<true>(P, Q, d, probs, ex) : seg_sum<false>(P, Q, d, probs, ex);
   if (!(seg > 0.0)) seg = 0.0;
 
   // (c) exclusive scan of the segment sums
@@ -1040,8 +1088,8 @@ __device__ __forceinline__ void locate(const RunParams& p, int b, const DrawDesc
       for (int k = 0; k < SegWords<DDT, SEG>::kWords; ++k) asm volatile("" : "+v"(Q.w[k]));
     }
     const double th = mine ? theta : __builtin_inf();
-    const int yo = pair ? seg_walk<true>(P, Q, d, probs, ex, rx, q, th, &lmine)
-                        : seg_walk<false>(P, Q, d, probs, ex, rx, q, th, &lmine);
+    const int yo = pair ? seg_walk<true>(P, Q, d, probs, ex, q, th, &lmine)
+                        : seg_walk<false>(P, Q, d, probs, ex, q, th, &lmine);
     if (yo >= 0) ymine = i0 + yo;
     if (mine) atomicMin(&s_y, ymine);
   }
@@ -1051,8 +1099,12 @@ __device__ __forceinline__ void locate(const RunParams& p, int b, const DrawDesc
   if (y == INT32_MAX) {  // theta past the chunk's recomputed total
     writer = s_lastseg >= 0 ? s_lastseg == tid : tid == 0;
     const bool have = s_lastseg >= 0 && ymine != INT32_MAX;
-    y = have ? ymine : 0;
-    if (!have) lmine = Elt<TDT>::at(prow, c0);
+    // no element with mass at all (only reachable when every element left
+    // underflows at the row's reference): a token of the range that is not
+    // the excluded draft
+    const int y0 = (c0 == excl && len > 1) ? 1 : 0;
+    y = have ? ymine : y0;
+    if (!have) lmine = Elt<TDT>::at(prow, c0 + y0);
     if (writer && theta != __builtin_inf()) atomicOr(p.flags, SV_DEVERR_DRAW_ROUNDING);
   }
   if (writer) {

@@ -374,13 +374,21 @@ __device__ __forceinline__ bool excluded(const int* ex, int nex, int i) {
   return false;
 }
 
+// The draw slot holding element i of the row.
+__device__ __forceinline__ int slot_of(const Geo& g, int nslot, int kv, int i) {
+  return i < g.v0 ? 0 : (i >= g.t0 ? nslot - 1 : 1 + (i - g.v0) / kv / 64);
+}
+
 // Inverse-CDF draw from the law with uniform u (whole workgroup), given its
 // sums per draw slot in s_slot (written by slot_pass); the
 // tokens in ex[0..nex) are removed.  A workgroup scan over the slot sums
 // finds the slot holding u * S, and wavefront 0 re-reads only that slot (one
 // vector per lane) to find the element.  Returns the token; *rounding is set
-// if u * S fell past the recomputed total, *empty if the law is 0.  The slot
-// sums of removed tokens are reduced in place.
+// if u * S fell past the recomputed total, *empty if the law is 0.  A slot
+// that holds removed tokens is summed again with them zeroed (not reduced
+// by their values: a removed sibling can hold nearly all of the slot, and
+// the difference of two rounded sums would leave a residue far above the
+// mass that remains).
 template <int TDT, int DDT>
 __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, const void* qrow, int V,
                                const int* ex, int nex, double u, double* s_slot, double* s_woff,
@@ -392,18 +400,36 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
   const bool qvec = L.pair && same_alignment(prow, qrow);
   const int nslot = num_slots(g);
   __syncthreads();
-  if (tid == 0) {  // removed tokens leave their slots
-    for (int k = 0; k < nex; ++k) {
-      const int e = ex[k];
-      const int sl = e < g.v0 ? 0 : (e >= g.t0 ? nslot - 1 : 1 + (e - g.v0) / KV / 64);
-      s_slot[sl] -= (double)law_at<TDT, DDT>(L, prow, qrow, e);
+  if (w == 0) {  // slots holding removed tokens, summed again without them
+    for (int k = 0; k < nex; ++k) {  // uniform over the wavefront
+      const int sl = slot_of(g, nslot, KV, ex[k]);
+      bool seen = false;
+      for (int k2 = 0; k2 < k; ++k2) seen = seen || slot_of(g, nslot, KV, ex[k2]) == sl;
+      if (seen) continue;
+      float r[KV];
+      int base;
+#pragma unroll
+      for (int j = 0; j < KV; ++j) r[j] = 0.f;
+      if (sl == 0 || sl == nslot - 1) {
+        base = sl == 0 ? lane : g.t0 + lane;
+        if (sl == 0 ? lane < g.v0 : base < V) r[0] = law_at<TDT, DDT>(L, prow, qrow, base);
+      } else {
+        const int vi = (sl - 1) * 64 + lane;
+        base = g.v0 + vi * KV;
+        if (vi < g.nvec) law_vec<TDT, DDT>(L, prow, qrow, g, vi, qvec, r);
+      }
+      for (int e = 0; e < nex; ++e) {  // a select per element, no early exit
+        const int t = ex[e];
+#pragma unroll
+        for (int j = 0; j < KV; ++j) r[j] = t == base + j ? 0.f : r[j];
+      }
+      // the same sums slot_pass makes: a scalar per lane for the head and
+      // tail slots, fp32 vector sums otherwise
+      const double sum = (sl == 0 || sl == nslot - 1) ? wave_sum((double)r[0])
+                                                       : (double)wave_sum_f32(pairwise_sum(r));
+      if (lane == 0) s_slot[sl] = sum;
     }
-    for (int k = 0; k < nex; ++k) {  // rounding can leave a tiny negative
-      const int e = ex[k];
-      const int sl = e < g.v0 ? 0 : (e >= g.t0 ? nslot - 1 : 1 + (e - g.v0) / KV / 64);
-      if (!(s_slot[sl] > 0.0)) s_slot[sl] = 0.0;
-    }
-    *s_sel = -1;
+    if (lane == 0) *s_sel = -1;
   }
   __syncthreads();
 

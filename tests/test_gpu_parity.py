@@ -275,3 +275,22 @@ def test_draw_sizes_pair_dtypes(svlib, B, dtypes):
                           n_mode="ragged", corr=0.6, draft_is_probs=probs, seed=B + 7,
                           device="cuda")
     check(svlib, w, seed=2, offset=B)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_onehot_dominant_draft(svlib, dtype):
+    """One-hot drafts that hold almost all of p (p(x) about 0.99 at T = 0.3):
+    the rare rejections draw from the remaining 1% of the mass, so x's share
+    must leave its chunk exactly, not as a difference of rounded sums.  Every
+    request has its own Philox counter; about 1% reject."""
+    g = torch.Generator().manual_seed(41)
+    B, K, V, T = 4096, 1, 20000, 0.3
+    t = torch.randn((B, K + 1, V), generator=g) * 0.5
+    ids = torch.randint(0, V, (B, K), generator=g, dtype=torch.int32)
+    for b in range(B):  # x about 0.99 of p_0 (1 - 1e-2 of the mass)
+        t[b, 0, ids[b, 0]] = 4.6 + 0.3 * float(np.log(V / 50000))
+    w = synth.Workload("one-hot dominant drafts", t.to(dtype), None,
+                       torch.ones(B, dtype=torch.uint8), ids,
+                       torch.full((B,), K, dtype=torch.int32), torch.full((B,), T))
+    rep = check(svlib, w, seed=5, offset=3)
+    assert rep.proposed - rep.accepted >= 10  # enough rejections drawn from the rest

@@ -140,3 +140,33 @@ def test_max_vocab(svlib):
         w = synth.make_tree(4, 6, 983040, dtype=dtype, temps=(1.0, 0.0, 0.6, 1.0), seed=seed,
                             corr=0.97, device="cuda")
         check(svlib, w, seed=seed, offset=3)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_onehot_dominant_sibling(svlib, dtype):
+    """One-hot trees whose first child holds almost all of the root's p
+    (about 0.99 at T = 0.3): after its rare rejection the second child and
+    the draw see the remaining 1%, so the removed token must leave its draw
+    slot exactly, not as a difference of rounded sums."""
+    g = torch.Generator().manual_seed(43)
+    B, N, V, T = 2048, 3, 20000, 0.3
+    t = torch.randn((B, N, V), generator=g) * 0.5
+    tok = torch.randint(0, V, (B, N), generator=g, dtype=torch.int32)
+    tok[:, 0] = 0
+    for b in range(B):
+        t[b, 0, tok[b, 1]] = 4.6 + 0.3 * float(np.log(V / 50000))
+    w = synth.TreeWorkload("one-hot trees, dominant first child", t.to(dtype), None, tok,
+                           torch.tensor([[-1, 0, 0]] * B, dtype=torch.int32),
+                           torch.full((B,), N, dtype=torch.int32), torch.full((B,), T))
+    rep, ref = check(svlib, w, seed=6, offset=2)
+    assert int((ref["last_node"] == 0).sum()) >= 10  # enough walks past the first child
+
+
+def test_benchmark_shape(svlib):
+    """The tree benchmark's own shape and law: 256 random recursive trees of
+    16 nodes over V = 152064, bf16 target and draft logits, T in
+    {0.6, 1.0, 0.0, 0.8}, correlation 0.95, every node in use."""
+    w = synth.make_tree(256, 16, 152064, dtype=torch.bfloat16, seed=31,
+                        temps=(0.6, 1.0, 0.0, 0.8), corr=0.95, ragged=False, device="cuda")
+    rep, _ = check(svlib, w, seed=0, offset=0)
+    assert rep.accepted > 0
