@@ -294,3 +294,36 @@ def test_onehot_dominant_draft(svlib, dtype):
                        torch.full((B,), K, dtype=torch.int32), torch.full((B,), T))
     rep = check(svlib, w, seed=5, offset=3)
     assert rep.proposed - rep.accepted >= 10  # enough rejections drawn from the rest
+
+
+def test_mode_bytes_at_the_end_of_an_allocation(svlib):
+    """draft_mode is read through the aligned 4-byte word that holds each
+    byte.  With the array alone in its own hipMalloc allocation of B = 37
+    bytes, the last word reaches past the array's end: the run must give the
+    same outputs as with the array inside a larger tensor."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipFree.argtypes = [ctypes.c_void_p]
+    w = synth.make_random(37, 3, 4099, dtype=torch.bfloat16, temps=(1.0, 0.7, 0.0),
+                          onehot_frac=0.5, n_mode="ragged", seed=37).to("cuda")
+    assert w.draft_mode is not None and w.B % 4 == 1
+    ref = run_gpu(svlib, w, seed=8, offset=2)
+    ptr = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(ptr), w.B) == 0
+    try:
+        assert hip.hipMemcpy(ptr, w.draft_mode.data_ptr(), w.B, 3) == 0  # device to device
+        h = svlib.SpecVerify(w.B, w.K, w.V, w.target.dtype, draft_dtype=w.draft.dtype)
+        tok = torch.empty((w.B, w.K + 1), dtype=torch.int32, device="cuda")
+        nacc = torch.empty((w.B,), dtype=torch.int32, device="cuda")
+        rc = svlib.spec_verify_run(h.handle, w.B, w.K, w.target.data_ptr(), w.draft.data_ptr(),
+                                   ptr.value, w.draft_ids.data_ptr(), w.num_drafts.data_ptr(),
+                                   w.temperatures.data_ptr(), 8, 2, tok.data_ptr(),
+                                   nacc.data_ptr(), None, torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        assert np.array_equal(tok.cpu().numpy(), ref[0]) and np.array_equal(nacc.cpu().numpy(), ref[1])
+        h.close()
+    finally:
+        hip.hipFree(ptr)
