@@ -55,6 +55,9 @@ DOMINANT = "stats"  # the kernel that streams every needed logits row
 KERNEL_SRC = [os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", f)
               for f in ("sv_kernels.hip", "sv_device.h", "sv_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_traffic_B256_K7_V152064_bf16.txt")
+TREE_SRC = [os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", f)
+            for f in ("sv_tree.hip", "sv_device.h", "sv_internal.h")]
+TREE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_traffic_B256_N16_V152064_bf16.txt")
 
 
 def _code_only(text):
@@ -67,26 +70,26 @@ def _code_only(text):
     return " ".join(text.split())
 
 
-def kernel_source_hash():
+def kernel_source_hash(paths=None):
     h = hashlib.sha256()
-    for path in KERNEL_SRC:
+    for path in paths or KERNEL_SRC:
         with open(path, encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_idx):
-    """HBM bytes per stats launch measured with rocprofv3 --pmc
-    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), valid only
-    for the kernel source it was taken on."""
-    if workload_idx != 3 or not os.path.exists(TRAFFIC_FILE):
+def read_traffic(workload_idx, path=TRAFFIC_FILE, src=None):
+    """HBM bytes per launch of the dominant kernel measured with rocprofv3
+    --pmc (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), valid
+    only for the workload and the kernel source it was taken on."""
+    if workload_idx != 3 or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -355,6 +358,10 @@ def bench_tree(args):
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
     assert h.device_errors() & ~8 == 0
+    if args.copy_probe_mib:  # a known-size reference for HBM counters
+        a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(a).copy_(a)
+        torch.cuda.synchronize()
     # bytes of the visited nodes' rows (target and draft), from the last
     # steps' walks: the least the walk must read
     row = c["V"] * 2
@@ -381,7 +388,8 @@ def bench_tree(args):
         "clock_ramp": {"steps": ramp[0], "ms": round(ramp[1], 1)},
         "roofline": {"bound": "hbm", "kernel": "tree", "achieved": alg / (ms_step * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "traffic": read_traffic(3, TREE_TRAFFIC_FILE, TREE_SRC)},
     }
     if not args.no_cpu_baseline:
         import oracle
