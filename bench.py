@@ -390,6 +390,7 @@ def bench_tree(args):
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                      "traffic": read_traffic(3, TREE_TRAFFIC_FILE, TREE_SRC)},
+        "team_size": h.tree_team_size(c["B"]),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -406,7 +407,49 @@ def bench_tree(args):
                                    sample=f"{n_req} requests of the same batch, {dt:.1f} s of "
                                           "the single-threaded fp64 C oracle")
     h.close()
+    del copies, outs, w
+    if args.tree_batches:
+        out["batches"] = {str(b): tree_batch(b, args) for b in args.tree_batches.split(",")
+                          if b.strip()}
     print(json.dumps(out), flush=True)
+
+
+def tree_batch(B, args):
+    """The tree workload's recipe at another batch size: step time, tree
+    elements per second and the workgroups per request the library picks."""
+    import torch
+    import synth
+    import rejection_sampling_verify_temp_amd as sv
+    B = int(B)
+    c = TREE
+    dev = torch.device("cuda:0")
+    copies = [synth.make_tree(B, c["N"], c["V"], dtype=torch.bfloat16, seed=31 + i,
+                              temps=(0.6, 1.0, 0.0, 0.8), corr=0.95, ragged=False, device=dev)
+              for i in range(args.rotate)]
+    h = sv.SpecVerify(B, 1, c["V"], torch.bfloat16, draft_dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        t = copies[i % len(copies)]
+        return h.run_tree(t.target, t.draft, t.tokens, t.parents, t.num_nodes, t.temperatures,
+                          seed=0, offset=i, stream=stream)
+
+    clock_ramp(step, args.ramp_ms, first=1 << 40)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert h.device_errors() & ~8 == 0
+    team = h.tree_team_size(B)
+    h.close()
+    return {"ms_per_step": ms, "value": B * c["N"] * c["V"] / (ms * 1e-3), "unit": "elems/s",
+            "team_size": team}
 
 
 def clock_ramp(step, ms, first):
@@ -573,6 +616,8 @@ def main():
                     help="--op typical: the probability threshold")
     ap.add_argument("--top-k", type=int, default=2, help="--op typical: the top-k clause")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tree-batches", default="32,128",
+                    help="--op tree: other batch sizes timed with the same recipe")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run one plain device copy of this "
                          "size (a known-size reference for HBM counters)")

@@ -81,6 +81,9 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
                                        with mass taken */
 #define SV_DEVERR_BAD_TREE 16u      /* a tree node whose parent is not an
                                        earlier node: never visited */
+#define SV_DEVERR_TREE_SYNC 32u     /* a team walk's exchange did not complete
+                                       within its time bound: that team's
+                                       outputs are invalid */
 
 typedef struct {
   int32_t max_batch;      /* largest B of any run, >= 1 */
@@ -294,8 +297,12 @@ int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K,
  *   out_num_accepted device [B] int32; out_last_node device [B] int32: the
  *                  deepest accepted node (0 = root).
  *
- * One workgroup per request walks its tree and reads only the rows of the
- * nodes it visits.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
+ * A team of workgroups walks each request's tree and reads only the rows of
+ * the nodes it visits: where the device launches cooperatively, four
+ * workgroups on different compute units each take a quarter of every row and
+ * exchange their partial statistics through device memory; otherwise one
+ * workgroup walks each request.  Calls on one handle share its exchange
+ * buffers and must not overlap.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
  * B < 0, N outside [1, SPEC_TREE_MAX_NODES]), SV_ERR_CAPACITY (B >
  * max_batch) or SV_ERR_HIP. */
 int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N,
@@ -374,6 +381,13 @@ const char *spec_verify_kernel_name(int32_t i);
 
 /* Chunk length (vocabulary elements per work item) the handle uses. */
 int32_t spec_verify_chunk_elems(spec_verify_t h);
+
+/* Workgroups that walk each request's tree in spec_verify_run_tree for a
+ * batch of B (has_draft != 0: with draft rows): 8 or 4 for a team walk, 1
+ * for one workgroup per request; 0 for a null handle or B < 1.  The handle
+ * picks the team by B against the teams its device holds at once (measured
+ * crossovers, stated where the pick is made).  Host-only. */
+int32_t spec_verify_tree_team_size(spec_verify_t h, int32_t B, int32_t has_draft);
 
 /* Frees the workspace and the handle (waits for the device first).
  * NULL is accepted. */

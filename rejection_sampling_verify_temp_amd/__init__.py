@@ -14,5 +14,5 @@ from .binding import (SpecVerify, SpecVerifyError, load_library, sv_config,  # n
                       spec_verify_chunk_elems, spec_draft_sample,
                       spec_ngram_propose, ngram_propose, spec_verify_run_typical,
                       spec_verify_run_tree, spec_verify_set_request_base,
-                      spec_verify_run_noalloc,
+                      spec_verify_run_noalloc, spec_verify_tree_team_size,
                       header_functions)

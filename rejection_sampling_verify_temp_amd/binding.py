@@ -23,6 +23,7 @@ SV_DEVERR_BAD_NUM_DRAFTS = 2
 SV_DEVERR_ZERO_RESIDUAL = 4
 SV_DEVERR_DRAW_ROUNDING = 8
 SV_DEVERR_BAD_TREE = 16
+SV_DEVERR_TREE_SYNC = 32
 
 
 class sv_config(ctypes.Structure):
@@ -87,6 +88,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.spec_verify_kernel_name.restype = ctypes.c_char_p
     lib.spec_verify_chunk_elems.argtypes = [P]
     lib.spec_verify_chunk_elems.restype = i32
+    lib.spec_verify_tree_team_size.argtypes = [P, i32, i32]
+    lib.spec_verify_tree_team_size.restype = i32
     lib.spec_verify_destroy.argtypes = [P]
     lib.spec_verify_destroy.restype = ctypes.c_int
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
@@ -214,6 +217,10 @@ def spec_verify_set_request_base(h, base: int) -> None:
     rc = load_library().spec_verify_set_request_base(h, int(base))
     if rc != SV_OK:
         raise SpecVerifyError("spec_verify_set_request_base", rc)
+
+
+def spec_verify_tree_team_size(h, B: int, has_draft: bool) -> int:
+    return load_library().spec_verify_tree_team_size(h, int(B), int(bool(has_draft)))
 
 
 def spec_verify_get_device_errors(h, clear: bool = False) -> int:
@@ -422,6 +429,10 @@ class SpecVerify:
 
     def device_errors(self, clear=False):
         return spec_verify_get_device_errors(self.handle, clear)
+
+    def tree_team_size(self, B, has_draft=True):
+        """Workgroups per request that run_tree uses for a batch of B."""
+        return spec_verify_tree_team_size(self.handle, B, has_draft)
 
     def set_request_base(self, base):
         """Global index of request 0 for later runs (a shard of a batch)."""

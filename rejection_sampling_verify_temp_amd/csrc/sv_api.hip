@@ -132,6 +132,12 @@ struct spec_verify_s {
   bool has_run = false;
   int32_t b_base = 0;  // global index of request 0 (spec_verify_set_request_base)
   int lds_per_cu = 0;  // bytes of LDS per compute unit (0: unknown, stats launches uncapped)
+  // token trees: teams of 4 and 8 resident at once (without and with draft
+  // rows; 0: no team walks) and their exchange words and counters (0
+  // between launches)
+  int tree_cap[2][2] = {{0, 0}, {0, 0}};
+  uint64_t* tree_xdat = nullptr;
+  uint32_t* tree_xdone = nullptr;
   // timing: per run, one start/stop pair per kernel
   bool timing = false;
   hipEvent_t ev[kTimingSlots][kEventsPerRun] = {};
@@ -149,6 +155,8 @@ void free_all(spec_verify_s* h) {
   if (h->desc) (void)hipFree(h->desc);
   if (h->rsum) (void)hipFree(h->rsum);
   if (h->flags) (void)hipFree(h->flags);
+  if (h->tree_xdat) (void)hipFree(h->tree_xdat);
+  if (h->tree_xdone) (void)hipFree(h->tree_xdone);
   for (int s = 0; s < kTimingSlots; ++s)
     for (int k = 0; k < kEventsPerRun; ++k)
       if (h->ev[s][k]) (void)hipEventDestroy(h->ev[s][k]);
@@ -252,6 +260,24 @@ int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
             hipMalloc(&h->rsum, (size_t)c.max_batch * nchunk * sv::kResidSplitMax * sizeof(double)) == hipSuccess &&
             hipMalloc(&h->flags, sizeof(uint32_t)) == hipSuccess &&
             hipMemset(h->flags, 0, sizeof(uint32_t)) == hipSuccess;
+  if (ok) {
+    size_t members = 0, teams = 0;  // the most over both team sizes
+    for (int d = 0; d < 2; ++d)
+      for (int k = 0; k < 2; ++k) {
+        const int g = k == 0 ? 4 : 8;
+        const int cap = sv::tree_team_capacity(c.device, c.target_dtype, c.draft_dtype, d != 0, g);
+        h->tree_cap[d][k] = cap;
+        if ((size_t)cap * g > members) members = (size_t)cap * g;
+        if ((size_t)cap > teams) teams = (size_t)cap;
+      }
+    if (teams > 0) {
+      const size_t bytes = members * sv::tree_team_words() * sizeof(uint64_t);
+      ok = hipMalloc(&h->tree_xdat, bytes) == hipSuccess &&
+           hipMalloc(&h->tree_xdone, teams * sizeof(uint32_t)) == hipSuccess &&
+           hipMemset(h->tree_xdat, 0, bytes) == hipSuccess &&
+           hipMemset(h->tree_xdone, 0, teams * sizeof(uint32_t)) == hipSuccess;
+    }
+  }
   if (!ok) {
     free_all(h);
     delete h;
@@ -370,10 +396,13 @@ int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N, const void* targ
   tp.V = c.vocab;
   tp.draft_is_probs = c.draft_is_probs;
   tp.b_base = h->b_base;
+  tp.xdat = h->tree_xdat;
+  tp.xdone = h->tree_xdone;
   DeviceGuard g(c.device);
   if (!g.ok) return SV_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (sv::launch_tree(tp, c.target_dtype, c.draft_dtype, s) != hipSuccess) return SV_ERR_HIP;
+  const int team = sv::tree_team_pick(B, h->tree_cap[draft_logits != nullptr]);
+  if (sv::launch_tree(tp, c.target_dtype, c.draft_dtype, team, s) != hipSuccess) return SV_ERR_HIP;
   h->last_stream = s;
   h->has_run = true;
   return SV_OK;
@@ -464,6 +493,11 @@ int spec_verify_timing_read(spec_verify_t h, float* total_ms, int32_t n, int32_t
 }
 
 int32_t spec_verify_chunk_elems(spec_verify_t h) { return h ? h->chunk : 0; }
+
+int32_t spec_verify_tree_team_size(spec_verify_t h, int32_t B, int32_t has_draft) {
+  if (h == nullptr || B < 1) return 0;
+  return sv::tree_team_pick(B, h->tree_cap[has_draft != 0]);
+}
 
 int spec_verify_destroy(spec_verify_t h) {
   if (h == nullptr) return SV_OK;

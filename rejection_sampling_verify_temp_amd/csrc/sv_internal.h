@@ -129,9 +129,27 @@ struct TreeParams {
   int B, N, V;
   int draft_is_probs;
   int b_base;  // global index of request 0 (Philox counters use b_base + b)
+  // Team walks (several workgroups per request): the exchange words and the
+  // per-team counters, all 0 between launches (zeroed once; every launch
+  // returns them to 0).
+  uint64_t* xdat;   // [teams][2][team size][8]
+  uint32_t* xdone;  // [teams]
 };
 
-hipError_t launch_tree(const TreeParams& p, int target_dtype, int draft_dtype,
+// 64-bit exchange words per team member.
+int tree_team_words();
+
+// Teams of g members (4 or 8) that can be resident at once on `device` for
+// these dtypes (the largest cooperative launch), or 0 where the device
+// cannot launch cooperatively.
+int tree_team_capacity(int device, int target_dtype, int draft_dtype, bool has_draft, int g);
+
+// Members per request for a batch of B, given the capacities of teams of 4
+// and 8 (cap[0], cap[1]); 1 is one 1024-thread workgroup per request.
+int tree_team_pick(int B, const int cap[2]);
+
+// Enqueues the walk with g members per request (from tree_team_pick).
+hipError_t launch_tree(const TreeParams& p, int target_dtype, int draft_dtype, int g,
                        hipStream_t stream);
 
 }  // namespace sv

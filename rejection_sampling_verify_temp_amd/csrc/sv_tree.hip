@@ -6,34 +6,55 @@
 // applied child by child (multi-step speculative sampling; the header of
 // include/spec_verify.h states it).
 //
-// One 1024-thread workgroup per request walks its tree and streams only the
-// rows of the nodes it visits:
-//   - at node v, one pass over target row v (and draft row v) gives the row
-//     max and normalizer (or the lowest argmax for greedy requests);
-//   - the children of v are tested in index order; after k rejections the
-//     law is max(0, p - c_k q) / Z_k, and each further sibling test needs
-//     Z_k, one more pass over the row pair;
-//   - where the walk stops, the emitted token is drawn by inverse CDF: one
-//     pass sums the law per slot of 64 vectors, a workgroup scan over the
-//     slot sums finds the slot holding u * S, and one wavefront re-reads that
-//     slot to find the element.
-// Row passes issue 160-224 KiB of 16-byte loads per workgroup before using any
-// (one round trip per round), through buffer resources, so the loads of a
+// A team of G workgroups walks one request's tree and streams only the rows
+// of the nodes it visits.  Each workgroup of the team takes a fixed share of
+// every row (G contiguous runs of 64-vector pieces), so a row pass runs on G
+// compute units at once:
+//   - at node v, one pass over target row v (and draft row v) gives each
+//     share's max and normalizer (or its lowest argmax for greedy requests);
+//     the team exchanges the shares and every workgroup folds them in the same
+//     order, so all hold the same row statistics;
+//   - the children of v are tested in index order by every workgroup alike
+//     (the same loads, the same Philox block, the same fp64 arithmetic); after
+//     k rejections the law is max(0, p - c_k q) / Z_k, and each further
+//     sibling test needs Z_k: one more pass over the row pair and one more
+//     exchange;
+//   - where the walk stops, the emitted token is drawn by inverse CDF: each
+//     workgroup sums the law per slot of 64 vectors of its share, the team
+//     exchanges the share totals, and the workgroup whose share holds u * S
+//     scans its slots and re-reads one slot to find the element.
+// The team is launched cooperatively, so its workgroups are resident
+// together; an exchange writes each value beside the exchange's tag in one
+// agent-scope atomic store, and spins (bounded in time) until every member's
+// words carry the tag.
+// Without a cooperative launch the team is one 1024-thread workgroup and the
+// exchanges vanish.
+//
+// Row passes issue 160-224 KiB of 16-byte loads per 1024 threads before using
+// any (one round trip per round), through buffer resources, so the loads of a
 // round cost no address registers and no branches, and no round waits at a
-// workgroup barrier.  The walk is sequential per request; requests run in
-// parallel, one per compute unit at the usual batch sizes.  A walk left
-// running alone is bound by its compute unit's arithmetic (~6 VALU slots per
-// element) more than by memory, so the inner loops keep per-element work to
-// the minimum: uniform tests for the row's end, fp32 sums per round.
+// workgroup barrier.  A walk that a single compute unit runs alone is bound by
+// that unit's arithmetic (~6 VALU slots per element) more than by memory;
+// spreading each row over a team's units is what shortens the longest walks,
+// which set the kernel's time once most requests are done.
 #include "sv_device.h"
 #include "sv_internal.h"
+
+// Tuning knob: a team size that overrides the pick (0: none).
+#ifndef SV_TREE_FORCE_TEAM
+#define SV_TREE_FORCE_TEAM 0
+#endif
 
 namespace sv {
 namespace {
 
-constexpr int kTreeThreads = 1024;
-constexpr int kTreeWaves = kTreeThreads / 64;
+constexpr int kSoloThreads = 1024;  // the workgroup of a walk without a team
+constexpr int kTeamThreads = 256;   // a team member's workgroup
 constexpr int kMaxNodes = SPEC_TREE_MAX_NODES;
+// A bounded wait: an exchange that has not completed within 20 ms of the
+// 100 MHz real-time clock gives up, flags the request and lets the team run
+// to its end without further waits.
+constexpr uint64_t kSpinTicks = 2000000;
 
 struct RowStats {
   float m;     // row max
@@ -44,32 +65,53 @@ struct RowStats {
 
 // A row is a scalar head [0, v0) up to the first 16-byte boundary, nvec
 // vectors from v0 and a scalar tail [t0, V) (chunk_geo over the whole row).
-// A pass takes the vectors in rounds: every thread issues all its loads of a
-// round (vectors b0 + u * 1024 + tid) before it uses any, so one round trip
-// to memory covers kRowVecs * 16 KiB of a single row (160 KiB), or kPairVecs
-// * 16 KiB of each row of a pair (224 KiB).  The 10 or 14 vectors take 40 or
-// 56 of the 128 registers a thread of a 1024-thread workgroup has; the
-// walk's own state takes most of the rest.
+// Workgroup gi of a team of G takes the vectors [vb, vb + nv): the row's
+// pieces of 64 vectors split into G contiguous runs, the head going to the
+// first workgroup and the tail to the last.
+struct Rng {
+  int vb, nv;
+  bool head, tail;
+};
+
+template <int G>
+__device__ __forceinline__ Rng row_range(const Geo& g, int gi) {
+  const int per = ((g.nvec + G - 1) / G + 63) / 64 * 64;
+  const int vb = min(g.nvec, gi * per);
+  Rng r;
+  r.vb = vb;
+  r.nv = min(g.nvec, vb + per) - vb;
+  r.head = gi == 0;
+  r.tail = gi == G - 1;
+  return r;
+}
+
+// A pass takes the share's vectors in rounds: every thread issues all its
+// loads of a round (vectors b0 + u * NT + tid of the share) before it uses
+// any, so one round trip to memory covers kRowVecs * 16 bytes per thread of
+// a single row, or kPairVecs * 16 of each row of a pair.  The 10 or 14
+// vectors take 40 or 56 of the 128 registers a thread has at four
+// wavefronts per SIMD; the walk's own state takes most of the rest.
 constexpr int kRowVecs = 10;
 constexpr int kPairVecs = 7;
-constexpr int kRound = kTreeThreads;  // vectors per unroll step of a round
 
-// Draw slots: slot 0 is the head, slot 1 + k the 64 vectors [64 k, 64 k + 64)
-// (one wavefront's share of one unroll step), the last slot the tail.
-__device__ __forceinline__ int num_slots(const Geo& g) { return (g.nvec + 63) / 64 + 2; }
+// Draw slots of a share: slot 0 is the row's head (empty but in the first
+// workgroup), slot 1 + k the share's 64 vectors [64 k, 64 k + 64) (one
+// wavefront's share of one unroll step), the last slot the row's tail.
+__device__ __forceinline__ int num_slots(const Rng& r) { return (r.nv + 63) / 64 + 2; }
 
 __device__ __forceinline__ const u32x4* vec_base(const void* row, const Geo& g, int bytes) {
   return reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + (size_t)g.v0 * bytes);
 }
 
-// The vectors of a row as a buffer resource (loads past the row return 0).
-__device__ __forceinline__ VecBuf vec_buf(const void* row, const Geo& g, int bytes) {
-  return make_vec_buf(vec_base(row, g, bytes), (uint32_t)g.nvec * 16u);
+// The share's vectors as a buffer resource (loads past the share return 0).
+__device__ __forceinline__ VecBuf vec_buf(const void* row, const Geo& g, const Rng& r, int bytes) {
+  return make_vec_buf(vec_base(row, g, bytes) + r.vb, (uint32_t)r.nv * 16u);
 }
 
-// Vector b0 + tid + u * kRound of the row, or 0 past its end.
+// Vector b0 + tid + u * NT of the share, or 0 past its end.
+template <int NT>
 __device__ __forceinline__ u32x4 vec_load(const VecBuf& vb, int b0, int u, int tid) {
-  return buf_load<false>(vb, (uint32_t)(b0 + u * kRound + tid) * 16u);
+  return buf_load<false>(vb, (uint32_t)(b0 + u * NT + tid) * 16u);
 }
 
 // The thread index, hidden from loop-invariant code motion: each pass
@@ -82,24 +124,118 @@ __device__ __forceinline__ int pass_tid() {
   return t;
 }
 
-// Statistics of one row (whole workgroup).  Sampling rows take each round in
-// two phases per wavefront: the wavefront's max of the round first, which
-// fixes one exponent reference for its 64 lanes, then the sums of
+// ---------------------------------------------------------------------------
+// The team: its workgroups exchange up to eight 32-bit values each per step
+// ---------------------------------------------------------------------------
+constexpr int kXWords = 8;  // words per member and exchange
+
+struct Team {
+  uint64_t* xdat;  // [teams][2][G][kXWords]: (exchange tag << 32) | value bits,
+                   // double-buffered by the exchange's parity; all 0 between launches
+  uint32_t* xdone; // [teams]: members that finished this launch; 0 between launches
+  int t, gi;       // team index, this workgroup's index in the team
+  uint32_t k;      // exchanges made so far in this launch
+  bool dead;       // a wait timed out: no more waits in this launch
+};
+
+// A double as two floats whose sum is within 2^-48 of it, and back.
+__device__ __forceinline__ void split_f64(double v, float& hi, float& lo) {
+  hi = (float)v;
+  lo = (float)(v - (double)hi);
+}
+__device__ __forceinline__ double join_f64(float hi, float lo) { return (double)hi + (double)lo; }
+
+// Every workgroup of the team calls this with its values mine[0..nw) (the
+// same in all of its threads); on return s_all[kXWords g + j] holds member
+// g's value j, in every workgroup.  Each value travels in a 64-bit word
+// beside the exchange's tag k + 1, written by one agent-scope atomic store,
+// so a reader that sees the tag in a word has that word's value: one round
+// trip per poll, and nothing for the writer to wait for.  Double buffering is
+// enough: a member can write exchange k + 2 only after every member has
+// written k + 1, which each does after reading exchange k.  The tags restart
+// at 1 in every launch, since team_done() returns the words to 0.
+template <int G>
+__device__ __forceinline__ void exchange(Team& tm, const float (&mine)[kXWords], int nw,
+                                         float* s_all, int* s_dead) {
+  const int tid = threadIdx.x;
+  __syncthreads();  // s_all's previous contents are read
+  if (tid < 64) {
+    bool dead = tm.dead;
+    uint64_t* slot = tm.xdat + ((size_t)tm.t * 2 + (tm.k & 1u)) * G * kXWords;
+    const uint32_t tag = tm.k + 1u;
+    const int j = tid & (kXWords - 1), g = tid / kXWords;
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < kXWords; ++i) v = j == i ? mine[i] : v;
+    if (!dead && tid < kXWords && j < nw)
+      __hip_atomic_store(slot + tm.gi * kXWords + j,
+                         ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    const bool reader = g < G && j < nw;
+    uint64_t w = 0;
+    if (!dead) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      for (;;) {
+        if (reader) w = __hip_atomic_load(slot + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__all(!reader || (uint32_t)(w >> 32) == tag)) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+          dead = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    // no partner's values after a timeout: the walk goes on with this one's, flagged
+    if (tid < kXWords * G) s_all[tid] = dead ? v : __builtin_bit_cast(float, (uint32_t)w);
+    if (tid == 0) *s_dead = dead ? 1 : 0;
+  }
+  __syncthreads();
+  tm.dead = *s_dead != 0;
+  ++tm.k;
+}
+
+// The end of a team's launch: the last member to arrive returns the team's
+// words and its counter to 0.  Every member arrives only after its last
+// exchange's reads, so no member still reads what is cleared.
+template <int G>
+__device__ __forceinline__ void team_done(Team& tm) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(tm.xdone + tm.t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == G - 1) {
+      uint64_t* w = tm.xdat + (size_t)tm.t * 2 * G * kXWords;
+      for (int i = 0; i < 2 * G * kXWords; ++i)
+        __hip_atomic_store(w + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the words are clear before the count
+      __hip_atomic_store(tm.xdone + tm.t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics
+// ---------------------------------------------------------------------------
+
+// Statistics of this workgroup's share of one row.  Sampling rows take each
+// round in two phases per wavefront: the wavefront's max of the round first,
+// which fixes one exponent reference for its 64 lanes, then the sums of
 // exp2(l c + ref) with no per-element max test.  A later round that raises a
 // wavefront's max rescales its sums once.  No round needs a workgroup
 // barrier, so the wavefronts drift apart and one's loads overlap another's
-// arithmetic; the wavefronts' sums meet once, at the row's reference.
-// Greedy rows keep the max and its lowest index.
-template <int DT>
+// arithmetic; the wavefronts' sums meet once, at the share's reference.
+// Greedy rows keep the max and its lowest index (INT32_MAX: none).
+template <int DT, int NT, int G>
 __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampling, float c,
-                                              float* ldsf, double* ldsd, int* ldsi) {
+                                              int gi, float* ldsf, double* ldsd, int* ldsi) {
   using E = Elt<DT>;
   constexpr int U = kRowVecs;
   const int tid = pass_tid();
   const Geo g = chunk_geo<DT>(row, 0, V);
-  const VecBuf vb = vec_buf(row, g, E::kBytes);
-  // each thread's scalar elements: one of the head, one of the tail
-  const bool has_h = tid < g.v0, has_t = g.t0 + tid < V;
+  const Rng rg = row_range<G>(g, gi);
+  const VecBuf vb = vec_buf(row, g, rg, E::kBytes);
+  // the head's scalar elements in the first workgroup, the tail's in the last
+  const bool has_h = rg.head && tid < g.v0, has_t = rg.tail && g.t0 + tid < V;
   const float hx = has_h ? E::at(row, tid) : kNegInf;
   const float tx = has_t ? E::at(row, g.t0 + tid) : kNegInf;
   RowStats st;
@@ -110,20 +246,20 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
       const int ix[1] = {tid};
       am_tile(a, x, ix);
     }
-    for (int b0 = 0; b0 < g.nvec; b0 += U * kRound) {
+    for (int b0 = 0; b0 < rg.nv; b0 += U * NT) {
       u32x4 d[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (b0 + u * kRound + tid < g.nvec) d[u] = vec_load(vb, b0, u, tid);
+        if (b0 + u * NT + tid < rg.nv) d[u] = vec_load<NT>(vb, b0, u, tid);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int vi = b0 + u * kRound + tid;
-        if (vi < g.nvec) {
+        const int vi = b0 + u * NT + tid;
+        if (vi < rg.nv) {
           float x[E::kVec];
           int ix[E::kVec];
           E::unpack(d[u], x);
 #pragma unroll
-          for (int k = 0; k < E::kVec; ++k) ix[k] = g.v0 + vi * E::kVec + k;
+          for (int k = 0; k < E::kVec; ++k) ix[k] = g.v0 + (rg.vb + vi) * E::kVec + k;
           am_tile(a, x, ix);
         }
       }
@@ -133,25 +269,25 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
       const int ix[1] = {g.t0 + tid};
       am_tile(a, x, ix);
     }
-    block_argmax<kTreeThreads>(a.M, a.I, ldsf, ldsi);
+    block_argmax<NT>(a.M, a.I, ldsf, ldsi);
     st.m = a.M;
-    st.arg = a.I == INT32_MAX ? 0 : a.I;
+    st.arg = a.I;
     st.ref = 0.f;
     st.z = 0.0;
     return st;
   }
   float Mw = kNegInf, Rw = 0.f;  // the wavefront's max and reference so far
   double S = 0.0;                // this thread's sum, relative to Rw
-  for (int b0 = 0; b0 == 0 || b0 < g.nvec; b0 += U * kRound) {
+  for (int b0 = 0; b0 == 0 || b0 < rg.nv; b0 += U * NT) {
     u32x4 d[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) d[u] = vec_load(vb, b0, u, tid);
-    // vectors past the row are skipped by a test that is uniform in all but
-    // one wavefront of the row (the loads there returned 0)
+    for (int u = 0; u < U; ++u) d[u] = vec_load<NT>(vb, b0, u, tid);
+    // vectors past the share are skipped by a test that is uniform in all
+    // but one wavefront (the loads there returned 0)
     float t = b0 == 0 ? fmaxf(hx, tx) : kNegInf;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (b0 + u * kRound + tid < g.nvec) {
+      if (b0 + u * NT + tid < rg.nv) {
         float x[E::kVec];
         E::unpack(d[u], x);
 #pragma unroll
@@ -169,7 +305,7 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
     float sr = b0 == 0 ? fast_exp2(fmaf(hx, c, Rw)) + fast_exp2(fmaf(tx, c, Rw)) : 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (b0 + u * kRound + tid < g.nvec) {
+      if (b0 + u * NT + tid < rg.nv) {
         // unpack again rather than keep the floats live: the empty asm hides
         // the first unpack from common-subexpression elimination
         u32x4 wv = d[u];
@@ -184,20 +320,76 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
     }
     S += (double)sr;
   }
-  const float M = block_max<kTreeThreads>(Mw, ldsf);
+  const float M = block_max<NT>(Mw, ldsf);
   const float R = ref_of(M, c);
   const double f = Mw == kNegInf ? 0.0 : (Mw == M ? 1.0 : exp2_diff(R, Rw));
   st.m = M;
   st.ref = R;
-  st.z = block_sum<kTreeThreads>(S * f, ldsd);
+  st.z = block_sum<NT>(S * f, ldsd);
   st.arg = 0;
   return st;
 }
 
-// The law the stop node draws from, per element (unnormalized, relative to
-// the target row's reference): p~ = exp2(l_p c + ref_p); for a pair,
-// max(0, p~ - kappa q~) with q~ = exp2(l_q c + ref_q) (or q itself for
-// probability drafts) and kappa split in two floats.
+// The row's statistics from the team's shares: member g's words at
+// x[kXWords g + o ...] are its max and then its sum (sampling: relative to its
+// own reference, split in two floats) or lowest argmax (greedy).  The shares
+// are folded in member order, so every member gets the same bits.
+template <int G>
+__device__ __forceinline__ RowStats fold_stats(const float* x, int o, bool sampling, float c) {
+  RowStats st;
+  float M = kNegInf;
+#pragma unroll
+  for (int g = 0; g < G; ++g) M = fmaxf(M, x[kXWords * g + o]);
+  st.m = M;
+  if (!sampling) {
+    int arg = INT32_MAX;
+#pragma unroll
+    for (int g = 0; g < G; ++g)  // the shares are in index order: the first one at M
+      if (arg == INT32_MAX && x[kXWords * g + o] == M)
+        arg = __builtin_bit_cast(int, x[kXWords * g + o + 1]);
+    st.arg = arg == INT32_MAX ? 0 : arg;
+    st.ref = 0.f;
+    st.z = 0.0;
+    return st;
+  }
+  const float R = ref_of(M, c);
+  double z = 0.0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float mg = x[kXWords * g + o];
+    const double zg = join_f64(x[kXWords * g + o + 1], x[kXWords * g + o + 2]);
+    z += mg == kNegInf ? 0.0 : (mg == M ? zg : zg * exp2_diff(R, ref_of(mg, c)));
+  }
+  st.ref = R;
+  st.z = z;
+  st.arg = 0;
+  return st;
+}
+
+// The sum of a value that every member sent split at x[kXWords g], in
+// member order.
+template <int G>
+__device__ __forceinline__ double fold_sum(const float* x) {
+  double z = 0.0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) z += join_f64(x[kXWords * g], x[kXWords * g + 1]);
+  return z;
+}
+
+// A workgroup's own share as the whole row's statistics (a team of one).
+__device__ __forceinline__ RowStats solo_stats(RowStats st, bool sampling) {
+  if (!sampling && st.arg == INT32_MAX) st.arg = 0;
+  return st;
+}
+
+// ---------------------------------------------------------------------------
+// The law the stop node draws from, and passes over it
+// ---------------------------------------------------------------------------
+
+// Per element (unnormalized, relative to the target row's reference):
+// p~ = exp2(l_p c + ref_p); for a pair, max(0, p~ - kappa q~) with
+// q~ = exp2(l_q c + ref_q) (or q itself for probability drafts) and kappa
+// split in two floats.
 struct Law {
   bool pair;
   float c, ref_p, ref_q, kap_hi, kap_lo;
@@ -218,9 +410,9 @@ __device__ __forceinline__ float law_at(const Law& L, const void* prow, const vo
   return law_of(L, Elt<TDT>::at(prow, i), L.pair ? Elt<DDT>::at(qrow, i) : 0.f);
 }
 
-// The law at the kVec elements of target vector vi.  The draft row's
-// elements come by one vector load when both rows have the same element
-// type and alignment (qvec), else element by element.
+// The law at the kVec elements of target vector vi (an index over the whole
+// row).  The draft row's elements come by one vector load when both rows have
+// the same element type and alignment (qvec), else element by element.
 template <int TDT, int DDT>
 __device__ __forceinline__ void law_vec(const Law& L, const void* prow, const void* qrow,
                                         const Geo& g, int vi, bool qvec, float* r) {
@@ -248,54 +440,54 @@ __device__ __forceinline__ bool same_alignment(const void* a, const void* b) {
   return ((reinterpret_cast<uintptr_t>(a) ^ reinterpret_cast<uintptr_t>(b)) & 15u) == 0;
 }
 
-// One pass over the law of a row (and, for a pair, of its draft row): calls
-// f(b, s) once per unroll step of every round, convergently, with s the
-// thread's fp32 sum of the law over its vector b + tid (0 past the vectors).
-// When the draft row has the target's element type and 16-byte alignment,
-// both rows' vectors of a round are loaded together, kPairVecs each (or
-// kRowVecs of a single row); otherwise the draft elements are loaded one by
-// one, a vector of the target at a time.
-template <int TDT, int DDT, typename F>
+// One pass over the law on this workgroup's share of a row (and, for a pair,
+// of its draft row): calls f(b, s) once per unroll step of every round,
+// convergently, with s the thread's fp32 sum of the law over the share's
+// vector b + tid (0 past the share).  When the draft row has the target's
+// element type and 16-byte alignment, both rows' vectors of a round are
+// loaded together, kPairVecs each (or kRowVecs of a single row); otherwise
+// the draft elements are loaded one by one, a vector of the target at a time.
+template <int TDT, int DDT, int NT, typename F>
 __device__ __forceinline__ void law_pass(const Law& L, const void* prow, const void* qrow,
-                                         const Geo& g, F&& f) {
+                                         const Geo& g, const Rng& rg, F&& f) {
   using EP = Elt<TDT>;
   constexpr int KV = EP::kVec;
   const int tid = pass_tid();
-  const VecBuf pb = vec_buf(prow, g, EP::kBytes);
+  const VecBuf pb = vec_buf(prow, g, rg, EP::kBytes);
   if (!L.pair) {
-    for (int b0 = 0; b0 < g.nvec; b0 += kRowVecs * kRound) {
+    for (int b0 = 0; b0 < rg.nv; b0 += kRowVecs * NT) {
       u32x4 d[kRowVecs];
 #pragma unroll
-      for (int u = 0; u < kRowVecs; ++u) d[u] = vec_load(pb, b0, u, tid);
+      for (int u = 0; u < kRowVecs; ++u) d[u] = vec_load<NT>(pb, b0, u, tid);
 #pragma unroll
       for (int u = 0; u < kRowVecs; ++u) {
-        float sv = 0.f;  // vectors past the row: a test uniform in all but one wavefront
-        if (b0 + u * kRound + tid < g.nvec) {
+        float sv = 0.f;  // vectors past the share: a test uniform in all but one wavefront
+        if (b0 + u * NT + tid < rg.nv) {
           float r[KV];
           EP::unpack(d[u], r);
 #pragma unroll
           for (int k = 0; k < KV; ++k) r[k] = law_of(L, r[k], 0.f);
           sv = pairwise_sum(r);
         }
-        f(b0 + u * kRound, sv);
+        f(b0 + u * NT, sv);
       }
     }
     return;
   }
   if constexpr (TDT == DDT) {
     if (same_alignment(prow, qrow)) {
-      const VecBuf qb = vec_buf(qrow, g, EP::kBytes);
-      for (int b0 = 0; b0 < g.nvec; b0 += kPairVecs * kRound) {
+      const VecBuf qb = vec_buf(qrow, g, rg, EP::kBytes);
+      for (int b0 = 0; b0 < rg.nv; b0 += kPairVecs * NT) {
         u32x4 dp[kPairVecs], dq[kPairVecs];
 #pragma unroll
         for (int u = 0; u < kPairVecs; ++u) {
-          dp[u] = vec_load(pb, b0, u, tid);
-          dq[u] = vec_load(qb, b0, u, tid);
+          dp[u] = vec_load<NT>(pb, b0, u, tid);
+          dq[u] = vec_load<NT>(qb, b0, u, tid);
         }
 #pragma unroll
         for (int u = 0; u < kPairVecs; ++u) {
           float sv = 0.f;
-          if (b0 + u * kRound + tid < g.nvec) {
+          if (b0 + u * NT + tid < rg.nv) {
             float lp[KV], lq[KV], r[KV];
             EP::unpack(dp[u], lp);
             EP::unpack(dq[u], lq);
@@ -303,35 +495,37 @@ __device__ __forceinline__ void law_pass(const Law& L, const void* prow, const v
             for (int k = 0; k < KV; ++k) r[k] = law_of(L, lp[k], lq[k]);
             sv = pairwise_sum(r);
           }
-          f(b0 + u * kRound, sv);
+          f(b0 + u * NT, sv);
         }
       }
       return;
     }
   }
-  for (int b0 = 0; b0 < g.nvec; b0 += kRound) {
+  for (int b0 = 0; b0 < rg.nv; b0 += NT) {
     float sv = 0.f;
-    if (b0 + tid < g.nvec) {
+    if (b0 + tid < rg.nv) {
       float r[KV];
-      law_vec<TDT, DDT>(L, prow, qrow, g, b0 + tid, false, r);
+      law_vec<TDT, DDT>(L, prow, qrow, g, rg.vb + b0 + tid, false, r);
       sv = pairwise_sum(r);
     }
     f(b0, sv);
   }
 }
 
-// Sum of the law over the row (whole workgroup, fp64 across vectors).
-template <int TDT, int DDT>
-__device__ __forceinline__ double law_sum(const Law& L, const void* prow, const void* qrow, int V, double* ldsd) {
+// Sum of the law over this workgroup's share (fp64 across vectors).
+template <int TDT, int DDT, int NT, int G>
+__device__ __forceinline__ double law_sum(const Law& L, const void* prow, const void* qrow, int V,
+                                          int gi, double* ldsd) {
   const int tid = pass_tid();
   const Geo g = chunk_geo<TDT>(prow, 0, V);
+  const Rng rg = row_range<G>(g, gi);
   double acc = 0.0;
-  if (tid < g.v0) acc += (double)law_at<TDT, DDT>(L, prow, qrow, tid);
+  if (rg.head && tid < g.v0) acc += (double)law_at<TDT, DDT>(L, prow, qrow, tid);
   // eight vector sums in fp32, then one fp64 add (every thread makes the
   // same number of calls, so the flush is uniform)
   float part = 0.f;
   int nv = 0;
-  law_pass<TDT, DDT>(L, prow, qrow, g, [&](int, float sv) {
+  law_pass<TDT, DDT, NT>(L, prow, qrow, g, rg, [&](int, float sv) {
     part += sv;
     asm volatile("" : "+v"(part));  // fold in order: no sums wait in registers
     if (++nv == 8) {
@@ -341,26 +535,29 @@ __device__ __forceinline__ double law_sum(const Law& L, const void* prow, const 
     }
   });
   acc += (double)part;
-  if (g.t0 + tid < V) acc += (double)law_at<TDT, DDT>(L, prow, qrow, g.t0 + tid);
-  return block_sum<kTreeThreads>(acc, ldsd);
+  if (rg.tail && g.t0 + tid < V) acc += (double)law_at<TDT, DDT>(L, prow, qrow, g.t0 + tid);
+  return block_sum<NT>(acc, ldsd);
 }
 
-// The law's sums per draw slot, by one pass over the row (or row pair).
-template <int TDT, int DDT>
+// The law's sums per draw slot of this workgroup's share, by one pass.
+template <int TDT, int DDT, int NT, int G>
 __device__ __forceinline__ void slot_pass(const Law& L, const void* prow, const void* qrow, int V,
-                          double* s_slot) {
+                                          int gi, double* s_slot) {
   const int tid = pass_tid(), lane = tid & 63, w = tid >> 6;
   const Geo g = chunk_geo<TDT>(prow, 0, V);
-  const int npieces = (g.nvec + 63) / 64, nslot = npieces + 2;
-  law_pass<TDT, DDT>(L, prow, qrow, g, [&](int b, float sv) {
+  const Rng rg = row_range<G>(g, gi);
+  const int npieces = (rg.nv + 63) / 64, nslot = npieces + 2;
+  law_pass<TDT, DDT, NT>(L, prow, qrow, g, rg, [&](int b, float sv) {
     const int piece = b / 64 + w;
     const double ws = (double)wave_sum_f32(sv);  // 64 vector sums: fp32 is ample
     if (lane == 0 && piece < npieces) s_slot[1 + piece] = ws;
   });
   if (w == 0) {
-    const double h = wave_sum(lane < g.v0 ? (double)law_at<TDT, DDT>(L, prow, qrow, lane) : 0.0);
-    const double t =
-        wave_sum(g.t0 + lane < V ? (double)law_at<TDT, DDT>(L, prow, qrow, g.t0 + lane) : 0.0);
+    const double h =
+        wave_sum(rg.head && lane < g.v0 ? (double)law_at<TDT, DDT>(L, prow, qrow, lane) : 0.0);
+    const double t = wave_sum(rg.tail && g.t0 + lane < V
+                                  ? (double)law_at<TDT, DDT>(L, prow, qrow, g.t0 + lane)
+                                  : 0.0);
     if (lane == 0) {
       s_slot[0] = h;
       s_slot[nslot - 1] = t;
@@ -374,37 +571,52 @@ __device__ __forceinline__ bool excluded(const int* ex, int nex, int i) {
   return false;
 }
 
-// The draw slot holding element i of the row.
-__device__ __forceinline__ int slot_of(const Geo& g, int nslot, int kv, int i) {
-  return i < g.v0 ? 0 : (i >= g.t0 ? nslot - 1 : 1 + (i - g.v0) / kv / 64);
+// The draw slot of this workgroup's share that holds element i of the row,
+// or -1 if another member's share holds it.
+__device__ __forceinline__ int slot_of(const Geo& g, const Rng& rg, int nslot, int kv, int i) {
+  if (i < g.v0) return rg.head ? 0 : -1;
+  if (i >= g.t0) return rg.tail ? nslot - 1 : -1;
+  const int vi = (i - g.v0) / kv;
+  if (vi < rg.vb || vi >= rg.vb + rg.nv) return -1;
+  return 1 + (vi - rg.vb) / 64;
 }
 
-// Inverse-CDF draw from the law with uniform u (whole workgroup), given its
-// sums per draw slot in s_slot (written by slot_pass); the
-// tokens in ex[0..nex) are removed.  A workgroup scan over the slot sums
-// finds the slot holding u * S, and wavefront 0 re-reads only that slot (one
-// vector per lane) to find the element.  Returns the token; *rounding is set
-// if u * S fell past the recomputed total, *empty if the law is 0.  A slot
-// that holds removed tokens is summed again with them zeroed (not reduced
-// by their values: a removed sibling can hold nearly all of the slot, and
-// the difference of two rounded sums would leave a residue far above the
-// mass that remains).
-template <int TDT, int DDT>
-__device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, const void* qrow, int V,
-                               const int* ex, int nex, double u, double* s_slot, double* s_woff,
-                               int* s_sel, double* s_th, bool* rounding, bool* empty) {
+struct DrawOut {
+  int token;      // the drawn token (in the member that found it; -1 elsewhere)
+  bool rounding;  // u * S fell past a recomputed total: nearest token with mass taken
+  bool empty;     // the law is 0
+};
+
+// Inverse-CDF draw from the law with uniform u, given its sums per draw slot
+// of this workgroup's share in s_slot (written by slot_pass); the tokens in
+// ex[0..nex) are removed.  A slot that holds removed tokens is summed again
+// with them zeroed (not reduced by their values: a removed sibling can hold
+// nearly all of the slot, and the difference of two rounded sums would leave
+// a residue far above the mass that remains).  The share totals are
+// exchanged; the member whose share holds u * S scans its slot sums to find
+// the slot, and its wavefront 0 re-reads only that slot (one vector per
+// lane) to find the element.
+template <int TDT, int DDT, int NT, int G>
+__device__ __forceinline__ DrawOut draw_from_slots(const Law& L, const void* prow, const void* qrow,
+                                                   int V, Team& tm, const int* ex, int nex, double u,
+                                                   double* s_slot, double* s_woff, int* s_sel,
+                                                   double* s_th, float* s_x, int* s_dead) {
   using EP = Elt<TDT>;
   constexpr int KV = EP::kVec;
+  constexpr int W = NT / 64;
   const int tid = pass_tid(), lane = tid & 63, w = tid >> 6;
   const Geo g = chunk_geo<TDT>(prow, 0, V);
+  const Rng rg = row_range<G>(g, tm.gi);
   const bool qvec = L.pair && same_alignment(prow, qrow);
-  const int nslot = num_slots(g);
+  const int nslot = num_slots(rg);
+  DrawOut out{-1, false, false};
   __syncthreads();
   if (w == 0) {  // slots holding removed tokens, summed again without them
     for (int k = 0; k < nex; ++k) {  // uniform over the wavefront
-      const int sl = slot_of(g, nslot, KV, ex[k]);
+      const int sl = slot_of(g, rg, nslot, KV, ex[k]);
+      if (sl < 0) continue;
       bool seen = false;
-      for (int k2 = 0; k2 < k; ++k2) seen = seen || slot_of(g, nslot, KV, ex[k2]) == sl;
+      for (int k2 = 0; k2 < k; ++k2) seen = seen || slot_of(g, rg, nslot, KV, ex[k2]) == sl;
       if (seen) continue;
       float r[KV];
       int base;
@@ -414,9 +626,9 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
         base = sl == 0 ? lane : g.t0 + lane;
         if (sl == 0 ? lane < g.v0 : base < V) r[0] = law_at<TDT, DDT>(L, prow, qrow, base);
       } else {
-        const int vi = (sl - 1) * 64 + lane;
+        const int vi = rg.vb + (sl - 1) * 64 + lane;
         base = g.v0 + vi * KV;
-        if (vi < g.nvec) law_vec<TDT, DDT>(L, prow, qrow, g, vi, qvec, r);
+        if (vi < rg.vb + rg.nv) law_vec<TDT, DDT>(L, prow, qrow, g, vi, qvec, r);
       }
       for (int e = 0; e < nex; ++e) {  // a select per element, no early exit
         const int t = ex[e];
@@ -433,8 +645,8 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
   }
   __syncthreads();
 
-  // (2) scan of the slot sums: thread t takes slots [t sp, t sp + sp)
-  const int sp = (nslot + kTreeThreads - 1) / kTreeThreads;
+  // (2) scan of the share's slot sums: thread t takes slots [t sp, t sp + sp)
+  const int sp = (nslot + NT - 1) / NT;
   const int k0 = min(nslot, tid * sp), k1 = min(nslot, k0 + sp);
   double loc = 0.0;
   int lastpos = -1;
@@ -447,19 +659,58 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
   double q = lane_before(incl);
   if (lane == 0) q = 0.0;
   __syncthreads();
-  double total = 0.0;
-  for (int k = 0; k < kTreeWaves; ++k) {
+  double mine_total = 0.0;
+  for (int k = 0; k < W; ++k) {
     if (k < w) q += s_woff[k];
-    total += s_woff[k];
+    mine_total += s_woff[k];
   }
-  *empty = !(total > 0.0);
-  if (*empty) {
+  // (3) the team's totals, in member order: the prefix before this share,
+  // the total, and the member whose share holds theta
+  double before = 0.0, total = mine_total;
+  int owner = 0;
+  bool past = false;
+  if constexpr (G > 1) {
+    float mine[kXWords] = {};
+    split_f64(mine_total, mine[0], mine[1]);
+    exchange<G>(tm, mine, 2, s_x, s_dead);
+    total = 0.0;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+      if (m == tm.gi) before = total;
+      total += join_f64(s_x[kXWords * m], s_x[kXWords * m + 1]);
+    }
+  }
+  out.empty = !(total > 0.0);
+  if (out.empty) {
     __syncthreads();
-    return -1;
+    return out;
   }
   const double theta = u * total;
-  if (loc > 0.0 && q <= theta && theta < q + loc) {
-    double acc = q;
+  if constexpr (G > 1) {
+    owner = -1;
+    int lastm = 0;
+    double acc = 0.0;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+      const double tm_ = join_f64(s_x[kXWords * m], s_x[kXWords * m + 1]);
+      if (tm_ > 0.0) {
+        lastm = m;
+        if (owner < 0 && acc <= theta && theta < acc + tm_) owner = m;
+      }
+      acc += tm_;
+    }
+    if (owner < 0) {  // theta at or past the total: the last share with mass
+      owner = lastm;
+      past = true;
+    }
+  }
+  if (owner != tm.gi) {
+    __syncthreads();
+    out.rounding = past;
+    return out;
+  }
+  if (!past && loc > 0.0 && before + q <= theta && theta < before + q + loc) {
+    double acc = before + q;
     for (int k = k0; k < k1; ++k) {
       if (s_slot[k] > 0.0 && theta < acc + s_slot[k]) {
         *s_sel = k;
@@ -470,9 +721,9 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
     }
   }
   __syncthreads();
-  *rounding = false;
-  if (*s_sel < 0) {  // theta at or past the total: the last slot with mass
-    *rounding = true;
+  out.rounding = past;
+  if (*s_sel < 0) {  // theta at or past the share's total: its last slot with mass
+    out.rounding = true;
     __syncthreads();
     if (lastpos >= 0) atomicMax(s_sel, lastpos);
     if (tid == 0) *s_th = __builtin_inf();
@@ -481,7 +732,7 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
   const int sel = *s_sel;
   const double th = *s_th;
 
-  // (3) wavefront 0 finds the element inside slot sel
+  // (4) wavefront 0 finds the element inside slot sel
   if (w == 0) {
     float r[KV];
     int base;  // index of r[0]
@@ -493,9 +744,9 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
 #pragma unroll
       for (int k = 1; k < KV; ++k) r[k] = 0.f;
     } else {
-      const int vi = (sel - 1) * 64 + lane;
+      const int vi = rg.vb + (sel - 1) * 64 + lane;
       base = g.v0 + vi * KV;
-      cnt = vi < g.nvec ? KV : 0;
+      cnt = vi < rg.vb + rg.nv ? KV : 0;
       if (cnt) {
         law_vec<TDT, DDT>(L, prow, qrow, g, vi, qvec, r);
       } else {
@@ -516,13 +767,13 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
 #pragma unroll
     for (int k = 0; k < KV; ++k) ls += (double)r[k];
     const double li = wave_incl_scan(ls, lane);
-    double before = lane_before(li);
-    if (lane == 0) before = 0.0;
-    const uint64_t hit = __ballot(ls > 0.0 && before <= th && th < li);
+    double lb = lane_before(li);
+    if (lane == 0) lb = 0.0;
+    const uint64_t hit = __ballot(ls > 0.0 && lb <= th && th < li);
     const uint64_t has = __ballot(ls > 0.0);
     const int src = hit ? (int)__builtin_ctzll(hit) : (has ? 63 - (int)__builtin_clzll(has) : 0);
     if (lane == src) {
-      double a = before;
+      double a = lb;
       int y = -1, lp = -1;
 #pragma unroll
       for (int k = 0; k < KV; ++k) {
@@ -532,16 +783,15 @@ __device__ __forceinline__ int draw_from_slots(const Law& L, const void* prow, c
           lp = base + k;
         }
       }
-      if (!hit) *rounding = true;
       *s_sel = y >= 0 ? y : (lp >= 0 ? lp : base);
       if (!hit || y < 0) *s_th = -1.0;  // marks a rounding fallback
     }
   }
   __syncthreads();
-  const int token = *s_sel;
-  if (*s_th == -1.0) *rounding = true;
+  out.token = *s_sel;
+  if (*s_th == -1.0) out.rounding = true;
   __syncthreads();
-  return token;
+  return out;
 }
 
 // The walk's per-child scalar math (fp64 exponentials, Philox).  Every lane
@@ -579,148 +829,271 @@ __device__ __forceinline__ Uniforms tree_uniforms(uint64_t seed, uint64_t offset
   return u;
 }
 
-template <int TDT, int DDT, bool HAS_DRAFT>
-__global__ __launch_bounds__(kTreeThreads) void k_tree(const TreeParams p) {
+// NT threads per workgroup, G workgroups per team.  Team t walks requests
+// t, t + teams, ...; member 0 writes the accepted path, the count, the last
+// node and the padding, the member that draws writes the emitted token.
+template <int TDT, int DDT, bool HAS_DRAFT, int NT, int G>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_tree(
+    const TreeParams p) {
+  constexpr int W = NT / 64;
   __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_ex[kMaxNodes];
-  __shared__ float ldsf[kTreeWaves];
-  __shared__ double ldsd[kTreeWaves];
-  __shared__ int ldsi[kTreeWaves];
-  __shared__ double s_woff[kTreeWaves];
-  __shared__ double s_slot[kMaxVocab / 256 + 2];  // draw slots: 64 vectors each
+  __shared__ float ldsf[W];
+  __shared__ double ldsd[W];
+  __shared__ int ldsi[W];
+  __shared__ double s_woff[W];
+  __shared__ double s_slot[kMaxVocab / (256 * G) + 4];  // draw slots of a share: 64 vectors each
   __shared__ int s_sel;
   __shared__ double s_th;
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ float s_x[kXWords * G];
+  __shared__ int s_dead;
+  const int tid = threadIdx.x;
   const int N = p.N, V = p.V;
-  int n = p.nn[b];
-  const bool bad_n = n < 1 || n > N;
-  n = n < 1 ? 1 : (n > N ? N : n);
-  for (int i = tid; i < n; i += kTreeThreads) {
-    s_par[i] = p.parents[(size_t)b * N + i];
-    s_tok[i] = p.tokens[(size_t)b * N + i];
-  }
-  __syncthreads();
-  uint32_t fl = bad_n ? SV_DEVERR_BAD_NUM_DRAFTS : 0u;
-  if (tid == 0)
-    for (int i = 1; i < n; ++i)
-      if (s_par[i] < 0 || s_par[i] >= i) fl |= SV_DEVERR_BAD_TREE;
+  Team tm;
+  tm.xdat = p.xdat;
+  tm.xdone = p.xdone;
+  tm.gi = G == 1 ? 0 : (int)(blockIdx.x % G);
+  tm.t = G == 1 ? (int)blockIdx.x : (int)(blockIdx.x / G);
+  tm.k = 0;
+  tm.dead = false;
+  const int teams = G == 1 ? (int)gridDim.x : (int)(gridDim.x / G);
+  const bool lead = tm.gi == 0;
 
-  const float T = p.temps[b];
-  const bool sampling = is_sampling(T);
-  const float c = sampling ? temp_scale(T) : 0.f;
-  const bool probs = p.draft_is_probs != 0;
-  int v = 0, nacc = 0, y = 0;
-  int32_t* out = p.out_tokens + (size_t)b * N;
+  for (int b = tm.t; b < p.B; b += teams) {
+    int n = p.nn[b];
+    const bool bad_n = n < 1 || n > N;
+    n = n < 1 ? 1 : (n > N ? N : n);
+    __syncthreads();  // the previous request's tree is no longer read
+    for (int i = tid; i < n; i += NT) {
+      s_par[i] = p.parents[(size_t)b * N + i];
+      s_tok[i] = p.tokens[(size_t)b * N + i];
+    }
+    __syncthreads();
+    uint32_t fl = bad_n ? SV_DEVERR_BAD_NUM_DRAFTS : 0u;
+    if (tid == 0 && lead)
+      for (int i = 1; i < n; ++i)
+        if (s_par[i] < 0 || s_par[i] >= i) fl |= SV_DEVERR_BAD_TREE;
 
-  for (;;) {
-    const void* prow = row_ptr(p.target, TDT, (size_t)b * N + v, V);
-    const void* qrow = HAS_DRAFT ? row_ptr(p.draft, DDT, (size_t)b * N + v, V) : nullptr;
-    const RowStats ps = row_stats<TDT>(prow, V, sampling, c, ldsf, ldsd, ldsi);
-    RowStats qs{0.f, 0.f, 1.0, 0};
-    if (HAS_DRAFT && sampling && !probs) qs = row_stats<DDT>(qrow, V, true, c, ldsf, ldsd, ldsi);
+    const float T = p.temps[b];
+    const bool sampling = is_sampling(T);
+    const float c = sampling ? temp_scale(T) : 0.f;
+    const bool probs = p.draft_is_probs != 0;
+    int v = 0, nacc = 0, y = 0;
+    bool drew = false;  // this member drew the emitted token
+    int32_t* out = p.out_tokens + (size_t)b * N;
 
-    // the children of v, in index order
-    double ck = 0.0, Zk = 1.0;  // law after k rejections (probabilistic)
-    int nex = 0, nrej = 0, next = -1;
-    for (int ch = v + 1; ch < n; ++ch) {
-      if (s_par[ch] != v) continue;
-      const int x = s_tok[ch];
-      const bool valid = x >= 0 && x < V;
-      if (!valid) fl |= SV_DEVERR_BAD_DRAFT_ID;
-      bool accept;
-      if (!sampling) {
-        accept = valid && Elt<TDT>::at(prow, x) == ps.m;
+    for (;;) {
+      const void* prow = row_ptr(p.target, TDT, (size_t)b * N + v, V);
+      const void* qrow = HAS_DRAFT ? row_ptr(p.draft, DDT, (size_t)b * N + v, V) : nullptr;
+      const bool need_q = HAS_DRAFT && sampling && !probs;
+      RowStats ps = row_stats<TDT, NT, G>(prow, V, sampling, c, tm.gi, ldsf, ldsd, ldsi);
+      RowStats qs{0.f, 0.f, 1.0, 0};
+      if (need_q) qs = row_stats<DDT, NT, G>(qrow, V, true, c, tm.gi, ldsf, ldsd, ldsi);
+      if constexpr (G == 1) {
+        ps = solo_stats(ps, sampling);
       } else {
-        double ratio = 0.0, px = 0.0;
-        if (valid) {
-          const float lq = HAS_DRAFT ? Elt<DDT>::at(qrow, x) : 0.f;
-          const Odds o = child_odds(Elt<TDT>::at(prow, x), lq, c, ps.ref, ps.z, qs.ref, qs.z, ck,
-                                    Zk, !HAS_DRAFT ? 0 : (probs ? 2 : 1),
-                                    !HAS_DRAFT && excluded(s_ex, nex, x));
-          px = o.px;
-          ratio = o.ratio;
+        float mine[kXWords] = {};
+        mine[0] = ps.m;
+        if (sampling) {
+          split_f64(ps.z, mine[1], mine[2]);
+        } else {
+          mine[1] = __builtin_bit_cast(float, ps.arg);
         }
-        const Uniforms un = tree_uniforms(p.seed, p.offset, p.b_base + b, ch - 1);
-        accept = un.acc < ratio;
-        // one-hot: a rejected token leaves the law, which is renormalized
-        if (!accept && !HAS_DRAFT && valid && !excluded(s_ex, nex, x)) Zk -= px;
+        mine[3] = qs.m;
+        split_f64(qs.z, mine[4], mine[5]);
+        exchange<G>(tm, mine, need_q ? 6 : (sampling ? 3 : 2), s_x, &s_dead);
+        ps = fold_stats<G>(s_x, 0, sampling, c);
+        if (need_q) qs = fold_stats<G>(s_x, 3, true, c);
       }
-      if (accept) {
-        next = ch;
-        break;
-      }
-      ++nrej;
-      if (sampling && !HAS_DRAFT) {
-        if (valid && !excluded(s_ex, nex, x)) {
-          __syncthreads();
-          if (tid == 0) s_ex[nex] = x;
-          __syncthreads();
-          ++nex;
+
+      // the children of v, in index order
+      double ck = 0.0, Zk = 1.0;  // law after k rejections (probabilistic)
+      int nex = 0, nrej = 0, next = -1;
+      for (int ch = v + 1; ch < n; ++ch) {
+        if (s_par[ch] != v) continue;
+        const int x = s_tok[ch];
+        const bool valid = x >= 0 && x < V;
+        if (!valid) fl |= SV_DEVERR_BAD_DRAFT_ID;
+        bool accept;
+        if (!sampling) {
+          accept = valid && Elt<TDT>::at(prow, x) == ps.m;
+        } else {
+          double ratio = 0.0, px = 0.0;
+          if (valid) {
+            const float lq = HAS_DRAFT ? Elt<DDT>::at(qrow, x) : 0.f;
+            const Odds o = child_odds(Elt<TDT>::at(prow, x), lq, c, ps.ref, ps.z, qs.ref, qs.z, ck,
+                                      Zk, !HAS_DRAFT ? 0 : (probs ? 2 : 1),
+                                      !HAS_DRAFT && excluded(s_ex, nex, x));
+            px = o.px;
+            ratio = o.ratio;
+          }
+          const Uniforms un = tree_uniforms(p.seed, p.offset, p.b_base + b, ch - 1);
+          accept = un.acc < ratio;
+          // one-hot: a rejected token leaves the law, which is renormalized
+          if (!accept && !HAS_DRAFT && valid && !excluded(s_ex, nex, x)) Zk -= px;
         }
-      } else if (sampling) {  // the law left by this rejection: needs Z_{k+1}
-        ck += Zk;
-        bool more = false;
-        for (int c2 = ch + 1; c2 < n && !more; ++c2) more = s_par[c2] == v;
-        if (more) {
-          Law L{true, c, ps.ref, qs.ref, 0.f, 0.f, probs};
+        if (accept) {
+          next = ch;
+          break;
+        }
+        ++nrej;
+        if (sampling && !HAS_DRAFT) {
+          if (valid && !excluded(s_ex, nex, x)) {
+            __syncthreads();
+            if (tid == 0) s_ex[nex] = x;
+            __syncthreads();
+            ++nex;
+          }
+        } else if (sampling) {  // the law left by this rejection: needs Z_{k+1}
+          ck += Zk;
+          bool more = false;
+          for (int c2 = ch + 1; c2 < n && !more; ++c2) more = s_par[c2] == v;
+          if (more) {
+            Law L{true, c, ps.ref, qs.ref, 0.f, 0.f, probs};
+            const double kap = ck * ps.z / (probs ? 1.0 : qs.z);
+            L.kap_hi = (float)kap;
+            L.kap_lo = (float)(kap - (double)L.kap_hi);
+            double zs = law_sum<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, ldsd);
+            if constexpr (G > 1) {
+              float mine[kXWords] = {};
+              split_f64(zs, mine[0], mine[1]);
+              exchange<G>(tm, mine, 2, s_x, &s_dead);
+              zs = fold_sum<G>(s_x);
+            }
+            Zk = zs / ps.z;
+          }
+        }
+      }
+      if (next >= 0) {
+        if (tid == 0 && lead) out[nacc] = s_tok[next];
+        ++nacc;
+        v = next;
+        continue;
+      }
+      // every child rejected, or a leaf: the emitted token is drawn at v
+      if (!sampling) {
+        y = ps.arg;
+        drew = lead;
+      } else {
+        const double u_rec = tree_uniforms(p.seed, p.offset, p.b_base + b, v).rec;
+        Law L{false, c, ps.ref, qs.ref, 0.f, 0.f, probs};
+        if (HAS_DRAFT && nrej > 0) {
+          L.pair = true;
           const double kap = ck * ps.z / (probs ? 1.0 : qs.z);
           L.kap_hi = (float)kap;
           L.kap_lo = (float)(kap - (double)L.kap_hi);
-          Zk = law_sum<TDT, DDT>(L, prow, qrow, V, ldsd) / ps.z;
         }
+        slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, s_slot);
+        DrawOut d = draw_from_slots<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, nex, u_rec, s_slot,
+                                                     s_woff, &s_sel, &s_th, s_x, &s_dead);
+        if (d.empty) {  // no mass left: draw from p itself
+          fl |= SV_DEVERR_ZERO_RESIDUAL;
+          L.pair = false;
+          slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, s_slot);
+          d = draw_from_slots<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, 0, u_rec, s_slot, s_woff,
+                                               &s_sel, &s_th, s_x, &s_dead);
+        }
+        y = d.token;
+        drew = d.token >= 0;
+        if (d.empty) {  // p itself has no mass (a row of -inf)
+          y = -1;
+          drew = lead;
+        }
+        if (d.rounding) fl |= SV_DEVERR_DRAW_ROUNDING;
       }
+      break;
     }
-    if (next >= 0) {
-      if (tid == 0) out[nacc] = s_tok[next];
-      ++nacc;
-      v = next;
-      continue;
-    }
-    // every child rejected, or a leaf: the emitted token is drawn at v
-    if (!sampling) {
-      y = ps.arg;
-    } else {
-      const double u_rec = tree_uniforms(p.seed, p.offset, p.b_base + b, v).rec;
-      Law L{false, c, ps.ref, qs.ref, 0.f, 0.f, probs};
-      if (HAS_DRAFT && nrej > 0) {
-        L.pair = true;
-        const double kap = ck * ps.z / (probs ? 1.0 : qs.z);
-        L.kap_hi = (float)kap;
-        L.kap_lo = (float)(kap - (double)L.kap_hi);
+    if (tm.dead) fl |= SV_DEVERR_TREE_SYNC;
+    if (lead)
+      for (int i = nacc + 1 + tid; i < N; i += NT) out[i] = -1;
+    if (tid == 0) {
+      if (drew) out[nacc] = y;
+      if (lead) {
+        p.out_nacc[b] = nacc;
+        p.out_last[b] = v;
       }
-      slot_pass<TDT, DDT>(L, prow, qrow, V, s_slot);
-      bool rounding = false, empty = false;
-      y = draw_from_slots<TDT, DDT>(L, prow, qrow, V, s_ex, nex, u_rec, s_slot, s_woff, &s_sel,
-                                    &s_th, &rounding, &empty);
-      if (empty) {  // no mass left: draw from p itself
-        fl |= SV_DEVERR_ZERO_RESIDUAL;
-        L.pair = false;
-        slot_pass<TDT, DDT>(L, prow, qrow, V, s_slot);
-        y = draw_from_slots<TDT, DDT>(L, prow, qrow, V, s_ex, 0, u_rec, s_slot, s_woff, &s_sel,
-                                      &s_th, &rounding, &empty);
-      }
-      if (rounding) fl |= SV_DEVERR_DRAW_ROUNDING;
+      if (fl) atomicOr(p.flags, fl);
     }
-    break;
+    if constexpr (G == 1) break;  // one request per workgroup
   }
-  for (int i = nacc + 1 + tid; i < N; i += kTreeThreads) out[i] = -1;
-  if (tid == 0) {
-    out[nacc] = y;
-    p.out_nacc[b] = nacc;
-    p.out_last[b] = v;
-    if (fl) atomicOr(p.flags, fl);
-  }
+  if constexpr (G > 1) team_done<G>(tm);
+}
+
+template <int TDT, int DDT, bool HD, int G>
+const void* team_kernel() {
+  return reinterpret_cast<const void*>(&k_tree<TDT, DDT, HD, kTeamThreads, G>);
+}
+
+template <int TDT, int DDT, bool HD, int G>
+hipError_t launch_team(const TreeParams& p, int teams, hipStream_t s) {
+  TreeParams q = p;
+  void* args[] = {&q};
+  return hipLaunchCooperativeKernel(team_kernel<TDT, DDT, HD, G>(), dim3((unsigned)(teams * G)),
+                                    dim3(kTeamThreads), args, 0, s);
+}
+
+template <int TDT, int DDT, bool HD>
+hipError_t launch_one(const TreeParams& p, int g, int teams, hipStream_t s) {
+  if (g == 8) return launch_team<TDT, DDT, HD, 8>(p, teams, s);
+  if (g == 4) return launch_team<TDT, DDT, HD, 4>(p, teams, s);
+  hipLaunchKernelGGL((k_tree<TDT, DDT, HD, kSoloThreads, 1>), dim3((unsigned)p.B),
+                     dim3(kSoloThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int G>
+const void* team_kernel_for(int tdt, int ddt, bool has_draft) {
+  const bool t32 = tdt == SV_F32, d32 = ddt == SV_F32;
+  if (has_draft)
+    return t32 ? (d32 ? team_kernel<SV_F32, SV_F32, true, G>() : team_kernel<SV_F32, SV_BF16, true, G>())
+               : (d32 ? team_kernel<SV_BF16, SV_F32, true, G>()
+                      : team_kernel<SV_BF16, SV_BF16, true, G>());
+  return t32 ? (d32 ? team_kernel<SV_F32, SV_F32, false, G>() : team_kernel<SV_F32, SV_BF16, false, G>())
+             : (d32 ? team_kernel<SV_BF16, SV_F32, false, G>()
+                    : team_kernel<SV_BF16, SV_BF16, false, G>());
 }
 
 }  // namespace
 
-hipError_t launch_tree(const TreeParams& p, int tdt, int ddt, hipStream_t s) {
-  const dim3 g((unsigned)p.B), t(kTreeThreads);
+int tree_team_words() { return 2 * kXWords; }
+
+int tree_team_capacity(int device, int tdt, int ddt, bool has_draft, int g) {
+  int coop = 0, cus = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (!coop || (g != 4 && g != 8)) return 0;
+  const void* f = g == 8 ? team_kernel_for<8>(tdt, ddt, has_draft)
+                         : team_kernel_for<4>(tdt, ddt, has_draft);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kTeamThreads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return per_cu * cus / g;
+}
+
+int tree_team_pick(int B, const int cap[2]) {
+  if (SV_TREE_FORCE_TEAM == 1) return 1;
+  if (SV_TREE_FORCE_TEAM == 4 || SV_TREE_FORCE_TEAM == 8) {
+    const int c = cap[SV_TREE_FORCE_TEAM == 8 ? 1 : 0];
+    return c > 0 && B <= c ? SV_TREE_FORCE_TEAM : 1;
+  }
+  // measured on MI355X (B = 8 .. 512 trees of 16 nodes, V = 152064 bf16):
+  // the larger team wins while the teams fill at most three quarters of
+  // their slots (B <= 96 for eight members, B <= 192 for four); beyond that
+  // the exchanges cost more than the shorter row passes save
+  if (cap[1] > 0 && 4 * B <= 3 * cap[1]) return 8;
+  if (cap[0] > 0 && 4 * B <= 3 * cap[0]) return 4;
+  return 1;
+}
+
+hipError_t launch_tree(const TreeParams& p, int tdt, int ddt, int g, hipStream_t s) {
   const bool d = p.draft != nullptr;
-#define SV_TREE_LAUNCH(T, D)                                                   \
-  if (d)                                                                       \
-    hipLaunchKernelGGL((k_tree<T, D, true>), g, t, 0, s, p);                   \
-  else                                                                         \
-    hipLaunchKernelGGL((k_tree<T, D, false>), g, t, 0, s, p);
+  const int teams = p.B;  // a team per request (the pick keeps B within the teams' slots)
+#define SV_TREE_LAUNCH(T, D) \
+  return d ? launch_one<T, D, true>(p, g, teams, s) : launch_one<T, D, false>(p, g, teams, s);
   if (tdt == SV_F32 && ddt == SV_F32) {
     SV_TREE_LAUNCH(SV_F32, SV_F32)
   } else if (tdt == SV_F32) {
@@ -731,7 +1104,6 @@ hipError_t launch_tree(const TreeParams& p, int tdt, int ddt, hipStream_t s) {
     SV_TREE_LAUNCH(SV_BF16, SV_BF16)
   }
 #undef SV_TREE_LAUNCH
-  return hipGetLastError();
 }
 
 }  // namespace sv

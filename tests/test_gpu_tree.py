@@ -170,3 +170,59 @@ def test_benchmark_shape(svlib):
                         temps=(0.6, 1.0, 0.0, 0.8), corr=0.95, ragged=False, device="cuda")
     rep, _ = check(svlib, w, seed=0, offset=0)
     assert rep.accepted > 0
+
+
+# Batches whose team walks differ on MI355X (256 compute units): eight
+# workgroups per request up to B = 96, four up to B = 192, one beyond.
+TEAM_CASES = {
+    40: dict(dtype=torch.bfloat16, temps=(1.0, 0.6, 0.0)),
+    100: dict(dtype=torch.bfloat16, temps=(0.8, 0.0, 1.2)),
+    200: dict(temps=(1.0, 0.7)),
+}
+
+
+@pytest.mark.parametrize("B", sorted(TEAM_CASES))
+def test_team_sizes(svlib, B):
+    """Logit, one-hot and probability-draft trees at batches that run teams of
+    8 and 4 workgroups and single workgroups, against the oracle."""
+    V = 20011  # an odd vocabulary: unaligned rows, a head and a tail in every row
+    h = svlib.SpecVerify(B, 1, V, torch.float32)
+    say(f"[gpu] tree team size at B={B}: {h.tree_team_size(B)} (one-hot {h.tree_team_size(B, False)})")
+    h.close()
+    w = synth.make_tree(B, 12, V, seed=50 + B, corr=0.9, device="cuda", **TEAM_CASES[B])
+    check(svlib, w, seed=B, offset=1)
+    w = synth.make_tree(B, 10, V, seed=51 + B, onehot=True, temps=(1.0, 0.5), device="cuda")
+    check(svlib, w, seed=B, offset=2)
+    w = synth.make_tree(B, 8, V, seed=52 + B, temps=(1.0,), device="cuda")
+    w.draft = torch.softmax(w.draft.float(), -1)
+    check(svlib, w, seed=B, offset=3, draft_is_probs=True)
+
+
+@pytest.mark.parametrize("B", [40, 100])
+def test_team_launches_in_a_row(svlib, B):
+    """One handle, the same trees launched five times with a different
+    offset each and then again with the first: a team walk returns its
+    exchange words to 0 at its end, so every launch starts clean and the
+    repeat matches the first launch bit for bit."""
+    V = 8192
+    w = synth.make_tree(B, 16, V, dtype=torch.bfloat16, seed=60 + B, corr=0.95,
+                        temps=(1.0, 0.8, 0.0), ragged=False, device="cuda")
+    h = svlib.SpecVerify(B, 1, V, torch.bfloat16, draft_dtype=torch.bfloat16)
+    assert h.tree_team_size(B) in (4, 8)
+    outs = []
+    for off in (0, 1, 2, 3, 4, 0):
+        outs.append([x.cpu() for x in h.run_tree(w.target, w.draft, w.tokens, w.parents,
+                                                   w.num_nodes, w.temperatures, seed=5,
+                                                   offset=off)])
+    torch.cuda.synchronize()
+    flags = h.device_errors(clear=True)
+    h.close()
+    assert flags & ~8 == 0, flags
+    for a, b in zip(outs[0], outs[-1]):
+        assert torch.equal(a, b)
+    hs = w.host_arrays()
+    ref = oracle.verify_tree(hs["target"], hs["draft"], hs["tokens"], hs["parents"],
+                             hs["num_nodes"], hs["temperatures"], seed=5, offset=4)
+    rep = compare_tree(hs["tokens"], hs["parents"], hs["num_nodes"], V, ref,
+                       outs[4][0].numpy(), outs[4][1].numpy(), outs[4][2].numpy())
+    assert rep.ok(), rep.mismatches
