@@ -82,8 +82,9 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_DEVERR_BAD_TREE 16u      /* a tree node whose parent is not an
                                        earlier node: never visited */
 #define SV_DEVERR_TREE_SYNC 32u     /* a team walk's exchange did not complete
-                                       within its time bound: that team's
-                                       outputs are invalid */
+                                       within its time bound (a member not yet
+                                       running): the walk was finished by
+                                       single workgroups, outputs valid */
 
 typedef struct {
   int32_t max_batch;      /* largest B of any run, >= 1 */
@@ -298,11 +299,11 @@ int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K,
  *                  deepest accepted node (0 = root).
  *
  * A team of workgroups walks each request's tree and reads only the rows of
- * the nodes it visits: where the device launches cooperatively, four
- * workgroups on different compute units each take a quarter of every row and
- * exchange their partial statistics through device memory; otherwise one
- * workgroup walks each request.  Calls on one handle share its exchange
- * buffers and must not overlap.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
+ * the nodes it visits: while the teams fit the device at once, eight (or
+ * four) workgroups on different compute units each take a share of every row
+ * and exchange their partial statistics through device memory; beyond that
+ * one workgroup walks each request (spec_verify_tree_team_size).  Calls on
+ * one handle share its exchange buffers and must not overlap.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
  * B < 0, N outside [1, SPEC_TREE_MAX_NODES]), SV_ERR_CAPACITY (B >
  * max_batch) or SV_ERR_HIP. */
 int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N,
@@ -388,6 +389,15 @@ int32_t spec_verify_chunk_elems(spec_verify_t h);
  * picks the team by B against the teams its device holds at once (measured
  * crossovers, stated where the pick is made).  Host-only. */
 int32_t spec_verify_tree_team_size(spec_verify_t h, int32_t B, int32_t has_draft);
+
+/* Bound, in microseconds, on how long a team member of spec_verify_run_tree
+ * waits for its partners at an exchange (default 20000).  A member that
+ * reaches it sets SV_DEVERR_TREE_SYNC and finishes the walk alone, computing
+ * every member's share itself in member order, so the outputs are the same
+ * bit for bit; only the time differs.  0 makes members stop waiting at once
+ * (the outputs still match).  Host-only; for runs enqueued after it.
+ * Returns SV_ERR_INVALID_ARG for a null handle or a negative bound. */
+int spec_verify_set_tree_wait_us(spec_verify_t h, int32_t microseconds);
 
 /* Frees the workspace and the handle (waits for the device first).
  * NULL is accepted. */

@@ -90,6 +90,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.spec_verify_chunk_elems.restype = i32
     lib.spec_verify_tree_team_size.argtypes = [P, i32, i32]
     lib.spec_verify_tree_team_size.restype = i32
+    lib.spec_verify_set_tree_wait_us.argtypes = [P, i32]
+    lib.spec_verify_set_tree_wait_us.restype = ctypes.c_int
     lib.spec_verify_destroy.argtypes = [P]
     lib.spec_verify_destroy.restype = ctypes.c_int
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
@@ -221,6 +223,12 @@ def spec_verify_set_request_base(h, base: int) -> None:
 
 def spec_verify_tree_team_size(h, B: int, has_draft: bool) -> int:
     return load_library().spec_verify_tree_team_size(h, int(B), int(bool(has_draft)))
+
+
+def spec_verify_set_tree_wait_us(h, microseconds: int) -> None:
+    rc = load_library().spec_verify_set_tree_wait_us(h, int(microseconds))
+    if rc != SV_OK:
+        raise SpecVerifyError("spec_verify_set_tree_wait_us", rc)
 
 
 def spec_verify_get_device_errors(h, clear: bool = False) -> int:
@@ -429,6 +437,10 @@ class SpecVerify:
 
     def device_errors(self, clear=False):
         return spec_verify_get_device_errors(self.handle, clear)
+
+    def set_tree_wait_us(self, microseconds):
+        """Bound on a tree team member's wait at an exchange."""
+        spec_verify_set_tree_wait_us(self.handle, microseconds)
 
     def tree_team_size(self, B, has_draft=True):
         """Workgroups per request that run_tree uses for a batch of B."""

@@ -133,11 +133,12 @@ struct spec_verify_s {
   int32_t b_base = 0;  // global index of request 0 (spec_verify_set_request_base)
   int lds_per_cu = 0;  // bytes of LDS per compute unit (0: unknown, stats launches uncapped)
   // token trees: teams of 4 and 8 resident at once (without and with draft
-  // rows; 0: no team walks) and their exchange words and counters (0
+  // rows; 0: no team walks) and their exchange words and counters (all 0
   // between launches)
   int tree_cap[2][2] = {{0, 0}, {0, 0}};
   uint64_t* tree_xdat = nullptr;
   uint32_t* tree_xdone = nullptr;
+  uint64_t tree_wait_ticks = 2000000;  // 20 ms of the 100 MHz real-time clock
   // timing: per run, one start/stop pair per kernel
   bool timing = false;
   hipEvent_t ev[kTimingSlots][kEventsPerRun] = {};
@@ -398,6 +399,7 @@ int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N, const void* targ
   tp.b_base = h->b_base;
   tp.xdat = h->tree_xdat;
   tp.xdone = h->tree_xdone;
+  tp.spin_ticks = h->tree_wait_ticks;
   DeviceGuard g(c.device);
   if (!g.ok) return SV_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -493,6 +495,12 @@ int spec_verify_timing_read(spec_verify_t h, float* total_ms, int32_t n, int32_t
 }
 
 int32_t spec_verify_chunk_elems(spec_verify_t h) { return h ? h->chunk : 0; }
+
+int spec_verify_set_tree_wait_us(spec_verify_t h, int32_t microseconds) {
+  if (h == nullptr || microseconds < 0) return SV_ERR_INVALID_ARG;
+  h->tree_wait_ticks = (uint64_t)microseconds * 100u;
+  return SV_OK;
+}
 
 int32_t spec_verify_tree_team_size(spec_verify_t h, int32_t B, int32_t has_draft) {
   if (h == nullptr || B < 1) return 0;

@@ -134,14 +134,14 @@ struct TreeParams {
   // returns them to 0).
   uint64_t* xdat;   // [teams][2][team size][8]
   uint32_t* xdone;  // [teams]
+  uint64_t spin_ticks;  // bound of an exchange's wait (100 MHz ticks)
 };
 
 // 64-bit exchange words per team member.
 int tree_team_words();
 
 // Teams of g members (4 or 8) that can be resident at once on `device` for
-// these dtypes (the largest cooperative launch), or 0 where the device
-// cannot launch cooperatively.
+// these dtypes, or 0 if that cannot be known.
 int tree_team_capacity(int device, int target_dtype, int draft_dtype, bool has_draft, int g);
 
 // Members per request for a batch of B, given the capacities of teams of 4

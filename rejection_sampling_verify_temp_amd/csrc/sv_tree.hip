@@ -23,12 +23,13 @@
 //     workgroup sums the law per slot of 64 vectors of its share, the team
 //     exchanges the share totals, and the workgroup whose share holds u * S
 //     scans its slots and re-reads one slot to find the element.
-// The team is launched cooperatively, so its workgroups are resident
-// together; an exchange writes each value beside the exchange's tag in one
-// agent-scope atomic store, and spins (bounded in time) until every member's
-// words carry the tag.
-// Without a cooperative launch the team is one 1024-thread workgroup and the
-// exchanges vanish.
+// An exchange writes each value beside the exchange's tag in one agent-scope
+// atomic store, and spins until every member's words carry the tag.  A team
+// is launched only when all teams fit the device at once, so on an idle
+// device every member runs; the wait is still bounded, and a member that
+// times out finishes the walk alone over whole rows, with the same results.
+// At large batches (more teams than the device holds) a single 1024-thread
+// workgroup walks each request and the exchanges vanish.
 //
 // Row passes issue 160-224 KiB of 16-byte loads per 1024 threads before using
 // any (one round trip per round), through buffer resources, so the loads of a
@@ -51,10 +52,6 @@ namespace {
 constexpr int kSoloThreads = 1024;  // the workgroup of a walk without a team
 constexpr int kTeamThreads = 256;   // a team member's workgroup
 constexpr int kMaxNodes = SPEC_TREE_MAX_NODES;
-// A bounded wait: an exchange that has not completed within 20 ms of the
-// 100 MHz real-time clock gives up, flags the request and lets the team run
-// to its end without further waits.
-constexpr uint64_t kSpinTicks = 2000000;
 
 struct RowStats {
   float m;     // row max
@@ -67,7 +64,7 @@ struct RowStats {
 // vectors from v0 and a scalar tail [t0, V) (chunk_geo over the whole row).
 // Workgroup gi of a team of G takes the vectors [vb, vb + nv): the row's
 // pieces of 64 vectors split into G contiguous runs, the head going to the
-// first workgroup and the tail to the last.
+// first workgroup and the tail to the last (gi < 0: the whole row).
 struct Rng {
   int vb, nv;
   bool head, tail;
@@ -75,6 +72,7 @@ struct Rng {
 
 template <int G>
 __device__ __forceinline__ Rng row_range(const Geo& g, int gi) {
+  if (G == 1 || gi < 0) return Rng{0, g.nvec, true, true};  // the whole row
   const int per = ((g.nvec + G - 1) / G + 63) / 64 * 64;
   const int vb = min(g.nvec, gi * per);
   Rng r;
@@ -135,7 +133,8 @@ struct Team {
   uint32_t* xdone; // [teams]: members that finished this launch; 0 between launches
   int t, gi;       // team index, this workgroup's index in the team
   uint32_t k;      // exchanges made so far in this launch
-  bool dead;       // a wait timed out: no more waits in this launch
+  bool solo;       // a wait timed out: this workgroup walks alone from there
+  uint64_t spin;   // the wait's bound in ticks of the 100 MHz real-time clock
 };
 
 // A double as two floats whose sum is within 2^-48 of it, and back.
@@ -154,43 +153,48 @@ __device__ __forceinline__ double join_f64(float hi, float lo) { return (double)
 // enough: a member can write exchange k + 2 only after every member has
 // written k + 1, which each does after reading exchange k.  The tags restart
 // at 1 in every launch, since team_done() returns the words to 0.
+//
+// The wait is bounded.  A member whose partners do not all show the tag
+// within the bound (a partner not yet running on a device shared with other
+// work) turns solo: s_all is not filled, and from then on the workgroup
+// computes every member's share itself, in member order, and folds the same
+// words the exchange would have carried.  Alone or in the team, every member
+// therefore computes the same outputs, bit for bit, and the request's results
+// do not depend on which members finish it.
 template <int G>
 __device__ __forceinline__ void exchange(Team& tm, const float (&mine)[kXWords], int nw,
-                                         float* s_all, int* s_dead) {
+                                         float* s_all, int* s_solo) {
   const int tid = threadIdx.x;
   __syncthreads();  // s_all's previous contents are read
   if (tid < 64) {
-    bool dead = tm.dead;
+    bool solo = false;
     uint64_t* slot = tm.xdat + ((size_t)tm.t * 2 + (tm.k & 1u)) * G * kXWords;
     const uint32_t tag = tm.k + 1u;
     const int j = tid & (kXWords - 1), g = tid / kXWords;
     float v = 0.f;
 #pragma unroll
     for (int i = 0; i < kXWords; ++i) v = j == i ? mine[i] : v;
-    if (!dead && tid < kXWords && j < nw)
+    if (tid < kXWords && j < nw)
       __hip_atomic_store(slot + tm.gi * kXWords + j,
                          ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     const bool reader = g < G && j < nw;
     uint64_t w = 0;
-    if (!dead) {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      for (;;) {
-        if (reader) w = __hip_atomic_load(slot + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__all(!reader || (uint32_t)(w >> 32) == tag)) break;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-          dead = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+      if (reader) w = __hip_atomic_load(slot + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__all(!reader || (uint32_t)(w >> 32) == tag)) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > tm.spin) {
+        solo = true;
+        break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
-    // no partner's values after a timeout: the walk goes on with this one's, flagged
-    if (tid < kXWords * G) s_all[tid] = dead ? v : __builtin_bit_cast(float, (uint32_t)w);
-    if (tid == 0) *s_dead = dead ? 1 : 0;
+    if (!solo && tid < kXWords * G) s_all[tid] = __builtin_bit_cast(float, (uint32_t)w);
+    if (tid == 0) *s_solo = solo ? 1 : 0;
   }
   __syncthreads();
-  tm.dead = *s_dead != 0;
+  tm.solo = *s_solo != 0;
   ++tm.k;
 }
 
@@ -328,6 +332,21 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
   st.z = block_sum<NT>(S * f, ldsd);
   st.arg = 0;
   return st;
+}
+
+// A share's statistics as the words a member sends: target max, its sum
+// split in two floats (or its argmax, greedy), draft max and sum.
+__device__ __forceinline__ void stat_words(const RowStats& a, const RowStats& bq, bool sampling,
+                                           float (&w)[kXWords]) {
+  w[0] = a.m;
+  if (sampling) {
+    split_f64(a.z, w[1], w[2]);
+  } else {
+    w[1] = __builtin_bit_cast(float, a.arg);
+    w[2] = 0.f;
+  }
+  w[3] = bq.m;
+  split_f64(bq.z, w[4], w[5]);
 }
 
 // The row's statistics from the team's shares: member g's words at
@@ -587,31 +606,33 @@ struct DrawOut {
   bool empty;     // the law is 0
 };
 
-// Inverse-CDF draw from the law with uniform u, given its sums per draw slot
-// of this workgroup's share in s_slot (written by slot_pass); the tokens in
-// ex[0..nex) are removed.  A slot that holds removed tokens is summed again
-// with them zeroed (not reduced by their values: a removed sibling can hold
-// nearly all of the slot, and the difference of two rounded sums would leave
-// a residue far above the mass that remains).  The share totals are
-// exchanged; the member whose share holds u * S scans its slot sums to find
-// the slot, and its wavefront 0 re-reads only that slot (one vector per
-// lane) to find the element.
+// A thread's part of the scan over a share's slot sums: slots [k0, k1),
+// their sum, the sum of the slots before them, the last one with mass, and
+// the share's total.
+struct SlotScan {
+  double q, loc, total;
+  int k0, k1, lastpos;
+};
+
+// The slot sums of share sh after slot_pass: slots that hold removed tokens
+// (ex[0..nex)) are summed again with them zeroed (not reduced by their
+// values: a removed sibling can hold nearly all of the slot, and the
+// difference of two rounded sums would leave a residue far above the mass
+// that remains), then scanned.
 template <int TDT, int DDT, int NT, int G>
-__device__ __forceinline__ DrawOut draw_from_slots(const Law& L, const void* prow, const void* qrow,
-                                                   int V, Team& tm, const int* ex, int nex, double u,
-                                                   double* s_slot, double* s_woff, int* s_sel,
-                                                   double* s_th, float* s_x, int* s_dead) {
+__device__ __forceinline__ SlotScan slot_scan(const Law& L, const void* prow, const void* qrow,
+                                              int V, int sh, const int* ex, int nex, double* s_slot,
+                                              double* s_woff) {
   using EP = Elt<TDT>;
   constexpr int KV = EP::kVec;
   constexpr int W = NT / 64;
   const int tid = pass_tid(), lane = tid & 63, w = tid >> 6;
   const Geo g = chunk_geo<TDT>(prow, 0, V);
-  const Rng rg = row_range<G>(g, tm.gi);
+  const Rng rg = row_range<G>(g, sh);
   const bool qvec = L.pair && same_alignment(prow, qrow);
   const int nslot = num_slots(rg);
-  DrawOut out{-1, false, false};
   __syncthreads();
-  if (w == 0) {  // slots holding removed tokens, summed again without them
+  if (w == 0) {
     for (int k = 0; k < nex; ++k) {  // uniform over the wavefront
       const int sl = slot_of(g, rg, nslot, KV, ex[k]);
       if (sl < 0) continue;
@@ -641,77 +662,56 @@ __device__ __forceinline__ DrawOut draw_from_slots(const Law& L, const void* pro
                                                        : (double)wave_sum_f32(pairwise_sum(r));
       if (lane == 0) s_slot[sl] = sum;
     }
-    if (lane == 0) *s_sel = -1;
   }
   __syncthreads();
-
-  // (2) scan of the share's slot sums: thread t takes slots [t sp, t sp + sp)
+  // thread t takes slots [t sp, t sp + sp)
+  SlotScan sc;
   const int sp = (nslot + NT - 1) / NT;
-  const int k0 = min(nslot, tid * sp), k1 = min(nslot, k0 + sp);
-  double loc = 0.0;
-  int lastpos = -1;
-  for (int k = k0; k < k1; ++k) {
-    loc += s_slot[k];
-    if (s_slot[k] > 0.0) lastpos = k;
+  sc.k0 = min(nslot, tid * sp);
+  sc.k1 = min(nslot, sc.k0 + sp);
+  sc.loc = 0.0;
+  sc.lastpos = -1;
+  for (int k = sc.k0; k < sc.k1; ++k) {
+    sc.loc += s_slot[k];
+    if (s_slot[k] > 0.0) sc.lastpos = k;
   }
-  const double incl = wave_incl_scan(loc, lane);
+  const double incl = wave_incl_scan(sc.loc, lane);
   if (lane == 63) s_woff[w] = incl;
-  double q = lane_before(incl);
-  if (lane == 0) q = 0.0;
+  sc.q = lane_before(incl);
+  if (lane == 0) sc.q = 0.0;
   __syncthreads();
-  double mine_total = 0.0;
+  sc.total = 0.0;
   for (int k = 0; k < W; ++k) {
-    if (k < w) q += s_woff[k];
-    mine_total += s_woff[k];
+    if (k < w) sc.q += s_woff[k];
+    sc.total += s_woff[k];
   }
-  // (3) the team's totals, in member order: the prefix before this share,
-  // the total, and the member whose share holds theta
-  double before = 0.0, total = mine_total;
-  int owner = 0;
-  bool past = false;
-  if constexpr (G > 1) {
-    float mine[kXWords] = {};
-    split_f64(mine_total, mine[0], mine[1]);
-    exchange<G>(tm, mine, 2, s_x, s_dead);
-    total = 0.0;
-#pragma unroll
-    for (int m = 0; m < G; ++m) {
-      if (m == tm.gi) before = total;
-      total += join_f64(s_x[kXWords * m], s_x[kXWords * m + 1]);
-    }
-  }
-  out.empty = !(total > 0.0);
-  if (out.empty) {
-    __syncthreads();
-    return out;
-  }
-  const double theta = u * total;
-  if constexpr (G > 1) {
-    owner = -1;
-    int lastm = 0;
-    double acc = 0.0;
-#pragma unroll
-    for (int m = 0; m < G; ++m) {
-      const double tm_ = join_f64(s_x[kXWords * m], s_x[kXWords * m + 1]);
-      if (tm_ > 0.0) {
-        lastm = m;
-        if (owner < 0 && acc <= theta && theta < acc + tm_) owner = m;
-      }
-      acc += tm_;
-    }
-    if (owner < 0) {  // theta at or past the total: the last share with mass
-      owner = lastm;
-      past = true;
-    }
-  }
-  if (owner != tm.gi) {
-    __syncthreads();
-    out.rounding = past;
-    return out;
-  }
-  if (!past && loc > 0.0 && before + q <= theta && theta < before + q + loc) {
-    double acc = before + q;
-    for (int k = k0; k < k1; ++k) {
+  __syncthreads();  // s_woff is free again
+  return sc;
+}
+
+// The element of share sh that holds theta, from its scan sc (the share's
+// slot sums still in s_slot): the slot whose running sum, after `before` (the
+// shares ahead of this one), passes theta, then wavefront 0 re-reads only
+// that slot (one vector per lane) to find the element.  past: theta is at
+// or past the law's total, which takes the share's last slot with mass.
+template <int TDT, int DDT, int NT, int G>
+__device__ __forceinline__ int slot_find(const Law& L, const void* prow, const void* qrow, int V,
+                                         int sh, const int* ex, int nex, const SlotScan& sc,
+                                         double before, double theta, bool past,
+                                         const double* s_slot, int* s_sel, double* s_th,
+                                         bool* rounding) {
+  using EP = Elt<TDT>;
+  constexpr int KV = EP::kVec;
+  const int tid = pass_tid(), lane = tid & 63, w = tid >> 6;
+  const Geo g = chunk_geo<TDT>(prow, 0, V);
+  const Rng rg = row_range<G>(g, sh);
+  const bool qvec = L.pair && same_alignment(prow, qrow);
+  const int nslot = num_slots(rg);
+  if (tid == 0) *s_sel = -1;
+  __syncthreads();
+  if (!past && sc.loc > 0.0 && before + sc.q <= theta && theta < before + sc.q + sc.loc) {
+    double acc = before + sc.q;
+    for (int k = sc.k0; k < sc.k1; ++k) {
       if (s_slot[k] > 0.0 && theta < acc + s_slot[k]) {
         *s_sel = k;
         *s_th = theta - acc;
@@ -721,18 +721,16 @@ __device__ __forceinline__ DrawOut draw_from_slots(const Law& L, const void* pro
     }
   }
   __syncthreads();
-  out.rounding = past;
+  *rounding = past;
   if (*s_sel < 0) {  // theta at or past the share's total: its last slot with mass
-    out.rounding = true;
+    *rounding = true;
     __syncthreads();
-    if (lastpos >= 0) atomicMax(s_sel, lastpos);
+    if (sc.lastpos >= 0) atomicMax(s_sel, sc.lastpos);
     if (tid == 0) *s_th = __builtin_inf();
     __syncthreads();
   }
   const int sel = *s_sel;
   const double th = *s_th;
-
-  // (4) wavefront 0 finds the element inside slot sel
   if (w == 0) {
     float r[KV];
     int base;  // index of r[0]
@@ -788,9 +786,100 @@ __device__ __forceinline__ DrawOut draw_from_slots(const Law& L, const void* pro
     }
   }
   __syncthreads();
-  out.token = *s_sel;
-  if (*s_th == -1.0) out.rounding = true;
+  const int token = *s_sel;
+  if (*s_th == -1.0) *rounding = true;
   __syncthreads();
+  return token;
+}
+
+// Inverse-CDF draw from the law with uniform u at the stop node (whole
+// team).  Each member sums the law per slot of its share and the team
+// exchanges the share totals; the member whose share holds u * S finds the
+// element.  A workgroup alone after a timed-out exchange goes through every
+// share in member order, with the totals rounded as the exchange rounds
+// them, so it draws the token the team would.  A team of one takes its one
+// share's total as it is.
+template <int TDT, int DDT, int NT, int G>
+__device__ __forceinline__ DrawOut team_draw(const Law& L, const void* prow, const void* qrow, int V,
+                                             Team& tm, const int* ex, int nex, double u,
+                                             double* s_slot, double* s_woff, int* s_sel,
+                                             double* s_th, float* s_x, int* s_solo) {
+  DrawOut out{-1, false, false};
+  const int tid = threadIdx.x;
+  SlotScan sc;
+  int sc_share;  // the share whose slot sums are in s_slot
+  double total, before = 0.0;
+  int owner = 0;
+  bool past = false;
+  if constexpr (G == 1) {
+    slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, -1, s_slot);
+    sc = slot_scan<TDT, DDT, NT, G>(L, prow, qrow, V, -1, ex, nex, s_slot, s_woff);
+    sc_share = -1;
+    total = sc.total;
+  } else {
+    bool have = false;  // s_x holds every share's total
+    if (!tm.solo) {
+      slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, s_slot);
+      sc = slot_scan<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, ex, nex, s_slot, s_woff);
+      sc_share = tm.gi;
+      float mine[kXWords] = {};
+      split_f64(sc.total, mine[0], mine[1]);
+      exchange<G>(tm, mine, 2, s_x, s_solo);
+      have = !tm.solo;
+    }
+    if (!have) {  // alone: every share in member order
+      for (int m = 0; m < G; ++m) {
+        slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, m, s_slot);
+        sc = slot_scan<TDT, DDT, NT, G>(L, prow, qrow, V, m, ex, nex, s_slot, s_woff);
+        sc_share = m;
+        if (tid == 0) split_f64(sc.total, s_x[kXWords * m], s_x[kXWords * m + 1]);
+      }
+      __syncthreads();
+    }
+    total = 0.0;
+    double acc = 0.0;
+    int lastm = 0;
+    owner = -1;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+      const double tmm = join_f64(s_x[kXWords * m], s_x[kXWords * m + 1]);
+      total += tmm;
+    }
+    const double theta = u * total;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+      const double tmm = join_f64(s_x[kXWords * m], s_x[kXWords * m + 1]);
+      if (tmm > 0.0) {
+        lastm = m;
+        if (owner < 0 && acc <= theta && theta < acc + tmm) {
+          owner = m;
+          before = acc;
+        }
+      }
+      acc += tmm;
+    }
+    if (owner < 0) {  // theta at or past the total: the last share with mass
+      owner = lastm;
+      past = true;
+      before = 0.0;
+#pragma unroll
+      for (int m = 0; m < G; ++m)
+        if (m < owner) before += join_f64(s_x[kXWords * m], s_x[kXWords * m + 1]);
+    }
+  }
+  out.empty = !(total > 0.0);
+  if (out.empty) return out;
+  out.rounding = past;
+  const int mine_share = G == 1 ? -1 : (tm.solo ? owner : tm.gi);
+  if (G > 1 && owner != mine_share) return out;  // another member draws
+  if (G > 1 && sc_share != owner) {  // alone: the owner's slot sums again
+    slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, owner, s_slot);
+    sc = slot_scan<TDT, DDT, NT, G>(L, prow, qrow, V, owner, ex, nex, s_slot, s_woff);
+  }
+  bool rounding = false;
+  out.token = slot_find<TDT, DDT, NT, G>(L, prow, qrow, V, G == 1 ? -1 : owner, ex, nex, sc, before,
+                                         u * total, past, s_slot, s_sel, s_th, &rounding);
+  out.rounding = rounding;
   return out;
 }
 
@@ -845,18 +934,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   __shared__ int s_sel;
   __shared__ double s_th;
   __shared__ float s_x[kXWords * G];
-  __shared__ int s_dead;
+  __shared__ int s_solo;
+  __shared__ int s_path[kMaxNodes];  // the accepted path's tokens
   const int tid = threadIdx.x;
   const int N = p.N, V = p.V;
   Team tm;
   tm.xdat = p.xdat;
   tm.xdone = p.xdone;
+  // team t = workgroups [G t, G t + G): consecutive ids, so on different XCDs
   tm.gi = G == 1 ? 0 : (int)(blockIdx.x % G);
   tm.t = G == 1 ? (int)blockIdx.x : (int)(blockIdx.x / G);
   tm.k = 0;
-  tm.dead = false;
+  tm.solo = false;
+  tm.spin = p.spin_ticks;
   const int teams = G == 1 ? (int)gridDim.x : (int)(gridDim.x / G);
-  const bool lead = tm.gi == 0;
 
   for (int b = tm.t; b < p.B; b += teams) {
     int n = p.nn[b];
@@ -869,7 +960,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     }
     __syncthreads();
     uint32_t fl = bad_n ? SV_DEVERR_BAD_NUM_DRAFTS : 0u;
-    if (tid == 0 && lead)
+    if (tid == 0 && tm.gi == 0)
       for (int i = 1; i < n; ++i)
         if (s_par[i] < 0 || s_par[i] >= i) fl |= SV_DEVERR_BAD_TREE;
 
@@ -885,22 +976,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       const void* prow = row_ptr(p.target, TDT, (size_t)b * N + v, V);
       const void* qrow = HAS_DRAFT ? row_ptr(p.draft, DDT, (size_t)b * N + v, V) : nullptr;
       const bool need_q = HAS_DRAFT && sampling && !probs;
-      RowStats ps = row_stats<TDT, NT, G>(prow, V, sampling, c, tm.gi, ldsf, ldsd, ldsi);
-      RowStats qs{0.f, 0.f, 1.0, 0};
-      if (need_q) qs = row_stats<DDT, NT, G>(qrow, V, true, c, tm.gi, ldsf, ldsd, ldsi);
+      // the row statistics: the team's shares folded in member order; a
+      // workgroup alone after a timed-out exchange computes every share itself
+      // and folds the same words, so it gets the same bits
+      RowStats ps, qs{0.f, 0.f, 1.0, 0};
       if constexpr (G == 1) {
-        ps = solo_stats(ps, sampling);
+        ps = solo_stats(row_stats<TDT, NT, G>(prow, V, sampling, c, -1, ldsf, ldsd, ldsi), sampling);
+        if (need_q) qs = row_stats<DDT, NT, G>(qrow, V, true, c, -1, ldsf, ldsd, ldsi);
       } else {
-        float mine[kXWords] = {};
-        mine[0] = ps.m;
-        if (sampling) {
-          split_f64(ps.z, mine[1], mine[2]);
-        } else {
-          mine[1] = __builtin_bit_cast(float, ps.arg);
+        bool have = false;
+        for (int m = tm.solo ? 0 : tm.gi; !have; ++m) {  // own share; alone: 0 .. G-1
+          const RowStats a = row_stats<TDT, NT, G>(prow, V, sampling, c, m, ldsf, ldsd, ldsi);
+          RowStats bq{0.f, 0.f, 1.0, 0};
+          if (need_q) bq = row_stats<DDT, NT, G>(qrow, V, true, c, m, ldsf, ldsd, ldsi);
+          float mine[kXWords] = {};
+          stat_words(a, bq, sampling, mine);
+          if (!tm.solo) {
+            exchange<G>(tm, mine, need_q ? 6 : (sampling ? 3 : 2), s_x, &s_solo);
+            if (tm.solo) m = -1;  // timed out: start over, alone
+            have = !tm.solo;
+          } else {
+            if (threadIdx.x == 0)
+              for (int j = 0; j < 6; ++j) s_x[kXWords * m + j] = mine[j];
+            __syncthreads();
+            have = m == G - 1;
+          }
         }
-        mine[3] = qs.m;
-        split_f64(qs.z, mine[4], mine[5]);
-        exchange<G>(tm, mine, need_q ? 6 : (sampling ? 3 : 2), s_x, &s_dead);
         ps = fold_stats<G>(s_x, 0, sampling, c);
         if (need_q) qs = fold_stats<G>(s_x, 3, true, c);
       }
@@ -952,11 +1053,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             const double kap = ck * ps.z / (probs ? 1.0 : qs.z);
             L.kap_hi = (float)kap;
             L.kap_lo = (float)(kap - (double)L.kap_hi);
-            double zs = law_sum<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, ldsd);
-            if constexpr (G > 1) {
-              float mine[kXWords] = {};
-              split_f64(zs, mine[0], mine[1]);
-              exchange<G>(tm, mine, 2, s_x, &s_dead);
+            double zs;
+            if constexpr (G == 1) {
+              zs = law_sum<TDT, DDT, NT, G>(L, prow, qrow, V, -1, ldsd);
+            } else {  // as for the row statistics
+              bool have = false;
+              for (int m = tm.solo ? 0 : tm.gi; !have; ++m) {
+                const double zm = law_sum<TDT, DDT, NT, G>(L, prow, qrow, V, m, ldsd);
+                float mine[kXWords] = {};
+                split_f64(zm, mine[0], mine[1]);
+                if (!tm.solo) {
+                  exchange<G>(tm, mine, 2, s_x, &s_solo);
+                  if (tm.solo) m = -1;
+                  have = !tm.solo;
+                } else {
+                  if (threadIdx.x == 0) {
+                    s_x[kXWords * m] = mine[0];
+                    s_x[kXWords * m + 1] = mine[1];
+                  }
+                  __syncthreads();
+                  have = m == G - 1;
+                }
+              }
               zs = fold_sum<G>(s_x);
             }
             Zk = zs / ps.z;
@@ -964,7 +1082,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         }
       }
       if (next >= 0) {
-        if (tid == 0 && lead) out[nacc] = s_tok[next];
+        if (tid == 0) s_path[nacc] = s_tok[next];
         ++nacc;
         v = next;
         continue;
@@ -972,7 +1090,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       // every child rejected, or a leaf: the emitted token is drawn at v
       if (!sampling) {
         y = ps.arg;
-        drew = lead;
+        drew = tm.gi == 0 || tm.solo;
       } else {
         const double u_rec = tree_uniforms(p.seed, p.offset, p.b_base + b, v).rec;
         Law L{false, c, ps.ref, qs.ref, 0.f, 0.f, probs};
@@ -982,32 +1100,35 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
           L.kap_hi = (float)kap;
           L.kap_lo = (float)(kap - (double)L.kap_hi);
         }
-        slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, s_slot);
-        DrawOut d = draw_from_slots<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, nex, u_rec, s_slot,
-                                                     s_woff, &s_sel, &s_th, s_x, &s_dead);
+        DrawOut d = team_draw<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, nex, u_rec, s_slot,
+                                               s_woff, &s_sel, &s_th, s_x, &s_solo);
         if (d.empty) {  // no mass left: draw from p itself
           fl |= SV_DEVERR_ZERO_RESIDUAL;
           L.pair = false;
-          slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, s_slot);
-          d = draw_from_slots<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, 0, u_rec, s_slot, s_woff,
-                                               &s_sel, &s_th, s_x, &s_dead);
+          d = team_draw<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, 0, u_rec, s_slot, s_woff,
+                                         &s_sel, &s_th, s_x, &s_solo);
         }
         y = d.token;
         drew = d.token >= 0;
         if (d.empty) {  // p itself has no mass (a row of -inf)
           y = -1;
-          drew = lead;
+          drew = tm.gi == 0 || tm.solo;
         }
         if (d.rounding) fl |= SV_DEVERR_DRAW_ROUNDING;
       }
       break;
     }
-    if (tm.dead) fl |= SV_DEVERR_TREE_SYNC;
-    if (lead)
-      for (int i = nacc + 1 + tid; i < N; i += NT) out[i] = -1;
+    if (tm.solo) fl |= SV_DEVERR_TREE_SYNC;
+    // member 0 writes the path, the count and the last node, and any member
+    // that finished the walk alone writes them too (the same values)
+    const bool writer = tm.gi == 0 || tm.solo;
+    __syncthreads();  // s_path is complete
+    if (writer)
+      for (int i = tid; i < N; i += NT)
+        if (i != nacc) out[i] = i < nacc ? s_path[i] : -1;
     if (tid == 0) {
       if (drew) out[nacc] = y;
-      if (lead) {
+      if (writer) {
         p.out_nacc[b] = nacc;
         p.out_last[b] = v;
       }
@@ -1025,10 +1146,9 @@ const void* team_kernel() {
 
 template <int TDT, int DDT, bool HD, int G>
 hipError_t launch_team(const TreeParams& p, int teams, hipStream_t s) {
-  TreeParams q = p;
-  void* args[] = {&q};
-  return hipLaunchCooperativeKernel(team_kernel<TDT, DDT, HD, G>(), dim3((unsigned)(teams * G)),
-                                    dim3(kTeamThreads), args, 0, s);
+  hipLaunchKernelGGL((k_tree<TDT, DDT, HD, kTeamThreads, G>), dim3((unsigned)(teams * G)),
+                     dim3(kTeamThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 template <int TDT, int DDT, bool HD>
@@ -1057,13 +1177,12 @@ const void* team_kernel_for(int tdt, int ddt, bool has_draft) {
 int tree_team_words() { return 2 * kXWords; }
 
 int tree_team_capacity(int device, int tdt, int ddt, bool has_draft, int g) {
-  int coop = 0, cus = 0;
-  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
-  if (!coop || (g != 4 && g != 8)) return 0;
+  if (g != 4 && g != 8) return 0;
   const void* f = g == 8 ? team_kernel_for<8>(tdt, ddt, has_draft)
                          : team_kernel_for<4>(tdt, ddt, has_draft);
   int per_cu = 0;
@@ -1080,12 +1199,13 @@ int tree_team_pick(int B, const int cap[2]) {
     const int c = cap[SV_TREE_FORCE_TEAM == 8 ? 1 : 0];
     return c > 0 && B <= c ? SV_TREE_FORCE_TEAM : 1;
   }
-  // measured on MI355X (B = 8 .. 512 trees of 16 nodes, V = 152064 bf16):
-  // the larger team wins while the teams fill at most three quarters of
-  // their slots (B <= 96 for eight members, B <= 192 for four); beyond that
-  // the exchanges cost more than the shorter row passes save
-  if (cap[1] > 0 && 4 * B <= 3 * cap[1]) return 8;
-  if (cap[0] > 0 && 4 * B <= 3 * cap[0]) return 4;
+  // measured on MI355X (B = 32 .. 512 trees of 16 nodes, V = 152064 bf16):
+  // eight members per request while their teams fit the device at once
+  // (B <= 128 on 256 compute units), four while theirs do (B <= 256), one
+  // workgroup beyond (where four-member teams that walk two requests each
+  // only tie it)
+  if (cap[1] > 0 && B <= cap[1]) return 8;
+  if (cap[0] > 0 && B <= cap[0]) return 4;
   return 1;
 }
 

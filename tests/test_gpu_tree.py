@@ -173,11 +173,11 @@ def test_benchmark_shape(svlib):
 
 
 # Batches whose team walks differ on MI355X (256 compute units): eight
-# workgroups per request up to B = 96, four up to B = 192, one beyond.
+# workgroups per request up to B = 128, four up to B = 256, one beyond.
 TEAM_CASES = {
     40: dict(dtype=torch.bfloat16, temps=(1.0, 0.6, 0.0)),
-    100: dict(dtype=torch.bfloat16, temps=(0.8, 0.0, 1.2)),
-    200: dict(temps=(1.0, 0.7)),
+    200: dict(dtype=torch.bfloat16, temps=(0.8, 0.0, 1.2)),
+    300: dict(temps=(1.0, 0.7)),
 }
 
 
@@ -198,7 +198,7 @@ def test_team_sizes(svlib, B):
     check(svlib, w, seed=B, offset=3, draft_is_probs=True)
 
 
-@pytest.mark.parametrize("B", [40, 100])
+@pytest.mark.parametrize("B", [40, 200])
 def test_team_launches_in_a_row(svlib, B):
     """One handle, the same trees launched five times with a different
     offset each and then again with the first: a team walk returns its
@@ -226,3 +226,32 @@ def test_team_launches_in_a_row(svlib, B):
     rep = compare_tree(hs["tokens"], hs["parents"], hs["num_nodes"], V, ref,
                        outs[4][0].numpy(), outs[4][1].numpy(), outs[4][2].numpy())
     assert rep.ok(), rep.mismatches
+
+
+@pytest.mark.parametrize("B", [40, 200])
+def test_team_members_finishing_alone(svlib, B):
+    """With the team wait bound at 0 the members give up on their partners at
+    once, in a mix of team and solo walks that differs run to run; each then
+    computes every member's share itself, so the outputs match a normal run's
+    bit for bit, and the condition is flagged."""
+    V = 20011
+    w = synth.make_tree(B, 12, V, dtype=torch.bfloat16, seed=70 + B, corr=0.9,
+                        temps=(1.0, 0.6, 0.0), device="cuda")
+    outs, flags = [], []
+    for wait in (20000, 0, 0):
+        h = svlib.SpecVerify(B, 1, V, torch.bfloat16, draft_dtype=torch.bfloat16)
+        assert h.tree_team_size(B) in (4, 8)
+        h.set_tree_wait_us(wait)
+        outs.append([x.cpu() for x in h.run_tree(w.target, w.draft, w.tokens, w.parents,
+                                                   w.num_nodes, w.temperatures, seed=3,
+                                                   offset=1)])
+        torch.cuda.synchronize()
+        flags.append(h.device_errors(clear=True))
+        h.close()
+    say(f"      device flags by wait bound 20000/0/0 us: {flags}")
+    assert flags[0] & ~8 == 0
+    for f in flags[1:]:
+        assert f & ~(8 | 32) == 0
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
