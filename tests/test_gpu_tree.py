@@ -176,6 +176,7 @@ def test_benchmark_shape(svlib):
 # workgroups per request up to B = 128, four up to B = 256, one beyond.
 TEAM_CASES = {
     40: dict(dtype=torch.bfloat16, temps=(1.0, 0.6, 0.0)),
+    100: dict(temps=(0.9, 0.0)),
     200: dict(dtype=torch.bfloat16, temps=(0.8, 0.0, 1.2)),
     300: dict(temps=(1.0, 0.7)),
 }
@@ -198,7 +199,7 @@ def test_team_sizes(svlib, B):
     check(svlib, w, seed=B, offset=3, draft_is_probs=True)
 
 
-@pytest.mark.parametrize("B", [40, 200])
+@pytest.mark.parametrize("B", [40, 100, 200])
 def test_team_launches_in_a_row(svlib, B):
     """One handle, the same trees launched five times with a different
     offset each and then again with the first: a team walk returns its
@@ -228,7 +229,7 @@ def test_team_launches_in_a_row(svlib, B):
     assert rep.ok(), rep.mismatches
 
 
-@pytest.mark.parametrize("B", [40, 200])
+@pytest.mark.parametrize("B", [40, 100, 200])
 def test_team_members_finishing_alone(svlib, B):
     """With the team wait bound at 0 the members give up on their partners at
     once, in a mix of team and solo walks that differs run to run; each then
