@@ -100,7 +100,9 @@ typedef struct {
                              (raised to ceil(V / 64) if smaller) */
 } sv_config;
 
-/* Creates a handle on cfg->device and allocates its workspace.
+/* Creates a handle on cfg->device and allocates its workspace (zeroing its
+ * counters, then waiting for the device, so any stream may use the handle
+ * once this returns).  A setup call: it allocates and synchronizes.
  * Returns SV_ERR_INVALID_ARG for a null argument or a field out of range,
  * SV_ERR_UNSUPPORTED for an unknown dtype, SV_ERR_HIP if allocation fails.
  * On failure *out is set to NULL. */

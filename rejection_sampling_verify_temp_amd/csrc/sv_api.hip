@@ -279,6 +279,9 @@ int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
            hipMemset(h->tree_xdone, 0, teams * sizeof(uint32_t)) == hipSuccess;
     }
   }
+  // the zeroed words are in place before any stream can launch on them (a
+  // stream created non-blocking does not wait for the null stream's work)
+  ok = ok && hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     free_all(h);
     delete h;
