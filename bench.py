@@ -56,7 +56,7 @@ KERNEL_SRC = [os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", f
               for f in ("sv_kernels.hip", "sv_device.h", "sv_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stats_traffic_B256_K7_V152064_bf16.txt")
 TREE_SRC = [os.path.join(ROOT, "rejection_sampling_verify_temp_amd", "csrc", f)
-            for f in ("sv_tree.hip", "sv_device.h", "sv_internal.h")]
+            for f in ("sv_tree.hip", "sv_tree.h", "sv_device.h", "sv_internal.h")]
 TREE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_traffic_B256_N16_V152064_bf16.txt")
 
 

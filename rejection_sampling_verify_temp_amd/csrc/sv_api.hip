@@ -9,6 +9,7 @@
 #include <new>
 
 #include "sv_internal.h"
+#include "sv_tree.h"
 
 namespace {
 

@@ -113,43 +113,4 @@ const char* kernel_name(int i);
 // (the draft sampler has no decisions; runs without draft rows no residual).
 bool kernel_launched(int k, const RunParams& p);
 
-// Token-tree verification of a batch (one workgroup per request).
-struct TreeParams {
-  const void* target;  // [B][N][V]
-  const void* draft;   // [B][N][V] or nullptr (one-hot tree)
-  const int32_t* tokens;
-  const int32_t* parents;
-  const int32_t* nn;
-  const float* temps;
-  int32_t* out_tokens;
-  int32_t* out_nacc;
-  int32_t* out_last;
-  uint32_t* flags;
-  uint64_t seed, offset;
-  int B, N, V;
-  int draft_is_probs;
-  int b_base;  // global index of request 0 (Philox counters use b_base + b)
-  // Team walks (several workgroups per request): the exchange words and the
-  // per-team counters, all 0 between launches (zeroed once; every launch
-  // returns them to 0).
-  uint64_t* xdat;   // [teams][2][team size][8]
-  uint32_t* xdone;  // [teams]
-  uint64_t spin_ticks;  // bound of an exchange's wait (100 MHz ticks)
-};
-
-// 64-bit exchange words per team member.
-int tree_team_words();
-
-// Teams of g members (4 or 8) that can be resident at once on `device` for
-// these dtypes, or 0 if that cannot be known.
-int tree_team_capacity(int device, int target_dtype, int draft_dtype, bool has_draft, int g);
-
-// Members per request for a batch of B, given the capacities of teams of 4
-// and 8 (cap[0], cap[1]); 1 is one 1024-thread workgroup per request.
-int tree_team_pick(int B, const int cap[2]);
-
-// Enqueues the walk with g members per request (from tree_team_pick).
-hipError_t launch_tree(const TreeParams& p, int target_dtype, int draft_dtype, int g,
-                       hipStream_t stream);
-
 }  // namespace sv

@@ -40,6 +40,7 @@
 // which set the kernel's time once most requests are done.
 #include "sv_device.h"
 #include "sv_internal.h"
+#include "sv_tree.h"
 
 // Tuning knob: a team size that overrides the pick (0: none).
 #ifndef SV_TREE_FORCE_TEAM
