@@ -976,7 +976,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     for (;;) {
       const void* prow = row_ptr(p.target, TDT, (size_t)b * N + v, V);
       const void* qrow = HAS_DRAFT ? row_ptr(p.draft, DDT, (size_t)b * N + v, V) : nullptr;
-      const bool need_q = HAS_DRAFT && sampling && !probs;
+      // q's statistics serve only the child tests: a node without children
+      // draws from p alone
+      bool has_kids = false;
+      for (int ch = v + 1; ch < n && !has_kids; ++ch) has_kids = s_par[ch] == v;
+      const bool need_q = HAS_DRAFT && sampling && !probs && has_kids;
       // the row statistics: the team's shares folded in member order; a
       // workgroup alone after a timed-out exchange computes every share itself
       // and folds the same words, so it gets the same bits
