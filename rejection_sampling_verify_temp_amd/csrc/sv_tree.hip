@@ -230,9 +230,16 @@ __device__ __forceinline__ void team_done(Team& tm) {
 // barrier, so the wavefronts drift apart and one's loads overlap another's
 // arithmetic; the wavefronts' sums meet once, at the share's reference.
 // Greedy rows keep the max and its lowest index (INT32_MAX: none).
-template <int DT, int NT, int G>
+//
+// SLOTS (sampling rows, at a node whose draw is from p alone): the same pass
+// also leaves the draw's slot sums of the share in s_slot, each relative to
+// the reference its wavefront held when it summed the slot, which goes to
+// s_sref (rescale_slots moves them to the row's reference).  The slot of 64
+// vectors is one wavefront's share of one unroll step, as in slot_pass.
+template <int DT, int NT, int G, bool SLOTS = false>
 __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampling, float c,
-                                              int gi, float* ldsf, double* ldsd, int* ldsi) {
+                                              int gi, float* ldsf, double* ldsd, int* ldsi,
+                                              double* s_slot = nullptr, float* s_sref = nullptr) {
   using E = Elt<DT>;
   constexpr int U = kRowVecs;
   const int tid = pass_tid();
@@ -307,9 +314,26 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
       Mw = wm;
     }
     // the round's sum in fp32, added to the fp64 total once
-    float sr = b0 == 0 ? fast_exp2(fmaf(hx, c, Rw)) + fast_exp2(fmaf(tx, c, Rw)) : 0.f;
+    float sr = 0.f;
+    if (b0 == 0) {
+      const float eh = fast_exp2(fmaf(hx, c, Rw)), et = fast_exp2(fmaf(tx, c, Rw));
+      sr = eh + et;
+      if constexpr (SLOTS) {
+        if ((tid >> 6) == 0) {  // the head and tail lie in wavefront 0
+          const float hs = wave_sum_f32(eh), ts = wave_sum_f32(et);
+          if (tid == 0) {
+            const int last = num_slots(rg) - 1;
+            s_slot[0] = (double)hs;
+            s_slot[last] = (double)ts;
+            s_sref[0] = Rw;
+            s_sref[last] = Rw;
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      float sv = 0.f;
       if (b0 + u * NT + tid < rg.nv) {
         // unpack again rather than keep the floats live: the empty asm hides
         // the first unpack from common-subexpression elimination
@@ -319,8 +343,17 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
         E::unpack(wv, e);
 #pragma unroll
         for (int k = 0; k < E::kVec; ++k) e[k] = fast_exp2(fmaf(e[k], c, Rw));
-        sr += pairwise_sum(e);
+        sv = pairwise_sum(e);
+        sr += sv;
         asm volatile("" : "+v"(sr));  // fold in order: no sums wait in registers
+      }
+      if constexpr (SLOTS) {  // convergent: every lane, past the share or not
+        const float ws = wave_sum_f32(sv);
+        const int piece = (b0 + u * NT) / 64 + (tid >> 6);
+        if ((tid & 63) == 0 && piece < (rg.nv + 63) / 64) {
+          s_slot[1 + piece] = (double)ws;
+          s_sref[1 + piece] = Rw;
+        }
       }
     }
     S += (double)sr;
@@ -585,6 +618,33 @@ __device__ __forceinline__ void slot_pass(const Law& L, const void* prow, const 
   }
 }
 
+// Slot sums that a SLOTS statistics pass left relative to its wavefronts'
+// references, moved to the law's reference ref (a factor 2^(ref - sref) <= 1;
+// an empty slot stays 0 whatever its reference).
+template <int NT>
+__device__ __forceinline__ void rescale_slots(int nslot, float ref, double* s_slot,
+                                              const float* s_sref) {
+  __syncthreads();  // the pass's slot writes are visible
+  for (int k = pass_tid(); k < nslot; k += NT)
+    if (s_slot[k] > 0.0) s_slot[k] *= s_sref[k] == ref ? 1.0 : exp2_diff(ref, s_sref[k]);
+}
+
+// The law's slot sums of share sh in s_slot.  fused: the law is p alone and
+// the node's statistics pass kept its slot sums, so they are made again by
+// that pass (the bits the member of share sh got), not by a slot pass.
+template <int TDT, int DDT, int NT, int G>
+__device__ __forceinline__ void share_slots(const Law& L, const void* prow, const void* qrow, int V,
+                                            int sh, bool fused, double* s_slot, float* s_sref,
+                                            float* ldsf, double* ldsd, int* ldsi) {
+  if (fused) {
+    (void)row_stats<TDT, NT, G, true>(prow, V, true, L.c, sh, ldsf, ldsd, ldsi, s_slot, s_sref);
+    const Geo g = chunk_geo<TDT>(prow, 0, V);
+    rescale_slots<NT>(num_slots(row_range<G>(g, sh)), L.ref_p, s_slot, s_sref);
+  } else {
+    slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, sh, s_slot);
+  }
+}
+
 __device__ __forceinline__ bool excluded(const int* ex, int nex, int i) {
   for (int k = 0; k < nex; ++k)
     if (ex[k] == i) return true;
@@ -799,12 +859,15 @@ __device__ __forceinline__ int slot_find(const Law& L, const void* prow, const v
 // element.  A workgroup alone after a timed-out exchange goes through every
 // share in member order, with the totals rounded as the exchange rounds
 // them, so it draws the token the team would.  A team of one takes its one
-// share's total as it is.
+// share's total as it is.  fused: the law is p alone and s_slot holds this
+// workgroup's share's slot sums from the node's statistics pass (relative to
+// that pass's references), so no slot pass is needed.
 template <int TDT, int DDT, int NT, int G>
 __device__ __forceinline__ DrawOut team_draw(const Law& L, const void* prow, const void* qrow, int V,
-                                             Team& tm, const int* ex, int nex, double u,
-                                             double* s_slot, double* s_woff, int* s_sel,
-                                             double* s_th, float* s_x, int* s_solo) {
+                                             Team& tm, const int* ex, int nex, double u, bool fused,
+                                             double* s_slot, float* s_sref, double* s_woff,
+                                             int* s_sel, double* s_th, float* s_x, int* s_solo,
+                                             float* ldsf, double* ldsd, int* ldsi) {
   DrawOut out{-1, false, false};
   const int tid = threadIdx.x;
   SlotScan sc;
@@ -812,15 +875,22 @@ __device__ __forceinline__ DrawOut team_draw(const Law& L, const void* prow, con
   double total, before = 0.0;
   int owner = 0;
   bool past = false;
+  const Geo geo = chunk_geo<TDT>(prow, 0, V);
   if constexpr (G == 1) {
-    slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, -1, s_slot);
+    if (fused)
+      rescale_slots<NT>(num_slots(row_range<G>(geo, -1)), L.ref_p, s_slot, s_sref);
+    else
+      slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, -1, s_slot);
     sc = slot_scan<TDT, DDT, NT, G>(L, prow, qrow, V, -1, ex, nex, s_slot, s_woff);
     sc_share = -1;
     total = sc.total;
   } else {
     bool have = false;  // s_x holds every share's total
-    if (!tm.solo) {
-      slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, s_slot);
+    if (!tm.solo) {  // never alone so far: s_slot holds this member's share if fused
+      if (fused)
+        rescale_slots<NT>(num_slots(row_range<G>(geo, tm.gi)), L.ref_p, s_slot, s_sref);
+      else
+        slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, s_slot);
       sc = slot_scan<TDT, DDT, NT, G>(L, prow, qrow, V, tm.gi, ex, nex, s_slot, s_woff);
       sc_share = tm.gi;
       float mine[kXWords] = {};
@@ -830,7 +900,7 @@ __device__ __forceinline__ DrawOut team_draw(const Law& L, const void* prow, con
     }
     if (!have) {  // alone: every share in member order
       for (int m = 0; m < G; ++m) {
-        slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, m, s_slot);
+        share_slots<TDT, DDT, NT, G>(L, prow, qrow, V, m, fused, s_slot, s_sref, ldsf, ldsd, ldsi);
         sc = slot_scan<TDT, DDT, NT, G>(L, prow, qrow, V, m, ex, nex, s_slot, s_woff);
         sc_share = m;
         if (tid == 0) split_f64(sc.total, s_x[kXWords * m], s_x[kXWords * m + 1]);
@@ -874,7 +944,7 @@ __device__ __forceinline__ DrawOut team_draw(const Law& L, const void* prow, con
   const int mine_share = G == 1 ? -1 : (tm.solo ? owner : tm.gi);
   if (G > 1 && owner != mine_share) return out;  // another member draws
   if (G > 1 && sc_share != owner) {  // alone: the owner's slot sums again
-    slot_pass<TDT, DDT, NT, G>(L, prow, qrow, V, owner, s_slot);
+    share_slots<TDT, DDT, NT, G>(L, prow, qrow, V, owner, fused, s_slot, s_sref, ldsf, ldsd, ldsi);
     sc = slot_scan<TDT, DDT, NT, G>(L, prow, qrow, V, owner, ex, nex, s_slot, s_woff);
   }
   bool rounding = false;
@@ -932,6 +1002,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   __shared__ int ldsi[W];
   __shared__ double s_woff[W];
   __shared__ double s_slot[kMaxVocab / (256 * G) + 4];  // draw slots of a share: 64 vectors each
+  __shared__ float s_sref[kMaxVocab / (256 * G) + 4];   // their references, from a statistics pass
   __shared__ int s_sel;
   __shared__ double s_th;
   __shared__ float s_x[kXWords * G];
@@ -981,17 +1052,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       bool has_kids = false;
       for (int ch = v + 1; ch < n && !has_kids; ++ch) has_kids = s_par[ch] == v;
       const bool need_q = HAS_DRAFT && sampling && !probs && has_kids;
+      // a sampling node without children draws from p alone: its statistics
+      // pass keeps the draw's slot sums too, which saves the draw a pass
+      const bool fuse = sampling && !has_kids;
       // the row statistics: the team's shares folded in member order; a
       // workgroup alone after a timed-out exchange computes every share itself
       // and folds the same words, so it gets the same bits
       RowStats ps, qs{0.f, 0.f, 1.0, 0};
       if constexpr (G == 1) {
-        ps = solo_stats(row_stats<TDT, NT, G>(prow, V, sampling, c, -1, ldsf, ldsd, ldsi), sampling);
+        ps = solo_stats(fuse ? row_stats<TDT, NT, G, true>(prow, V, true, c, -1, ldsf, ldsd, ldsi,
+                                                          s_slot, s_sref)
+                             : row_stats<TDT, NT, G>(prow, V, sampling, c, -1, ldsf, ldsd, ldsi),
+                        sampling);
         if (need_q) qs = row_stats<DDT, NT, G>(qrow, V, true, c, -1, ldsf, ldsd, ldsi);
       } else {
         bool have = false;
         for (int m = tm.solo ? 0 : tm.gi; !have; ++m) {  // own share; alone: 0 .. G-1
-          const RowStats a = row_stats<TDT, NT, G>(prow, V, sampling, c, m, ldsf, ldsd, ldsi);
+          const RowStats a =
+              fuse ? row_stats<TDT, NT, G, true>(prow, V, true, c, m, ldsf, ldsd, ldsi, s_slot, s_sref)
+                   : row_stats<TDT, NT, G>(prow, V, sampling, c, m, ldsf, ldsd, ldsi);
           RowStats bq{0.f, 0.f, 1.0, 0};
           if (need_q) bq = row_stats<DDT, NT, G>(qrow, V, true, c, m, ldsf, ldsd, ldsi);
           float mine[kXWords] = {};
@@ -1105,13 +1184,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
           L.kap_hi = (float)kap;
           L.kap_lo = (float)(kap - (double)L.kap_hi);
         }
-        DrawOut d = team_draw<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, nex, u_rec, s_slot,
-                                               s_woff, &s_sel, &s_th, s_x, &s_solo);
+        DrawOut d = team_draw<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, nex, u_rec, fuse, s_slot,
+                                               s_sref, s_woff, &s_sel, &s_th, s_x, &s_solo, ldsf,
+                                               ldsd, ldsi);
         if (d.empty) {  // no mass left: draw from p itself
           fl |= SV_DEVERR_ZERO_RESIDUAL;
           L.pair = false;
-          d = team_draw<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, 0, u_rec, s_slot, s_woff,
-                                         &s_sel, &s_th, s_x, &s_solo);
+          d = team_draw<TDT, DDT, NT, G>(L, prow, qrow, V, tm, s_ex, 0, u_rec, false, s_slot, s_sref,
+                                         s_woff, &s_sel, &s_th, s_x, &s_solo, ldsf, ldsd, ldsi);
         }
         y = d.token;
         drew = d.token >= 0;
