@@ -40,6 +40,10 @@ int tree_team_words();
 // these dtypes, or 0 if that cannot be known.
 int tree_team_capacity(int device, int target_dtype, int draft_dtype, bool has_draft, int g);
 
+// Teams a launch for a batch of B runs: B rounded up to whole groups of
+// eight (one team per XCD in each group; the extra teams have no request).
+inline int tree_team_slots(int B) { return (B + 7) / 8 * 8; }
+
 // Members per request for a batch of B, given the capacities of teams of 4
 // and 8 (cap[0], cap[1]); 1 is one 1024-thread workgroup per request.
 int tree_team_pick(int B, const int cap[2]);

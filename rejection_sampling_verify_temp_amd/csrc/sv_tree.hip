@@ -790,7 +790,9 @@ __device__ __forceinline__ int slot_find(const Law& L, const void* prow, const v
     if (tid == 0) *s_th = __builtin_inf();
     __syncthreads();
   }
-  const int sel = *s_sel;
+  // no slot with mass (sums that no longer agree with the share's total):
+  // the head slot, whose loads stay within the row whatever it holds
+  const int sel = *s_sel < 0 ? 0 : *s_sel;
   const double th = *s_th;
   if (w == 0) {
     float r[KV];
@@ -979,6 +981,24 @@ __device__ __forceinline__ Odds child_odds(float lp, float lq, float c, float pr
   return o;
 }
 
+// The children of v among nodes [base, base + 64) below n, as a mask (bit
+// l: node base + l), by one LDS read per lane and a ballot; the same in
+// every wavefront.  A node is v's child iff it comes after v and names v as
+// its parent, so a node whose parent is not an earlier node is nobody's.
+__device__ __forceinline__ uint64_t kids_in(const int* s_par, int v, int base, int n) {
+  const int j = base + (int)(threadIdx.x & 63);
+  return __ballot(j > v && j < n && s_par[j] == v);
+}
+
+// The first child of v at or after node `from` (below n), or -1.
+__device__ __forceinline__ int first_kid(const int* s_par, int v, int from, int n) {
+  for (int base = from; base < n; base += 64) {
+    const uint64_t k = kids_in(s_par, v, base, n);
+    if (k != 0) return base + (int)__builtin_ctzll(k);
+  }
+  return -1;
+}
+
 struct Uniforms {
   double acc, rec;
 };
@@ -1013,9 +1033,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   Team tm;
   tm.xdat = p.xdat;
   tm.xdone = p.xdone;
-  // team t = workgroups [G t, G t + G): consecutive ids, so on different XCDs
-  tm.gi = G == 1 ? 0 : (int)(blockIdx.x % G);
-  tm.t = G == 1 ? (int)blockIdx.x : (int)(blockIdx.x / G);
+  // a team's members on one XCD: workgroup i runs on XCD i % 8 under the
+  // round-robin dispatch, and the grid is a whole number of 8 G workgroups
+  // (team t's members are workgroups 8 (G (t / 8) + gi) + t % 8).  On one
+  // XCD, members start together: the XCDs start a launch's workgroups up to
+  // ~3 us apart, which a team spread over them waits out at its first
+  // exchange.  The exchanges stay agent-scope, so placement only moves time.
+  if constexpr (G == 1) {
+    tm.gi = 0;
+    tm.t = (int)blockIdx.x;
+  } else {
+    const int x = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+    tm.gi = j % G;
+    tm.t = (j / G) * 8 + x;
+  }
   tm.k = 0;
   tm.solo = false;
   tm.spin = p.spin_ticks;
@@ -1049,8 +1080,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       const void* qrow = HAS_DRAFT ? row_ptr(p.draft, DDT, (size_t)b * N + v, V) : nullptr;
       // q's statistics serve only the child tests: a node without children
       // draws from p alone
-      bool has_kids = false;
-      for (int ch = v + 1; ch < n && !has_kids; ++ch) has_kids = s_par[ch] == v;
+      const int kid0 = first_kid(s_par, v, v + 1, n);
+      const bool has_kids = kid0 >= 0;
       const bool need_q = HAS_DRAFT && sampling && !probs && has_kids;
       // a sampling node without children draws from p alone: its statistics
       // pass keeps the draw's slot sums too, which saves the draw a pass
@@ -1093,8 +1124,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       // the children of v, in index order
       double ck = 0.0, Zk = 1.0;  // law after k rejections (probabilistic)
       int nex = 0, nrej = 0, next = -1;
-      for (int ch = v + 1; ch < n; ++ch) {
-        if (s_par[ch] != v) continue;
+      for (int ch = kid0; ch >= 0;) {
         const int x = s_tok[ch];
         const bool valid = x >= 0 && x < V;
         if (!valid) fl |= SV_DEVERR_BAD_DRAFT_ID;
@@ -1105,8 +1135,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
           double ratio = 0.0, px = 0.0;
           if (valid) {
             const float lq = HAS_DRAFT ? Elt<DDT>::at(qrow, x) : 0.f;
-            const Odds o = child_odds(Elt<TDT>::at(prow, x), lq, c, ps.ref, ps.z, qs.ref, qs.z, ck,
-                                      Zk, !HAS_DRAFT ? 0 : (probs ? 2 : 1),
+            const Odds o = child_odds(Elt<TDT>::at(prow, x), lq, c, ps.ref, ps.z, qs.ref,
+                                      qs.z, ck, Zk, !HAS_DRAFT ? 0 : (probs ? 2 : 1),
                                       !HAS_DRAFT && excluded(s_ex, nex, x));
             px = o.px;
             ratio = o.ratio;
@@ -1121,6 +1151,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
           break;
         }
         ++nrej;
+        const int after = first_kid(s_par, v, ch + 1, n);  // the next sibling
         if (sampling && !HAS_DRAFT) {
           if (valid && !excluded(s_ex, nex, x)) {
             __syncthreads();
@@ -1130,9 +1161,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
           }
         } else if (sampling) {  // the law left by this rejection: needs Z_{k+1}
           ck += Zk;
-          bool more = false;
-          for (int c2 = ch + 1; c2 < n && !more; ++c2) more = s_par[c2] == v;
-          if (more) {
+          if (after >= 0) {
             Law L{true, c, ps.ref, qs.ref, 0.f, 0.f, probs};
             const double kap = ck * ps.z / (probs ? 1.0 : qs.z);
             L.kap_hi = (float)kap;
@@ -1164,6 +1193,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             Zk = zs / ps.z;
           }
         }
+        ch = after;
       }
       if (next >= 0) {
         if (tid == 0) s_path[nacc] = s_tok[next];
@@ -1280,23 +1310,26 @@ int tree_team_capacity(int device, int tdt, int ddt, bool has_draft, int g) {
 
 int tree_team_pick(int B, const int cap[2]) {
   if (SV_TREE_FORCE_TEAM == 1) return 1;
+  const int slots = tree_team_slots(B);
   if (SV_TREE_FORCE_TEAM == 4 || SV_TREE_FORCE_TEAM == 8) {
     const int c = cap[SV_TREE_FORCE_TEAM == 8 ? 1 : 0];
-    return c > 0 && B <= c ? SV_TREE_FORCE_TEAM : 1;
+    return c > 0 && slots <= c ? SV_TREE_FORCE_TEAM : 1;
   }
   // measured on MI355X (B = 32 .. 512 trees of 16 nodes, V = 152064 bf16):
   // eight members per request while their teams fit the device at once
   // (B <= 128 on 256 compute units), four while theirs do (B <= 256), one
   // workgroup beyond (where four-member teams that walk two requests each
   // only tie it)
-  if (cap[1] > 0 && B <= cap[1]) return 8;
-  if (cap[0] > 0 && B <= cap[0]) return 4;
+  if (cap[1] > 0 && slots <= cap[1]) return 8;
+  if (cap[0] > 0 && slots <= cap[0]) return 4;
   return 1;
 }
 
 hipError_t launch_tree(const TreeParams& p, int tdt, int ddt, int g, hipStream_t s) {
   const bool d = p.draft != nullptr;
-  const int teams = p.B;  // a team per request (the pick keeps B within the teams' slots)
+  // a team per request, in whole groups of eight teams (one per XCD); the
+  // pick keeps the padded count within the teams' slots
+  const int teams = g > 1 ? tree_team_slots(p.B) : p.B;
 #define SV_TREE_LAUNCH(T, D) \
   return d ? launch_one<T, D, true>(p, g, teams, s) : launch_one<T, D, false>(p, g, teams, s);
   if (tdt == SV_F32 && ddt == SV_F32) {
