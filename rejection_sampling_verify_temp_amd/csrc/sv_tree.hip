@@ -9,7 +9,7 @@
 // A team of G workgroups walks one request's tree and streams only the rows
 // of the nodes it visits.  Each workgroup of the team takes a fixed share of
 // every row (G contiguous runs of 64-vector pieces), so a row pass runs on G
-// compute units at once:
+// compute units at once, all on one XCD:
 //   - at node v, one pass over target row v (and draft row v) gives each
 //     share's max and normalizer (or its lowest argmax for greedy requests);
 //     the team exchanges the shares and every workgroup folds them in the same
@@ -20,9 +20,10 @@
 //     sibling test needs Z_k: one more pass over the row pair and one more
 //     exchange;
 //   - where the walk stops, the emitted token is drawn by inverse CDF: each
-//     workgroup sums the law per slot of 64 vectors of its share, the team
-//     exchanges the share totals, and the workgroup whose share holds u * S
-//     scans its slots and re-reads one slot to find the element.
+//     workgroup sums the law per slot of 64 vectors of its share (at a node
+//     without children, whose law is p, its statistics pass already did), the
+//     team exchanges the share totals, and the workgroup whose share holds
+//     u * S scans its slots and re-reads one slot to find the element.
 // An exchange writes each value beside the exchange's tag in one agent-scope
 // atomic store, and spins until every member's words carry the tag.  A team
 // is launched only when all teams fit the device at once, so on an idle
