@@ -223,24 +223,29 @@ __device__ __forceinline__ void team_done(Team& tm) {
 // Row statistics
 // ---------------------------------------------------------------------------
 
-// Statistics of this workgroup's share of one row.  Sampling rows take each
-// round in two phases per wavefront: the wavefront's max of the round first,
-// which fixes one exponent reference for its 64 lanes, then the sums of
-// exp2(l c + ref) with no per-element max test.  A later round that raises a
-// wavefront's max rescales its sums once.  No round needs a workgroup
-// barrier, so the wavefronts drift apart and one's loads overlap another's
-// arithmetic; the wavefronts' sums meet once, at the share's reference.
-// Greedy rows keep the max and its lowest index (INT32_MAX: none).
+// One wavefront's part of a sampling row's statistics over this
+// workgroup's share: the wavefront's max Mw (the same in its 64 lanes; its
+// reference is ref_of(Mw, c)) and this thread's sum of exp2(l c +
+// ref_of(Mw, c)).  Each round goes in two phases per wavefront: the
+// wavefront's max of the round first, which fixes one exponent reference for
+// its 64 lanes, then the sums of exp2(l c + ref) with no per-element max
+// test.  A later round that raises a wavefront's max rescales its sums once.
+// No round needs a workgroup barrier, so the wavefronts drift apart and one's
+// loads overlap another's arithmetic.
 //
-// SLOTS (sampling rows, at a node whose draw is from p alone): the same pass
-// also leaves the draw's slot sums of the share in s_slot, each relative to
-// the reference its wavefront held when it summed the slot, which goes to
-// s_sref (rescale_slots moves them to the row's reference).  The slot of 64
-// vectors is one wavefront's share of one unroll step, as in slot_pass.
-template <int DT, int NT, int G, bool SLOTS = false>
-__device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampling, float c,
-                                              int gi, float* ldsf, double* ldsd, int* ldsi,
-                                              double* s_slot = nullptr, float* s_sref = nullptr) {
+// SLOTS (at a node whose draw is from p alone): the same pass also leaves the
+// draw's slot sums of the share in s_slot, each relative to the reference
+// its wavefront held when it summed the slot, which goes to s_sref
+// (rescale_slots moves them to the row's reference).  The slot of 64 vectors
+// is one wavefront's share of one unroll step, as in slot_pass.
+struct WavePart {
+  float Mw;
+  double S;
+};
+
+template <int DT, int NT, int G, bool SLOTS>
+__device__ __forceinline__ WavePart wave_pass(const void* row, int V, float c, int gi,
+                                              double* s_slot, float* s_sref) {
   using E = Elt<DT>;
   constexpr int U = kRowVecs;
   const int tid = pass_tid();
@@ -251,44 +256,6 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
   const bool has_h = rg.head && tid < g.v0, has_t = rg.tail && g.t0 + tid < V;
   const float hx = has_h ? E::at(row, tid) : kNegInf;
   const float tx = has_t ? E::at(row, g.t0 + tid) : kNegInf;
-  RowStats st;
-  if (!sampling) {
-    AmAcc a{kNegInf, INT32_MAX};
-    if (has_h) {
-      const float x[1] = {hx};
-      const int ix[1] = {tid};
-      am_tile(a, x, ix);
-    }
-    for (int b0 = 0; b0 < rg.nv; b0 += U * NT) {
-      u32x4 d[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (b0 + u * NT + tid < rg.nv) d[u] = vec_load<NT>(vb, b0, u, tid);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int vi = b0 + u * NT + tid;
-        if (vi < rg.nv) {
-          float x[E::kVec];
-          int ix[E::kVec];
-          E::unpack(d[u], x);
-#pragma unroll
-          for (int k = 0; k < E::kVec; ++k) ix[k] = g.v0 + (rg.vb + vi) * E::kVec + k;
-          am_tile(a, x, ix);
-        }
-      }
-    }
-    if (has_t) {
-      const float x[1] = {tx};
-      const int ix[1] = {g.t0 + tid};
-      am_tile(a, x, ix);
-    }
-    block_argmax<NT>(a.M, a.I, ldsf, ldsi);
-    st.m = a.M;
-    st.arg = a.I;
-    st.ref = 0.f;
-    st.z = 0.0;
-    return st;
-  }
   float Mw = kNegInf, Rw = 0.f;  // the wavefront's max and reference so far
   double S = 0.0;                // this thread's sum, relative to Rw
   for (int b0 = 0; b0 == 0 || b0 < rg.nv; b0 += U * NT) {
@@ -359,14 +326,114 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
     }
     S += (double)sr;
   }
-  const float M = block_max<NT>(Mw, ldsf);
+  return WavePart{Mw, S};
+}
+
+// Statistics of this workgroup's share of one row.  Sampling rows: the
+// wavefront parts of wave_pass meet once, at the share's reference.  Greedy
+// rows keep the max and its lowest index (INT32_MAX: none).
+template <int DT, int NT, int G, bool SLOTS = false>
+__device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampling, float c,
+                                              int gi, float* ldsf, double* ldsd, int* ldsi,
+                                              double* s_slot = nullptr, float* s_sref = nullptr) {
+  using E = Elt<DT>;
+  constexpr int U = kRowVecs;
+  const int tid = pass_tid();
+  const Geo g = chunk_geo<DT>(row, 0, V);
+  const Rng rg = row_range<G>(g, gi);
+  const VecBuf vb = vec_buf(row, g, rg, E::kBytes);
+  // the head's scalar elements in the first workgroup, the tail's in the last
+  const bool has_h = rg.head && tid < g.v0, has_t = rg.tail && g.t0 + tid < V;
+  const float hx = has_h ? E::at(row, tid) : kNegInf;
+  const float tx = has_t ? E::at(row, g.t0 + tid) : kNegInf;
+  RowStats st;
+  if (!sampling) {
+    AmAcc a{kNegInf, INT32_MAX};
+    if (has_h) {
+      const float x[1] = {hx};
+      const int ix[1] = {tid};
+      am_tile(a, x, ix);
+    }
+    for (int b0 = 0; b0 < rg.nv; b0 += U * NT) {
+      u32x4 d[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (b0 + u * NT + tid < rg.nv) d[u] = vec_load<NT>(vb, b0, u, tid);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int vi = b0 + u * NT + tid;
+        if (vi < rg.nv) {
+          float x[E::kVec];
+          int ix[E::kVec];
+          E::unpack(d[u], x);
+#pragma unroll
+          for (int k = 0; k < E::kVec; ++k) ix[k] = g.v0 + (rg.vb + vi) * E::kVec + k;
+          am_tile(a, x, ix);
+        }
+      }
+    }
+    if (has_t) {
+      const float x[1] = {tx};
+      const int ix[1] = {g.t0 + tid};
+      am_tile(a, x, ix);
+    }
+    block_argmax<NT>(a.M, a.I, ldsf, ldsi);
+    st.m = a.M;
+    st.arg = a.I;
+    st.ref = 0.f;
+    st.z = 0.0;
+    return st;
+  }
+  const WavePart wp = wave_pass<DT, NT, G, SLOTS>(row, V, c, gi, s_slot, s_sref);
+  const float M = block_max<NT>(wp.Mw, ldsf);
   const float R = ref_of(M, c);
-  const double f = Mw == kNegInf ? 0.0 : (Mw == M ? 1.0 : exp2_diff(R, Rw));
+  const double f =
+      wp.Mw == kNegInf ? 0.0 : (wp.Mw == M ? 1.0 : exp2_diff(R, ref_of(wp.Mw, c)));
   st.m = M;
   st.ref = R;
-  st.z = block_sum<NT>(S * f, ldsd);
+  st.z = block_sum<NT>(wp.S * f, ldsd);
   st.arg = 0;
   return st;
+}
+
+// The statistics of a workgroup's wavefront parts, folded (every thread
+// reads the W parts from LDS, in wavefront order).
+template <int W>
+__device__ __forceinline__ RowStats fold_waves(const float* wm, const double* ws, float c) {
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < W; ++k) M = fmaxf(M, wm[k]);
+  const float R = ref_of(M, c);
+  double z = 0.0;
+#pragma unroll
+  for (int k = 0; k < W; ++k)
+    z += wm[k] == kNegInf ? 0.0 : (wm[k] == M ? ws[k] : ws[k] * exp2_diff(R, ref_of(wm[k], c)));
+  return RowStats{M, R, z, 0};
+}
+
+// Target and draft statistics of this workgroup's shares of a row pair
+// (sampling): both passes first, then one LDS exchange of the wavefront
+// parts for the two folds, so the draft row's loads follow the target's
+// arithmetic with no block reduction in between.
+template <int TDT, int DDT, int NT, int G>
+__device__ __forceinline__ void pair_stats(const void* prow, const void* qrow, int V, float c,
+                                           int gi, float* s_wm, double* s_ws, RowStats& ps,
+                                           RowStats& qs) {
+  constexpr int W = NT / 64;
+  const WavePart a = wave_pass<TDT, NT, G, false>(prow, V, c, gi, nullptr, nullptr);
+  const WavePart d = wave_pass<DDT, NT, G, false>(qrow, V, c, gi, nullptr, nullptr);
+  const double sa = wave_sum(a.S), sd = wave_sum(d.S);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    s_wm[w] = a.Mw;
+    s_wm[W + w] = d.Mw;
+    s_ws[w] = sa;
+    s_ws[W + w] = sd;
+  }
+  __syncthreads();
+  ps = fold_waves<W>(s_wm, s_ws, c);
+  qs = fold_waves<W>(s_wm + W, s_ws + W, c);
+  __syncthreads();  // s_wm and s_ws are free again
 }
 
 // A share's statistics as the words a member sends: target max, its sum
@@ -1022,6 +1089,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   __shared__ double ldsd[W];
   __shared__ int ldsi[W];
   __shared__ double s_woff[W];
+  __shared__ float s_wm[2 * W];  // wavefront parts of a row pair's statistics
+  __shared__ double s_ws[2 * W];
   __shared__ double s_slot[kMaxVocab / (256 * G) + 4];  // draw slots of a share: 64 vectors each
   __shared__ float s_sref[kMaxVocab / (256 * G) + 4];   // their references, from a statistics pass
   __shared__ int s_sel;
@@ -1091,7 +1160,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       // workgroup alone after a timed-out exchange computes every share itself
       // and folds the same words, so it gets the same bits
       RowStats ps, qs{0.f, 0.f, 1.0, 0};
-      if constexpr (G == 1) {
+      if constexpr (G == 1) {  // pair_stats measured slower at 1024 threads
         ps = solo_stats(fuse ? row_stats<TDT, NT, G, true>(prow, V, true, c, -1, ldsf, ldsd, ldsi,
                                                           s_slot, s_sref)
                              : row_stats<TDT, NT, G>(prow, V, sampling, c, -1, ldsf, ldsd, ldsi),
@@ -1100,11 +1169,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       } else {
         bool have = false;
         for (int m = tm.solo ? 0 : tm.gi; !have; ++m) {  // own share; alone: 0 .. G-1
-          const RowStats a =
-              fuse ? row_stats<TDT, NT, G, true>(prow, V, true, c, m, ldsf, ldsd, ldsi, s_slot, s_sref)
-                   : row_stats<TDT, NT, G>(prow, V, sampling, c, m, ldsf, ldsd, ldsi);
-          RowStats bq{0.f, 0.f, 1.0, 0};
-          if (need_q) bq = row_stats<DDT, NT, G>(qrow, V, true, c, m, ldsf, ldsd, ldsi);
+          RowStats a, bq{0.f, 0.f, 1.0, 0};
+          if (need_q)
+            pair_stats<TDT, DDT, NT, G>(prow, qrow, V, c, m, s_wm, s_ws, a, bq);
+          else
+            a = fuse ? row_stats<TDT, NT, G, true>(prow, V, true, c, m, ldsf, ldsd, ldsi, s_slot,
+                                                   s_sref)
+                     : row_stats<TDT, NT, G>(prow, V, sampling, c, m, ldsf, ldsd, ldsi);
           float mine[kXWords] = {};
           stat_words(a, bq, sampling, mine);
           if (!tm.solo) {
