@@ -301,11 +301,12 @@ int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K,
  *                  deepest accepted node (0 = root).
  *
  * A team of workgroups walks each request's tree and reads only the rows of
- * the nodes it visits: while the teams fit the device at once, eight (or
- * four) workgroups on different compute units each take a share of every row
- * and exchange their partial statistics through device memory; beyond that
- * one workgroup walks each request (spec_verify_tree_team_size).  Calls on
- * one handle share its exchange buffers and must not overlap.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
+ * the nodes it visits: eight (or four) workgroups on different compute units
+ * of one XCD each take a share of every row and exchange their partial
+ * statistics through device memory.  Eight while a team per request fits
+ * the device at once; beyond that, teams of four that walk several requests
+ * each (spec_verify_tree_team_size, spec_verify_set_tree_team_size).  Calls
+ * on one handle share its exchange buffers and must not overlap.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
  * B < 0, N outside [1, SPEC_TREE_MAX_NODES]), SV_ERR_CAPACITY (B >
  * max_batch) or SV_ERR_HIP. */
 int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N,
@@ -387,10 +388,24 @@ int32_t spec_verify_chunk_elems(spec_verify_t h);
 
 /* Workgroups that walk each request's tree in spec_verify_run_tree for a
  * batch of B (has_draft != 0: with draft rows): 8 or 4 for a team walk, 1
- * for one workgroup per request; 0 for a null handle or B < 1.  The handle
- * picks the team by B against the teams its device holds at once (measured
- * crossovers, stated where the pick is made).  Host-only. */
+ * for one 1024-thread workgroup per request; 0 for a null handle or B < 1.
+ * Unless set by spec_verify_set_tree_team_size, the handle picks it by B
+ * against the teams its device holds at once (measured crossovers, stated
+ * where the pick is made): 8 while a team per request fits, else 4, whose
+ * teams then walk several requests each; 1 only if the device's team
+ * capacity is unknown.  Host-only. */
 int32_t spec_verify_tree_team_size(spec_verify_t h, int32_t B, int32_t has_draft);
+
+/* Sets the workgroups per request of later spec_verify_run_tree calls on the
+ * handle: 0 restores the handle's pick, 1 is one 1024-thread workgroup per
+ * request, 4 or 8 a team of that size (whose teams walk several requests
+ * each when they outnumber the teams that fit).  Team sizes fold a row's
+ * sums in different orders, so outputs can differ only where a draw or an
+ * acceptance test falls within rounding of a boundary.  Host-only; for runs
+ * enqueued after it.  Returns SV_ERR_INVALID_ARG for a
+ * null handle or another value, SV_ERR_UNSUPPORTED if fewer than eight
+ * teams of that size fit the device. */
+int spec_verify_set_tree_team_size(spec_verify_t h, int32_t members);
 
 /* Bound, in microseconds, on how long a team member of spec_verify_run_tree
  * waits for its partners at an exchange (default 20000).  A member that

@@ -15,5 +15,5 @@ from .binding import (SpecVerify, SpecVerifyError, load_library, sv_config,  # n
                       spec_ngram_propose, ngram_propose, spec_verify_run_typical,
                       spec_verify_run_tree, spec_verify_set_request_base,
                       spec_verify_run_noalloc, spec_verify_tree_team_size,
-                      spec_verify_set_tree_wait_us,
+                      spec_verify_set_tree_wait_us, spec_verify_set_tree_team_size,
                       header_functions)

@@ -92,6 +92,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.spec_verify_tree_team_size.restype = i32
     lib.spec_verify_set_tree_wait_us.argtypes = [P, i32]
     lib.spec_verify_set_tree_wait_us.restype = ctypes.c_int
+    lib.spec_verify_set_tree_team_size.argtypes = [P, i32]
+    lib.spec_verify_set_tree_team_size.restype = ctypes.c_int
     lib.spec_verify_destroy.argtypes = [P]
     lib.spec_verify_destroy.restype = ctypes.c_int
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
@@ -229,6 +231,12 @@ def spec_verify_set_tree_wait_us(h, microseconds: int) -> None:
     rc = load_library().spec_verify_set_tree_wait_us(h, int(microseconds))
     if rc != SV_OK:
         raise SpecVerifyError("spec_verify_set_tree_wait_us", rc)
+
+
+def spec_verify_set_tree_team_size(h, members: int) -> None:
+    rc = load_library().spec_verify_set_tree_team_size(h, int(members))
+    if rc != SV_OK:
+        raise SpecVerifyError("spec_verify_set_tree_team_size", rc)
 
 
 def spec_verify_get_device_errors(h, clear: bool = False) -> int:
@@ -445,6 +453,10 @@ class SpecVerify:
     def tree_team_size(self, B, has_draft=True):
         """Workgroups per request that run_tree uses for a batch of B."""
         return spec_verify_tree_team_size(self.handle, B, has_draft)
+
+    def set_tree_team_size(self, members):
+        """Workgroups per request for later run_tree calls (0: the handle's pick)."""
+        spec_verify_set_tree_team_size(self.handle, members)
 
     def set_request_base(self, base):
         """Global index of request 0 for later runs (a shard of a batch)."""

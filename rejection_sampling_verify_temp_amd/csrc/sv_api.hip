@@ -139,7 +139,8 @@ struct spec_verify_s {
   int tree_cap[2][2] = {{0, 0}, {0, 0}};
   uint64_t* tree_xdat = nullptr;
   uint32_t* tree_xdone = nullptr;
-  uint64_t tree_wait_ticks = 2000000;  // 20 ms of the 100 MHz real-time clock
+  uint64_t tree_wait_ticks = 2000000;
+  int tree_force = 0;  // members per request set by the caller (0: the pick)  // 20 ms of the 100 MHz real-time clock
   // timing: per run, one start/stop pair per kernel
   bool timing = false;
   hipEvent_t ev[kTimingSlots][kEventsPerRun] = {};
@@ -407,8 +408,11 @@ int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N, const void* targ
   DeviceGuard g(c.device);
   if (!g.ok) return SV_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int team = sv::tree_team_pick(B, h->tree_cap[draft_logits != nullptr]);
-  if (sv::launch_tree(tp, c.target_dtype, c.draft_dtype, team, s) != hipSuccess) return SV_ERR_HIP;
+  const int* cap = h->tree_cap[draft_logits != nullptr];
+  const int team = h->tree_force ? h->tree_force : sv::tree_team_pick(B, cap);
+  const int teams = sv::tree_team_count(B, team, cap);
+  if (sv::launch_tree(tp, c.target_dtype, c.draft_dtype, team, teams, s) != hipSuccess)
+    return SV_ERR_HIP;
   h->last_stream = s;
   h->has_run = true;
   return SV_OK;
@@ -506,9 +510,20 @@ int spec_verify_set_tree_wait_us(spec_verify_t h, int32_t microseconds) {
   return SV_OK;
 }
 
+int spec_verify_set_tree_team_size(spec_verify_t h, int32_t members) {
+  if (h == nullptr || (members != 0 && members != 1 && members != 4 && members != 8))
+    return SV_ERR_INVALID_ARG;
+  if (members == 4 || members == 8) {  // a group of eight teams must fit, with or without drafts
+    const int k = members == 8 ? 1 : 0;
+    if (h->tree_cap[0][k] < 8 || h->tree_cap[1][k] < 8) return SV_ERR_UNSUPPORTED;
+  }
+  h->tree_force = members;
+  return SV_OK;
+}
+
 int32_t spec_verify_tree_team_size(spec_verify_t h, int32_t B, int32_t has_draft) {
   if (h == nullptr || B < 1) return 0;
-  return sv::tree_team_pick(B, h->tree_cap[has_draft != 0]);
+  return h->tree_force ? h->tree_force : sv::tree_team_pick(B, h->tree_cap[has_draft != 0]);
 }
 
 int spec_verify_destroy(spec_verify_t h) {

@@ -45,11 +45,19 @@ int tree_team_capacity(int device, int target_dtype, int draft_dtype, bool has_d
 inline int tree_team_slots(int B) { return (B + 7) / 8 * 8; }
 
 // Members per request for a batch of B, given the capacities of teams of 4
-// and 8 (cap[0], cap[1]); 1 is one 1024-thread workgroup per request.
+// and 8 (cap[0], cap[1]): eight while a team per request fits the device,
+// else four (each team then walks several requests in turn); 1, one
+// 1024-thread workgroup per request, only where no team capacity is known.
 int tree_team_pick(int B, const int cap[2]);
 
-// Enqueues the walk with g members per request (from tree_team_pick).
-hipError_t launch_tree(const TreeParams& p, int target_dtype, int draft_dtype, int g,
+// Teams a launch with g members per request runs for a batch of B: one per
+// request in whole groups of eight, at most as many whole groups as fit
+// (team t then walks requests t, t + teams, ...); B for g = 1.
+int tree_team_count(int B, int g, const int cap[2]);
+
+// Enqueues the walk with g members per request and `teams` teams (from
+// tree_team_pick and tree_team_count).
+hipError_t launch_tree(const TreeParams& p, int target_dtype, int draft_dtype, int g, int teams,
                        hipStream_t stream);
 
 }  // namespace sv

@@ -29,8 +29,10 @@
 // is launched only when all teams fit the device at once, so on an idle
 // device every member runs; the wait is still bounded, and a member that
 // times out finishes the walk alone over whole rows, with the same results.
-// At large batches (more teams than the device holds) a single 1024-thread
-// workgroup walks each request and the exchanges vanish.
+// At large batches (more requests than teams the device holds) each team of
+// four walks several requests in turn.  One 1024-thread workgroup per
+// request, with no exchanges, remains where the device's team capacity is
+// unknown, or on request.
 //
 // Row passes issue 160-224 KiB of 16-byte loads per 1024 threads before using
 // any (one round trip per round), through buffer resources, so the loads of a
@@ -43,10 +45,6 @@
 #include "sv_internal.h"
 #include "sv_tree.h"
 
-// Tuning knob: a team size that overrides the pick (0: none).
-#ifndef SV_TREE_FORCE_TEAM
-#define SV_TREE_FORCE_TEAM 0
-#endif
 
 namespace sv {
 namespace {
@@ -1122,7 +1120,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   tm.spin = p.spin_ticks;
   const int teams = G == 1 ? (int)gridDim.x : (int)(gridDim.x / G);
 
-  for (int b = tm.t; b < p.B; b += teams) {
+  for (int b = tm.t; b < p.B; b += teams) {  // a team walks requests t, t + teams, ...
     int n = p.nn[b];
     const bool bad_n = n < 1 || n > N;
     n = n < 1 ? 1 : (n > N ? N : n);
@@ -1381,27 +1379,26 @@ int tree_team_capacity(int device, int tdt, int ddt, bool has_draft, int g) {
 }
 
 int tree_team_pick(int B, const int cap[2]) {
-  if (SV_TREE_FORCE_TEAM == 1) return 1;
-  const int slots = tree_team_slots(B);
-  if (SV_TREE_FORCE_TEAM == 4 || SV_TREE_FORCE_TEAM == 8) {
-    const int c = cap[SV_TREE_FORCE_TEAM == 8 ? 1 : 0];
-    return c > 0 && slots <= c ? SV_TREE_FORCE_TEAM : 1;
-  }
-  // measured on MI355X (B = 32 .. 512 trees of 16 nodes, V = 152064 bf16):
-  // eight members per request while their teams fit the device at once
-  // (B <= 128 on 256 compute units), four while theirs do (B <= 256), one
-  // workgroup beyond (where four-member teams that walk two requests each
-  // only tie it)
-  if (cap[1] > 0 && slots <= cap[1]) return 8;
-  if (cap[0] > 0 && slots <= cap[0]) return 4;
+  // measured on MI355X (random trees of 16 nodes, V = 152064 bf16): eight
+  // members per request while a team per request fits the device (B <= 128
+  // on 256 compute units), four beyond, where teams of four that walk
+  // several requests each beat one 1024-thread workgroup per request (B = 320:
+  // 182 against 235 us; B = 512: 265 against 297; B = 768: 373 against 402)
+  // and teams of eight that walk several do not (B = 256: 195 against 159)
+  if (cap[1] >= 8 && tree_team_slots(B) <= cap[1]) return 8;
+  if (cap[0] >= 8) return 4;
   return 1;
 }
 
-hipError_t launch_tree(const TreeParams& p, int tdt, int ddt, int g, hipStream_t s) {
+int tree_team_count(int B, int g, const int cap[2]) {
+  if (g <= 1) return B;
+  const int fit = cap[g == 8 ? 1 : 0] / 8 * 8;
+  const int slots = tree_team_slots(B);
+  return slots < fit ? slots : fit;
+}
+
+hipError_t launch_tree(const TreeParams& p, int tdt, int ddt, int g, int teams, hipStream_t s) {
   const bool d = p.draft != nullptr;
-  // a team per request, in whole groups of eight teams (one per XCD); the
-  // pick keeps the padded count within the teams' slots
-  const int teams = g > 1 ? tree_team_slots(p.B) : p.B;
 #define SV_TREE_LAUNCH(T, D) \
   return d ? launch_one<T, D, true>(p, g, teams, s) : launch_one<T, D, false>(p, g, teams, s);
   if (tdt == SV_F32 && ddt == SV_F32) {

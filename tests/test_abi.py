@@ -82,6 +82,7 @@ def test_ngram_rejects_bad_arguments_without_device():
     assert lib.spec_verify_chunk_elems(None) == 0
     assert lib.spec_verify_tree_team_size(None, 8, 1) == 0
     assert lib.spec_verify_set_tree_wait_us(None, 10) == binding.SV_ERR_INVALID_ARG
+    assert lib.spec_verify_set_tree_team_size(None, 4) == binding.SV_ERR_INVALID_ARG
     assert lib.spec_verify_set_request_base(None, 0) == binding.SV_ERR_INVALID_ARG
     assert lib.spec_verify_destroy(None) == 0
 

@@ -29,12 +29,15 @@ def svlib():
     return m
 
 
-def check(svlib, w, seed=0, offset=0, draft_is_probs=False, expect_flags=0):
-    say(f"[gpu] tree {w.name} seed={seed} offset={offset}")
+def check(svlib, w, seed=0, offset=0, draft_is_probs=False, expect_flags=0, members=0):
+    say(f"[gpu] tree {w.name} seed={seed} offset={offset} members={members or 'picked'}")
     w = w.to("cuda")
     h = svlib.SpecVerify(w.B, 1, w.V, w.target.dtype,
                          draft_dtype=w.draft.dtype if w.draft is not None else None,
                          draft_is_probs=draft_is_probs)
+    if members:
+        h.set_tree_team_size(members)
+        assert h.tree_team_size(w.B, w.draft is not None) == members
     tokens, nacc, last = h.run_tree(w.target, w.draft, w.tokens, w.parents, w.num_nodes,
                                     w.temperatures, seed=seed, offset=offset)
     torch.cuda.synchronize()
@@ -172,34 +175,60 @@ def test_benchmark_shape(svlib):
     assert rep.accepted > 0
 
 
-# Batches whose team walks differ on MI355X (256 compute units): eight
-# workgroups per request up to B = 128, four up to B = 256, one beyond.
+# Batches and team settings whose walks differ on MI355X (256 compute
+# units).  Picked: eight workgroups per request up to B = 128, four beyond,
+# where at B = 300 each team of four walks one or two requests.  Set: teams
+# of four at B = 100, teams of eight that walk two or three requests each,
+# and one 1024-thread workgroup per request, at B = 300.
 TEAM_CASES = {
-    40: dict(dtype=torch.bfloat16, temps=(1.0, 0.6, 0.0)),
-    100: dict(temps=(0.9, 0.0)),
-    200: dict(dtype=torch.bfloat16, temps=(0.8, 0.0, 1.2)),
-    300: dict(temps=(1.0, 0.7)),
+    (40, 0): dict(dtype=torch.bfloat16, temps=(1.0, 0.6, 0.0)),
+    (100, 0): dict(temps=(0.9, 0.0)),
+    (100, 4): dict(dtype=torch.bfloat16, temps=(1.0, 0.0, 0.7)),
+    (200, 0): dict(dtype=torch.bfloat16, temps=(0.8, 0.0, 1.2)),
+    (300, 0): dict(temps=(1.0, 0.7)),
+    (300, 1): dict(temps=(1.0, 0.7)),
+    (300, 8): dict(dtype=torch.bfloat16, temps=(1.0, 0.0, 0.6)),
 }
 
 
-@pytest.mark.parametrize("B", sorted(TEAM_CASES))
-def test_team_sizes(svlib, B):
-    """Logit, one-hot and probability-draft trees at batches that run teams of
-    8 and 4 workgroups and single workgroups, against the oracle."""
+@pytest.mark.parametrize("B,members", sorted(TEAM_CASES))
+def test_team_sizes(svlib, B, members):
+    """Logit, one-hot and probability-draft trees at batches and team
+    settings that run teams of 8 and 4 workgroups (one request per team, or
+    several in turn) and single workgroups, against the oracle."""
     V = 20011  # an odd vocabulary: unaligned rows, a head and a tail in every row
     h = svlib.SpecVerify(B, 1, V, torch.float32)
-    say(f"[gpu] tree team size at B={B}: {h.tree_team_size(B)} (one-hot {h.tree_team_size(B, False)})")
+    say(f"[gpu] tree team size picked at B={B}: {h.tree_team_size(B)} "
+        f"(one-hot {h.tree_team_size(B, False)}); set: {members or 'none'}")
     h.close()
-    w = synth.make_tree(B, 12, V, seed=50 + B, corr=0.9, device="cuda", **TEAM_CASES[B])
-    check(svlib, w, seed=B, offset=1)
-    w = synth.make_tree(B, 10, V, seed=51 + B, onehot=True, temps=(1.0, 0.5), device="cuda")
-    check(svlib, w, seed=B, offset=2)
-    w = synth.make_tree(B, 8, V, seed=52 + B, temps=(1.0,), device="cuda")
+    w = synth.make_tree(B, 12, V, seed=50 + B + members, corr=0.9, device="cuda",
+                        **TEAM_CASES[(B, members)])
+    check(svlib, w, seed=B, offset=1, members=members)
+    w = synth.make_tree(B, 10, V, seed=51 + B + members, onehot=True, temps=(1.0, 0.5),
+                        device="cuda")
+    check(svlib, w, seed=B, offset=2, members=members)
+    w = synth.make_tree(B, 8, V, seed=52 + B + members, temps=(1.0,), device="cuda")
     w.draft = torch.softmax(w.draft.float(), -1)
-    check(svlib, w, seed=B, offset=3, draft_is_probs=True)
+    check(svlib, w, seed=B, offset=3, draft_is_probs=True, members=members)
 
 
-@pytest.mark.parametrize("B", [40, 100, 200])
+def test_team_size_setting(svlib):
+    """The setting's contract on the host: 0, 1, 4 and 8 are taken and
+    reported, anything else is refused, and 0 restores the pick."""
+    h = svlib.SpecVerify(64, 1, 1000, torch.float32)
+    picked = h.tree_team_size(300)
+    for m in (1, 4, 8):
+        h.set_tree_team_size(m)
+        assert h.tree_team_size(300) == m and h.tree_team_size(8, False) == m
+    for bad in (2, 3, 16, -1):
+        with pytest.raises(svlib.SpecVerifyError):
+            h.set_tree_team_size(bad)
+    h.set_tree_team_size(0)
+    assert h.tree_team_size(300) == picked == 4
+    h.close()
+
+
+@pytest.mark.parametrize("B", [40, 100, 200, 300])
 def test_team_launches_in_a_row(svlib, B):
     """One handle, the same trees launched five times with a different
     offset each and then again with the first: a team walk returns its
@@ -229,7 +258,7 @@ def test_team_launches_in_a_row(svlib, B):
     assert rep.ok(), rep.mismatches
 
 
-@pytest.mark.parametrize("B", [40, 100, 200])
+@pytest.mark.parametrize("B", [40, 100, 200, 300])
 def test_team_members_finishing_alone(svlib, B):
     """With the team wait bound at 0 the members give up on their partners at
     once, in a mix of team and solo walks that differs run to run; each then
