@@ -305,8 +305,10 @@ int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K,
  * of one XCD each take a share of every row and exchange their partial
  * statistics through device memory.  Eight while a team per request fits
  * the device at once; beyond that, teams of four that walk several requests
- * each (spec_verify_tree_team_size, spec_verify_set_tree_team_size).  Calls
- * on one handle share its exchange buffers and must not overlap.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
+ * each, a team taking the next free request whenever its walk ends
+ * (spec_verify_tree_team_size, spec_verify_set_tree_team_size).  Calls on one
+ * handle share its exchange buffers and request counter and must not
+ * overlap.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
  * B < 0, N outside [1, SPEC_TREE_MAX_NODES]), SV_ERR_CAPACITY (B >
  * max_batch) or SV_ERR_HIP. */
 int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N,

@@ -139,6 +139,7 @@ struct spec_verify_s {
   int tree_cap[2][2] = {{0, 0}, {0, 0}};
   uint64_t* tree_xdat = nullptr;
   uint32_t* tree_xdone = nullptr;
+  uint32_t* tree_next = nullptr;  // [2] request counter of teams that walk several
   uint64_t tree_wait_ticks = 2000000;
   int tree_force = 0;  // members per request set by the caller (0: the pick)  // 20 ms of the 100 MHz real-time clock
   // timing: per run, one start/stop pair per kernel
@@ -160,6 +161,7 @@ void free_all(spec_verify_s* h) {
   if (h->flags) (void)hipFree(h->flags);
   if (h->tree_xdat) (void)hipFree(h->tree_xdat);
   if (h->tree_xdone) (void)hipFree(h->tree_xdone);
+  if (h->tree_next) (void)hipFree(h->tree_next);
   for (int s = 0; s < kTimingSlots; ++s)
     for (int k = 0; k < kEventsPerRun; ++k)
       if (h->ev[s][k]) (void)hipEventDestroy(h->ev[s][k]);
@@ -277,8 +279,10 @@ int spec_verify_create(const sv_config* cfg, spec_verify_t* out) {
       const size_t bytes = members * sv::tree_team_words() * sizeof(uint64_t);
       ok = hipMalloc(&h->tree_xdat, bytes) == hipSuccess &&
            hipMalloc(&h->tree_xdone, teams * sizeof(uint32_t)) == hipSuccess &&
+           hipMalloc(&h->tree_next, 2 * sizeof(uint32_t)) == hipSuccess &&
            hipMemset(h->tree_xdat, 0, bytes) == hipSuccess &&
-           hipMemset(h->tree_xdone, 0, teams * sizeof(uint32_t)) == hipSuccess;
+           hipMemset(h->tree_xdone, 0, teams * sizeof(uint32_t)) == hipSuccess &&
+           hipMemset(h->tree_next, 0, 2 * sizeof(uint32_t)) == hipSuccess;
     }
   }
   // the zeroed words are in place before any stream can launch on them (a
@@ -404,6 +408,7 @@ int spec_verify_run_tree(spec_verify_t h, int32_t B, int32_t N, const void* targ
   tp.b_base = h->b_base;
   tp.xdat = h->tree_xdat;
   tp.xdone = h->tree_xdone;
+  tp.next_req = h->tree_next;
   tp.spin_ticks = h->tree_wait_ticks;
   DeviceGuard g(c.device);
   if (!g.ok) return SV_ERR_HIP;

@@ -31,6 +31,9 @@ struct TreeParams {
   uint64_t* xdat;   // [teams][2][team size][8]
   uint32_t* xdone;  // [teams]
   uint64_t spin_ticks;  // bound of an exchange's wait (100 MHz ticks)
+  uint32_t* next_req;   // [2]: requests handed out past the first round, and
+                        // teams done (teams that walk several requests); 0
+                        // between launches
 };
 
 // 64-bit exchange words per team member.
@@ -52,7 +55,8 @@ int tree_team_pick(int B, const int cap[2]);
 
 // Teams a launch with g members per request runs for a batch of B: one per
 // request in whole groups of eight, at most as many whole groups as fit
-// (team t then walks requests t, t + teams, ...); B for g = 1.
+// (team t then walks request t first and takes the next free request from
+// a launch-wide counter at the end of each walk); B for g = 1.
 int tree_team_count(int B, int g, const int cap[2]);
 
 // Enqueues the walk with g members per request and `teams` teams (from

@@ -30,7 +30,8 @@
 // device every member runs; the wait is still bounded, and a member that
 // times out finishes the walk alone over whole rows, with the same results.
 // At large batches (more requests than teams the device holds) each team of
-// four walks several requests in turn.  One 1024-thread workgroup per
+// four walks several requests in turn, taking the next free request from a
+// launch-wide counter whenever a walk ends.  One 1024-thread workgroup per
 // request, with no exchanges, remains where the device's team capacity is
 // unknown, or on request.
 //
@@ -202,7 +203,7 @@ __device__ __forceinline__ void exchange(Team& tm, const float (&mine)[kXWords],
 // words and its counter to 0.  Every member arrives only after its last
 // exchange's reads, so no member still reads what is cleared.
 template <int G>
-__device__ __forceinline__ void team_done(Team& tm) {
+__device__ __forceinline__ void team_done(Team& tm, uint32_t* next_req, int teams) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t before =
@@ -213,8 +214,46 @@ __device__ __forceinline__ void team_done(Team& tm) {
         __hip_atomic_store(w + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the words are clear before the count
       __hip_atomic_store(tm.xdone + tm.t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // teams that walked several requests: the last team returns the
+      // request counter to 0 (every member has taken its last request)
+      if (next_req != nullptr &&
+          __hip_atomic_fetch_add(next_req + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (uint32_t)teams - 1) {
+        __hip_atomic_store(next_req, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __hip_atomic_store(next_req + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
+}
+
+// The team's next request once a walk is done (teams that walk several
+// requests): member 0 takes the next free one from the launch's counter and
+// sends it in an exchange, so the team walks it together.  A workgroup
+// alone (a wait timed out) takes its own.  Every request is taken once, and
+// the workgroup that took it walks it, in the team or alone.
+template <int G>
+__device__ __forceinline__ int next_request(Team& tm, uint32_t* next_req, int teams, float* s_x,
+                                            int* s_solo, int* s_next) {
+  const bool take = tm.solo || tm.gi == 0;
+  __syncthreads();
+  if (take && threadIdx.x == 0)
+    *s_next = teams + (int)__hip_atomic_fetch_add(next_req, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int nb = take ? *s_next : 0;
+  if (tm.solo) return nb;
+  float mine[kXWords] = {};
+  mine[0] = __builtin_bit_cast(float, nb);
+  exchange<G>(tm, mine, 1, s_x, s_solo);
+  if (!tm.solo) return __builtin_bit_cast(int, s_x[0]);  // member 0's
+  if (tm.gi == 0) return nb;  // alone now, with the request it took
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_next = teams + (int)__hip_atomic_fetch_add(next_req, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return *s_next;
 }
 
 // ---------------------------------------------------------------------------
@@ -1096,6 +1135,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   __shared__ float s_x[kXWords * G];
   __shared__ int s_solo;
   __shared__ int s_path[kMaxNodes];  // the accepted path's tokens
+  __shared__ int s_next;
   const int tid = threadIdx.x;
   const int N = p.N, V = p.V;
   Team tm;
@@ -1120,7 +1160,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   tm.spin = p.spin_ticks;
   const int teams = G == 1 ? (int)gridDim.x : (int)(gridDim.x / G);
 
-  for (int b = tm.t; b < p.B; b += teams) {  // a team walks requests t, t + teams, ...
+  // the first request by team index; where teams walk several requests,
+  // each further one is the next free request, taken at the end of a walk
+  for (int b = tm.t; b < p.B;) {
     int n = p.nn[b];
     const bool bad_n = n < 1 || n > N;
     n = n < 1 ? 1 : (n > N ? N : n);
@@ -1319,9 +1361,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
       }
       if (fl) atomicOr(p.flags, fl);
     }
-    if constexpr (G == 1) break;  // one request per workgroup
+    if constexpr (G == 1) {
+      break;  // one request per workgroup
+    } else {
+      if (teams >= p.B) break;  // one request per team
+      b = next_request<G>(tm, p.next_req, teams, s_x, &s_solo, &s_next);
+    }
   }
-  if constexpr (G > 1) team_done<G>(tm);
+  if constexpr (G > 1) team_done<G>(tm, teams < p.B ? p.next_req : nullptr, teams);
 }
 
 template <int TDT, int DDT, bool HD, int G>
@@ -1383,8 +1430,9 @@ int tree_team_pick(int B, const int cap[2]) {
   // members per request while a team per request fits the device (B <= 128
   // on 256 compute units), four beyond, where teams of four that walk
   // several requests each beat one 1024-thread workgroup per request (B = 320:
-  // 182 against 235 us; B = 512: 265 against 297; B = 768: 373 against 402)
-  // and teams of eight that walk several do not (B = 256: 195 against 159)
+  // 165 against 235 us; B = 512: 226 against 297; B = 768: 302 against 402)
+  // and teams of eight that walk several do not (B = 256: 165 against 158;
+  // B = 512: 267 against 226)
   if (cap[1] >= 8 && tree_team_slots(B) <= cap[1]) return 8;
   if (cap[0] >= 8) return 4;
   return 1;
