@@ -128,21 +128,25 @@ def test_realistic_size(svlib):
     assert rep.accepted > 0
 
 
-def test_max_nodes(svlib):
-    """Trees of 256 nodes, the most the entry point takes."""
+@pytest.mark.parametrize("members", [0, 1])
+def test_max_nodes(svlib, members):
+    """Trees of 256 nodes, the most the entry point takes, in teams (the
+    pick) and in one 1024-thread workgroup per request."""
     w = synth.make_tree(8, 256, 600, temps=(1.0, 0.0, 0.7), seed=12, corr=0.97)
-    check(svlib, w, seed=3, offset=2)
+    check(svlib, w, seed=3, offset=2, members=members)
     w = synth.make_tree(8, 256, 600, temps=(1.0, 0.8), seed=13, onehot=True, shape="wide")
-    check(svlib, w, seed=4, offset=1)
+    check(svlib, w, seed=4, offset=1, members=members)
 
 
-def test_max_vocab(svlib):
-    """V = 983040: fp32 rows fill the draw's slot table (3840 slots of 64
-    vectors plus head and tail); bf16 rows take two rounds per pass."""
+@pytest.mark.parametrize("members", [0, 1])
+def test_max_vocab(svlib, members):
+    """V = 983040.  In one 1024-thread workgroup per request, fp32 rows fill
+    the draw's slot table (3840 slots of 64 vectors plus head and tail) and
+    bf16 rows take two rounds per pass; teams (the pick) split both."""
     for dtype, seed in ((torch.float32, 14), (torch.bfloat16, 15)):
         w = synth.make_tree(4, 6, 983040, dtype=dtype, temps=(1.0, 0.0, 0.6, 1.0), seed=seed,
                             corr=0.97, device="cuda")
-        check(svlib, w, seed=seed, offset=3)
+        check(svlib, w, seed=seed, offset=3, members=members)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
