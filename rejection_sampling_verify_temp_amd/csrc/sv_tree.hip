@@ -1116,9 +1116,11 @@ __device__ __forceinline__ Uniforms tree_uniforms(uint64_t seed, uint64_t offset
   return u;
 }
 
-// NT threads per workgroup, G workgroups per team.  Team t walks requests
-// t, t + teams, ...; member 0 writes the accepted path, the count, the last
-// node and the padding, the member that draws writes the emitted token.
+// NT threads per workgroup, G workgroups per team.  Team t walks request t,
+// then (where teams are fewer than requests) the next free request from the
+// launch's counter after each walk; member 0 writes the accepted path, the
+// count, the last node and the padding, the member that draws writes the
+// emitted token.
 template <int TDT, int DDT, bool HAS_DRAFT, int NT, int G>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_tree(
     const TreeParams p) {
