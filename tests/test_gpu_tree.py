@@ -216,6 +216,29 @@ def test_team_sizes(svlib, B, members):
     check(svlib, w, seed=B, offset=3, draft_is_probs=True, members=members)
 
 
+def test_many_requests_per_team(svlib):
+    """B = 1000 requests on 256 teams of four: each team takes about four
+    requests from the launch's counter, in an order that depends on timing.
+    The outputs match the oracle, and five launches in a row on one handle
+    repeat the first bit for bit (the counter is back at 0 after every
+    launch)."""
+    B, V = 1000, 2053
+    w = synth.make_tree(B, 10, V, dtype=torch.bfloat16, seed=80, corr=0.9,
+                        temps=(1.0, 0.0, 0.7), device="cuda")
+    check(svlib, w, seed=9, offset=1)
+    h = svlib.SpecVerify(B, 1, V, torch.bfloat16, draft_dtype=torch.bfloat16)
+    assert h.tree_team_size(B) == 4
+    outs = [[x.cpu() for x in h.run_tree(w.target, w.draft, w.tokens, w.parents, w.num_nodes,
+                                         w.temperatures, seed=9, offset=off)]
+            for off in (1, 2, 3, 4, 1)]
+    torch.cuda.synchronize()
+    flags = h.device_errors(clear=True)
+    h.close()
+    assert flags & ~8 == 0, flags
+    for a, b in zip(outs[0], outs[-1]):
+        assert torch.equal(a, b)
+
+
 def test_team_size_setting(svlib):
     """The setting's contract on the host: 0, 1, 4 and 8 are taken and
     reported, anything else is refused, and 0 restores the pick."""
