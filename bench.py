@@ -394,6 +394,23 @@ def bench_tree(args):
     }
     if not args.no_cpu_baseline:
         import oracle
+        from oracle.parity import compare_tree
+        # parity of the last timed step (whole batch, its inputs, seed and
+        # offset) against the oracle, untimed
+        last = args.warmup + args.steps - 1
+        t0 = time.perf_counter()
+        hl = copies[last % len(copies)].host_arrays()
+        ref = oracle.verify_tree(hl["target"], hl["draft"], hl["tokens"], hl["parents"],
+                                 hl["num_nodes"], hl["temperatures"], seed=0, offset=last)
+        tok, nacc, lastn = (x.cpu().numpy() for x in outs[-1])
+        rep = compare_tree(hl["tokens"], hl["parents"], hl["num_nodes"], c["V"], ref, tok, nacc,
+                           lastn)
+        out["parity"] = {"status": "ok" if rep.ok() else "FAIL", "checked": rep.requests,
+                         "flagged": rep.flagged, "flagged_differing": rep.flagged_mismatch,
+                         "mismatches": len(rep.mismatches),
+                         "first_mismatches": [str(m) for m in rep.mismatches[:3]],
+                         "what": f"the whole batch of the last timed step (Philox offset {last}) "
+                                 f"against the fp64 C oracle, {time.perf_counter() - t0:.1f} s"}
         hs = w.host_arrays()
         t0, n_req = time.perf_counter(), 0
         while time.perf_counter() - t0 < 12.0 and n_req < c["B"]:
