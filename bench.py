@@ -303,7 +303,19 @@ def bench_ngram(args):
                      "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None},
     }
     if not args.no_cpu_baseline:
+        import numpy as np
         import oracle
+        # parity of the last timed step: the oracle's proposals on its
+        # contexts, bit for bit (integer work)
+        last = args.warmup + args.steps - 1
+        lc, ll = (t.cpu().numpy() for t in copies[last % len(copies)])
+        rd, rn = oracle.ngram_propose(lc, ll, **kw)
+        gd, gn = drafts.cpu().numpy(), num.cpu().numpy()
+        bad = int(np.sum((gn != rn) | np.any(gd != rd, axis=1)))
+        out["parity"] = {"status": "ok" if bad == 0 else "FAIL", "checked": int(c["B"]),
+                         "mismatches": bad,
+                         "what": "the last timed step's drafts and counts against the C oracle, "
+                                 "bit for bit"}
         ctx, lens = (t.cpu().numpy() for t in copies[0])
         t0, reps = time.perf_counter(), 0
         while time.perf_counter() - t0 < 10.0:
