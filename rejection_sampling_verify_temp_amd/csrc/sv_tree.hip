@@ -1140,6 +1140,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   __shared__ int s_solo;
   __shared__ int s_path[kMaxNodes];  // the accepted path's tokens
   __shared__ int s_next;
+  // the request's uniforms at each node index (24-bit values, exact in a
+  // float): acceptance of child j + 1 from s_ua[j], the draw at node j from
+  // s_ur[j]
+  __shared__ float s_ua[kMaxNodes], s_ur[kMaxNodes];
   const int tid = threadIdx.x;
   const int N = p.N, V = p.V;
   Team tm;
@@ -1183,6 +1187,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
 
     const float T = p.temps[b];
     const bool sampling = is_sampling(T);
+    // one Philox block per node index, the request's indices in parallel
+    // (the walk's tests and draw read them after the first pass's barriers)
+    if (sampling)
+      for (int j = tid; j < n; j += NT) {
+        const Uniforms un = tree_uniforms(p.seed, p.offset, p.b_base + b, j);
+        s_ua[j] = (float)un.acc;
+        s_ur[j] = (float)un.rec;
+      }
     const float c = sampling ? temp_scale(T) : 0.f;
     const bool probs = p.draft_is_probs != 0;
     int v = 0, nacc = 0, y = 0;
@@ -1257,8 +1269,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             px = o.px;
             ratio = o.ratio;
           }
-          const Uniforms un = tree_uniforms(p.seed, p.offset, p.b_base + b, ch - 1);
-          accept = un.acc < ratio;
+          accept = (double)s_ua[ch - 1] < ratio;
           // one-hot: a rejected token leaves the law, which is renormalized
           if (!accept && !HAS_DRAFT && valid && !excluded(s_ex, nex, x)) Zk -= px;
         }
@@ -1322,7 +1333,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         y = ps.arg;
         drew = tm.gi == 0 || tm.solo;
       } else {
-        const double u_rec = tree_uniforms(p.seed, p.offset, p.b_base + b, v).rec;
+        const double u_rec = (double)s_ur[v];
         Law L{false, c, ps.ref, qs.ref, 0.f, 0.f, probs};
         if (HAS_DRAFT && nrej > 0) {
           L.pair = true;
