@@ -1070,17 +1070,27 @@ struct Odds {
   double ratio;  // acceptance ratio of x under the current law
 };
 
+// 2^x for x <= 0 (an exponent against a row's reference): the integer part
+// to the exponent, v_exp_f32 for the fraction, so as accurate as the
+// exponentials the row sums hold (a few 1e-8 relative); 0 far below.
+__device__ __forceinline__ double exp2_nonpos(double x) {
+  if (!(x > -1070.0)) return 0.0;
+  const double n = floor(x);
+  return ldexp((double)fast_exp2((float)(x - n)), (int)n);
+}
+
 // mode 0: one-hot drafts (ratio p(x) / Zk, 0 for a removed token); 1: draft
 // logits; 2: draft probabilities.
 __device__ __forceinline__ Odds child_odds(float lp, float lq, float c, float pref, double pz,
                                         float qref, double qz, double ck, double Zk, int mode,
                                         bool removed) {
   Odds o;
-  o.px = exp2((double)lp * (double)c + (double)pref) / pz;
+  o.px = exp2_nonpos((double)lp * (double)c + (double)pref) / pz;
   if (mode == 0) {
     o.ratio = removed ? 0.0 : o.px / Zk;
   } else {
-    const double qx = mode == 2 ? (double)lq : exp2((double)lq * (double)c + (double)qref) / qz;
+    const double qx =
+        mode == 2 ? (double)lq : exp2_nonpos((double)lq * (double)c + (double)qref) / qz;
     double num = o.px - ck * qx;
     num = num > 0.0 ? num / Zk : 0.0;
     o.ratio = qx > 0.0 ? num / qx : (num > 0.0 ? __builtin_inf() : 0.0);
