@@ -368,6 +368,31 @@ __device__ __forceinline__ WavePart wave_pass(const void* row, int V, float c, i
   return WavePart{Mw, S};
 }
 
+// A sum of parts, each with its own max m_k (its sum z_k relative to
+// ref_of(m_k, c)), moved to the reference R of the overall max M: lane k
+// holds part k (mine) and scales it, and the wavefront adds the lanes in
+// one fixed DPP order.  Every wavefront, every member of a team and a member
+// alone therefore get the same bits, and the parts' scale factors take one
+// latency instead of one each in turn.
+__device__ __forceinline__ double lane_fold(bool mine, float mk, double zk, float M, float R,
+                                            float c) {
+  const double t =
+      (!mine || mk == kNegInf) ? 0.0 : (mk == M ? zk : zk * exp2_diff(R, ref_of(mk, c)));
+  return wave_sum(t);
+}
+
+// The statistics of a workgroup's wavefront parts, folded (every wavefront
+// reads the W parts from LDS).
+template <int W>
+__device__ __forceinline__ RowStats fold_waves(const float* wm, const double* ws, float c) {
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < W; ++k) M = fmaxf(M, wm[k]);
+  const float R = ref_of(M, c);
+  const int lane = threadIdx.x & 63, k = lane < W ? lane : 0;
+  return RowStats{M, R, lane_fold(lane < W, wm[k], ws[k], M, R, c), 0};
+}
+
 // Statistics of this workgroup's share of one row.  Sampling rows: the
 // wavefront parts of wave_pass meet once, at the share's reference.  Greedy
 // rows keep the max and its lowest index (INT32_MAX: none).
@@ -435,21 +460,6 @@ __device__ __forceinline__ RowStats row_stats(const void* row, int V, bool sampl
   return st;
 }
 
-// The statistics of a workgroup's wavefront parts, folded (every thread
-// reads the W parts from LDS, in wavefront order).
-template <int W>
-__device__ __forceinline__ RowStats fold_waves(const float* wm, const double* ws, float c) {
-  float M = kNegInf;
-#pragma unroll
-  for (int k = 0; k < W; ++k) M = fmaxf(M, wm[k]);
-  const float R = ref_of(M, c);
-  double z = 0.0;
-#pragma unroll
-  for (int k = 0; k < W; ++k)
-    z += wm[k] == kNegInf ? 0.0 : (wm[k] == M ? ws[k] : ws[k] * exp2_diff(R, ref_of(wm[k], c)));
-  return RowStats{M, R, z, 0};
-}
-
 // Target and draft statistics of this workgroup's shares of a row pair
 // (sampling): both passes first, then one LDS exchange of the wavefront
 // parts for the two folds, so the draft row's loads follow the target's
@@ -493,7 +503,8 @@ __device__ __forceinline__ void stat_words(const RowStats& a, const RowStats& bq
 // The row's statistics from the team's shares: member g's words at
 // x[kXWords g + o ...] are its max and then its sum (sampling: relative to its
 // own reference, split in two floats) or lowest argmax (greedy).  The shares
-// are folded in member order, so every member gets the same bits.
+// are folded in one fixed order (lane_fold), so every member gets the same
+// bits.
 template <int G>
 __device__ __forceinline__ RowStats fold_stats(const float* x, int o, bool sampling, float c) {
   RowStats st;
@@ -513,27 +524,20 @@ __device__ __forceinline__ RowStats fold_stats(const float* x, int o, bool sampl
     return st;
   }
   const float R = ref_of(M, c);
-  double z = 0.0;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float mg = x[kXWords * g + o];
-    const double zg = join_f64(x[kXWords * g + o + 1], x[kXWords * g + o + 2]);
-    z += mg == kNegInf ? 0.0 : (mg == M ? zg : zg * exp2_diff(R, ref_of(mg, c)));
-  }
+  const int lane = threadIdx.x & 63, g = lane < G ? lane : 0;
   st.ref = R;
-  st.z = z;
+  st.z = lane_fold(lane < G, x[kXWords * g + o],
+                   join_f64(x[kXWords * g + o + 1], x[kXWords * g + o + 2]), M, R, c);
   st.arg = 0;
   return st;
 }
 
-// The sum of a value that every member sent split at x[kXWords g], in
-// member order.
+// The sum of a value that every member sent split at x[kXWords g], one
+// member per lane, added in one fixed order.
 template <int G>
 __device__ __forceinline__ double fold_sum(const float* x) {
-  double z = 0.0;
-#pragma unroll
-  for (int g = 0; g < G; ++g) z += join_f64(x[kXWords * g], x[kXWords * g + 1]);
-  return z;
+  const int lane = threadIdx.x & 63, g = lane < G ? lane : 0;
+  return wave_sum(lane < G ? join_f64(x[kXWords * g], x[kXWords * g + 1]) : 0.0);
 }
 
 // A workgroup's own share as the whole row's statistics (a team of one).
