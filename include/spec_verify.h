@@ -303,9 +303,10 @@ int spec_draft_sample(spec_verify_t h, int32_t B, int32_t K,
  * A team of workgroups walks each request's tree and reads only the rows of
  * the nodes it visits: eight (or four) workgroups on different compute units
  * of one XCD each take a share of every row and exchange their partial
- * statistics through device memory.  Eight while a team per request fits
- * the device at once; beyond that, teams of four that walk several requests
- * each, a team taking the next free request whenever its walk ends
+ * statistics through device memory.  Eight while the teams of eight that fit
+ * the device at once walk at most two requests each; beyond that, teams of
+ * four that walk several requests each.  A team that walks several takes the
+ * next free request whenever its walk ends
  * (spec_verify_tree_team_size, spec_verify_set_tree_team_size).  Calls on one
  * handle share its exchange buffers and request counter and must not
  * overlap.  Returns SV_ERR_INVALID_ARG (null or misaligned pointer,
@@ -393,9 +394,9 @@ int32_t spec_verify_chunk_elems(spec_verify_t h);
  * for one 1024-thread workgroup per request; 0 for a null handle or B < 1.
  * Unless set by spec_verify_set_tree_team_size, the handle picks it by B
  * against the teams its device holds at once (measured crossovers, stated
- * where the pick is made): 8 while a team per request fits, else 4, whose
- * teams then walk several requests each; 1 only if the device's team
- * capacity is unknown.  Host-only. */
+ * where the pick is made): 8 while the teams of eight that fit walk at most
+ * two requests each, else 4, whose teams then walk several requests each; 1
+ * only if the device's team capacity is unknown.  Host-only. */
 int32_t spec_verify_tree_team_size(spec_verify_t h, int32_t B, int32_t has_draft);
 
 /* Sets the workgroups per request of later spec_verify_run_tree calls on the

@@ -48,9 +48,10 @@ int tree_team_capacity(int device, int target_dtype, int draft_dtype, bool has_d
 inline int tree_team_slots(int B) { return (B + 7) / 8 * 8; }
 
 // Members per request for a batch of B, given the capacities of teams of 4
-// and 8 (cap[0], cap[1]): eight while a team per request fits the device,
-// else four (each team then walks several requests in turn); 1, one
-// 1024-thread workgroup per request, only where no team capacity is known.
+// and 8 (cap[0], cap[1]): eight while the teams of eight that fit the device
+// walk at most two requests each, else four (each team then walks several
+// requests in turn); 1, one 1024-thread workgroup per request, only where no
+// team capacity is known.
 int tree_team_pick(int B, const int cap[2]);
 
 // Teams a launch with g members per request runs for a batch of B: one per

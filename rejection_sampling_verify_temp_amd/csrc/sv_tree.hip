@@ -1456,13 +1456,15 @@ int tree_team_capacity(int device, int tdt, int ddt, bool has_draft, int g) {
 
 int tree_team_pick(int B, const int cap[2]) {
   // measured on MI355X (random trees of 16 nodes, V = 152064 bf16): eight
-  // members per request while a team per request fits the device (B <= 128
-  // on 256 compute units), four beyond, where teams of four that walk
-  // several requests each beat one 1024-thread workgroup per request (B = 320:
+  // members per request while the teams of eight that fit the device walk
+  // at most two requests each (B <= 256 on 256 compute units: B = 160 103
+  // against 116 us with teams of four, B = 192 113 against 118, B = 224 125
+  // against 131, B = 256 144 against 146), four beyond (B = 288: 143 against
+  // 152; B = 512: 208 against 234), where teams of four that walk several
+  // requests each also beat one 1024-thread workgroup per request (B = 320:
   // 165 against 235 us; B = 512: 226 against 297; B = 768: 302 against 402)
-  // and teams of eight that walk several do not (B = 256: 165 against 158;
-  // B = 512: 267 against 226)
-  if (cap[1] >= 8 && tree_team_slots(B) <= cap[1]) return 8;
+  const int fit8 = cap[1] / 8 * 8;
+  if (fit8 >= 8 && tree_team_slots(B) <= 2 * fit8) return 8;
   if (cap[0] >= 8) return 4;
   return 1;
 }

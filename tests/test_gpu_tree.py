@@ -180,10 +180,11 @@ def test_benchmark_shape(svlib):
 
 
 # Batches and team settings whose walks differ on MI355X (256 compute
-# units).  Picked: eight workgroups per request up to B = 128, four beyond,
-# where at B = 300 each team of four walks one or two requests.  Set: teams
-# of four at B = 100, teams of eight that walk two or three requests each,
-# and one 1024-thread workgroup per request, at B = 300.
+# units).  Picked: eight workgroups per request up to B = 256 (at B = 200 each
+# of the 128 teams of eight walks one or two requests), four beyond, where at
+# B = 300 each team of four walks one or two requests.  Set: teams of four at
+# B = 100, teams of eight that walk two or three requests each, and one
+# 1024-thread workgroup per request, at B = 300.
 TEAM_CASES = {
     (40, 0): dict(dtype=torch.bfloat16, temps=(1.0, 0.6, 0.0)),
     (100, 0): dict(temps=(0.9, 0.0)),
