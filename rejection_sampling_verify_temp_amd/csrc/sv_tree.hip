@@ -381,16 +381,24 @@ __device__ __forceinline__ double lane_fold(bool mine, float mk, double zk, floa
   return wave_sum(t);
 }
 
-// The statistics of a workgroup's wavefront parts, folded (every wavefront
-// reads the W parts from LDS).
-template <int W>
-__device__ __forceinline__ RowStats fold_waves(const float* wm, const double* ws, float c) {
-  float M = kNegInf;
-#pragma unroll
-  for (int k = 0; k < W; ++k) M = fmaxf(M, wm[k]);
-  const float R = ref_of(M, c);
-  const int lane = threadIdx.x & 63, k = lane < W ? lane : 0;
-  return RowStats{M, R, lane_fold(lane < W, wm[k], ws[k], M, R, c), 0};
+// Two such sums at once: lanes 0..31 hold the first sum's parts and lanes
+// 32..63 the second's, and the DPP steps of wave_sum stop where each half of
+// the wavefront has its own total (lanes 31 and 63).
+__device__ __forceinline__ void lane_fold2(bool mine, float mk, double zk, float M, float R,
+                                           float c, double& z0, double& z1) {
+  double t = (!mine || mk == kNegInf) ? 0.0 : (mk == M ? zk : zk * exp2_diff(R, ref_of(mk, c)));
+  t = dpp_sum_step<kDppShr1, 0xf>(t);
+  t = dpp_sum_step<kDppShr2, 0xf>(t);
+  t = dpp_sum_step<kDppShr4, 0xf>(t);
+  t = dpp_sum_step<kDppShr8, 0xf>(t);
+  t = dpp_sum_step<kDppBcast15, 0xa>(t);
+  const uint64_t b = (uint64_t)__double_as_longlong(t);
+  const uint32_t lo0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 31);
+  const uint32_t hi0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 31);
+  const uint32_t lo1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  z0 = __longlong_as_double((long long)(((uint64_t)hi0 << 32) | lo0));
+  z1 = __longlong_as_double((long long)(((uint64_t)hi1 << 32) | lo1));
 }
 
 // Statistics of this workgroup's share of one row.  Sampling rows: the
@@ -480,8 +488,22 @@ __device__ __forceinline__ void pair_stats(const void* prow, const void* qrow, i
     s_ws[W + w] = sd;
   }
   __syncthreads();
-  ps = fold_waves<W>(s_wm, s_ws, c);
-  qs = fold_waves<W>(s_wm + W, s_ws + W, c);
+  // both rows' folds in one pass: the target's parts in the wavefront's lower
+  // half, the draft's in the upper
+  static_assert(W <= 32, "one half-wavefront per row");
+  float Mp = kNegInf, Mq = kNegInf;
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    Mp = fmaxf(Mp, s_wm[k]);
+    Mq = fmaxf(Mq, s_wm[W + k]);
+  }
+  const float Rp = ref_of(Mp, c), Rq = ref_of(Mq, c);
+  const bool upper = lane >= 32;
+  const int k = lane & 31, at = (upper ? W : 0) + (k < W ? k : 0);
+  double zp, zq;
+  lane_fold2(k < W, s_wm[at], s_ws[at], upper ? Mq : Mp, upper ? Rq : Rp, c, zp, zq);
+  ps = RowStats{Mp, Rp, zp, 0};
+  qs = RowStats{Mq, Rq, zq, 0};
   __syncthreads();  // s_wm and s_ws are free again
 }
 
@@ -530,6 +552,29 @@ __device__ __forceinline__ RowStats fold_stats(const float* x, int o, bool sampl
                    join_f64(x[kXWords * g + o + 1], x[kXWords * g + o + 2]), M, R, c);
   st.arg = 0;
   return st;
+}
+
+// The target's and the draft's statistics from the team's shares of a row
+// pair (sampling; member g's words at x[kXWords g ...]: target max and sum,
+// draft max and sum), both folded in one pass as in pair_stats.
+template <int G>
+__device__ __forceinline__ void fold_pair(const float* x, float c, RowStats& ps, RowStats& qs) {
+  static_assert(G <= 32, "one half-wavefront per row");
+  float Mp = kNegInf, Mq = kNegInf;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    Mp = fmaxf(Mp, x[kXWords * g]);
+    Mq = fmaxf(Mq, x[kXWords * g + 3]);
+  }
+  const float Rp = ref_of(Mp, c), Rq = ref_of(Mq, c);
+  const int lane = threadIdx.x & 63, k = lane & 31;
+  const bool upper = lane >= 32;
+  const int at = kXWords * (k < G ? k : 0) + (upper ? 3 : 0);
+  double zp, zq;
+  lane_fold2(k < G, x[at], join_f64(x[at + 1], x[at + 2]), upper ? Mq : Mp, upper ? Rq : Rp, c,
+             zp, zq);
+  ps = RowStats{Mp, Rp, zp, 0};
+  qs = RowStats{Mq, Rq, zq, 0};
 }
 
 // The sum of a value that every member sent split at x[kXWords g], one
@@ -1259,8 +1304,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             have = m == G - 1;
           }
         }
-        ps = fold_stats<G>(s_x, 0, sampling, c);
-        if (need_q) qs = fold_stats<G>(s_x, 3, true, c);
+        if (need_q)
+          fold_pair<G>(s_x, c, ps, qs);
+        else
+          ps = fold_stats<G>(s_x, 0, sampling, c);
       }
 
       // the children of v, in index order
