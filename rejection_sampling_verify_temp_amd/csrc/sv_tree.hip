@@ -149,7 +149,8 @@ __device__ __forceinline__ double join_f64(float hi, float lo) { return (double)
 
 // Every workgroup of the team calls this with its values mine[0..nw) (the
 // same in all of its threads); on return s_all[kXWords g + j] holds member
-// g's value j, in every workgroup.  Each value travels in a 64-bit word
+// g's value j, in every workgroup.  Wavefront 0 stores and polls; the others
+// run `idle` meanwhile (work the caller needs only after the exchange).  Each value travels in a 64-bit word
 // beside the exchange's tag k + 1, written by one agent-scope atomic store,
 // so a reader that sees the tag in a word has that word's value: one round
 // trip per poll, and nothing for the writer to wait for.  Double buffering is
@@ -164,12 +165,18 @@ __device__ __forceinline__ double join_f64(float hi, float lo) { return (double)
 // words the exchange would have carried.  Alone or in the team, every member
 // therefore computes the same outputs, bit for bit, and the request's results
 // do not depend on which members finish it.
-template <int G>
+struct NoIdle {
+  __device__ void operator()() const {}
+};
+
+template <int G, typename Idle = NoIdle>
 __device__ __forceinline__ void exchange(Team& tm, const float (&mine)[kXWords], int nw,
-                                         float* s_all, int* s_solo) {
+                                         float* s_all, int* s_solo, const Idle& idle = Idle{}) {
   const int tid = threadIdx.x;
   __syncthreads();  // s_all's previous contents are read
-  if (tid < 64) {
+  if (tid >= 64) {
+    idle();  // the other wavefronts' work while wavefront 0 waits
+  } else {
     bool solo = false;
     uint64_t* slot = tm.xdat + ((size_t)tm.t * 2 + (tm.k & 1u)) * G * kXWords;
     const uint32_t tag = tm.k + 1u;
@@ -1231,6 +1238,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   // each further one is the next free request, taken at the end of a walk
   for (int b = tm.t; b < p.B;) {
     int n = p.nn[b];
+    const float T = p.temps[b];  // in the same round trip as the count
     const bool bad_n = n < 1 || n > N;
     n = n < 1 ? 1 : (n > N ? N : n);
     __syncthreads();  // the previous request's tree is no longer read
@@ -1240,11 +1248,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     }
     __syncthreads();
     uint32_t fl = bad_n ? SV_DEVERR_BAD_NUM_DRAFTS : 0u;
-    if (tid == 0 && tm.gi == 0)
-      for (int i = 1; i < n; ++i)
-        if (s_par[i] < 0 || s_par[i] >= i) fl |= SV_DEVERR_BAD_TREE;
+    if (tm.gi == 0 && tid < 64) {  // every parent an earlier node: one ballot per 64 nodes
+      bool bad = false;
+      for (int i = tid; i < n; i += 64) bad |= i > 0 && (s_par[i] < 0 || s_par[i] >= i);
+      if (__ballot(bad) != 0) fl |= SV_DEVERR_BAD_TREE;
+    }
 
-    const float T = p.temps[b];
     const bool sampling = is_sampling(T);
     // one Philox block per node index, the request's indices in parallel
     // (the walk's tests and draw read them after the first pass's barriers)
