@@ -13,7 +13,7 @@
 //   - at node v, one pass over target row v (and draft row v) gives each
 //     share's max and normalizer (or its lowest argmax for greedy requests);
 //     the team exchanges the shares and every workgroup folds them in the same
-//     order, so all hold the same row statistics;
+//     fixed order (one share per lane), so all hold the same row statistics;
 //   - the children of v are tested in index order by every workgroup alike
 //     (the same loads, the same Philox block, the same fp64 arithmetic); after
 //     k rejections the law is max(0, p - c_k q) / Z_k, and each further
@@ -29,16 +29,16 @@
 // is launched only when all teams fit the device at once, so on an idle
 // device every member runs; the wait is still bounded, and a member that
 // times out finishes the walk alone over whole rows, with the same results.
-// At large batches (more requests than teams the device holds) each team of
-// four walks several requests in turn, taking the next free request from a
+// At large batches (more requests than teams the device holds) each team
+// walks several requests in turn, taking the next free request from a
 // launch-wide counter whenever a walk ends.  One 1024-thread workgroup per
 // request, with no exchanges, remains where the device's team capacity is
 // unknown, or on request.
 //
-// Row passes issue 160-224 KiB of 16-byte loads per 1024 threads before using
-// any (one round trip per round), through buffer resources, so the loads of a
-// round cost no address registers and no branches, and no round waits at a
-// workgroup barrier.  A walk that a single compute unit runs alone is bound by
+// Row passes issue all of a round's 16-byte loads (10 vectors of a row, or 5
+// of each row of a pair, per thread) before using any (one round trip per
+// round), through buffer resources, so the loads of a round cost no address
+// registers and no branches, and no round waits at a workgroup barrier.  A walk that a single compute unit runs alone is bound by
 // that unit's arithmetic (~6 VALU slots per element) more than by memory;
 // spreading each row over a team's units is what shortens the longest walks,
 // which set the kernel's time once most requests are done.
