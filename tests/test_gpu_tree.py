@@ -120,6 +120,18 @@ def test_malformed_trees_are_flagged(svlib):
     check(svlib, w, expect_flags=16 | 1 | 2)
 
 
+def test_malformed_large_trees_are_flagged(svlib):
+    """Trees of 200 nodes, where the parent check runs over several groups
+    of 64 nodes: a parent after its node at index 70, one at index 150, and
+    a negative parent at index 2, each in a request of its own, against two
+    well-formed requests."""
+    w = synth.make_tree(5, 200, 700, temps=(1.0, 0.0, 0.7), seed=41, ragged=False)
+    w.parents[0, 70] = 120
+    w.parents[1, 150] = 150
+    w.parents[2, 2] = -1
+    check(svlib, w, seed=5, offset=2, expect_flags=16)
+
+
 def test_realistic_size(svlib):
     """64 requests, trees of 16 nodes over a 32000-token vocabulary."""
     w = synth.make_tree(64, 16, 32000, dtype=torch.bfloat16, temps=(1.0, 0.6, 0.0), seed=8,
